@@ -1,0 +1,105 @@
+"""CPU oracle for the sparse MLA prefill forward -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. It shares no code with the HIP library
+(``sparse_attention_top_amd``) and neither imports the other; the seeded input
+generator is the only module both sides use.
+
+The arithmetic lives in ``smla_oracle.c`` (plain C, double precision, one
+sequential loop per token and head); this module only compiles it with gcc and
+marshals numpy arrays through ctypes. The definition it follows, with every
+reading of the pages it takes, is in that file's header comment.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "smla_oracle.c")
+_LIB = os.path.join(_HERE, "libsmla_oracle.so")
+D = 512
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (portable x86-64 code, OpenMP)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra",
+               "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        lib.smla_oracle_forward.restype = ctypes.c_int
+        lib.smla_oracle_forward.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_double, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ]
+        lib.smla_oracle_threads.restype = ctypes.c_int
+        lib.smla_oracle_threads.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def forward(q, kv, topk, sink, scale, tokens=None, *, want_exact=True, want_bf16=True, threads=0):
+    """Evaluate the definition for the given tokens (all tokens when None).
+
+    q: uint16 bf16 bits [T, H, 512]; kv: uint16 bf16 bits [num_kv, 512];
+    topk: int32 [T, topk]; sink: float32 [H] or None; scale: float.
+    Returns a dict with ``o`` (float64 [n, H, 512], unrounded), ``o_bf16``
+    (uint16 bits [n, H, 512]), ``lse`` (float64 [n, H], natural log) and
+    ``n_valid`` (int64 [n]).
+    """
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    kv = np.ascontiguousarray(kv, dtype=np.uint16)
+    topk = np.ascontiguousarray(topk, dtype=np.int32)
+    T, H, d = q.shape
+    if d != D or kv.ndim != 2 or (kv.shape[0] > 0 and kv.shape[1] != D):
+        raise ValueError("head dim must be 512")
+    if topk.ndim != 2 or topk.shape[0] != T:
+        raise ValueError("topk must be [T, topk]")
+    num_kv = kv.shape[0]
+    if sink is not None:
+        sink = np.ascontiguousarray(sink, dtype=np.float32)
+        if sink.shape != (H,):
+            raise ValueError("sink must be [H]")
+    if tokens is None:
+        tok = None
+        n = T
+    else:
+        tok = np.ascontiguousarray(tokens, dtype=np.int64)
+        n = tok.size
+    o = np.empty((n, H, D), np.float64) if want_exact else None
+    ob = np.empty((n, H, D), np.uint16) if want_bf16 else None
+    lse = np.empty((n, H), np.float64)
+    nv = np.empty((n,), np.int64)
+    rc = _load().smla_oracle_forward(
+        _ptr(q), _ptr(kv) if num_kv > 0 else None, _ptr(topk), _ptr(sink), float(scale),
+        T, H, num_kv, topk.shape[1], _ptr(tok), n, _ptr(o), _ptr(ob), _ptr(lse), _ptr(nv), int(threads))
+    if rc != 0:
+        raise RuntimeError("oracle rejected its arguments (rc=%d)" % rc)
+    return {"o": o, "o_bf16": ob, "lse": lse, "n_valid": nv}
+
+
+def threads() -> int:
+    return int(_load().smla_oracle_threads())

@@ -1,0 +1,84 @@
+"""The seeded input generator: structure, counts and determinism (CPU only)."""
+
+import numpy as np
+import pytest
+
+from sparse_attention_top_amd import synth
+
+# Valid-slot totals: for window W, pool P and compression c the count is
+# sum_t min(t+1, W) + min((t+1)//c, P), independent of which pool rows the rng
+# picks. Written out here as numbers so that a change of recipe is caught.
+EXPECTED_VALID = {"tiny": 1400, "tp4": 9952832, "wide": 1793728, "large": 5994368}
+SMALL_VALID_BEFORE_DROPS = 251872
+
+
+def closed_form_valid(cfg):
+    t = np.arange(cfg.T)
+    return int(np.minimum(t + 1, cfg.window).sum() + np.minimum((t + 1) // cfg.compression, cfg.pool_slots).sum())
+
+
+@pytest.mark.parametrize("name", ["tiny", "small", "tp4", "wide", "large"])
+def test_valid_counts_closed_form(name):
+    cfg = synth.CONFIGS[name]
+    n = closed_form_valid(cfg)
+    if name == "small":
+        assert n == SMALL_VALID_BEFORE_DROPS
+    else:
+        assert n == EXPECTED_VALID[name]
+
+
+@pytest.mark.parametrize("name", ["tiny", "small", "wide"])
+def test_topk_structure(name):
+    cfg = synth.CONFIGS[name]
+    rng = np.random.default_rng(7)
+    idx = synth.build_topk(rng, cfg.T, cfg.topk, cfg.window, cfg.pool_slots, cfg.compression)
+    assert idx.shape == (cfg.T, cfg.topk) and idx.dtype == np.int32
+    assert synth.valid_slot_count(idx, cfg.num_kv) == closed_form_valid(cfg)
+    W, P, c, T = cfg.window, cfg.pool_slots, cfg.compression, cfg.T
+    for t in range(0, T, max(1, T // 97)):
+        row = idx[t]
+        win = row[:W]
+        exp_win = np.arange(t - W + 1, t + 1)
+        assert np.array_equal(win, np.where(exp_win >= 0, exp_win, -1))
+        assert row[W - 1] == t  # the token's own row is always in its window
+        pool = row[W:W + P]
+        pool = pool[pool >= 0]
+        assert np.all(np.diff(pool) > 0)  # sorted, no duplicates
+        j = pool - T
+        assert np.all(j >= 0) and np.all(c * (j + 1) <= t + 1)  # causally visible
+        assert pool.size == min((t + 1) // c, P)
+        assert np.all(row[W + P:] == -1)
+
+
+def test_deterministic_and_seeded():
+    a = synth.make_inputs("tiny")
+    b = synth.make_inputs("tiny")
+    assert synth.fingerprint(a) == synth.fingerprint(b)
+    other = synth.make_inputs(synth.Config("x", T=64, H=16, topk=32, window=16, pool_slots=16,
+                                           compression=4, seed=999))
+    assert synth.fingerprint(other) != synth.fingerprint(a)
+
+
+def test_small_config_drops_and_nan_rows():
+    inp = synth.make_inputs("small")
+    idx, kv, T = inp["topk"], inp["kv"], inp["T"]
+    n = synth.valid_slot_count(idx, inp["num_kv"])
+    frac = 1.0 - n / idx.size
+    assert 0.08 < frac < 0.12  # "about 10%" invalid
+    assert np.all(idx[:, inp["config"].window - 1] == np.arange(T))  # own slot never dropped
+    used = np.zeros(inp["num_kv"], bool)
+    used[idx[idx >= 0]] = True
+    nan_rows = np.all(kv == synth.BF16_NAN, axis=1)
+    assert np.array_equal(nan_rows, ~used)
+    assert inp["sink"] is None
+
+
+def test_bf16_rounding_rne():
+    x = np.array([1.0, 1.0 + 2.0**-8, 1.0 + 3 * 2.0**-8, -2.5, 0.0, np.float32(3.0e38)], np.float32)
+    b = synth.f32_to_bf16_bits(x)
+    back = synth.bf16_bits_to_f32(b)
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: even mantissa (1.0) wins;
+    # 1 + 3*2^-8 is a tie between 1 + 2^-7 and 1 + 2^-6: even (1 + 2^-6) wins.
+    assert back[0] == 1.0 and back[1] == 1.0 and back[2] == 1.0 + 2.0**-6
+    assert back[3] == -2.5 and back[4] == 0.0
+    assert np.isnan(synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(np.array([np.nan], np.float32))))[0]
