@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse MLA prefill forward on one MI355X.
+
+One step = one call of the forward over one synthetic batch (the whole path:
+top-k compaction, KV gather, both contractions, softmax, store). Inputs are
+resident in HBM before the timed region. Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wide|large|tp4|small|tiny]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+D = 512
+
+
+def algorithmic(inp: dict) -> dict:
+    """Work the operation must do (valid slots only)."""
+    T, H, k = inp["T"], inp["H"], inp["topk_n"]
+    nvalid = int(((inp["topk"] >= 0) & (inp["topk"] < inp["num_kv"])).sum())
+    flops = 4.0 * H * D * nvalid  # S = QK^T and O = PV, 2 flop per MAC each
+    gathered = 1024.0 * nvalid  # one 1 KiB row per valid slot (K == V)
+    io = T * H * 1024.0 * 2 + T * H * 4.0 + T * k * 4.0  # q + o + lse + indices
+    return {"valid_slots": nvalid, "flops": flops, "gathered_bytes": gathered, "bytes": gathered + io}
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for rel in ("sparse_attention_top_amd/csrc/sparse_mla.hip", "include/sparse_mla.h"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel: str, workload: str):
+    """HBM bytes per launch measured by rocprofv3 (FETCH_SIZE + WRITE_SIZE, scaled
+    by the copy-kernel calibration), if recorded for the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    digest = source_digest()
+    for line in open(path):
+        m = re.match(r"\|\s*%s\s*\|\s*([0-9a-f]+)\s*\|\s*([0-9.eE+]+)\s*\|" % re.escape(workload), line)
+        if m and m.group(1) == digest:
+            return float(m.group(2))
+    return None
+
+
+def time_gpu(run, steps, warmup, stream):
+    import torch
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        run()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall, float(np.mean(per_launch)), float(np.median(per_launch))
+
+
+def cpu_baseline(inp: dict, target_s: float = 10.0):
+    """The oracle, untuned, on the host cores over an evenly spaced token sample."""
+    import oracle
+
+    T = inp["T"]
+    n = max(1, min(T, 128))
+    tokens = np.linspace(0, T - 1, n).round().astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.forward(inp["q"], inp["kv"], inp["topk"], inp["sink"], inp["scale"], tokens=tokens,
+                   want_exact=False, want_bf16=True)
+    dt = time.perf_counter() - t0
+    if dt < target_s / 4 and n < T:  # grow the sample toward the target wall time
+        n = int(min(T, n * max(1.0, target_s / max(dt, 1e-3))))
+        tokens = np.linspace(0, T - 1, n).round().astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.forward(inp["q"], inp["kv"], inp["topk"], inp["sink"], inp["scale"], tokens=tokens,
+                       want_exact=False, want_bf16=True)
+        dt = time.perf_counter() - t0
+    nv = int(((inp["topk"][tokens] >= 0) & (inp["topk"][tokens] < inp["num_kv"])).sum())
+    flops = 4.0 * inp["H"] * D * nv
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": "%d of %d tokens (evenly spaced), %d valid slots, %.2f s wall" % (len(tokens), T, nv, dt),
+            "ms_per_call_extrapolated": dt * 1e3 * inp["T"] / len(tokens)}
+
+
+def measure(name: str, steps: int, warmup: int):
+    import torch
+
+    from sparse_attention_top_amd import kernel_name, sparse_mla_prefill, synth
+
+    inp = synth.make_inputs(name)
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(inp["q"].view(np.int16)).view(torch.bfloat16).to(dev)
+    kv = torch.from_numpy(inp["kv"].view(np.int16)).view(torch.bfloat16).to(dev)
+    topk = torch.from_numpy(inp["topk"]).to(dev)
+    sink = torch.from_numpy(inp["sink"]).to(dev) if inp["sink"] is not None else None
+    out = torch.empty_like(q)
+    lse = torch.empty((inp["T"], inp["H"]), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run():
+        sparse_mla_prefill(q, kv, topk, sink, inp["scale"], out=out, lse=lse)
+
+    wall, mean_ms, med_ms = time_gpu(run, steps, warmup, stream)
+    alg = algorithmic(inp)
+    return inp, alg, {"wall_s": wall, "ms_per_call": wall * 1e3 / steps, "kernel_ms_mean": mean_ms,
+                      "kernel_ms_median": med_ms, "kernel": kernel_name(inp["H"])}
+
+
+def roofline(alg, t, kernel, workload, bound):
+    if bound == "mfma":
+        achieved = alg["flops"] / (t["kernel_ms_mean"] * 1e-3) / 1e12
+        peak, unit = PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved = alg["bytes"] / (t["kernel_ms_mean"] * 1e-3) / 1e9
+        peak, unit = PEAK_HBM_GBS, "GB/s"
+    return {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+            "traffic": traffic_from_profiles(kernel, workload), "kernel": kernel}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="wide", choices=["tiny", "small", "tp4", "wide", "large"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    from sparse_attention_top_amd import synth
+
+    print("bench: workload %s, %d warmup + %d timed steps" % (args.workload, args.warmup, args.steps),
+          file=sys.stderr, flush=True)
+    inp, alg, t = measure(args.workload, args.steps, args.warmup)
+    bound = "mfma" if inp["H"] > 16 else "hbm"
+    tflops = alg["flops"] / (t["ms_per_call"] * 1e-3) / 1e12
+    gbs = alg["gathered_bytes"] / (t["ms_per_call"] * 1e-3) / 1e9
+    if bound == "mfma":
+        metric, value, unit = "sparse MLA prefill fwd TFLOPS (valid slots, H=%d)" % inp["H"], tflops, "TFLOP/s"
+    else:
+        metric, value, unit = "sparse MLA prefill fwd gathered-KV GB/s (H=%d)" % inp["H"], gbs, "GB/s"
+    cfg = inp["config"]
+    line = {
+        "metric": metric,
+        "value": value,
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": t["ms_per_call"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "topk": cfg.topk, "num_kv": cfg.num_kv,
+                   "head_dim": D, "valid_slots": alg["valid_slots"], "seed": cfg.seed,
+                   "inputs_sha256": synth.fingerprint(inp)[:16], "parallelism": "none"},
+        "tflops": tflops,
+        "gathered_gbs": gbs,
+        "kernel_ms_mean": t["kernel_ms_mean"],
+        "kernel_ms_median": t["kernel_ms_median"],
+        "roofline": roofline(alg, t, t["kernel"], cfg.name, bound),
+    }
+    print("bench: %s %.4f ms/call, %.1f TFLOP/s, %.1f GB/s gathered" % (cfg.name, t["ms_per_call"], tflops, gbs),
+          file=sys.stderr, flush=True)
+    if not args.no_secondary:
+        sec = []
+        for other in ("tp4", "large", "small"):
+            if other == args.workload:
+                continue
+            i2, a2, t2 = measure(other, max(10, args.steps // 2), args.warmup)
+            b2 = "mfma" if i2["H"] > 16 else "hbm"
+            sec.append({"workload": other, "ms_per_call": t2["ms_per_call"], "kernel_ms_mean": t2["kernel_ms_mean"],
+                        "tflops": a2["flops"] / (t2["ms_per_call"] * 1e-3) / 1e12,
+                        "gathered_gbs": a2["gathered_bytes"] / (t2["ms_per_call"] * 1e-3) / 1e9,
+                        "valid_slots": a2["valid_slots"], "roofline": roofline(a2, t2, t2["kernel"], other, b2)})
+            print("bench: %s %.4f ms/call" % (other, t2["ms_per_call"]), file=sys.stderr, flush=True)
+        line["secondary"] = sec
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle on a token sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,95 @@
+/*
+ * sparse_mla.h -- C ABI of the MI355X (gfx950) sparse MLA prefill forward.
+ *
+ * The operation is the DeepSeek-V4 sparse MLA prefill attention described on
+ * "[Triton/Gluon] [GFX950][DSV4] Sparse MLA training backward" (aiter PR #4766),
+ * section "Contract", whose forward is added by "[TRITON][GLUON] Add DSv4
+ * sparse MLA prefill Triton and unified with MLA Gluon kernel on GFX950"
+ * (aiter PR #3833):
+ *
+ *   for each token t and head h, over the valid slots s of row t of
+ *   topk_indices (valid iff 0 <= topk_indices[t,s] < num_kv):
+ *     x_s  = scale * dot(q[t,h,:], kv[topk_indices[t,s],:])        (K == V == kv)
+ *     o[t,h,:] = sum_s softmax_s * kv[topk_indices[t,s],:]
+ *   where the softmax denominator also holds exp(attn_sink[h]) (a logit with
+ *   no value row, not multiplied by scale), and
+ *     lse[t,h] = ln( sum_s exp(x_s) + exp(attn_sink[h]) )            (natural log)
+ *   A (t,h) with no valid slot gets o = 0 and lse = attn_sink[h] (or -inf
+ *   without a sink). attn_sink[h] == -inf is the same as no sink.
+ *
+ * This header is plain C: no HIP or torch types. Link against
+ * libsparse_mla.so.
+ */
+#ifndef SPARSE_MLA_H
+#define SPARSE_MLA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Head dimension of q, kv and o. Fixed: the operation's contract fixes it at 512. */
+#define SPARSE_MLA_HEAD_DIM 512
+
+/* Status codes. Every nonzero status is returned before anything is enqueued,
+ * except SMLA_ERR_LAUNCH, which reports a failed kernel launch. */
+typedef enum {
+  SMLA_OK = 0,
+  SMLA_ERR_NULL_POINTER = -1, /* a buffer with nonzero size is NULL                       */
+  SMLA_ERR_BAD_SIZE = -2,     /* T < 0, H < 1, num_kv < 0, topk < 0, or a size overflows   */
+  SMLA_ERR_MISALIGNED = -3,   /* q, kv or out not 16-byte aligned; lse, topk, sink not 4   */
+  SMLA_ERR_BAD_SCALE = -4,    /* scale is NaN or infinite                                  */
+  SMLA_ERR_NO_DEVICE = -5,    /* no usable HIP device is current                           */
+  SMLA_ERR_LAUNCH = -6        /* the kernel launch failed (hipGetLastError)                */
+} smla_status_t;
+
+/*
+ * sparse_mla_prefill -- enqueue the forward on `stream` and return.
+ *
+ * Arguments (all device pointers on the current HIP device, caller-owned):
+ *   q             bf16 [T, H, 512], contiguous, 16-byte aligned.
+ *   kv            bf16 [num_kv, 512], contiguous, 16-byte aligned. K == V: one
+ *                 gathered row serves both the score and the value. May be NULL
+ *                 when num_kv == 0.
+ *   topk_indices  int32 [T, topk], contiguous. Any value outside [0, num_kv)
+ *                 (-1 by convention) marks an invalid slot whose row is never
+ *                 read. Order within a row does not matter; a repeated valid
+ *                 index counts once per occurrence.
+ *   attn_sink     fp32 [H] or NULL (no sink).
+ *   scale         any finite float; 1/sqrt(512) by convention.
+ *   out           bf16 [T, H, 512], contiguous, 16-byte aligned; fully written.
+ *   lse           fp32 [T, H], contiguous; fully written; natural log,
+ *                 sink-inclusive.
+ *   T, H, num_kv, topk   sizes; T == 0 returns SMLA_OK without a launch.
+ *   stream        a hipStream_t, or NULL for the default stream.
+ *
+ * out and lse must not alias any input (not checked). The library allocates
+ * nothing, keeps no state between calls and never synchronises: results are
+ * ready when `stream` reaches this point. Faults during execution surface at
+ * the caller's next synchronisation, as usual for HIP. Results are
+ * bitwise-deterministic: the same inputs give the same bits on every call.
+ * Thread-safe and reentrant.
+ */
+int sparse_mla_prefill(const void* q, const void* kv, const int32_t* topk_indices, const float* attn_sink,
+                       float scale, void* out, float* lse, int64_t T, int64_t H, int64_t num_kv,
+                       int64_t topk, void* stream);
+
+/* Human-readable text for a status code (static storage; never NULL). */
+const char* sparse_mla_status_string(int status);
+
+/*
+ * Name of the kernel that sparse_mla_prefill launches for H heads (static
+ * storage, as it appears in profiler traces), or NULL when H < 1. Pure host
+ * function: no device access.
+ */
+const char* sparse_mla_kernel_name(int64_t H);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int sparse_mla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_MLA_H */

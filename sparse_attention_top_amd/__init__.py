@@ -1,0 +1,87 @@
+"""Sparse MLA prefill forward (DeepSeek-V4) for MI355X / gfx950.
+
+``sparse_mla_prefill`` marshals torch tensors to the C ABI of
+``libsparse_mla.so`` (declared in ``include/sparse_mla.h``); every step of the
+computation runs in the HIP kernels. torch provides device memory and the
+current stream only.
+"""
+
+from __future__ import annotations
+
+import math
+
+from . import _lib
+
+HEAD_DIM = 512
+DEFAULT_SCALE = 1.0 / math.sqrt(HEAD_DIM)
+
+__all__ = ["sparse_mla_prefill", "kernel_name", "HEAD_DIM", "DEFAULT_SCALE"]
+
+
+def _check(cond: bool, msg: str):
+    if not cond:
+        raise RuntimeError(msg)
+
+
+def sparse_mla_prefill(q, kv, topk_indices, attn_sink=None, scale=None, out=None, lse=None):
+    """Sparse MLA prefill forward; returns ``(out, lse)``.
+
+    q: bf16 [T, H, 512]; kv: bf16 [num_kv, 512] (K == V); topk_indices: int32
+    [T, topk] (any value outside [0, num_kv) is an invalid slot); attn_sink:
+    fp32 [H] or None; scale: float (default 1/sqrt(512)); out: optional bf16
+    [T, H, 512] buffer; lse: optional fp32 [T, H] buffer. All tensors on the
+    same GPU and contiguous. The work is enqueued on the current stream.
+    """
+    import torch
+
+    _check(q.is_cuda, "q must be a GPU tensor (got %s)" % q.device)
+    dev = q.device
+    _check(q.dtype == torch.bfloat16, "q must be bfloat16, got %s" % q.dtype)
+    _check(q.dim() == 3 and q.shape[2] == HEAD_DIM, "q must be [T, H, 512], got %s" % (tuple(q.shape),))
+    _check(q.is_contiguous(), "q must be contiguous")
+    T, H, _ = q.shape
+    _check(kv.device == dev, "kv must be on %s, got %s" % (dev, kv.device))
+    _check(kv.dtype == q.dtype, "kv dtype mismatch: kv is %s, q is %s" % (kv.dtype, q.dtype))
+    _check(kv.dim() == 2 and kv.shape[1] == HEAD_DIM, "kv must be [num_kv, 512], got %s" % (tuple(kv.shape),))
+    _check(kv.is_contiguous(), "kv must be contiguous")
+    _check(topk_indices.device == dev, "topk_indices must be on %s" % dev)
+    _check(topk_indices.dtype == torch.int32, "topk_indices must be int32, got %s" % topk_indices.dtype)
+    _check(topk_indices.dim() == 2 and topk_indices.shape[0] == T, "topk_indices must be [T, topk]")
+    _check(topk_indices.is_contiguous(), "topk_indices must be contiguous")
+    if attn_sink is not None:
+        _check(attn_sink.device == dev, "attn_sink must be on %s, got %s" % (dev, attn_sink.device))
+        _check(attn_sink.dtype == torch.float32, "attn_sink must be float32, got %s" % attn_sink.dtype)
+        _check(tuple(attn_sink.shape) == (H,), "attn_sink must be [H]")
+        _check(attn_sink.is_contiguous(), "attn_sink must be contiguous")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out.device == dev and out.dtype == q.dtype and out.shape == q.shape,
+               "out must match q's shape, dtype and device")
+        _check(out.is_contiguous(), "out must be contiguous")
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    else:
+        _check(lse.device == dev and lse.dtype == torch.float32 and tuple(lse.shape) == (T, H),
+               "lse must be float32 [T, H] on q's device")
+        _check(lse.is_contiguous(), "lse must be contiguous")
+    if scale is None:
+        scale = DEFAULT_SCALE
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib.sparse_mla_prefill(
+            q.data_ptr(), kv.data_ptr() if kv.numel() else None, topk_indices.data_ptr() if topk_indices.numel() else None,
+            attn_sink.data_ptr() if attn_sink is not None else None, float(scale),
+            out.data_ptr(), lse.data_ptr(), T, H, kv.shape[0], topk_indices.shape[1], stream)
+    if rc != 0:
+        raise RuntimeError("sparse_mla_prefill failed: %s (status %d)" % (_lib.status_string(rc), rc))
+    return out, lse
+
+
+def kernel_name(H: int) -> str:
+    """Name of the kernel launched for H heads (as profilers show it)."""
+    name = _lib.load().sparse_mla_kernel_name(int(H))
+    if name is None:
+        raise ValueError("H must be >= 1")
+    return name.decode()

@@ -1,0 +1,100 @@
+"""The C-ABI library: it loads, exports every function the header declares, and
+rejects bad arguments before touching a device (CPU only: no compute call)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_top_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_mla.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparse_mla_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert "sparse_mla_prefill" in names and "sparse_mla_status_string" in names
+    assert set(names) == set(_lib.SIGNATURES), names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    exported = os.popen("nm -D --defined-only %s" % _lib.LIB_PATH).read()
+    for name in declared_functions():
+        assert re.search(r"\bT %s\b" % name, exported), name
+
+
+def call(q=0x1000, kv=0x2000, topk=0x3000, sink=None, scale=0.0441, out=0x4000, lse=0x5000,
+         T=4, H=8, num_kv=16, k=8):
+    return _lib.load().sparse_mla_prefill(q, kv, topk, sink, scale, out, lse, T, H, num_kv, k, None)
+
+
+def test_status_strings_and_version():
+    lib = _lib.load()
+    for rc in range(-6, 1):
+        assert _lib.status_string(rc)
+    assert _lib.status_string(17) == "unknown status"
+    assert lib.sparse_mla_version() >= 100
+
+
+def test_kernel_names():
+    lib = _lib.load()
+    assert lib.sparse_mla_kernel_name(0) is None
+    assert lib.sparse_mla_kernel_name(8) == lib.sparse_mla_kernel_name(16)
+    assert lib.sparse_mla_kernel_name(128).startswith(b"smla_fwd_kernel")
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(T=-1), _lib.SMLA_ERR_BAD_SIZE),
+    (dict(H=0), _lib.SMLA_ERR_BAD_SIZE),
+    (dict(num_kv=-5), _lib.SMLA_ERR_BAD_SIZE),
+    (dict(k=-1), _lib.SMLA_ERR_BAD_SIZE),
+    (dict(T=2**31), _lib.SMLA_ERR_BAD_SIZE),
+    (dict(T=2**30, H=2**12), _lib.SMLA_ERR_BAD_SIZE),
+    (dict(scale=float("nan")), _lib.SMLA_ERR_BAD_SCALE),
+    (dict(scale=float("inf")), _lib.SMLA_ERR_BAD_SCALE),
+    (dict(scale=float("-inf")), _lib.SMLA_ERR_BAD_SCALE),
+    (dict(q=None), _lib.SMLA_ERR_NULL_POINTER),
+    (dict(out=None), _lib.SMLA_ERR_NULL_POINTER),
+    (dict(lse=None), _lib.SMLA_ERR_NULL_POINTER),
+    (dict(topk=None), _lib.SMLA_ERR_NULL_POINTER),
+    (dict(kv=None), _lib.SMLA_ERR_NULL_POINTER),
+    (dict(q=0x1008), _lib.SMLA_ERR_MISALIGNED),
+    (dict(kv=0x2004), _lib.SMLA_ERR_MISALIGNED),
+    (dict(out=0x4002), _lib.SMLA_ERR_MISALIGNED),
+    (dict(lse=0x5001), _lib.SMLA_ERR_MISALIGNED),
+    (dict(topk=0x3002), _lib.SMLA_ERR_MISALIGNED),
+    (dict(sink=0x6003), _lib.SMLA_ERR_MISALIGNED),
+])
+def test_argument_errors_return_before_any_launch(kw, rc):
+    assert call(**kw) == rc
+
+
+def test_empty_sequence_is_ok_without_a_device():
+    assert call(T=0, q=None, out=None, lse=None, topk=None, kv=None) == _lib.SMLA_OK
+
+
+def test_null_allowed_where_size_is_zero():
+    # with topk == 0 neither the index array nor the pool is read; kv may be NULL when num_kv == 0
+    rc_k0 = call(topk=None, k=0, kv=None)
+    rc_nkv0 = call(kv=None, num_kv=0)
+    # both pass validation; without a GPU the next step reports the missing device
+    for rc in (rc_k0, rc_nkv0):
+        assert rc in (_lib.SMLA_OK, _lib.SMLA_ERR_NO_DEVICE, _lib.SMLA_ERR_LAUNCH)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.load()

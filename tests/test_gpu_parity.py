@@ -1,0 +1,323 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Sizes the oracle finishes in seconds are compared element by element for every
+token; the full-size workloads (the launch the benchmark times) are compared
+on sampled tokens, which always include the first and last token and the
+tokens with the fewest and most valid slots.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from sparse_attention_top_amd import synth
+
+from gpu_util import DEV, compare, oracle_ref, run_case, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+_FULL = {}
+
+
+def full_case(name):
+    """Generate a full-size workload once per session and run the GPU on it once."""
+    if name not in _FULL:
+        inp = synth.make_inputs(name)
+        o, lse = run_case(inp)
+        _FULL[name] = (inp, o, lse)
+    return _FULL[name]
+
+
+def sample_tokens(topk, num_kv, k, seed):
+    T = topk.shape[0]
+    nv = ((topk >= 0) & (topk < num_kv)).sum(axis=1)
+    rng = np.random.default_rng(seed)
+    pick = {0, T - 1, int(np.argmin(nv)), int(np.argmax(nv))}
+    pick.update(rng.choice(T, size=min(T, k), replace=False).tolist())
+    return np.array(sorted(pick), dtype=np.int64)
+
+
+def test_tiny_all_tokens():
+    inp = synth.make_inputs("tiny")
+    o, lse = run_case(inp)
+    stats = compare(o, lse, oracle_ref(inp), what="tiny")
+    print("tiny", stats)
+
+
+@pytest.mark.parametrize("name,T", [("small", None), ("tp4", 768), ("wide", 384), ("large", 320)])
+def test_truncated_all_tokens(name, T):
+    """Same draw recipe at a size the oracle covers fully (several tiles and a ragged tail per token)."""
+    inp = synth.make_inputs(name, T=T)
+    o, lse = run_case(inp)
+    stats = compare(o, lse, oracle_ref(inp), what="%s T=%s" % (name, inp["T"]))
+    print(name, inp["T"], stats)
+
+
+@pytest.mark.parametrize("name,k", [("small", 48), ("tp4", 40), ("wide", 24), ("large", 16)])
+def test_full_size_sampled(name, k):
+    inp, o, lse = full_case(name)
+    tok = sample_tokens(inp["topk"], inp["num_kv"], k, seed=7)
+    ref = oracle_ref(inp, tokens=tok)
+    stats = compare(o, lse, ref, tokens=tok, what="%s full" % name)
+    print(name, "full", len(tok), "tokens", stats)
+
+
+def test_full_size_properties():
+    """Properties over every token of the full-size workloads: finite outputs and an lse
+    no smaller than the sink (the denominator holds exp(sink))."""
+    for name in ("small", "tp4", "wide", "large"):
+        inp, o, lse = full_case(name)
+        of = synth.bf16_bits_to_f32(o)
+        assert np.all(np.isfinite(of)), name
+        assert np.all(np.isfinite(lse)), name
+        if inp["sink"] is not None:
+            assert np.all(lse >= inp["sink"][None, :] - 1e-3), name
+
+
+def test_rerun_is_bitwise_deterministic_and_out_reuse():
+    inp = synth.make_inputs("wide", T=200)
+    o1, l1 = run_case(inp)
+    o2, l2 = run_case(inp)
+    assert np.array_equal(o1, o2) and np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
+    # writing into caller buffers (pre-filled with garbage) gives the same bits
+    out = torch.full((inp["T"], inp["H"], 512), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((inp["T"], inp["H"]), 12345.0, dtype=torch.float32, device=DEV)
+    o3, l3 = run_gpu(inp["q"], inp["kv"], inp["topk"], inp["sink"], inp["scale"], out=out, lse=lse)
+    assert np.array_equal(o1, o3) and np.array_equal(l1.view(np.uint32), l3.view(np.uint32))
+
+
+def random_rows(rng, T, topk, num_kv, p_invalid):
+    idx = np.empty((T, topk), np.int32)
+    for t in range(T):
+        idx[t] = rng.choice(num_kv, topk, replace=False)
+    idx[rng.random((T, topk)) < p_invalid] = -1
+    return idx
+
+
+def make_random(seed, T, H, num_kv, topk, p_invalid=0.2, sink=True):
+    rng = np.random.default_rng(seed)
+    q = synth.f32_to_bf16_bits(rng.standard_normal((T, H, 512), dtype=np.float32))
+    kv = synth.f32_to_bf16_bits(rng.standard_normal((num_kv, 512), dtype=np.float32))
+    idx = random_rows(rng, T, topk, num_kv, p_invalid)
+    s = rng.standard_normal(H).astype(np.float32) if sink else None
+    return {"q": q, "kv": kv, "topk": idx, "sink": s, "scale": synth.DEFAULT_SCALE}
+
+
+@pytest.mark.parametrize("H", [1, 3, 8, 16, 17, 24, 40, 64, 100, 128, 130, 200])
+def test_head_counts(H):
+    inp = make_random(1000 + H, T=24, H=H, num_kv=300, topk=96)
+    o, lse = run_case(inp)
+    compare(o, lse, oracle_ref(inp), what="H=%d" % H)
+
+
+@pytest.mark.parametrize("topk,num_kv", [(1, 50), (31, 40), (33, 100), (2048, 3000), (2500, 4000), (4500, 6000)])
+def test_topk_extremes(topk, num_kv):
+    """Single slots, tile-boundary counts and rows longer than one compaction segment."""
+    inp = make_random(2000 + topk, T=6, H=16, num_kv=num_kv, topk=topk, p_invalid=0.1)
+    o, lse = run_case(inp)
+    compare(o, lse, oracle_ref(inp), what="topk=%d" % topk)
+
+
+def test_permutation_invariance():
+    inp = synth.make_inputs("wide", T=160)
+    rng = np.random.default_rng(3)
+    perm = np.stack([rng.permutation(inp["topk_n"]) for _ in range(inp["T"])])
+    inp_p = dict(inp, topk=np.take_along_axis(inp["topk"], perm, axis=1))
+    o1, l1 = run_case(inp)
+    o2, l2 = run_case(inp_p)
+    compare(o2, l2, oracle_ref(inp), what="permuted")
+    assert np.max(np.abs(l1 - l2)) <= 1e-3
+
+
+def test_sink_minus_inf_equals_no_sink():
+    inp = make_random(5, T=20, H=16, num_kv=200, topk=64)
+    inp["topk"][3] = -1  # an all-invalid row
+    o1, l1 = run_gpu(inp["q"], inp["kv"], inp["topk"], np.full(16, -np.inf, np.float32), inp["scale"])
+    o2, l2 = run_gpu(inp["q"], inp["kv"], inp["topk"], None, inp["scale"])
+    assert np.array_equal(o1, o2) and np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
+
+
+@pytest.mark.parametrize("H", [16, 128])
+def test_all_invalid_rows(H):
+    inp = make_random(6, T=8, H=H, num_kv=100, topk=40)
+    inp["topk"][2] = -1
+    inp["topk"][5] = np.array([100, 2**31 - 1, -(2**31), -2] * 10, np.int32)
+    o, l = run_case(inp)
+    o_ns, l_ns = run_gpu(inp["q"], inp["kv"], inp["topk"], None, inp["scale"])
+    for t in (2, 5):
+        assert np.all(o[t] == 0) and np.all(o_ns[t] == 0)  # exactly +0.0
+        assert np.array_equal(l[t], inp["sink"])
+        assert np.all(np.isneginf(l_ns[t]))
+
+
+def test_empty_pool_and_empty_topk():
+    inp = make_random(7, T=4, H=16, num_kv=10, topk=8)
+    o, l = run_gpu(inp["q"], np.zeros((0, 512), np.uint16), inp["topk"], inp["sink"], inp["scale"])
+    assert np.all(o == 0) and np.array_equal(l, np.broadcast_to(inp["sink"], l.shape))
+    o, l = run_gpu(inp["q"], inp["kv"], np.zeros((4, 0), np.int32), None, inp["scale"])
+    assert np.all(o == 0) and np.all(np.isneginf(l))
+
+
+def test_zero_sequence():
+    q = torch.empty((0, 16, 512), dtype=torch.bfloat16, device=DEV)
+    kv = torch.zeros((5, 512), dtype=torch.bfloat16, device=DEV)
+    idx = torch.empty((0, 4), dtype=torch.int32, device=DEV)
+    from sparse_attention_top_amd import sparse_mla_prefill
+
+    o, l = sparse_mla_prefill(q, kv, idx)
+    assert o.shape == (0, 16, 512) and l.shape == (0, 16)
+
+
+def test_single_valid_slot_is_exact_gather():
+    inp = make_random(8, T=40, H=16, num_kv=500, topk=64, sink=False)
+    rng = np.random.default_rng(9)
+    rows = rng.choice(500, 40, replace=False)
+    inp["topk"][:] = -1
+    inp["topk"][np.arange(40), rng.integers(0, 64, 40)] = rows
+    o, l = run_case(inp)
+    for t in range(40):
+        assert np.array_equal(o[t], np.broadcast_to(inp["kv"][rows[t]], (16, 512)))
+
+
+@pytest.mark.parametrize("sink", [False, True])
+def test_zero_query_counts_exact_valid_slots(sink):
+    """q = 0 makes every logit 0, so lse = ln(n) (or ln(n + e^sink)): the count n of
+    gathered slots is pinned exactly (neighbouring counts differ by > 9e-4)."""
+    inp = synth.make_inputs("large", T=600)
+    inp["q"][:] = 0
+    if not sink:
+        inp["sink"] = None
+    o, l = run_case(inp)
+    n = ((inp["topk"] >= 0) & (inp["topk"] < inp["num_kv"])).sum(axis=1).astype(np.float64)
+    if sink:
+        expect = np.log(n[:, None] + np.exp(inp["sink"].astype(np.float64))[None, :])
+    else:
+        expect = np.log(n)[:, None]
+    assert np.max(np.abs(l - expect)) < 2e-4
+
+
+def test_poisoned_unused_rows_and_out_of_range_slots():
+    """Rows no valid slot references (row 0 included, and the row just past
+    num_kv inside the same allocation) are filled with NaN/Inf, and invalid
+    slots take -2, INT32_MIN, num_kv, num_kv+1, INT32_MAX: bitwise the same
+    output as the clean run with -1."""
+    inp = make_random(10, T=32, H=16, num_kv=400, topk=96, p_invalid=0.0)
+    rng = np.random.default_rng(11)
+    inp["topk"][inp["topk"] == 0] = 1  # row 0 unreferenced
+    inp["topk"] = np.where(inp["topk"] == 1, -1, inp["topk"]).astype(np.int32)
+    bad = rng.random(inp["topk"].shape) < 0.3
+    clean_idx = np.where(bad, -1, inp["topk"]).astype(np.int32)
+    vals = np.array([-2, -(2**31), 400, 401, 2**31 - 1], np.int64)
+    dirty_idx = np.where(bad, rng.choice(vals, bad.shape), inp["topk"]).astype(np.int32)
+    o1, l1 = run_gpu(inp["q"], inp["kv"], clean_idx, inp["sink"], inp["scale"])
+    used = np.zeros(401, bool)
+    used[clean_idx[clean_idx >= 0]] = True
+    kv_p = np.vstack([inp["kv"], np.zeros((1, 512), np.uint16)])
+    unused = np.flatnonzero(~used)
+    kv_p[unused[0::2]] = synth.BF16_NAN
+    kv_p[unused[1::2]] = np.uint16(0x7F80)  # +inf
+    kvd = torch.from_numpy(kv_p.view(np.int16)).view(torch.bfloat16).to(DEV)[:400]  # row 400 poisoned, past the pool
+    from gpu_util import bf16_bits, to_dev_bf16
+    from sparse_attention_top_amd import sparse_mla_prefill
+
+    o2, l2 = sparse_mla_prefill(to_dev_bf16(inp["q"]), kvd, torch.from_numpy(dirty_idx).to(DEV),
+                                torch.from_numpy(inp["sink"]).to(DEV), inp["scale"])
+    torch.cuda.synchronize()
+    assert np.array_equal(o1, bf16_bits(o2))
+    assert np.array_equal(l1.view(np.uint32), l2.cpu().numpy().view(np.uint32))
+
+
+def test_duplicate_slots_count_each_occurrence():
+    inp = make_random(12, T=16, H=16, num_kv=100, topk=48)
+    inp["topk"][:, 40:48] = inp["topk"][:, 0:8]  # repeats (valid or not)
+    o, l = run_case(inp)
+    compare(o, l, oracle_ref(inp), what="duplicates")
+
+
+def test_head_independence():
+    inp = make_random(13, T=12, H=40, num_kv=200, topk=80)
+    o, l = run_case(inp)
+    for h in (0, 17, 39):
+        o1, l1 = run_gpu(np.ascontiguousarray(inp["q"][:, h:h + 1]), inp["kv"], inp["topk"], inp["sink"][h:h + 1],
+                         inp["scale"])
+        a = synth.bf16_bits_to_f32(o1[:, 0]).astype(np.float64)
+        b = synth.bf16_bits_to_f32(o[:, h]).astype(np.float64)
+        assert np.all(np.abs(a - b) <= 2e-2 + 2e-2 * np.abs(b))
+        assert np.max(np.abs(l1[:, 0] - l[:, h])) <= 1e-3
+
+
+def test_large_logits_stay_finite():
+    inp = make_random(14, T=16, H=16, num_kv=200, topk=64)
+    inp["q"] = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(inp["q"]) * 100.0)
+    o, l = run_case(inp)
+    assert np.all(np.isfinite(synth.bf16_bits_to_f32(o))) and np.all(np.isfinite(l))
+    compare(o, l, oracle_ref(inp), what="large logits")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.05, 1.0])
+def test_any_finite_scale(scale):
+    inp = make_random(15, T=12, H=16, num_kv=150, topk=64)
+    inp["scale"] = scale
+    o, l = run_case(inp)
+    compare(o, l, oracle_ref(inp), what="scale=%g" % scale)
+
+
+def test_nan_in_referenced_row_stays_local():
+    inp = synth.make_inputs("tp4", T=300)
+    victim = 250  # a token row inside the windows of tokens 250..299 only
+    inp["kv"][victim, 7] = synth.BF16_NAN
+    o, l = run_case(inp)
+    refs = np.array([victim in set(r.tolist()) for r in inp["topk"]])
+    of = synth.bf16_bits_to_f32(o)
+    assert np.array_equal(np.isnan(l).all(axis=1), refs) and np.array_equal(np.isnan(l).any(axis=1), refs)
+    assert np.array_equal(np.isnan(of).any(axis=(1, 2)), refs)
+    ok = ~refs
+    tok = np.flatnonzero(ok)[::7]
+    compare(o, l, oracle_ref(inp, tokens=tok), tokens=tok, what="nan locality")
+
+
+def test_kv_inside_large_allocation():
+    """kv placed more than 4 GiB into one allocation: 64-bit row addressing."""
+    inp = synth.make_inputs("tp4", T=256)
+    nbytes = inp["kv"].nbytes
+    offset = (4 << 30) + 4096
+    try:
+        big = torch.empty(offset + nbytes, dtype=torch.uint8, device=DEV)
+    except RuntimeError:
+        pytest.skip("not enough device memory for the >4 GiB placement")
+    kv_view = big[offset:offset + nbytes].view(torch.bfloat16).view(-1, 512)
+    kv_view.copy_(torch.from_numpy(inp["kv"].view(np.int16)).view(torch.bfloat16))
+    from gpu_util import bf16_bits, to_dev_bf16
+    from sparse_attention_top_amd import sparse_mla_prefill
+
+    o, l = sparse_mla_prefill(to_dev_bf16(inp["q"]), kv_view, torch.from_numpy(inp["topk"]).to(DEV),
+                              torch.from_numpy(inp["sink"]).to(DEV), inp["scale"])
+    torch.cuda.synchronize()
+    o_ref, l_ref = run_case(inp)
+    assert np.array_equal(bf16_bits(o), o_ref)
+    assert np.array_equal(l.cpu().numpy().view(np.uint32), l_ref.view(np.uint32))
+    del big
+
+
+def test_binding_rejects_bad_inputs():
+    from sparse_attention_top_amd import sparse_mla_prefill
+
+    q = torch.zeros((4, 16, 512), dtype=torch.bfloat16, device=DEV)
+    kv = torch.zeros((10, 512), dtype=torch.bfloat16, device=DEV)
+    idx = torch.zeros((4, 8), dtype=torch.int32, device=DEV)
+    with pytest.raises(RuntimeError, match="kv dtype mismatch"):
+        sparse_mla_prefill(q, kv.float(), idx)
+    with pytest.raises(RuntimeError, match="bfloat16"):
+        sparse_mla_prefill(q.half(), kv, idx)
+    with pytest.raises(RuntimeError, match="int32"):
+        sparse_mla_prefill(q, kv, idx.long())
+    with pytest.raises(RuntimeError, match="GPU"):
+        sparse_mla_prefill(q.cpu(), kv, idx)
+    with pytest.raises(RuntimeError, match="contiguous"):
+        sparse_mla_prefill(q, kv, idx, out=torch.empty((16, 4, 512), dtype=torch.bfloat16, device=DEV).transpose(0, 1))
+    with pytest.raises(RuntimeError, match="attn_sink"):
+        sparse_mla_prefill(q, kv, idx, attn_sink=torch.zeros(16, device=DEV, dtype=torch.float64))
+    with pytest.raises(RuntimeError, match="scale"):
+        sparse_mla_prefill(q, kv, idx, scale=math.inf)
