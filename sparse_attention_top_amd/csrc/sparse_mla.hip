@@ -54,6 +54,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
 
 struct Params {
@@ -75,7 +76,7 @@ template <int NW, int NBUF>
 struct Smem {
   uint8_t tile[NBUF][kBK][kRowStride];
   int32_t list[kListCap];
-  int32_t wcount[NW];
+  int32_t wcount[kListCap / (NW * 64)][NW];
 };
 
 // Optimisation barrier on a per-tile base address: keeps loop strength
@@ -86,12 +87,73 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
   return x;
 }
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(LDS_AS const void*)p; }
-
-template <typename T>
-__device__ __forceinline__ T lds_load(uint32_t addr) {
-  return *(LDS_AS const T*)(uintptr_t)addr;
+// LDS fragment reads issued as raw instructions. The compiler does not track
+// them, so (a) it cannot assume they alias an in-flight LDS-DMA prefetch and
+// stall on that, and (b) every consumer must first pass the registers through
+// lds_wait<N>(), an explicit lgkmcnt wait taking them as in/out operands (no
+// use can be scheduled above it). LDS operations complete in order, so
+// waiting until at most N are outstanding -- N = the number of LDS reads
+// issued after this one -- completes it; any other LDS operation issued in
+// between only makes the wait stricter.
+template <int OFF>
+__device__ __forceinline__ u32x4 ds_read_b128(uint32_t addr) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
 }
+template <int OFF>
+__device__ __forceinline__ u32x2 ds_read_tr16_b64(uint32_t addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+template <int N, typename T>
+__device__ __forceinline__ void lds_wait(T& a, T& b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
+template <int N, typename T>
+__device__ __forceinline__ void lds_wait4(T& a, T& b, T& c, T& d) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "n"(N));
+}
+template <int N, typename T, typename U>
+__device__ __forceinline__ void lds_wait6(T& a, T& b, U& c, U& d, U& e, U& f) {
+  asm volatile("s_waitcnt lgkmcnt(%6)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f) : "n"(N));
+}
+
+// S-phase MFMAs with their accumulators pinned to VGPRs (the O accumulator
+// fills the AGPRs). The first k-step takes an inline-zero C operand, so no
+// VALU write precedes the chain; accumulation into the same registers is
+// interlocked by the hardware. Before VALU code reads the result,
+// mfma_vgpr_drain() pads the MFMA-write -> VALU-read distance with wait
+// states (more than the longest 16x16x32 latency).
+__device__ __forceinline__ void mfma_s_first(f32x4& c, const u32x4& a, const u32x4& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_s(f32x4& c, const u32x4& a, const u32x4& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+template <int N>
+__device__ __forceinline__ void mfma_vgpr_drain(f32x4 (&c)[2][N]) {
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < N; ++j) asm volatile("" : "+v"(c[i][j]));
+}
+
+template <int I>
+struct Int {
+  static constexpr int value = I;
+};
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(Int<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(LDS_AS const void*)p; }
 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
@@ -125,78 +187,135 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
   return ((p / kXcdChunk) * kNumXcd + x) * kXcdChunk + (p % kXcdChunk);
 }
 
-// Compact the valid entries of trow[0, len) into sm.list (order kept).
-// Returns the count (uniform across the workgroup).
+// Compact the valid entries of trow[0, len) into sm.list (order kept), with
+// one round of loads and two workgroup barriers. Returns the count (uniform
+// across the workgroup).
 template <int NW, int NBUF>
 __device__ int compact_segment(const int32_t* __restrict__ trow, int len, uint32_t nkv, Smem<NW, NBUF>& sm,
                                int lane, int w) {
-  int base = 0;
-  for (int c0 = 0; c0 < len; c0 += NW * 64) {
-    const int pos = c0 + w * 64 + lane;
-    const int raw = pos < len ? trow[pos] : -1;
-    const bool valid = (uint32_t)raw < nkv;
-    const uint64_t bal = __ballot(valid);
-    const int rank = lane_rank(bal);
-    const int wc = __popcll(bal);
-    if constexpr (NW == 1) {
-      if (valid) sm.list[base + rank] = raw;
-      base += wc;
-    } else {
-      if (lane == 0) sm.wcount[w] = wc;
-      lds_barrier();
+  constexpr int CH = NW * 64;              // entries per chunk (one per thread)
+  constexpr int MAXC = kListCap / CH;      // chunks per segment
+  int raw[MAXC];
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const int pos = c * CH + w * 64 + lane;
+    raw[c] = pos < len ? trow[pos] : -1;
+  }
+  uint64_t bal[MAXC];
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) bal[c] = __ballot((uint32_t)raw[c] < nkv);
+  if constexpr (NW == 1) {
+    int base = 0;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      if ((uint32_t)raw[c] < nkv) sm.list[base + lane_rank(bal[c])] = raw[c];
+      base += __popcll(bal[c]);
+    }
+    return __builtin_amdgcn_readfirstlane(base);
+  } else {
+    if (lane == 0) {
+#pragma unroll
+      for (int c = 0; c < MAXC; ++c) sm.wcount[c][w] = __popcll(bal[c]);
+    }
+    lds_barrier();
+    int base = 0;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
       int off = 0, tot = 0;
 #pragma unroll
       for (int i = 0; i < NW; ++i) {
-        const int ci = __builtin_amdgcn_readfirstlane(sm.wcount[i]);
+        const int ci = __builtin_amdgcn_readfirstlane(sm.wcount[c][i]);
         off += (i < w) ? ci : 0;
         tot += ci;
       }
-      if (valid) sm.list[base + off + rank] = raw;
+      if ((uint32_t)raw[c] < nkv) sm.list[base + off + lane_rank(bal[c])] = raw[c];
       base += tot;
-      lds_barrier();
     }
+    lds_barrier();
+    return __builtin_amdgcn_readfirstlane(base);
   }
-  return __builtin_amdgcn_readfirstlane(base);
 }
 
-template <int NW>
 __device__ __forceinline__ int tile_rows(int i, int n) { return min(kBK, n - i * kBK); }
 
-// Number of LDS-DMA loads this wave issues for tile i.
+// Number of LDS-DMA loads wave w issues for tile i.
 template <int NW>
 __device__ __forceinline__ int tile_dma(int i, int n, int w) {
   constexpr int RPW = kBK / NW;
-  return min(RPW, max(0, tile_rows<NW>(i, n) - w * RPW));
+  return min(RPW, max(0, tile_rows(i, n) - w * RPW));
 }
 
-// Issue the gather of tile i (rows list[32 i, 32 i + cnt)) into its ring
-// buffer; rows past cnt are zero-filled. Each wave moves rows
-// [w RPW, (w+1) RPW): one LDS-DMA instruction per row, lane L moving bytes
-// [16 L, 16 L + 16) of the row.
+// The gather of one tile, issued row by row so that it can be spread over a
+// compute phase: one LDS-DMA instruction per row (lane L moves bytes
+// [16 L, 16 L + 16) of the 1 KiB row); rows past the tile's count are
+// zero-filled. Wave w moves rows [w RPW, (w+1) RPW).
 template <int NW, int NBUF>
-__device__ __forceinline__ void issue_tile(int i, int n, Smem<NW, NBUF>& sm, const uint16_t* __restrict__ kv,
-                                           int lane, int w) {
-  constexpr int RPW = kBK / NW;
-  const int buf = i % NBUF;
-  const int cnt = tile_rows<NW>(i, n);
-  const int r0 = w * RPW;
-  const int my = (lane < RPW && r0 + lane < cnt) ? sm.list[i * kBK + r0 + lane] : 0;
-#pragma unroll
-  for (int rr = 0; rr < RPW; ++rr) {
-    const int r = r0 + rr;
-    uint8_t* dst = &sm.tile[buf][r][0];
-    if (r < cnt) {
-      const int row = __builtin_amdgcn_readlane(my, rr);
-      const uint16_t* src = kv + (size_t)(uint32_t)row * kD + 8 * lane;
-      __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)dst, 16, 0, 0);
+struct TileIssue {
+  static constexpr int RPW = kBK / NW;
+  const uint16_t* kv;
+  uint32_t dst0;  // LDS address of this wave's first row in the target buffer
+  int cnt;        // valid rows in the tile (rows >= cnt are zero-filled)
+  int r0;         // first row of this wave
+  int my;         // lane L < RPW: list entry of row r0 + L
+  bool active;
+
+  __device__ __forceinline__ void init(int i, int n, int ntiles, Smem<NW, NBUF>& sm, const uint16_t* kv_, int lane,
+                                       int w) {
+    kv = kv_;
+    active = i < ntiles;
+    r0 = w * RPW;
+    cnt = active ? tile_rows(i, n) : 0;
+    dst0 = lds_addr(&sm.tile[active ? i % NBUF : 0][r0][0]);
+    int e = 0;
+    if (active && lane < RPW && r0 + lane < cnt) e = sm.list[i * kBK + r0 + lane];
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(e));
+    my = e;
+  }
+  template <int RR>
+  __device__ __forceinline__ void row(int lane) const {
+    if (!active) return;
+    const uint32_t dst = dst0 + RR * kRowStride;
+    if (r0 + RR < cnt) {
+      const int idx = __builtin_amdgcn_readlane(my, RR);
+      const uint16_t* src = kv + (size_t)(uint32_t)idx * kD + 8 * lane;
+      __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(uintptr_t)dst, 16, 0, 0);
     } else {
-      *(u32x4*)(dst + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+      *(LDS_AS u32x4*)(uintptr_t)(dst + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
     }
   }
+  // Rows that go with step K of NS steps.
+  template <int K, int NS>
+  __device__ __forceinline__ void step(int lane) const {
+    constexpr int lo = K * RPW / NS, hi = (K + 1) * RPW / NS;
+    static_for<lo, hi>([&](auto rc) { row<decltype(rc)::value>(lane); });
+  }
+  __device__ __forceinline__ void all(int lane) const {
+    static_for<0, RPW>([&](auto rc) { row<decltype(rc)::value>(lane); });
+  }
+};
+
+// Max over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float row4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __builtin_fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __builtin_fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float row4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Iteration j runs S(j), its softmax, then P.V(j) on ring buffer j % NBUF,
+// while tiles j+1 .. j+NBUF-1 land; the rows of tile j+NBUF-1 are issued
+// spread over the compute steps of iteration j (a burst would stall the wave
+// at issue until the memory pipeline drains).
 template <int NHT, int NW, int NBUF>
 __global__ __launch_bounds__(NW * 64) void smla_fwd_kernel(const Params p) {
+  static_assert(NBUF == 2 || NBUF == 3, "ring of 2 or 3 tiles");
+  constexpr int AHEAD = NBUF - 1;  // tiles gathered ahead of the one being computed
   __shared__ __attribute__((aligned(16))) Smem<NW, NBUF> sm;
 
   const int lane = threadIdx.x & 63;
@@ -209,19 +328,15 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_kernel(const Params p) {
   const int hg = v % p.head_groups;
   const int head_base = (hg * NW + w) * (NHT * 16);
 
-  // Q^T fragments (MFMA B operand): lane holds q[t, head, 32k + 8g .. +8).
-  bf16x8 qf[NHT][16];
+  // Per-lane head state: lane (g, li) owns head head_base + 16 ht + li.
+  float sink_l2[NHT];  // sink * log2(e), or -inf
+  bool has_sink[NHT];
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht) {
     const int head = head_base + ht * 16 + li;
-    if (head < p.H) {
-      const bf16x8* src = (const bf16x8*)(p.q + ((size_t)t * p.H + head) * kD + 8 * g);
-#pragma unroll
-      for (int k = 0; k < 16; ++k) qf[ht][k] = src[4 * k];
-    } else {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) qf[ht][k] = bf16x8{};
-    }
+    const float sk = (p.sink != nullptr && head < p.H) ? p.sink[head] : -INFINITY;
+    has_sink[ht] = !(sk == -INFINITY);
+    sink_l2[ht] = sk * kLog2e;
   }
 
   f32x4 acc[NHT][32];
@@ -235,63 +350,127 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_kernel(const Params p) {
     m_ref[ht] = -INFINITY;
     l_part[ht] = 0.f;
   }
+  // Q^T fragments (MFMA B operand of S^T = K Q^T): lane holds q[t, head, 32k + 8g .. +8).
+  // Loaded first, so that their latency overlaps the top-k row's.
+  bf16x8 qf[NHT][16];
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) {
+    const int head = head_base + ht * 16 + li;
+    if (head < p.H) {
+      const bf16x8* src = (const bf16x8*)(p.q + ((size_t)t * p.H + head) * kD + 8 * g);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) qf[ht][k] = src[4 * k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) qf[ht][k] = bf16x8{};
+    }
+  }
+  bf16x8 pk[NHT];  // P of the current tile (MFMA B operand of P.V)
 
   const int32_t* trow = p.topk + (size_t)t * p.topk_n;
-  int n_total = 0;
   for (int seg0 = 0; seg0 < p.topk_n; seg0 += kListCap) {
-    if (seg0 > 0 && NW > 1) lds_barrier();  // previous segment's list fully consumed
+    if (seg0 > 0 && NW > 1) lds_barrier();  // previous segment's list and tiles fully consumed
     const int n = compact_segment<NW, NBUF>(trow + seg0, min(kListCap, p.topk_n - seg0), p.nkv, sm, lane, w);
-    n_total += n;
     const int ntiles = (n + kBK - 1) / kBK;
+    if (ntiles == 0) continue;
 
+    // Prologue: the first AHEAD tiles.
+    {
+      TileIssue<NW, NBUF> is;
+      is.init(0, n, ntiles, sm, p.kv, lane, w);
+      is.all(lane);
+    }
 #pragma unroll
-    for (int i = 0; i < NBUF - 1; ++i)
-      if (i < ntiles) issue_tile<NW, NBUF>(i, n, sm, p.kv, lane, w);
+    for (int i = 1; i < AHEAD; ++i) {
+      TileIssue<NW, NBUF> is;
+      is.init(i, n, ntiles, sm, p.kv, lane, w);
+      is.all(lane);
+    }
 
     for (int j = 0; j < ntiles; ++j) {
-      int after = 0;
+      int after = 0;  // this wave's gather loads issued after tile j's
 #pragma unroll
-      for (int i = 1; i <= NBUF - 2; ++i)
+      for (int i = 1; i < AHEAD; ++i)
         if (j + i < ntiles) after += tile_dma<NW>(j + i, n, w);
       wait_vmcnt_le(after);
       if constexpr (NW > 1) lds_barrier();
-      if (j + NBUF - 1 < ntiles) issue_tile<NW, NBUF>(j + NBUF - 1, n, sm, p.kv, lane, w);
+      TileIssue<NW, NBUF> is;
+      is.init(j + AHEAD, n, ntiles, sm, p.kv, lane, w);
 
-      const uint32_t tb = lds_addr(&sm.tile[j % NBUF][0][0]);
-      const int cnt = tile_rows<NW>(j, n);
+      const uint32_t tb_s = lds_addr(&sm.tile[j % NBUF][0][0]);
+      const uint32_t tb_v = tb_s;
+      // K fragment (MFMA A operand of S^T = K Q^T): lane holds K[slot sh*16 + li][32k + 8g .. +8).
+      const uint32_t krow = opaque(tb_s + li * kRowStride + 16 * g);
+      // V^T fragment (MFMA A operand of O^T += V^T P^T): two transposing reads give
+      // lane V[4g .. 4g+3 and 16+4g .. 16+4g+3][16 dt + li]; this lane addresses row
+      // 4g + li/4 (and that + 16), bytes 8 (li & 3) + 32 dt.
+      const uint32_t vrow = opaque(tb_v + (4 * g + (li >> 2)) * kRowStride + 8 * (li & 3));
 
-      // ---- S^T = K Q^T (two 16-slot halves) ----
-      // K fragment (MFMA A operand): lane holds K[slot sh*16 + li][32k + 8g .. +8),
-      // software-pipelined KPF k-steps ahead; the scheduler fence keeps the
-      // loads from being hoisted further (register pressure).
       f32x4 s[2][NHT];
-#pragma unroll
-      for (int sh = 0; sh < 2; ++sh)
-#pragma unroll
-        for (int ht = 0; ht < NHT; ++ht) s[sh][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-      constexpr int KPF = 2;
-      bf16x8 kf[KPF + 1][2];
-      const uint32_t krow = opaque(tb + li * kRowStride + 16 * g);
-#pragma unroll
-      for (int k = 0; k < 16 + KPF; ++k) {
-        if (k < 16) {
-          kf[k % (KPF + 1)][0] = lds_load<bf16x8>(krow + 64 * k);
-          kf[k % (KPF + 1)][1] = lds_load<bf16x8>(krow + 16 * kRowStride + 64 * k);
-        }
-        if (k >= KPF) {
-          const int kk = k - KPF;
-#pragma unroll
-          for (int sh = 0; sh < 2; ++sh)
-#pragma unroll
-            for (int ht = 0; ht < NHT; ++ht)
-              s[sh][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk % (KPF + 1)][sh], qf[ht][kk], s[sh][ht], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
 
-      // ---- online softmax (base 2) ----
-      float x[NHT][2][4], tmax[NHT];
+      // 16 steps; step k = S k-step k (2 K reads, 2*NHT MFMAs) and P.V d-tiles 2k, 2k+1
+      // (4 transposing reads, 2*NHT MFMAs), reads issued one step ahead.
+      auto run_steps = [&](auto s_flag, auto pv_flag, auto part) {
+        constexpr bool DS = decltype(s_flag)::value != 0;
+        constexpr bool DV = decltype(pv_flag)::value != 0;
+        constexpr int PART = decltype(part)::value;  // which 16 of the gather's 32 steps
+        constexpr int R = (DS ? 2 : 0) + (DV ? 4 : 0);  // LDS reads per step
+        u32x4 kf[2][2];
+        u32x2 vf[2][4];
+        auto issue_reads = [&](auto kc) {
+          constexpr int k = decltype(kc)::value;
+          constexpr int b = k & 1;
+          if constexpr (DS) {
+            kf[b][0] = ds_read_b128<64 * k>(krow);
+            kf[b][1] = ds_read_b128<16 * kRowStride + 64 * k>(krow);
+          }
+          if constexpr (DV) {
+            vf[b][0] = ds_read_tr16_b64<64 * k>(vrow);
+            vf[b][1] = ds_read_tr16_b64<16 * kRowStride + 64 * k>(vrow);
+            vf[b][2] = ds_read_tr16_b64<64 * k + 32>(vrow);
+            vf[b][3] = ds_read_tr16_b64<16 * kRowStride + 64 * k + 32>(vrow);
+          }
+        };
+        issue_reads(Int<0>{});
+        static_for<0, 16>([&](auto kc) {
+          constexpr int k = decltype(kc)::value;
+          constexpr int b = k & 1;
+          if constexpr (k + 1 < 16) issue_reads(Int<k + 1>{});
+          constexpr int younger = (k + 1 < 16) ? R : 0;
+          if constexpr (DS && DV) lds_wait6<younger>(kf[b][0], kf[b][1], vf[b][0], vf[b][1], vf[b][2], vf[b][3]);
+          else if constexpr (DS) lds_wait<younger>(kf[b][0], kf[b][1]);
+          else lds_wait4<younger>(vf[b][0], vf[b][1], vf[b][2], vf[b][3]);
+          if constexpr (DS) {
+#pragma unroll
+            for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+              for (int ht = 0; ht < NHT; ++ht) {
+                if constexpr (k == 0) mfma_s_first(s[sh][ht], kf[b][sh], __builtin_bit_cast(u32x4, qf[ht][k]));
+                else mfma_s(s[sh][ht], kf[b][sh], __builtin_bit_cast(u32x4, qf[ht][k]));
+              }
+          }
+          if constexpr (DV) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const bf16x8 a = __builtin_bit_cast(
+                  bf16x8, u32x4{vf[b][2 * e][0], vf[b][2 * e][1], vf[b][2 * e + 1][0], vf[b][2 * e + 1][1]});
+#pragma unroll
+              for (int ht = 0; ht < NHT; ++ht)
+                acc[ht][2 * k + e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pk[ht], acc[ht][2 * k + e], 0, 0, 0);
+            }
+          }
+          is.template step<PART * 16 + k, 32>(lane);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      };
+      run_steps(Int<1>{}, Int<0>{}, Int<0>{});
+
+      // ---- online softmax of tile j (base 2, lazy reference max) ----
+      mfma_vgpr_drain<NHT>(s);
+      const int cnt = tile_rows(j, n);
+      float x[NHT][2][4];
       bool need = false;
+      float tmax[NHT];
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
         float mx = -INFINITY;
@@ -302,37 +481,38 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_kernel(const Params p) {
             const int slot = sh * 16 + 4 * g + i;
             const float xv = slot < cnt ? s[sh][ht][i] * p.scale_log2 : -INFINITY;
             x[ht][sh][i] = xv;
-            mx = fmaxf(mx, xv);
+            mx = __builtin_fmaxf(mx, xv);
           }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = row4_max(mx);
         tmax[ht] = mx;
         need |= mx > m_ref[ht] + kLazyTau;
       }
       if (__ballot(need) != 0ull) {
 #pragma unroll
         for (int ht = 0; ht < NHT; ++ht) {
-          const float m_new = fmaxf(m_ref[ht], tmax[ht]);
-          const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref[ht] - m_new);
+          const float m_new = __builtin_fmaxf(m_ref[ht], tmax[ht]);
+          if (__ballot(m_ref[ht] != -INFINITY) != 0ull) {
+            // rescale what earlier tiles accumulated (lanes whose reference
+            // is still -inf have nothing accumulated: alpha = 0 keeps it 0)
+            const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref[ht] - m_new);
+            l_part[ht] *= alpha;
+            // in place, one accumulator register at a time (the accumulators
+            // live in AGPRs; a vector multiply would stage them all in VGPRs)
+#pragma unroll
+            for (int dt = 0; dt < 32; ++dt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                float e = acc[ht][dt][i];
+                float tmp;
+                asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                             : "+a"(e), "=&v"(tmp)
+                             : "v"(alpha));
+                acc[ht][dt][i] = e;
+              }
+          }
           m_ref[ht] = m_new;
-          l_part[ht] *= alpha;
-          // in place, one accumulator register at a time (the accumulators
-          // live in AGPRs; a plain vector multiply would stage all of them
-          // through VGPRs)
-#pragma unroll
-          for (int dt = 0; dt < 32; ++dt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              float e = acc[ht][dt][i];
-              float tmp;
-              asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                           : "+a"(e), "=&v"(tmp)
-                           : "v"(alpha));
-              acc[ht][dt][i] = e;
-            }
         }
       }
-      bf16x8 pk[NHT];
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
         const float mu = (m_ref[ht] == -INFINITY) ? 0.f : m_ref[ht];
@@ -347,66 +527,49 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_kernel(const Params p) {
           }
         l_part[ht] += ls;
       }
-
-      // ---- O^T += V^T P^T ----
-      // V^T fragment (MFMA A operand): lane holds V[rows 4g..4g+3 and
-      // 16+4g..16+4g+3][16 dt + li], via two transposing LDS reads.
-      // this lane addresses row 4g + li/4 (and that + 16), bytes 8 (li & 3) + 32 dt
-      const uint32_t vrow = opaque(tb + (4 * g + (li >> 2)) * kRowStride + 8 * (li & 3));
-      constexpr int VPF = 3;
-      bf16x4 vf[VPF + 1][2];
-#pragma unroll
-      for (int dt = 0; dt < 32 + VPF; ++dt) {
-        if (dt < 32) {
-          vf[dt % (VPF + 1)][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(uintptr_t)(vrow + 32 * dt));
-          vf[dt % (VPF + 1)][1] =
-              __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(uintptr_t)(vrow + 16 * kRowStride + 32 * dt));
-        }
-        if (dt >= VPF) {
-          const int d = dt - VPF;
-          const bf16x4 v0 = vf[d % (VPF + 1)][0], v1 = vf[d % (VPF + 1)][1];
-          const bf16x8 a = bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-#pragma unroll
-          for (int ht = 0; ht < NHT; ++ht) acc[ht][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pk[ht], acc[ht][d], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      asm volatile("s_nop 4" ::: "memory");  // P written by VALU just above, read by MFMA below
+      run_steps(Int<0>{}, Int<1>{}, Int<1>{});
     }
   }
-  (void)n_total;
 
   // ---- finalise: fold the sink, normalise, store ----
+  // o goes through LDS (row pitch kRowStride) so that each global store
+  // writes one whole 1 KiB row per instruction.
+  if constexpr (NW > 1) lds_barrier();  // all waves are done with the tiles
+  const uint32_t ob = lds_addr(&sm.tile[0][0][0]) + (uint32_t)w * 16 * kRowStride;
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht) {
-    float lsum = l_part[ht];
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
+    const float lsum = row4_sum(l_part[ht]);
     const int head = head_base + ht * 16 + li;
-    const bool hv = head < p.H;
-    const float sk = (p.sink != nullptr && hv) ? p.sink[head] : -INFINITY;
-    const bool has_sink = !(sk == -INFINITY);
     float oscale, lse_v;
-    if (lsum == 0.f) {  // no valid slot carried any mass
+    if (lsum == 0.f) {  // no valid slot carried any mass: lse is the sink itself (or -inf)
       oscale = 0.f;
-      lse_v = sk;
+      lse_v = has_sink[ht] ? p.sink[head] : -INFINITY;
     } else {
       const float mu = m_ref[ht];
-      const float s2 = sk * kLog2e;
-      const float mf = has_sink ? fmaxf(mu, s2) : mu;
+      const float mf = has_sink[ht] ? __builtin_fmaxf(mu, sink_l2[ht]) : mu;
       const float a = __builtin_amdgcn_exp2f(mu - mf);
-      const float lf = lsum * a + (has_sink ? __builtin_amdgcn_exp2f(s2 - mf) : 0.f);
+      const float lf = lsum * a + (has_sink[ht] ? __builtin_amdgcn_exp2f(sink_l2[ht] - mf) : 0.f);
       oscale = a / lf;
       lse_v = (mf + __builtin_amdgcn_logf(lf)) * kLn2;
     }
-    if (hv) {
-      uint16_t* orow = p.out + ((size_t)t * p.H + head) * kD + 4 * g;
+    if (g == 0 && head < p.H) p.lse[(size_t)t * p.H + head] = lse_v;
+    // lane (g, li) holds o[head li][16 dt + 4g .. +4): write it to LDS row li
 #pragma unroll
-      for (int dt = 0; dt < 32; ++dt) {
-        const f32x4 o = acc[ht][dt] * oscale;
-        *(bf16x4*)(orow + 16 * dt) = bf16x4{(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
-      }
-      if (g == 0) p.lse[(size_t)t * p.H + head] = lse_v;
+    for (int dt = 0; dt < 32; ++dt) {
+      const f32x4 o = acc[ht][dt] * oscale;
+      const bf16x4 ob4 = bf16x4{(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+      *(LDS_AS bf16x4*)(uintptr_t)(ob + li * kRowStride + 32 * dt + 8 * g) = ob4;
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // row r of this wave's 16: lane L stores bytes [16 L, 16 L + 16)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int hr = head_base + ht * 16 + r;
+      const u32x4 val = *(LDS_AS const u32x4*)(uintptr_t)(ob + r * kRowStride + 16 * lane);
+      if (hr < p.H) *(u32x4*)(p.out + ((size_t)t * p.H + hr) * kD + 8 * lane) = val;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
 }
 
@@ -421,7 +584,7 @@ struct Variant {
 Variant pick_variant(int64_t H) {
   if (H <= 16) return {1, 1, "smla_fwd_kernel<1, 1, 2>"};
   const int64_t waves = (H + 31) / 32;
-  if (waves <= 1) return {2, 1, "smla_fwd_kernel<2, 1, 2>"};
+  if (waves <= 1) return {2, 1, "smla_fwd_kernel<2, 1, 3>"};
   if (waves <= 2) return {2, 2, "smla_fwd_kernel<2, 2, 3>"};
   return {2, 4, "smla_fwd_kernel<2, 4, 3>"};
 }
@@ -478,7 +641,7 @@ extern "C" int sparse_mla_prefill(const void* q, const void* kv, const int32_t* 
   hipStream_t s = (hipStream_t)stream;
   hipError_t err;
   if (var.nht == 1) err = launch<1, 1, 2>(p, blocks, s);
-  else if (var.nw == 1) err = launch<2, 1, 2>(p, blocks, s);
+  else if (var.nw == 1) err = launch<2, 1, 3>(p, blocks, s);
   else if (var.nw == 2) err = launch<2, 2, 3>(p, blocks, s);
   else err = launch<2, 4, 3>(p, blocks, s);
   return err == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
