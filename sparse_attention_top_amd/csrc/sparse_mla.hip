@@ -41,7 +41,7 @@ namespace {
 
 constexpr int kD = SPARSE_MLA_HEAD_DIM;  // 512
 constexpr int kRowBytes = kD * 2;        // one bf16 row = 1 KiB
-constexpr int kRowStride = kRowBytes + 16;  // LDS row pitch: 16 B of padding spreads rows over the banks
+constexpr int kRowStride = kRowBytes + 32;  // LDS row pitch: 32 B of padding keeps both the K and the transposing V fragment reads free of bank conflicts (measured fastest of the pitches and swizzles tried)
 constexpr int kBK = 32;                  // valid slots per tile
 constexpr int kListCap = 2048;           // raw top-k entries compacted per segment
 constexpr int kNumXcd = 8;               // MI355X: 8 XCDs, workgroups dispatched round-robin
@@ -310,10 +310,11 @@ __device__ __forceinline__ float row4_sum(float x) {
 
 // Iteration j runs S(j), its softmax, then P.V(j) on ring buffer j % NBUF,
 // while tiles j+1 .. j+NBUF-1 land; the rows of tile j+NBUF-1 are issued
-// spread over the compute steps of iteration j (a burst would stall the wave
-// at issue until the memory pipeline drains).
+// spread over the S steps of iteration j (a burst would stall the wave at
+// issue until the memory pipeline drains).
 template <int NHT, int NW, int NBUF>
-__global__ __launch_bounds__(NW * 64) void smla_fwd_kernel(const Params p) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NHT == 1 ? 2 : 1))) void smla_fwd_kernel(
+    const Params p) {
   static_assert(NBUF == 2 || NBUF == 3, "ring of 2 or 3 tiles");
   constexpr int AHEAD = NBUF - 1;  // tiles gathered ahead of the one being computed
   __shared__ __attribute__((aligned(16))) Smem<NW, NBUF> sm;
@@ -410,10 +411,9 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_kernel(const Params p) {
 
       // 16 steps; step k = S k-step k (2 K reads, 2*NHT MFMAs) and P.V d-tiles 2k, 2k+1
       // (4 transposing reads, 2*NHT MFMAs), reads issued one step ahead.
-      auto run_steps = [&](auto s_flag, auto pv_flag, auto part) {
+      auto run_steps = [&](auto s_flag, auto pv_flag) {
         constexpr bool DS = decltype(s_flag)::value != 0;
         constexpr bool DV = decltype(pv_flag)::value != 0;
-        constexpr int PART = decltype(part)::value;  // which 16 of the gather's 32 steps
         constexpr int R = (DS ? 2 : 0) + (DV ? 4 : 0);  // LDS reads per step
         u32x4 kf[2][2];
         u32x2 vf[2][4];
@@ -459,11 +459,14 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_kernel(const Params p) {
                 acc[ht][2 * k + e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pk[ht], acc[ht][2 * k + e], 0, 0, 0);
             }
           }
-          is.template step<PART * 16 + k, 32>(lane);
+          // the gather goes with the S steps, where the MFMA accumulation
+          // chains leave the wave idle anyway; an LDS-DMA instruction can
+          // stall at issue for tens of cycles
+          if constexpr (DS) is.template step<k, 16>(lane);
           __builtin_amdgcn_sched_barrier(0);
         });
       };
-      run_steps(Int<1>{}, Int<0>{}, Int<0>{});
+      run_steps(Int<1>{}, Int<0>{});
 
       // ---- online softmax of tile j (base 2, lazy reference max) ----
       mfma_vgpr_drain<NHT>(s);
@@ -528,7 +531,7 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_kernel(const Params p) {
         l_part[ht] += ls;
       }
       asm volatile("s_nop 4" ::: "memory");  // P written by VALU just above, read by MFMA below
-      run_steps(Int<0>{}, Int<1>{}, Int<1>{});
+      run_steps(Int<0>{}, Int<1>{});
     }
   }
 
@@ -583,10 +586,9 @@ struct Variant {
 // LDS feeds two MFMAs), up to four waves (128 heads) per workgroup.
 Variant pick_variant(int64_t H) {
   if (H <= 16) return {1, 1, "smla_fwd_kernel<1, 1, 2>"};
-  const int64_t waves = (H + 31) / 32;
-  if (waves <= 1) return {2, 1, "smla_fwd_kernel<2, 1, 3>"};
-  if (waves <= 2) return {2, 2, "smla_fwd_kernel<2, 2, 3>"};
-  return {2, 4, "smla_fwd_kernel<2, 4, 3>"};
+  if (H <= 32) return {2, 1, "smla_fwd_kernel<2, 1, 3>"};
+  if (H <= 64) return {2, 2, "smla_fwd_kernel<2, 2, 3>"};
+  return {1, 4, "smla_fwd_kernel<1, 4, 2>"};
 }
 
 template <int NHT, int NW, int NBUF>
@@ -640,10 +642,10 @@ extern "C" int sparse_mla_prefill(const void* q, const void* kv, const int32_t* 
   const int blocks = (int)(T * head_groups);
   hipStream_t s = (hipStream_t)stream;
   hipError_t err;
-  if (var.nht == 1) err = launch<1, 1, 2>(p, blocks, s);
+  if (var.nht == 1 && var.nw == 1) err = launch<1, 1, 2>(p, blocks, s);
+  else if (var.nht == 1) err = launch<1, 4, 2>(p, blocks, s);
   else if (var.nw == 1) err = launch<2, 1, 3>(p, blocks, s);
-  else if (var.nw == 2) err = launch<2, 2, 3>(p, blocks, s);
-  else err = launch<2, 4, 3>(p, blocks, s);
+  else err = launch<2, 2, 3>(p, blocks, s);
   return err == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
 }
 
