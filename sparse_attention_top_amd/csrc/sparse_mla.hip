@@ -141,6 +141,17 @@ __device__ __forceinline__ void mfma_vgpr_drain(f32x4 (&c)[2][N]) {
     for (int j = 0; j < N; ++j) asm volatile("" : "+v"(c[i][j]));
 }
 
+template <int N>
+__device__ __forceinline__ void mfma_vgpr_drain2(f32x4 (&c)[2][2][N]) {
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < N; ++j) asm volatile("" : "+v"(c[i][h][j]));
+}
+
 template <int I>
 struct Int {
   static constexpr int value = I;
@@ -315,7 +326,8 @@ __device__ __forceinline__ float row4_sum(float x) {
 template <int NHT, int NW, int NBUF>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NHT == 1 ? 2 : 1))) void smla_fwd_kernel(
     const Params p) {
-  static_assert(NBUF == 2 || NBUF == 3, "ring of 2 or 3 tiles");
+  static_assert(NBUF >= 2 && NBUF <= 4, "ring of 2 to 4 tiles");
+  static_assert(NBUF * kBK >= NW * 16, "the output staging needs 16 LDS rows per wave");
   constexpr int AHEAD = NBUF - 1;  // tiles gathered ahead of the one being computed
   __shared__ __attribute__((aligned(16))) Smem<NW, NBUF> sm;
 
@@ -407,69 +419,47 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NHT == 
       // 4g + li/4 (and that + 16), bytes 8 (li & 3) + 32 dt.
       const uint32_t vrow = opaque(tb_v + (4 * g + (li >> 2)) * kRowStride + 8 * (li & 3));
 
+      // ---- S^T = K Q^T ----
+      // K fragment (MFMA A operand): lane holds K[slot sh*16 + li][32k + 8g .. +8),
+      // read KPF k-steps ahead. Even and odd k-steps accumulate into separate
+      // registers (2*2*NHT independent MFMA chains), summed at the end.
       f32x4 s[2][NHT];
-
-      // 16 steps; step k = S k-step k (2 K reads, 2*NHT MFMAs) and P.V d-tiles 2k, 2k+1
-      // (4 transposing reads, 2*NHT MFMAs), reads issued one step ahead.
-      auto run_steps = [&](auto s_flag, auto pv_flag) {
-        constexpr bool DS = decltype(s_flag)::value != 0;
-        constexpr bool DV = decltype(pv_flag)::value != 0;
-        constexpr int R = (DS ? 2 : 0) + (DV ? 4 : 0);  // LDS reads per step
-        u32x4 kf[2][2];
-        u32x2 vf[2][4];
-        auto issue_reads = [&](auto kc) {
+      {
+        constexpr int KPF = 2;
+        constexpr int KST = KPF + 1;
+        f32x4 sp[2][2][NHT];  // [k parity][half][head tile]
+        u32x4 kf[KST][2];
+        auto kread = [&](auto kc) {
           constexpr int k = decltype(kc)::value;
-          constexpr int b = k & 1;
-          if constexpr (DS) {
-            kf[b][0] = ds_read_b128<64 * k>(krow);
-            kf[b][1] = ds_read_b128<16 * kRowStride + 64 * k>(krow);
-          }
-          if constexpr (DV) {
-            vf[b][0] = ds_read_tr16_b64<64 * k>(vrow);
-            vf[b][1] = ds_read_tr16_b64<16 * kRowStride + 64 * k>(vrow);
-            vf[b][2] = ds_read_tr16_b64<64 * k + 32>(vrow);
-            vf[b][3] = ds_read_tr16_b64<16 * kRowStride + 64 * k + 32>(vrow);
-          }
+          kf[k % KST][0] = ds_read_b128<64 * k>(krow);
+          kf[k % KST][1] = ds_read_b128<16 * kRowStride + 64 * k>(krow);
         };
-        issue_reads(Int<0>{});
+        static_for<0, KPF>([&](auto kc) { kread(kc); });
         static_for<0, 16>([&](auto kc) {
           constexpr int k = decltype(kc)::value;
-          constexpr int b = k & 1;
-          if constexpr (k + 1 < 16) issue_reads(Int<k + 1>{});
-          constexpr int younger = (k + 1 < 16) ? R : 0;
-          if constexpr (DS && DV) lds_wait6<younger>(kf[b][0], kf[b][1], vf[b][0], vf[b][1], vf[b][2], vf[b][3]);
-          else if constexpr (DS) lds_wait<younger>(kf[b][0], kf[b][1]);
-          else lds_wait4<younger>(vf[b][0], vf[b][1], vf[b][2], vf[b][3]);
-          if constexpr (DS) {
+          if constexpr (k + KPF < 16) kread(Int<k + KPF>{});
+          constexpr int younger = 2 * (15 - k < KPF ? 15 - k : KPF);
+          lds_wait<younger>(kf[k % KST][0], kf[k % KST][1]);
 #pragma unroll
-            for (int sh = 0; sh < 2; ++sh)
+          for (int sh = 0; sh < 2; ++sh)
 #pragma unroll
-              for (int ht = 0; ht < NHT; ++ht) {
-                if constexpr (k == 0) mfma_s_first(s[sh][ht], kf[b][sh], __builtin_bit_cast(u32x4, qf[ht][k]));
-                else mfma_s(s[sh][ht], kf[b][sh], __builtin_bit_cast(u32x4, qf[ht][k]));
-              }
-          }
-          if constexpr (DV) {
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              const bf16x8 a = __builtin_bit_cast(
-                  bf16x8, u32x4{vf[b][2 * e][0], vf[b][2 * e][1], vf[b][2 * e + 1][0], vf[b][2 * e + 1][1]});
-#pragma unroll
-              for (int ht = 0; ht < NHT; ++ht)
-                acc[ht][2 * k + e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pk[ht], acc[ht][2 * k + e], 0, 0, 0);
+            for (int ht = 0; ht < NHT; ++ht) {
+              if constexpr (k < 2) mfma_s_first(sp[k & 1][sh][ht], kf[k % KST][sh], __builtin_bit_cast(u32x4, qf[ht][k]));
+              else mfma_s(sp[k & 1][sh][ht], kf[k % KST][sh], __builtin_bit_cast(u32x4, qf[ht][k]));
             }
-          }
-          // the gather goes with the S steps, where the MFMA accumulation
-          // chains leave the wave idle anyway; an LDS-DMA instruction can
-          // stall at issue for tens of cycles
-          if constexpr (DS) is.template step<k, 16>(lane);
+          // the gather goes with the S steps, where the MFMA chains leave the
+          // wave time to spare; an LDS-DMA instruction can stall at issue for
+          // tens of cycles
           __builtin_amdgcn_sched_barrier(0);
         });
-      };
-      run_steps(Int<1>{}, Int<0>{});
+        mfma_vgpr_drain2<NHT>(sp);
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+          for (int ht = 0; ht < NHT; ++ht) s[sh][ht] = sp[0][sh][ht] + sp[1][sh][ht];
+      }
 
       // ---- online softmax of tile j (base 2, lazy reference max) ----
-      mfma_vgpr_drain<NHT>(s);
       const int cnt = tile_rows(j, n);
       float x[NHT][2][4];
       bool need = false;
@@ -530,8 +520,36 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NHT == 
           }
         l_part[ht] += ls;
       }
+      // ---- O^T += V^T P^T ----
+      // V^T fragment (MFMA A operand): two transposing reads give lane
+      // V[4g .. 4g+3 and 16+4g .. 16+4g+3][16 dt + li] (this lane addresses
+      // row 4g + li/4 and that + 16, bytes 8 (li & 3) + 32 dt); VPF d-tiles
+      // in flight.
+      is.all(lane);
       asm volatile("s_nop 4" ::: "memory");  // P written by VALU just above, read by MFMA below
-      run_steps(Int<0>{}, Int<1>{});
+      {
+        constexpr int VPF = 5;
+        constexpr int VST = VPF + 1;
+        u32x2 vf[VST][2];
+        auto vread = [&](auto dc) {
+          constexpr int dt = decltype(dc)::value;
+          vf[dt % VST][0] = ds_read_tr16_b64<32 * dt>(vrow);
+          vf[dt % VST][1] = ds_read_tr16_b64<16 * kRowStride + 32 * dt>(vrow);
+        };
+        static_for<0, VPF>([&](auto dc) { vread(dc); });
+        static_for<0, 32>([&](auto dc) {
+          constexpr int dt = decltype(dc)::value;
+          if constexpr (dt + VPF < 32) vread(Int<dt + VPF>{});
+          constexpr int younger = 2 * (31 - dt < VPF ? 31 - dt : VPF);
+          lds_wait<younger>(vf[dt % VST][0], vf[dt % VST][1]);
+          const bf16x8 a = __builtin_bit_cast(
+              bf16x8, u32x4{vf[dt % VST][0][0], vf[dt % VST][0][1], vf[dt % VST][1][0], vf[dt % VST][1][1]});
+#pragma unroll
+          for (int ht = 0; ht < NHT; ++ht)
+            acc[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pk[ht], acc[ht][dt], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      }
     }
   }
 
@@ -576,6 +594,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NHT == 
   }
 }
 
+
 struct Variant {
   int nht, nw;
   const char* name;
@@ -586,9 +605,9 @@ struct Variant {
 // LDS feeds two MFMAs), up to four waves (128 heads) per workgroup.
 Variant pick_variant(int64_t H) {
   if (H <= 16) return {1, 1, "smla_fwd_kernel<1, 1, 2>"};
-  if (H <= 32) return {2, 1, "smla_fwd_kernel<2, 1, 3>"};
-  if (H <= 64) return {2, 2, "smla_fwd_kernel<2, 2, 3>"};
-  return {1, 4, "smla_fwd_kernel<1, 4, 2>"};
+  if (H <= 32) return {1, 2, "smla_fwd_kernel<1, 2, 2>"};
+  if (H <= 64) return {1, 4, "smla_fwd_kernel<1, 4, 2>"};
+  return {1, 8, "smla_fwd_kernel<1, 8, 4>"};
 }
 
 template <int NHT, int NW, int NBUF>
@@ -642,10 +661,10 @@ extern "C" int sparse_mla_prefill(const void* q, const void* kv, const int32_t* 
   const int blocks = (int)(T * head_groups);
   hipStream_t s = (hipStream_t)stream;
   hipError_t err;
-  if (var.nht == 1 && var.nw == 1) err = launch<1, 1, 2>(p, blocks, s);
-  else if (var.nht == 1) err = launch<1, 4, 2>(p, blocks, s);
-  else if (var.nw == 1) err = launch<2, 1, 3>(p, blocks, s);
-  else err = launch<2, 2, 3>(p, blocks, s);
+  if (var.nw == 1) err = launch<1, 1, 2>(p, blocks, s);
+  else if (var.nw == 2) err = launch<1, 2, 2>(p, blocks, s);
+  else if (var.nw == 4) err = launch<1, 4, 2>(p, blocks, s);
+  else err = launch<1, 8, 4>(p, blocks, s);
   return err == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
 }
 
