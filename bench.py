@@ -125,7 +125,7 @@ def measure(name: str, steps: int, warmup: int):
     wall, mean_ms, med_ms = time_gpu(run, steps, warmup, stream)
     alg = algorithmic(inp)
     return inp, alg, {"wall_s": wall, "ms_per_call": wall * 1e3 / steps, "kernel_ms_mean": mean_ms,
-                      "kernel_ms_median": med_ms, "kernel": kernel_name(inp["H"])}
+                      "kernel_ms_median": med_ms, "kernel": kernel_name(inp["H"], inp["topk_n"])}
 
 
 def roofline(alg, t, kernel, workload, bound):

@@ -79,11 +79,11 @@ int sparse_mla_prefill(const void* q, const void* kv, const int32_t* topk_indice
 const char* sparse_mla_status_string(int status);
 
 /*
- * Name of the kernel that sparse_mla_prefill launches for H heads (static
- * storage, as it appears in profiler traces), or NULL when H < 1. Pure host
- * function: no device access.
+ * Name of the kernel that sparse_mla_prefill launches for H heads and top-k
+ * rows of `topk` entries (static storage, as it appears in profiler traces),
+ * or NULL when H < 1 or topk < 0. Pure host function: no device access.
  */
-const char* sparse_mla_kernel_name(int64_t H);
+const char* sparse_mla_kernel_name(int64_t H, int64_t topk);
 
 /* Library version, major * 10000 + minor * 100 + patch. */
 int sparse_mla_version(void);

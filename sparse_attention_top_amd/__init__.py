@@ -79,9 +79,10 @@ def sparse_mla_prefill(q, kv, topk_indices, attn_sink=None, scale=None, out=None
     return out, lse
 
 
-def kernel_name(H: int) -> str:
-    """Name of the kernel launched for H heads (as profilers show it)."""
-    name = _lib.load().sparse_mla_kernel_name(int(H))
+def kernel_name(H: int, topk: int) -> str:
+    """Name of the kernel launched for H heads and top-k rows of `topk` entries
+    (as profilers show it)."""
+    name = _lib.load().sparse_mla_kernel_name(int(H), int(topk))
     if name is None:
-        raise ValueError("H must be >= 1")
+        raise ValueError("need H >= 1 and topk >= 0")
     return name.decode()

@@ -152,6 +152,19 @@ __device__ __forceinline__ void mfma_vgpr_drain2(f32x4 (&c)[2][2][N]) {
       for (int j = 0; j < N; ++j) asm volatile("" : "+v"(c[i][h][j]));
 }
 
+// P.V MFMA accumulating into AGPRs (the constraint keeps the 128-register O
+// accumulator in the AGPR file). Accumulating into the same registers is
+// interlocked by the hardware; VALU reads of the result must first pass
+// mfma_agpr_drain().
+__device__ __forceinline__ void mfma_acc(f32x4& c, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_agpr_drain(f32x4 (&c)[32]) {
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < 32; ++i) asm volatile("" : "+a"(c[i]));
+}
+
 template <int I>
 struct Int {
   static constexpr int value = I;
@@ -256,11 +269,10 @@ __device__ __forceinline__ int tile_dma(int i, int n, int w) {
   return min(RPW, max(0, tile_rows(i, n) - w * RPW));
 }
 
-// The gather of one tile, issued row by row so that it can be spread over a
-// compute phase: one LDS-DMA instruction per row (lane L moves bytes
-// [16 L, 16 L + 16) of the 1 KiB row); rows past the tile's count are
-// zero-filled. Wave w moves rows [w RPW, (w+1) RPW).
-template <int NW, int NBUF>
+// The gather of one tile into an LDS ring buffer: one LDS-DMA instruction per
+// row (lane L moves bytes [16 L, 16 L + 16) of the 1 KiB row); rows past the
+// tile's count are zero-filled. Wave w moves rows [w RPW, (w+1) RPW).
+template <int NW>
 struct TileIssue {
   static constexpr int RPW = kBK / NW;
   const uint16_t* kv;
@@ -270,15 +282,16 @@ struct TileIssue {
   int my;         // lane L < RPW: list entry of row r0 + L
   bool active;
 
-  __device__ __forceinline__ void init(int i, int n, int ntiles, Smem<NW, NBUF>& sm, const uint16_t* kv_, int lane,
-                                       int w) {
+  // Tile i of the n-entry LDS list `list`, into the ring buffer at LDS address buf.
+  __device__ __forceinline__ void init(const int32_t* list, int i, int n, bool act, uint32_t buf, const uint16_t* kv_,
+                                       int lane, int w) {
     kv = kv_;
-    active = i < ntiles;
+    active = act;
     r0 = w * RPW;
-    cnt = active ? tile_rows(i, n) : 0;
-    dst0 = lds_addr(&sm.tile[active ? i % NBUF : 0][r0][0]);
+    cnt = act ? tile_rows(i, n) : 0;
+    dst0 = buf + r0 * kRowStride;
     int e = 0;
-    if (active && lane < RPW && r0 + lane < cnt) e = sm.list[i * kBK + r0 + lane];
+    if (act && lane < RPW && r0 + lane < cnt) e = list[i * kBK + r0 + lane];
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(e));
     my = e;
   }
@@ -294,15 +307,11 @@ struct TileIssue {
       *(LDS_AS u32x4*)(uintptr_t)(dst + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
     }
   }
-  // Rows that go with step K of NS steps.
-  template <int K, int NS>
-  __device__ __forceinline__ void step(int lane) const {
-    constexpr int lo = K * RPW / NS, hi = (K + 1) * RPW / NS;
-    static_for<lo, hi>([&](auto rc) { row<decltype(rc)::value>(lane); });
-  }
   __device__ __forceinline__ void all(int lane) const {
     static_for<0, RPW>([&](auto rc) { row<decltype(rc)::value>(lane); });
   }
+  // LDS-DMA instructions all() issues
+  __device__ __forceinline__ int count() const { return active ? min(RPW, max(0, cnt - r0)) : 0; }
 };
 
 // Max over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48).
@@ -319,13 +328,172 @@ __device__ __forceinline__ float row4_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Iteration j runs S(j), its softmax, then P.V(j) on ring buffer j % NBUF,
-// while tiles j+1 .. j+NBUF-1 land; the rows of tile j+NBUF-1 are issued
-// spread over the S steps of iteration j (a burst would stall the wave at
-// issue until the memory pipeline drains).
-template <int NHT, int NW, int NBUF>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NHT == 1 ? 2 : 1))) void smla_fwd_kernel(
-    const Params p) {
+// ---- per-tile compute of one wave (16 heads x 32 slots) ----
+// Lane (g, li) owns head li of the wave's 16; LDS addresses are those of the
+// tile's buffer.
+
+// K fragment (MFMA A operand of S^T = K Q^T): lane holds K[slot sh*16 + li][32k + 8g .. +8).
+__device__ __forceinline__ uint32_t k_frag_addr(uint32_t tile, int g, int li) {
+  return opaque(tile + li * kRowStride + 16 * g);
+}
+// V^T fragment (MFMA A operand of O^T += V^T P^T): two transposing reads give
+// lane V[4g .. 4g+3 and 16+4g .. 16+4g+3][16 dt + li]; this lane addresses row
+// 4g + li/4 (and that + 16), bytes 8 (li & 3) + 32 dt.
+__device__ __forceinline__ uint32_t v_frag_addr(uint32_t tile, int g, int li) {
+  return opaque(tile + (4 * g + (li >> 2)) * kRowStride + 8 * (li & 3));
+}
+
+// S^T = K Q^T: s[sh] holds S^T[slot sh*16 + 4g + i][head li]. K fragments are
+// read KPF k-steps ahead; with CH = 2, even and odd k-steps accumulate into
+// separate registers (four independent MFMA chains), summed at the end.
+template <int KPF, int CH>
+__device__ __forceinline__ void tile_s(uint32_t krow, const bf16x8 (&qf)[16], f32x4 (&s)[2]) {
+  static_assert(CH == 1 || CH == 2, "one or two chains per half");
+  constexpr int KST = KPF + 1;
+  f32x4 sp[2][2][1];  // [k parity][half][1]
+  u32x4 kf[KST][2];
+  auto kread = [&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    kf[k % KST][0] = ds_read_b128<64 * k>(krow);
+    kf[k % KST][1] = ds_read_b128<16 * kRowStride + 64 * k>(krow);
+  };
+  static_for<0, KPF>([&](auto kc) { kread(kc); });
+  static_for<0, 16>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    constexpr int c = CH == 2 ? (k & 1) : 0;
+    if constexpr (k + KPF < 16) kread(Int<k + KPF>{});
+    constexpr int younger = 2 * (15 - k < KPF ? 15 - k : KPF);
+    lds_wait<younger>(kf[k % KST][0], kf[k % KST][1]);
+#pragma unroll
+    for (int sh = 0; sh < 2; ++sh) {
+      if constexpr (k < CH) mfma_s_first(sp[c][sh][0], kf[k % KST][sh], __builtin_bit_cast(u32x4, qf[k]));
+      else mfma_s(sp[c][sh][0], kf[k % KST][sh], __builtin_bit_cast(u32x4, qf[k]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  if constexpr (CH == 2) {
+    mfma_vgpr_drain2<1>(sp);
+#pragma unroll
+    for (int sh = 0; sh < 2; ++sh) s[sh] = sp[0][sh][0] + sp[1][sh][0];
+  } else {
+    f32x4 (&s0)[2][1] = sp[0];
+    mfma_vgpr_drain<1>(s0);
+#pragma unroll
+    for (int sh = 0; sh < 2; ++sh) s[sh] = sp[0][sh][0];
+  }
+}
+
+// Online softmax of one tile in base 2 with a lazy reference max: slots >= cnt
+// are masked; P is rounded to bf16 into pk, already in the B-operand layout of
+// the P.V MFMA (the C layout of S^T). When the tile's max exceeds the
+// reference by more than kLazyTau, the reference moves and what earlier tiles
+// accumulated is rescaled.
+__device__ __forceinline__ void tile_softmax(const f32x4 (&s)[2], int cnt, float scale_log2, int g, float& m_ref,
+                                             float& l_part, f32x4 (&acc)[32], bf16x8& pk) {
+  float x[2][4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int slot = sh * 16 + 4 * g + i;
+      const float xv = slot < cnt ? s[sh][i] * scale_log2 : -INFINITY;
+      x[sh][i] = xv;
+      mx = __builtin_fmaxf(mx, xv);
+    }
+  mx = row4_max(mx);
+  if (__ballot(mx > m_ref + kLazyTau) != 0ull) {
+    const float m_new = __builtin_fmaxf(m_ref, mx);
+    if (__ballot(m_ref != -INFINITY) != 0ull) {
+      // rescale what earlier tiles accumulated (lanes whose reference is
+      // still -inf have nothing accumulated: alpha = 0 keeps it 0)
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      l_part *= alpha;
+      // in place, one accumulator register at a time (the accumulators live
+      // in AGPRs; a vector multiply would stage them all in VGPRs)
+#pragma unroll
+      for (int dt = 0; dt < 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float e = acc[dt][i];
+          float tmp;
+          asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                       : "+a"(e), "=&v"(tmp)
+                       : "v"(alpha));
+          acc[dt][i] = e;
+        }
+    }
+    m_ref = m_new;
+  }
+  const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
+  float ls = 0.f;
+#pragma unroll
+  for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pv = __builtin_amdgcn_exp2f(x[sh][i] - mu);
+      ls += pv;
+      pk[sh * 4 + i] = (__bf16)pv;
+    }
+  l_part += ls;
+}
+
+// O^T += V^T P^T over the 32 d-tiles, VPF d-tiles of V^T fragments in flight.
+__device__ __forceinline__ void tile_pv(uint32_t vrow, const bf16x8& pk, f32x4 (&acc)[32]) {
+  asm volatile("s_nop 4" ::: "memory");  // P written by VALU, read by MFMA below
+  constexpr int VPF = 5;
+  constexpr int VST = VPF + 1;
+  u32x2 vf[VST][2];
+  auto vread = [&](auto dc) {
+    constexpr int dt = decltype(dc)::value;
+    vf[dt % VST][0] = ds_read_tr16_b64<32 * dt>(vrow);
+    vf[dt % VST][1] = ds_read_tr16_b64<16 * kRowStride + 32 * dt>(vrow);
+  };
+  static_for<0, VPF>([&](auto dc) { vread(dc); });
+  static_for<0, 32>([&](auto dc) {
+    constexpr int dt = decltype(dc)::value;
+    if constexpr (dt + VPF < 32) vread(Int<dt + VPF>{});
+    constexpr int younger = 2 * (31 - dt < VPF ? 31 - dt : VPF);
+    lds_wait<younger>(vf[dt % VST][0], vf[dt % VST][1]);
+    const bf16x8 a = __builtin_bit_cast(
+        bf16x8, u32x4{vf[dt % VST][0][0], vf[dt % VST][0][1], vf[dt % VST][1][0], vf[dt % VST][1][1]});
+    mfma_acc(acc[dt], a, pk);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
+// Sink and normalisation of one head: o = acc * oscale, lse in natural log.
+// With no mass on any valid slot, o = 0 and lse is the sink itself (or -inf).
+struct HeadEnd {
+  float oscale, lse;
+};
+__device__ __forceinline__ HeadEnd head_end(float l_part, float m_ref, float sink, bool has_sink, float sink_l2) {
+  const float lsum = row4_sum(l_part);
+  if (lsum == 0.f) return {0.f, has_sink ? sink : -INFINITY};
+  const float mf = has_sink ? __builtin_fmaxf(m_ref, sink_l2) : m_ref;
+  const float a = __builtin_amdgcn_exp2f(m_ref - mf);
+  const float lf = lsum * a + (has_sink ? __builtin_amdgcn_exp2f(sink_l2 - mf) : 0.f);
+  return {a / lf, (mf + __builtin_amdgcn_logf(lf)) * kLn2};
+}
+
+__device__ __forceinline__ void load_q(bf16x8 (&qf)[16], const Params& p, int t, int head, int g) {
+  // Q^T fragments (MFMA B operand of S^T = K Q^T): lane holds q[t, head, 32k + 8g .. +8)
+  if (head < p.H) {
+    const bf16x8* src = (const bf16x8*)(p.q + ((size_t)t * p.H + head) * kD + 8 * g);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) qf[k] = src[4 * k];
+  } else {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) qf[k] = bf16x8{};
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One workgroup per (token, group of 16 NW heads). Iteration j computes tile j
+// from ring buffer j % NBUF while tiles j+1 .. j+NBUF-1 land; the rows of tile
+// j+NBUF-1 are issued in one burst before P.V(j).
+template <int NW, int NBUF>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void smla_fwd_kernel(const Params p) {
   static_assert(NBUF >= 2 && NBUF <= 4, "ring of 2 to 4 tiles");
   static_assert(NBUF * kBK >= NW * 16, "the output staging needs 16 LDS rows per wave");
   constexpr int AHEAD = NBUF - 1;  // tiles gathered ahead of the one being computed
@@ -339,46 +507,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NHT == 
   const int v = xcd_remap(blockIdx.x, gridDim.x);
   const int t = p.T - 1 - v / p.head_groups;  // latest (heaviest) tokens first
   const int hg = v % p.head_groups;
-  const int head_base = (hg * NW + w) * (NHT * 16);
+  const int head_base = (hg * NW + w) * 16;
+  const int head = head_base + li;
 
-  // Per-lane head state: lane (g, li) owns head head_base + 16 ht + li.
-  float sink_l2[NHT];  // sink * log2(e), or -inf
-  bool has_sink[NHT];
+  f32x4 acc[32];
 #pragma unroll
-  for (int ht = 0; ht < NHT; ++ht) {
-    const int head = head_base + ht * 16 + li;
-    const float sk = (p.sink != nullptr && head < p.H) ? p.sink[head] : -INFINITY;
-    has_sink[ht] = !(sk == -INFINITY);
-    sink_l2[ht] = sk * kLog2e;
-  }
-
-  f32x4 acc[NHT][32];
-#pragma unroll
-  for (int ht = 0; ht < NHT; ++ht)
-#pragma unroll
-    for (int dt = 0; dt < 32; ++dt) acc[ht][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref[NHT], l_part[NHT];
-#pragma unroll
-  for (int ht = 0; ht < NHT; ++ht) {
-    m_ref[ht] = -INFINITY;
-    l_part[ht] = 0.f;
-  }
-  // Q^T fragments (MFMA B operand of S^T = K Q^T): lane holds q[t, head, 32k + 8g .. +8).
-  // Loaded first, so that their latency overlaps the top-k row's.
-  bf16x8 qf[NHT][16];
-#pragma unroll
-  for (int ht = 0; ht < NHT; ++ht) {
-    const int head = head_base + ht * 16 + li;
-    if (head < p.H) {
-      const bf16x8* src = (const bf16x8*)(p.q + ((size_t)t * p.H + head) * kD + 8 * g);
-#pragma unroll
-      for (int k = 0; k < 16; ++k) qf[ht][k] = src[4 * k];
-    } else {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) qf[ht][k] = bf16x8{};
-    }
-  }
-  bf16x8 pk[NHT];  // P of the current tile (MFMA B operand of P.V)
+  for (int dt = 0; dt < 32; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY, l_part = 0.f;
+  bf16x8 qf[16];
+  load_q(qf, p, t, head, g);  // first, so that its latency overlaps the top-k row's
+  bf16x8 pk;
 
   const int32_t* trow = p.topk + (size_t)t * p.topk_n;
   for (int seg0 = 0; seg0 < p.topk_n; seg0 += kListCap) {
@@ -387,16 +525,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NHT == 
     const int ntiles = (n + kBK - 1) / kBK;
     if (ntiles == 0) continue;
 
-    // Prologue: the first AHEAD tiles.
-    {
-      TileIssue<NW, NBUF> is;
-      is.init(0, n, ntiles, sm, p.kv, lane, w);
-      is.all(lane);
-    }
 #pragma unroll
-    for (int i = 1; i < AHEAD; ++i) {
-      TileIssue<NW, NBUF> is;
-      is.init(i, n, ntiles, sm, p.kv, lane, w);
+    for (int i = 0; i < AHEAD; ++i) {
+      TileIssue<NW> is;
+      is.init(sm.list, i, n, i < ntiles, lds_addr(&sm.tile[i][0][0]), p.kv, lane, w);
       is.all(lane);
     }
 
@@ -407,212 +539,65 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NHT == 
         if (j + i < ntiles) after += tile_dma<NW>(j + i, n, w);
       wait_vmcnt_le(after);
       if constexpr (NW > 1) lds_barrier();
-      TileIssue<NW, NBUF> is;
-      is.init(j + AHEAD, n, ntiles, sm, p.kv, lane, w);
-
-      const uint32_t tb_s = lds_addr(&sm.tile[j % NBUF][0][0]);
-      const uint32_t tb_v = tb_s;
-      // K fragment (MFMA A operand of S^T = K Q^T): lane holds K[slot sh*16 + li][32k + 8g .. +8).
-      const uint32_t krow = opaque(tb_s + li * kRowStride + 16 * g);
-      // V^T fragment (MFMA A operand of O^T += V^T P^T): two transposing reads give
-      // lane V[4g .. 4g+3 and 16+4g .. 16+4g+3][16 dt + li]; this lane addresses row
-      // 4g + li/4 (and that + 16), bytes 8 (li & 3) + 32 dt.
-      const uint32_t vrow = opaque(tb_v + (4 * g + (li >> 2)) * kRowStride + 8 * (li & 3));
-
-      // ---- S^T = K Q^T ----
-      // K fragment (MFMA A operand): lane holds K[slot sh*16 + li][32k + 8g .. +8),
-      // read KPF k-steps ahead. Even and odd k-steps accumulate into separate
-      // registers (2*2*NHT independent MFMA chains), summed at the end.
-      f32x4 s[2][NHT];
-      {
-        constexpr int KPF = 2;
-        constexpr int KST = KPF + 1;
-        f32x4 sp[2][2][NHT];  // [k parity][half][head tile]
-        u32x4 kf[KST][2];
-        auto kread = [&](auto kc) {
-          constexpr int k = decltype(kc)::value;
-          kf[k % KST][0] = ds_read_b128<64 * k>(krow);
-          kf[k % KST][1] = ds_read_b128<16 * kRowStride + 64 * k>(krow);
-        };
-        static_for<0, KPF>([&](auto kc) { kread(kc); });
-        static_for<0, 16>([&](auto kc) {
-          constexpr int k = decltype(kc)::value;
-          if constexpr (k + KPF < 16) kread(Int<k + KPF>{});
-          constexpr int younger = 2 * (15 - k < KPF ? 15 - k : KPF);
-          lds_wait<younger>(kf[k % KST][0], kf[k % KST][1]);
-#pragma unroll
-          for (int sh = 0; sh < 2; ++sh)
-#pragma unroll
-            for (int ht = 0; ht < NHT; ++ht) {
-              if constexpr (k < 2) mfma_s_first(sp[k & 1][sh][ht], kf[k % KST][sh], __builtin_bit_cast(u32x4, qf[ht][k]));
-              else mfma_s(sp[k & 1][sh][ht], kf[k % KST][sh], __builtin_bit_cast(u32x4, qf[ht][k]));
-            }
-          // the gather goes with the S steps, where the MFMA chains leave the
-          // wave time to spare; an LDS-DMA instruction can stall at issue for
-          // tens of cycles
-          __builtin_amdgcn_sched_barrier(0);
-        });
-        mfma_vgpr_drain2<NHT>(sp);
-#pragma unroll
-        for (int sh = 0; sh < 2; ++sh)
-#pragma unroll
-          for (int ht = 0; ht < NHT; ++ht) s[sh][ht] = sp[0][sh][ht] + sp[1][sh][ht];
-      }
-
-      // ---- online softmax of tile j (base 2, lazy reference max) ----
-      const int cnt = tile_rows(j, n);
-      float x[NHT][2][4];
-      bool need = false;
-      float tmax[NHT];
-#pragma unroll
-      for (int ht = 0; ht < NHT; ++ht) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int sh = 0; sh < 2; ++sh)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int slot = sh * 16 + 4 * g + i;
-            const float xv = slot < cnt ? s[sh][ht][i] * p.scale_log2 : -INFINITY;
-            x[ht][sh][i] = xv;
-            mx = __builtin_fmaxf(mx, xv);
-          }
-        mx = row4_max(mx);
-        tmax[ht] = mx;
-        need |= mx > m_ref[ht] + kLazyTau;
-      }
-      if (__ballot(need) != 0ull) {
-#pragma unroll
-        for (int ht = 0; ht < NHT; ++ht) {
-          const float m_new = __builtin_fmaxf(m_ref[ht], tmax[ht]);
-          if (__ballot(m_ref[ht] != -INFINITY) != 0ull) {
-            // rescale what earlier tiles accumulated (lanes whose reference
-            // is still -inf have nothing accumulated: alpha = 0 keeps it 0)
-            const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref[ht] - m_new);
-            l_part[ht] *= alpha;
-            // in place, one accumulator register at a time (the accumulators
-            // live in AGPRs; a vector multiply would stage them all in VGPRs)
-#pragma unroll
-            for (int dt = 0; dt < 32; ++dt)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                float e = acc[ht][dt][i];
-                float tmp;
-                asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                             : "+a"(e), "=&v"(tmp)
-                             : "v"(alpha));
-                acc[ht][dt][i] = e;
-              }
-          }
-          m_ref[ht] = m_new;
-        }
-      }
-#pragma unroll
-      for (int ht = 0; ht < NHT; ++ht) {
-        const float mu = (m_ref[ht] == -INFINITY) ? 0.f : m_ref[ht];
-        float ls = 0.f;
-#pragma unroll
-        for (int sh = 0; sh < 2; ++sh)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float pv = __builtin_amdgcn_exp2f(x[ht][sh][i] - mu);
-            ls += pv;
-            pk[ht][sh * 4 + i] = (__bf16)pv;
-          }
-        l_part[ht] += ls;
-      }
-      // ---- O^T += V^T P^T ----
-      // V^T fragment (MFMA A operand): two transposing reads give lane
-      // V[4g .. 4g+3 and 16+4g .. 16+4g+3][16 dt + li] (this lane addresses
-      // row 4g + li/4 and that + 16, bytes 8 (li & 3) + 32 dt); VPF d-tiles
-      // in flight.
+      TileIssue<NW> is;
+      is.init(sm.list, j + AHEAD, n, j + AHEAD < ntiles, lds_addr(&sm.tile[(j + AHEAD) % NBUF][0][0]), p.kv, lane,
+              w);
+      const uint32_t tb = lds_addr(&sm.tile[j % NBUF][0][0]);
+      f32x4 s[2];
+      tile_s<2, 2>(k_frag_addr(tb, g, li), qf, s);
+      tile_softmax(s, tile_rows(j, n), p.scale_log2, g, m_ref, l_part, acc, pk);
       is.all(lane);
-      asm volatile("s_nop 4" ::: "memory");  // P written by VALU just above, read by MFMA below
-      {
-        constexpr int VPF = 5;
-        constexpr int VST = VPF + 1;
-        u32x2 vf[VST][2];
-        auto vread = [&](auto dc) {
-          constexpr int dt = decltype(dc)::value;
-          vf[dt % VST][0] = ds_read_tr16_b64<32 * dt>(vrow);
-          vf[dt % VST][1] = ds_read_tr16_b64<16 * kRowStride + 32 * dt>(vrow);
-        };
-        static_for<0, VPF>([&](auto dc) { vread(dc); });
-        static_for<0, 32>([&](auto dc) {
-          constexpr int dt = decltype(dc)::value;
-          if constexpr (dt + VPF < 32) vread(Int<dt + VPF>{});
-          constexpr int younger = 2 * (31 - dt < VPF ? 31 - dt : VPF);
-          lds_wait<younger>(vf[dt % VST][0], vf[dt % VST][1]);
-          const bf16x8 a = __builtin_bit_cast(
-              bf16x8, u32x4{vf[dt % VST][0][0], vf[dt % VST][0][1], vf[dt % VST][1][0], vf[dt % VST][1][1]});
-#pragma unroll
-          for (int ht = 0; ht < NHT; ++ht)
-            acc[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pk[ht], acc[ht][dt], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        });
-      }
+      tile_pv(v_frag_addr(tb, g, li), pk, acc);
     }
   }
 
   // ---- finalise: fold the sink, normalise, store ----
   // o goes through LDS (row pitch kRowStride) so that each global store
-  // writes one whole 1 KiB row per instruction.
+  // writes one whole 1 KiB row per instruction. The sink is read only here,
+  // so that its load latency is not on the way to the first tile.
+  const float sk = (p.sink != nullptr && head < p.H) ? p.sink[head] : -INFINITY;
+  const bool has_sink = !(sk == -INFINITY);
+  const float sink_l2 = sk * kLog2e;
   if constexpr (NW > 1) lds_barrier();  // all waves are done with the tiles
   const uint32_t ob = lds_addr(&sm.tile[0][0][0]) + (uint32_t)w * 16 * kRowStride;
+  mfma_agpr_drain(acc);
+  const HeadEnd he = head_end(l_part, m_ref, sk, has_sink, sink_l2);
+  if (g == 0 && head < p.H) p.lse[(size_t)t * p.H + head] = he.lse;
+  // lane (g, li) holds o[head li][16 dt + 4g .. +4): write it to LDS row li
 #pragma unroll
-  for (int ht = 0; ht < NHT; ++ht) {
-    const float lsum = row4_sum(l_part[ht]);
-    const int head = head_base + ht * 16 + li;
-    float oscale, lse_v;
-    if (lsum == 0.f) {  // no valid slot carried any mass: lse is the sink itself (or -inf)
-      oscale = 0.f;
-      lse_v = has_sink[ht] ? p.sink[head] : -INFINITY;
-    } else {
-      const float mu = m_ref[ht];
-      const float mf = has_sink[ht] ? __builtin_fmaxf(mu, sink_l2[ht]) : mu;
-      const float a = __builtin_amdgcn_exp2f(mu - mf);
-      const float lf = lsum * a + (has_sink[ht] ? __builtin_amdgcn_exp2f(sink_l2[ht] - mf) : 0.f);
-      oscale = a / lf;
-      lse_v = (mf + __builtin_amdgcn_logf(lf)) * kLn2;
-    }
-    if (g == 0 && head < p.H) p.lse[(size_t)t * p.H + head] = lse_v;
-    // lane (g, li) holds o[head li][16 dt + 4g .. +4): write it to LDS row li
+  for (int dt = 0; dt < 32; ++dt) {
+    const f32x4 o = acc[dt] * he.oscale;
+    const bf16x4 ob4 = bf16x4{(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+    *(LDS_AS bf16x4*)(uintptr_t)(ob + li * kRowStride + 32 * dt + 8 * g) = ob4;
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  // row r of this wave's 16: lane L stores bytes [16 L, 16 L + 16)
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt) {
-      const f32x4 o = acc[ht][dt] * oscale;
-      const bf16x4 ob4 = bf16x4{(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
-      *(LDS_AS bf16x4*)(uintptr_t)(ob + li * kRowStride + 32 * dt + 8 * g) = ob4;
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    // row r of this wave's 16: lane L stores bytes [16 L, 16 L + 16)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int hr = head_base + ht * 16 + r;
-      const u32x4 val = *(LDS_AS const u32x4*)(uintptr_t)(ob + r * kRowStride + 16 * lane);
-      if (hr < p.H) *(u32x4*)(p.out + ((size_t)t * p.H + hr) * kD + 8 * lane) = val;
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  for (int r = 0; r < 16; ++r) {
+    const int hr = head_base + r;
+    const u32x4 val = *(LDS_AS const u32x4*)(uintptr_t)(ob + r * kRowStride + 16 * lane);
+    if (hr < p.H) *(u32x4*)(p.out + ((size_t)t * p.H + hr) * kD + 8 * lane) = val;
   }
 }
 
-
 struct Variant {
-  int nht, nw;
+  int nw;
   const char* name;
 };
 
-// Small head counts (H <= 16): one wave per token, one 16-head tile; the
-// gather dominates. More heads: 32 heads per wave (each K/V fragment read from
-// LDS feeds two MFMAs), up to four waves (128 heads) per workgroup.
-Variant pick_variant(int64_t H) {
-  if (H <= 16) return {1, 1, "smla_fwd_kernel<1, 1, 2>"};
-  if (H <= 32) return {1, 2, "smla_fwd_kernel<1, 2, 2>"};
-  if (H <= 64) return {1, 4, "smla_fwd_kernel<1, 4, 2>"};
-  return {1, 8, "smla_fwd_kernel<1, 8, 4>"};
+// One wave per 16 heads. H <= 64: 1 to 4 waves per workgroup, two workgroups
+// per CU. Wider: 8 waves (128 heads) per workgroup, one per CU.
+Variant pick_variant(int64_t H, int64_t topk) {
+  (void)topk;
+  if (H <= 16) return {1, "smla_fwd_kernel<1, 2>"};
+  if (H <= 32) return {2, "smla_fwd_kernel<2, 2>"};
+  if (H <= 64) return {4, "smla_fwd_kernel<4, 2>"};
+  return {8, "smla_fwd_kernel<8, 4>"};
 }
 
-template <int NHT, int NW, int NBUF>
+template <int NW, int NBUF>
 hipError_t launch(const Params& p, int blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((smla_fwd_kernel<NHT, NW, NBUF>), dim3(blocks), dim3(NW * 64), 0, stream, p);
+  hipLaunchKernelGGL((smla_fwd_kernel<NW, NBUF>), dim3(blocks), dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -627,8 +612,8 @@ extern "C" int sparse_mla_prefill(const void* q, const void* kv, const int32_t* 
   if (T > INT32_MAX || H > INT32_MAX || topk > INT32_MAX) return SMLA_ERR_BAD_SIZE;
   if (!isfinite(scale)) return SMLA_ERR_BAD_SCALE;
   if (T == 0) return SMLA_OK;
-  const Variant var = pick_variant(H);
-  const int64_t heads_per_wg = (int64_t)var.nht * 16 * var.nw;
+  const Variant var = pick_variant(H, topk);
+  const int64_t heads_per_wg = (int64_t)16 * var.nw;
   const int64_t head_groups = (H + heads_per_wg - 1) / heads_per_wg;
   if (T * head_groups > INT32_MAX) return SMLA_ERR_BAD_SIZE;
   if (T > INT64_MAX / H / kD || T > INT64_MAX / (topk > 0 ? topk : 1)) return SMLA_ERR_BAD_SIZE;
@@ -658,13 +643,18 @@ extern "C" int sparse_mla_prefill(const void* q, const void* kv, const int32_t* 
   p.topk_n = (int)topk;
   p.head_groups = (int)head_groups;
   p.scale_log2 = scale * kLog2e;
-  const int blocks = (int)(T * head_groups);
+  const int64_t units = T * head_groups;
   hipStream_t s = (hipStream_t)stream;
   hipError_t err;
-  if (var.nw == 1) err = launch<1, 1, 2>(p, blocks, s);
-  else if (var.nw == 2) err = launch<1, 2, 2>(p, blocks, s);
-  else if (var.nw == 4) err = launch<1, 4, 2>(p, blocks, s);
-  else err = launch<1, 8, 4>(p, blocks, s);
+  if (var.nw == 1) {
+    err = launch<1, 2>(p, (int)units, s);
+  } else if (var.nw == 2) {
+    err = launch<2, 2>(p, (int)units, s);
+  } else if (var.nw == 4) {
+    err = launch<4, 2>(p, (int)units, s);
+  } else {
+    err = launch<8, 4>(p, (int)units, s);
+  }
   return err == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
 }
 
@@ -681,9 +671,9 @@ extern "C" const char* sparse_mla_status_string(int status) {
   }
 }
 
-extern "C" const char* sparse_mla_kernel_name(int64_t H) {
-  if (H < 1) return nullptr;
-  return pick_variant(H).name;
+extern "C" const char* sparse_mla_kernel_name(int64_t H, int64_t topk) {
+  if (H < 1 || topk < 0) return nullptr;
+  return pick_variant(H, topk).name;
 }
 
-extern "C" int sparse_mla_version(void) { return 100; }
+extern "C" int sparse_mla_version(void) { return 101; }

@@ -49,9 +49,11 @@ def test_status_strings_and_version():
 
 def test_kernel_names():
     lib = _lib.load()
-    assert lib.sparse_mla_kernel_name(0) is None
-    assert lib.sparse_mla_kernel_name(8) == lib.sparse_mla_kernel_name(16)
-    assert lib.sparse_mla_kernel_name(128).startswith(b"smla_fwd_kernel")
+    assert lib.sparse_mla_kernel_name(0, 64) is None
+    assert lib.sparse_mla_kernel_name(8, -1) is None
+    assert lib.sparse_mla_kernel_name(8, 64) == lib.sparse_mla_kernel_name(16, 64)
+    assert lib.sparse_mla_kernel_name(64, 512).startswith(b"smla_fwd_kernel")
+    assert lib.sparse_mla_kernel_name(128, 2048).startswith(b"smla_fwd_kernel")
 
 
 @pytest.mark.parametrize("kw,rc", [
