@@ -144,7 +144,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="wide", choices=["tiny", "small", "tp4", "wide", "large"])
+    ap.add_argument("--workload", default="wide", choices=["tiny", "small", "tp4", "wide", "large", "glm", "decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -211,7 +211,7 @@ def main():
           file=sys.stderr, flush=True)
     if not args.no_secondary:
         sec = []
-        for other in ("tp4", "large", "small"):
+        for other in ("tp4", "large", "small", "glm", "decode"):
             if other == args.workload:
                 continue
             i2, a2, t2 = measure(other, max(10, args.steps // 2), args.warmup)

@@ -35,6 +35,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "sparse_mla.h"
 
 namespace {
@@ -70,6 +72,17 @@ struct Params {
   int topk_n;
   int head_groups;
   float scale_log2;  // scale * log2(e)
+};
+
+// Split over the top-k row (few tokens): split `sp` of a row covers raw
+// positions [sp * split_len, (sp + 1) * split_len); its partial results go to
+// part_ml (reference max in log2 units, row sum) and part_o (O not yet
+// normalised), indexed ((t * head_groups + hg) * nsplit + sp) * 16 NW + head.
+struct SplitArgs {
+  int nsplit;
+  int split_len;
+  float* part_o;
+  float* part_ml;
 };
 
 template <int NW, int NBUF>
@@ -215,7 +228,7 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
 // one round of loads and two workgroup barriers. Returns the count (uniform
 // across the workgroup).
 template <int NW, int NBUF>
-__device__ int compact_segment(const int32_t* __restrict__ trow, int len, uint32_t nkv, Smem<NW, NBUF>& sm,
+__device__ __forceinline__ int compact_segment(const int32_t* __restrict__ trow, int len, uint32_t nkv, Smem<NW, NBUF>& sm,
                                int lane, int w) {
   constexpr int CH = NW * 64;              // entries per chunk (one per thread)
   constexpr int MAXC = kListCap / CH;      // chunks per segment
@@ -492,8 +505,8 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[16], const Params& p, int t,
 // One workgroup per (token, group of 16 NW heads). Iteration j computes tile j
 // from ring buffer j % NBUF while tiles j+1 .. j+NBUF-1 land; the rows of tile
 // j+NBUF-1 are issued in one burst before P.V(j).
-template <int NW, int NBUF>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void smla_fwd_kernel(const Params p) {
+template <int NW, int NBUF, bool SPLIT>
+__device__ __forceinline__ void smla_fwd_body(const Params& p, const SplitArgs& sa) {
   static_assert(NBUF >= 2 && NBUF <= 4, "ring of 2 to 4 tiles");
   static_assert(NBUF * kBK >= NW * 16, "the output staging needs 16 LDS rows per wave");
   constexpr int AHEAD = NBUF - 1;  // tiles gathered ahead of the one being computed
@@ -504,11 +517,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int g = lane >> 4;   // 16-lane group
   const int li = lane & 15;  // index within the group
 
-  const int v = xcd_remap(blockIdx.x, gridDim.x);
+  const int vb = SPLIT ? (int)blockIdx.x : xcd_remap(blockIdx.x, gridDim.x);
+  const int sp = SPLIT ? vb % sa.nsplit : 0;
+  const int v = SPLIT ? vb / sa.nsplit : vb;
   const int t = p.T - 1 - v / p.head_groups;  // latest (heaviest) tokens first
   const int hg = v % p.head_groups;
   const int head_base = (hg * NW + w) * 16;
   const int head = head_base + li;
+  const int row_begin = SPLIT ? min(p.topk_n, sp * sa.split_len) : 0;
+  const int row_end = SPLIT ? min(p.topk_n, row_begin + sa.split_len) : p.topk_n;
 
   f32x4 acc[32];
 #pragma unroll
@@ -519,9 +536,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   bf16x8 pk;
 
   const int32_t* trow = p.topk + (size_t)t * p.topk_n;
-  for (int seg0 = 0; seg0 < p.topk_n; seg0 += kListCap) {
-    if (seg0 > 0 && NW > 1) lds_barrier();  // previous segment's list and tiles fully consumed
-    const int n = compact_segment<NW, NBUF>(trow + seg0, min(kListCap, p.topk_n - seg0), p.nkv, sm, lane, w);
+  for (int seg0 = row_begin; seg0 < row_end; seg0 += kListCap) {
+    if (seg0 > row_begin && NW > 1) lds_barrier();  // previous segment's list and tiles fully consumed
+    const int n = compact_segment<NW, NBUF>(trow + seg0, min(kListCap, row_end - seg0), p.nkv, sm, lane, w);
     const int ntiles = (n + kBK - 1) / kBK;
     if (ntiles == 0) continue;
 
@@ -549,6 +566,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       is.all(lane);
       tile_pv(v_frag_addr(tb, g, li), pk, acc);
     }
+  }
+
+  if constexpr (SPLIT) {
+    // partial results of this split; the merge kernel folds the splits and the sink
+    mfma_agpr_drain(acc);
+    const float lsum = row4_sum(l_part);
+    const size_t pi = ((size_t)v * sa.nsplit + sp) * (16 * NW) + w * 16 + li;
+    if (g == 0) {
+      sa.part_ml[2 * pi] = m_ref;
+      sa.part_ml[2 * pi + 1] = lsum;
+    }
+    float* dst = sa.part_o + pi * kD + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < 32; ++dt) *(f32x4*)(dst + 16 * dt) = acc[dt];
+    return;
   }
 
   // ---- finalise: fold the sink, normalise, store ----
@@ -580,6 +612,80 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
 }
 
+template <int NW, int NBUF>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void smla_fwd_kernel(const Params p) {
+  smla_fwd_body<NW, NBUF, false>(p, SplitArgs{});
+}
+
+// One workgroup per (token, head group, split of the top-k row); writes partial results.
+template <int NW, int NBUF>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void smla_fwd_split_kernel(
+    const Params p, const SplitArgs sa) {
+  smla_fwd_body<NW, NBUF, true>(p, sa);
+}
+
+// Merge of the splits of one (token, head), one wave each: lane s < nsplit
+// reads split s's reference max m_s and sum l_s; with Mv the largest m_s, the
+// splits are weighted by c_s = 2^(m_s - Mv) (0 for a split that saw no valid
+// slot), and lane L accumulates o[t, h, 8L .. 8L+8). The sink is then folded in
+// exactly as in the single-pass finalisation.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = __builtin_fmaxf(x, __shfl_xor(x, off, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+__global__ __launch_bounds__(256) void smla_merge_kernel(const Params p, const SplitArgs sa, int heads_per_group) {
+  const int lane = threadIdx.x & 63;
+  const int th = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (th >= p.T * p.H) return;
+  const int t = th / p.H;
+  const int h = th - t * p.H;
+  const int hg = h / heads_per_group;
+  const int hi = h - hg * heads_per_group;
+  const size_t base = ((size_t)(p.T - 1 - t) * p.head_groups + hg) * sa.nsplit * heads_per_group + hi;
+  float ms = -INFINITY, ls = 0.f;
+  if (lane < sa.nsplit) {
+    const size_t pi = base + (size_t)lane * heads_per_group;
+    ms = sa.part_ml[2 * pi];
+    ls = sa.part_ml[2 * pi + 1];
+  }
+  const float mv = wave_max(ms);
+  const float c = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - mv);
+  const float lsum = wave_sum(ls * c);
+  f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int sp = 0; sp < sa.nsplit; ++sp) {
+    const float cs = __shfl(c, sp, 64);
+    const f32x4* src = (const f32x4*)(sa.part_o + (base + (size_t)sp * heads_per_group) * kD + 8 * lane);
+    o0 += src[0] * cs;
+    o1 += src[1] * cs;
+  }
+  const float sk = p.sink != nullptr ? p.sink[h] : -INFINITY;
+  const bool has_sink = !(sk == -INFINITY);
+  const float sink_l2 = sk * kLog2e;
+  uint16_t* dst = p.out + ((size_t)t * p.H + h) * kD + 8 * lane;
+  if (lsum == 0.f) {  // no valid slot carried any mass
+    *(u32x4*)dst = u32x4{0u, 0u, 0u, 0u};
+    if (lane == 0) p.lse[(size_t)t * p.H + h] = has_sink ? sk : -INFINITY;
+    return;
+  }
+  const float mf = has_sink ? __builtin_fmaxf(mv, sink_l2) : mv;
+  const float a = __builtin_amdgcn_exp2f(mv - mf);
+  const float lf = lsum * a + (has_sink ? __builtin_amdgcn_exp2f(sink_l2 - mf) : 0.f);
+  const float oscale = a / lf;
+  o0 *= oscale;
+  o1 *= oscale;
+  *(bf16x8*)dst = bf16x8{(__bf16)o0[0], (__bf16)o0[1], (__bf16)o0[2], (__bf16)o0[3],
+                         (__bf16)o1[0], (__bf16)o1[1], (__bf16)o1[2], (__bf16)o1[3]};
+  if (lane == 0) p.lse[(size_t)t * p.H + h] = (mf + __builtin_amdgcn_logf(lf)) * kLn2;
+}
+
 struct Variant {
   int nw;
   const char* name;
@@ -595,10 +701,69 @@ Variant pick_variant(int64_t H, int64_t topk) {
   return {8, "smla_fwd_kernel<8, 4>"};
 }
 
-template <int NW, int NBUF>
-hipError_t launch(const Params& p, int blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((smla_fwd_kernel<NW, NBUF>), dim3(blocks), dim3(NW * 64), 0, stream, p);
+template <int NW, int NBUF, bool SPLIT>
+hipError_t launch(const Params& p, const SplitArgs& sa, int blocks, hipStream_t stream) {
+  if constexpr (SPLIT) {
+    hipLaunchKernelGGL((smla_fwd_split_kernel<NW, NBUF>), dim3(blocks), dim3(NW * 64), 0, stream, p, sa);
+  } else {
+    (void)sa;
+    hipLaunchKernelGGL((smla_fwd_kernel<NW, NBUF>), dim3(blocks), dim3(NW * 64), 0, stream, p);
+  }
   return hipGetLastError();
+}
+
+template <bool SPLIT>
+hipError_t launch_variant(int nw, const Params& p, const SplitArgs& sa, int blocks, hipStream_t s) {
+  if (nw == 1) return launch<1, 2, SPLIT>(p, sa, blocks, s);
+  if (nw == 2) return launch<2, 2, SPLIT>(p, sa, blocks, s);
+  if (nw == 4) return launch<4, 2, SPLIT>(p, sa, blocks, s);
+  return launch<8, 4, SPLIT>(p, sa, blocks, s);
+}
+
+// Compute units of a device (cached; 0 if unknown).
+int cu_count(int dev) {
+  static int cache[64];
+  if (dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return 0;
+    }
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// A split covers at least this many top-k positions (two full tiles); a row
+// is split at most kMaxSplit ways (one merge lane per split).
+constexpr int kMinSplitLen = 64;
+constexpr int kMaxSplit = 64;
+
+// Stream-ordered scratch for the split path comes from a pool of our own per
+// device that keeps freed memory (its high-water mark) instead of handing it
+// back at every synchronisation.
+hipMemPool_t scratch_pool(int dev) {
+  static std::mutex mu;
+  static hipMemPool_t pools[64];
+  if (dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (pools[dev] == nullptr) {
+    hipMemPoolProps props = {};
+    props.allocType = hipMemAllocationTypePinned;
+    props.handleTypes = hipMemHandleTypeNone;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool = nullptr;
+    if (hipMemPoolCreate(&pool, &props) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    uint64_t keep = UINT64_MAX;
+    (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+    pools[dev] = pool;
+  }
+  return pools[dev];
 }
 
 bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
@@ -643,18 +808,48 @@ extern "C" int sparse_mla_prefill(const void* q, const void* kv, const int32_t* 
   p.topk_n = (int)topk;
   p.head_groups = (int)head_groups;
   p.scale_log2 = scale * kLog2e;
+  SplitArgs sa;
+  sa.nsplit = 1;
+  sa.split_len = (int)topk;
+  sa.part_o = nullptr;
+  sa.part_ml = nullptr;
   const int64_t units = T * head_groups;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t err;
-  if (var.nw == 1) {
-    err = launch<1, 2>(p, (int)units, s);
-  } else if (var.nw == 2) {
-    err = launch<2, 2>(p, (int)units, s);
-  } else if (var.nw == 4) {
-    err = launch<4, 2>(p, (int)units, s);
-  } else {
-    err = launch<8, 4>(p, (int)units, s);
+
+  // Few (token, head group) units leave most CUs idle: split each top-k row
+  // over several workgroups, then merge (stream-ordered scratch; if it cannot
+  // be had, the single-pass path below still gives the result).
+  const int64_t cus = cu_count(dev);
+  if (cus > 0 && units < cus && topk >= 2 * kMinSplitLen) {
+    const int64_t slots = (var.nw == 8 ? 1 : 2) * cus;  // resident workgroups
+    int64_t ns = (slots + units - 1) / units;
+    ns = ns < topk / kMinSplitLen ? ns : topk / kMinSplitLen;
+    ns = ns < kMaxSplit ? ns : kMaxSplit;
+    if (ns >= 2) {
+      const int64_t len = (topk + ns - 1) / ns;
+      ns = (topk + len - 1) / len;
+      const int64_t parts = units * ns * 16 * var.nw;
+      const size_t bytes_o = (size_t)parts * kD * sizeof(float);
+      const size_t bytes = bytes_o + (size_t)parts * 2 * sizeof(float);
+      void* ws = nullptr;
+      hipMemPool_t pool = scratch_pool(dev);
+      if (pool != nullptr && hipMallocFromPoolAsync(&ws, bytes, pool, s) == hipSuccess && ws != nullptr) {
+        sa.nsplit = (int)ns;
+        sa.split_len = (int)len;
+        sa.part_o = (float*)ws;
+        sa.part_ml = (float*)((char*)ws + bytes_o);
+        hipError_t err = launch_variant<true>(var.nw, p, sa, (int)(units * ns), s);
+        if (err == hipSuccess) {
+          hipLaunchKernelGGL(smla_merge_kernel, dim3((unsigned)((T * H + 3) / 4)), dim3(256), 0, s, p, sa, 16 * var.nw);
+          err = hipGetLastError();
+        }
+        const hipError_t ferr = hipFreeAsync(ws, s);
+        return (err == hipSuccess && ferr == hipSuccess) ? SMLA_OK : SMLA_ERR_LAUNCH;
+      }
+      (void)hipGetLastError();
+    }
   }
+  const hipError_t err = launch_variant<false>(var.nw, p, sa, (int)units, s);
   return err == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
 }
 

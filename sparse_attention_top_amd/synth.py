@@ -22,10 +22,19 @@ itself):
   token's own slot, and optional NaN filling of every KV row that no valid slot
   references.
 
+A second layout, ``paged``, stands in for a serving engine's KV pool (the
+GLM-shaped test on the forward review page: 16 heads, top-k 2048, a pool over
+2 GiB): the sequence's ``T`` rows live in pages of ``page`` rows placed at
+random page slots of a pool of ``pool_rows`` rows; the other rows are zero.
+Row ``t`` of ``topk`` holds the window ``t-W+1 .. t`` then up to ``P``
+distinct earlier positions ``< t-W+1`` (all when at most ``P``, else a seeded
+``rng.choice``), sorted, each mapped through the page table; the rest ``-1``.
+
 ``q``, ``kv`` are N(0,1) fp32 rounded to bf16 (round to nearest, ties to even)
 and returned as their raw ``uint16`` bit patterns; ``attn_sink`` is N(0,1)
-fp32. The draw order is fixed: q, kv, sink, then per-token pool choices in
-token order, then the drop mask.
+fp32. The draw order is fixed: q, kv (the sequence's rows, for ``paged``),
+sink, then (``paged``) the page placement, then per-token choices in token
+order, then the drop mask.
 """
 
 from __future__ import annotations
@@ -54,9 +63,15 @@ class Config:
     sink: bool = True
     drop_p: float = 0.0
     nan_unused: bool = False
+    layout: str = "pool"  # "pool" (window + compressed pool) or "paged"
+    tail: int = 0         # keep only the last `tail` tokens' q and top-k rows (decode-sized calls)
+    pool_rows: int = 0    # paged: rows in the whole pool
+    page: int = 64        # paged: rows per page
 
     @property
     def num_kv(self) -> int:
+        if self.layout == "paged":
+            return self.pool_rows
         return self.T + self.T // self.compression
 
 
@@ -70,6 +85,12 @@ CONFIGS = {
     "tp4": Config("tp4", T=16384, H=16, topk=640, window=128, pool_slots=512, compression=4, seed=103),
     "wide": Config("wide", T=4096, H=128, topk=512, window=128, pool_slots=384, compression=4, seed=104),
     "large": Config("large", T=8192, H=128, topk=1024, window=256, pool_slots=768, compression=8, seed=105),
+    # GLM-shaped prefill on a server-sized paged pool (2.2 M rows = 2.1 GiB)
+    "glm": Config("glm", T=16384, H=16, topk=2048, window=128, pool_slots=1920, compression=1, seed=106,
+                  sink=False, layout="paged", pool_rows=2_200_000, page=64),
+    # a decode-sized call: the last 16 tokens of the tp4 sequence (same pool and rows)
+    "decode": Config("decode", T=16384, H=16, topk=640, window=128, pool_slots=512, compression=4, seed=103,
+                     tail=16),
 }
 
 
@@ -108,6 +129,27 @@ def build_topk(rng: np.random.Generator, T: int, topk: int, window: int, pool_sl
     return idx
 
 
+def build_topk_paged(rng: np.random.Generator, T: int, topk: int, window: int, pool_slots: int,
+                     row_of: np.ndarray) -> np.ndarray:
+    """Window + earlier-position top-k rows over sequence positions, mapped to pool rows."""
+    if window + pool_slots > topk:
+        raise ValueError("window + pool_slots must fit in topk")
+    pos = np.full((T, topk), -1, dtype=np.int64)
+    t = np.arange(T, dtype=np.int64)[:, None]
+    w = t - (window - 1) + np.arange(window, dtype=np.int64)[None, :]
+    pos[:, :window] = np.where(w >= 0, w, -1)
+    for tok in range(T):
+        vis = tok + 1 - window  # earlier positions 0 .. vis-1
+        if vis <= 0:
+            continue
+        if vis <= pool_slots:
+            rows = np.arange(vis, dtype=np.int64)
+        else:
+            rows = np.sort(rng.choice(vis, pool_slots, replace=False))
+        pos[tok, window:window + rows.size] = rows
+    return np.where(pos >= 0, row_of[np.maximum(pos, 0)], -1).astype(np.int32)
+
+
 def make_inputs(cfg: Config | str, *, T: int | None = None) -> dict:
     """Draw one seeded workload.
 
@@ -122,13 +164,30 @@ def make_inputs(cfg: Config | str, *, T: int | None = None) -> dict:
     T_, H = cfg.T, cfg.H
     num_kv = cfg.num_kv
     q = f32_to_bf16_bits(rng.standard_normal((T_, H, D), dtype=np.float32))
-    kv = f32_to_bf16_bits(rng.standard_normal((num_kv, D), dtype=np.float32))
-    sink = rng.standard_normal(H, dtype=np.float32) if cfg.sink else None
-    topk = build_topk(rng, T_, cfg.topk, cfg.window, cfg.pool_slots, cfg.compression)
+    if cfg.layout == "paged":
+        seq = f32_to_bf16_bits(rng.standard_normal((T_, D), dtype=np.float32))
+        sink = rng.standard_normal(H, dtype=np.float32) if cfg.sink else None
+        n_pages = -(-T_ // cfg.page)
+        if n_pages * cfg.page > num_kv:
+            raise ValueError("pool too small for the sequence")
+        slots = rng.permutation(num_kv // cfg.page)[:n_pages].astype(np.int64)
+        p_ = np.arange(T_, dtype=np.int64)
+        row_of = slots[p_ // cfg.page] * cfg.page + p_ % cfg.page
+        kv = np.zeros((num_kv, D), dtype=np.uint16)  # untouched pages stay unallocated
+        kv[row_of] = seq
+        topk = build_topk_paged(rng, T_, cfg.topk, cfg.window, cfg.pool_slots, row_of)
+    else:
+        kv = f32_to_bf16_bits(rng.standard_normal((num_kv, D), dtype=np.float32))
+        sink = rng.standard_normal(H, dtype=np.float32) if cfg.sink else None
+        topk = build_topk(rng, T_, cfg.topk, cfg.window, cfg.pool_slots, cfg.compression)
     if cfg.drop_p > 0.0:
         drop = rng.random((T_, cfg.topk)) < cfg.drop_p
         drop[:, cfg.window - 1] = False  # the token's own slot is always kept
         topk[drop & (topk >= 0)] = -1
+    if cfg.tail:
+        q = np.ascontiguousarray(q[-cfg.tail:])
+        topk = np.ascontiguousarray(topk[-cfg.tail:])
+        T_ = cfg.tail
     n_unused = 0
     if cfg.nan_unused:
         used = np.zeros(num_kv, dtype=bool)

@@ -46,7 +46,7 @@ def test_tiny_all_tokens():
     print("tiny", stats)
 
 
-@pytest.mark.parametrize("name,T", [("small", None), ("tp4", 768), ("wide", 384), ("large", 320)])
+@pytest.mark.parametrize("name,T", [("small", None), ("tp4", 768), ("wide", 384), ("large", 320), ("glm", 512)])
 def test_truncated_all_tokens(name, T):
     """Same draw recipe at a size the oracle covers fully (several tiles and a ragged tail per token)."""
     inp = synth.make_inputs(name, T=T)
@@ -55,7 +55,7 @@ def test_truncated_all_tokens(name, T):
     print(name, inp["T"], stats)
 
 
-@pytest.mark.parametrize("name,k", [("small", 48), ("tp4", 40), ("wide", 24), ("large", 16)])
+@pytest.mark.parametrize("name,k", [("small", 48), ("tp4", 40), ("wide", 24), ("large", 16), ("glm", 24)])
 def test_full_size_sampled(name, k):
     inp, o, lse = full_case(name)
     tok = sample_tokens(inp["topk"], inp["num_kv"], k, seed=7)
@@ -67,7 +67,7 @@ def test_full_size_sampled(name, k):
 def test_full_size_properties():
     """Properties over every token of the full-size workloads: finite outputs and an lse
     no smaller than the sink (the denominator holds exp(sink))."""
-    for name in ("small", "tp4", "wide", "large"):
+    for name in ("small", "tp4", "wide", "large", "glm"):
         inp, o, lse = full_case(name)
         of = synth.bf16_bits_to_f32(o)
         assert np.all(np.isfinite(of)), name
@@ -321,3 +321,43 @@ def test_binding_rejects_bad_inputs():
         sparse_mla_prefill(q, kv, idx, attn_sink=torch.zeros(16, device=DEV, dtype=torch.float64))
     with pytest.raises(RuntimeError, match="scale"):
         sparse_mla_prefill(q, kv, idx, scale=math.inf)
+
+
+# ---- few tokens: each top-k row is split over several workgroups, then merged ----
+
+@pytest.mark.parametrize("T,H,topk,num_kv", [(1, 16, 640, 20480), (2, 16, 2048, 4096), (4, 128, 1024, 9216),
+                                             (8, 64, 4500, 6000), (16, 16, 640, 2000), (3, 200, 1500, 3000),
+                                             (5, 8, 600, 900), (12, 32, 777, 1000)])
+def test_split_rows_few_tokens(T, H, topk, num_kv):
+    inp = make_random(3000 + T * 7 + H, T=T, H=H, num_kv=num_kv, topk=topk, p_invalid=0.15)
+    o, lse = run_case(inp)
+    compare(o, lse, oracle_ref(inp), what="split T=%d H=%d topk=%d" % (T, H, topk))
+
+
+@pytest.mark.parametrize("sink", [False, True])
+def test_split_rows_with_empty_splits(sink):
+    """Rows whose valid slots sit in one split, or nowhere: empty splits carry no mass and an
+    all-invalid row gives o = 0 and lse = sink (or -inf) exactly."""
+    rng = np.random.default_rng(77)
+    T, H, topk, num_kv = 4, 16, 1024, 2000
+    inp = make_random(78, T=T, H=H, num_kv=num_kv, topk=topk, p_invalid=0.0, sink=sink)
+    idx = inp["topk"]
+    idx[0, :] = -1                       # no valid slot at all
+    idx[1, :-1] = -1                     # one valid slot, in the last split
+    idx[2, 300:] = num_kv + 5            # valid slots only at the front (out-of-range values elsewhere)
+    idx[3, rng.random(topk) < 0.5] = -1  # random half
+    o, lse = run_case(inp)
+    ref = oracle_ref(inp)
+    compare(o, lse, ref, what="split empty sink=%s" % sink)
+    assert np.all(synth.bf16_bits_to_f32(o[0]) == 0.0)
+    if sink:
+        assert np.array_equal(lse[0], inp["sink"])
+    else:
+        assert np.all(lse[0] == -np.inf)
+
+
+def test_decode_workload_full():
+    """The decode-sized call (last 16 tokens of the tp4 sequence) against the oracle, every token."""
+    inp = synth.make_inputs("decode")
+    o, lse = run_case(inp)
+    compare(o, lse, oracle_ref(inp), what="decode")

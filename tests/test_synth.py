@@ -50,6 +50,37 @@ def test_topk_structure(name):
         assert np.all(row[W + P:] == -1)
 
 
+def closed_form_valid_paged(cfg):
+    t = np.arange(cfg.T)
+    return int(np.minimum(t + 1, cfg.window).sum() + np.minimum(np.maximum(t + 1 - cfg.window, 0), cfg.pool_slots).sum())
+
+
+def test_paged_layout_counts_and_structure():
+    cfg = synth.CONFIGS["glm"]
+    assert closed_form_valid_paged(cfg) == 31458304  # written out: catches a change of recipe
+    inp = synth.make_inputs("glm", T=700)
+    idx, kv, W, P = inp["topk"], inp["kv"], cfg.window, cfg.pool_slots
+    assert inp["num_kv"] == cfg.pool_rows and inp["num_kv"] * 1024 > 2 * 2**30  # the pool is over 2 GiB
+    small = synth.dataclasses.replace(cfg, T=700)
+    assert synth.valid_slot_count(idx, inp["num_kv"]) == closed_form_valid_paged(small)
+    assert np.all((idx == -1) | ((idx >= 0) & (idx < inp["num_kv"])))
+    # the token's own row: its row is the last window slot, and it is the only slot holding it
+    own = idx[:, W - 1]
+    assert np.all(own >= 0) and len(set(own.tolist())) == 700
+    for t in range(0, 700, 37):
+        row = idx[t]
+        valid = row[row >= 0]
+        assert len(set(valid.tolist())) == valid.size  # distinct rows
+        assert valid.size == min(t + 1, W) + min(max(t + 1 - W, 0), P)
+        assert np.all(row[W + P:] == -1)
+    # referenced rows carry the sequence's values, the rest of the pool is zero
+    ref = np.unique(idx[idx >= 0])
+    assert ref.size == 700
+    assert not np.all(kv[ref] == 0)
+    untouched = np.setdiff1d(np.arange(0, inp["num_kv"], 997), ref)
+    assert np.all(kv[untouched] == 0)
+
+
 def test_deterministic_and_seeded():
     a = synth.make_inputs("tiny")
     b = synth.make_inputs("tiny")
