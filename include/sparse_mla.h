@@ -64,12 +64,24 @@ typedef enum {
  *   T, H, num_kv, topk   sizes; T == 0 returns SMLA_OK without a launch.
  *   stream        a hipStream_t, or NULL for the default stream.
  *
- * out and lse must not alias any input (not checked). The library allocates
- * nothing, keeps no state between calls and never synchronises: results are
- * ready when `stream` reaches this point. Faults during execution surface at
- * the caller's next synchronisation, as usual for HIP. Results are
- * bitwise-deterministic: the same inputs give the same bits on every call.
- * Thread-safe and reentrant.
+ * out and lse must not alias any input (not checked). The call never
+ * synchronises: results are ready when `stream` reaches this point. Faults
+ * during execution surface at the caller's next synchronisation, as usual for
+ * HIP. Results are bitwise-deterministic: the same inputs give the same bits
+ * on every call. Thread-safe and reentrant.
+ *
+ * Calls with few (token, head group) units -- fewer than the device has
+ * compute units -- and top-k rows of at least 128 entries split each row over
+ * several workgroups and merge the partial results in a second kernel (the
+ * review of "[Triton/Gluon] [CI] [gfx942] Tuned sparse MLA prefill for
+ * DSv4.1-Flash TP4; fix attn_sink in Triton fallback" (aiter PR #6002) notes
+ * that a per-token grid leaves the GPU idle for decode-sized calls). The
+ * partials live in stream-ordered scratch taken from a memory pool the library
+ * creates once per device and keeps until the process ends (it retains its
+ * high-water mark: 2 KiB per (unit, split, head), under 140 MB in all; a few
+ * MiB for decode-sized calls). If that scratch cannot
+ * be had, the call runs the single-pass path instead; the result differs only
+ * by floating-point rounding order. No other call allocates.
  */
 int sparse_mla_prefill(const void* q, const void* kv, const int32_t* topk_indices, const float* attn_sink,
                        float scale, void* out, float* lse, int64_t T, int64_t H, int64_t num_kv,
