@@ -60,7 +60,9 @@ def traffic_from_profiles(kernel: str, workload: str):
     return None
 
 
-def time_gpu(run, steps, warmup, stream):
+def time_gpu(run, steps, warmup, stream, flush=None):
+    """Warm (back-to-back) timing, or cold when `flush` is given: it runs before every
+    launch, outside the bracketing events. Returns wall seconds and per-launch stats (ms)."""
     import torch
 
     for _ in range(warmup):
@@ -70,13 +72,26 @@ def time_gpu(run, steps, warmup, stream):
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
+        if flush is not None:
+            flush()
         starts[i].record(stream)
         run()
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per_launch = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return wall, float(np.mean(per_launch)), float(np.median(per_launch))
+    return wall, {"mean": float(np.mean(per_launch)), "median": float(np.median(per_launch)),
+                  "min": float(np.min(per_launch))}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(inp: dict, target_s: float = 10.0):
@@ -101,10 +116,10 @@ def cpu_baseline(inp: dict, target_s: float = 10.0):
     flops = 4.0 * inp["H"] * D * nv
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
             "sample": "%d of %d tokens (evenly spaced), %d valid slots, %.2f s wall" % (len(tokens), T, nv, dt),
-            "ms_per_call_extrapolated": dt * 1e3 * inp["T"] / len(tokens)}
+            "ms_per_call_extrapolated": dt * 1e3 * inp["T"] / len(tokens), "cpu_model": cpu_model()}
 
 
-def measure(name: str, steps: int, warmup: int):
+def measure(name: str, steps: int, warmup: int, cold_steps: int = 0):
     import torch
 
     from sparse_attention_top_amd import kernel_name, sparse_mla_prefill, synth
@@ -122,10 +137,19 @@ def measure(name: str, steps: int, warmup: int):
     def run():
         sparse_mla_prefill(q, kv, topk, sink, inp["scale"], out=out, lse=lse)
 
-    wall, mean_ms, med_ms = time_gpu(run, steps, warmup, stream)
+    wall, st = time_gpu(run, steps, warmup, stream)
     alg = algorithmic(inp)
-    return inp, alg, {"wall_s": wall, "ms_per_call": wall * 1e3 / steps, "kernel_ms_mean": mean_ms,
-                      "kernel_ms_median": med_ms, "kernel": kernel_name(inp["H"], inp["topk_n"])}
+    t = {"wall_s": wall, "ms_per_call": wall * 1e3 / steps, "kernel_ms_mean": st["mean"],
+         "kernel_ms_median": st["median"], "kernel_ms_min": st["min"],
+         "kernel": kernel_name(inp["H"], inp["topk_n"])}
+    if cold_steps:
+        # cold caches: overwrite 512 MiB (more than the 256 MB MALL plus 8 x 4 MB of L2) before each launch
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        _, cst = time_gpu(run, cold_steps, 1, stream, flush=lambda: scratch.fill_(1))
+        t["cold"] = {"kernel_ms_mean": cst["mean"], "kernel_ms_median": cst["median"], "kernel_ms_min": cst["min"],
+                     "launches": cold_steps, "flush_bytes": 512 << 20}
+        del scratch
+    return inp, alg, t
 
 
 def roofline(alg, t, kernel, workload, bound):
@@ -147,6 +171,7 @@ def main():
     ap.add_argument("--workload", default="wide", choices=["tiny", "small", "tp4", "wide", "large", "glm", "decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timing of the main workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -176,7 +201,7 @@ def main():
 
     print("bench: workload %s, %d warmup + %d timed steps" % (args.workload, args.warmup, args.steps),
           file=sys.stderr, flush=True)
-    inp, alg, t = measure(args.workload, args.steps, args.warmup)
+    inp, alg, t = measure(args.workload, args.steps, args.warmup, cold_steps=0 if args.no_cold else min(args.steps, 20))
     bound = "mfma" if inp["H"] > 16 else "hbm"
     tflops = alg["flops"] / (t["ms_per_call"] * 1e-3) / 1e12
     gbs = alg["gathered_bytes"] / (t["ms_per_call"] * 1e-3) / 1e9
@@ -205,6 +230,8 @@ def main():
         "gathered_gbs": gbs,
         "kernel_ms_mean": t["kernel_ms_mean"],
         "kernel_ms_median": t["kernel_ms_median"],
+        "kernel_ms_min": t["kernel_ms_min"],
+        "cold": t.get("cold"),
         "roofline": roofline(alg, t, t["kernel"], cfg.name, bound),
     }
     print("bench: %s %.4f ms/call, %.1f TFLOP/s, %.1f GB/s gathered" % (cfg.name, t["ms_per_call"], tflops, gbs),
@@ -217,9 +244,13 @@ def main():
             i2, a2, t2 = measure(other, max(10, args.steps // 2), args.warmup)
             b2 = "mfma" if i2["H"] > 16 else "hbm"
             sec.append({"workload": other, "ms_per_call": t2["ms_per_call"], "kernel_ms_mean": t2["kernel_ms_mean"],
+                        "kernel_ms_median": t2["kernel_ms_median"], "kernel_ms_min": t2["kernel_ms_min"],
                         "tflops": a2["flops"] / (t2["ms_per_call"] * 1e-3) / 1e12,
                         "gathered_gbs": a2["gathered_bytes"] / (t2["ms_per_call"] * 1e-3) / 1e9,
                         "valid_slots": a2["valid_slots"], "roofline": roofline(a2, t2, t2["kernel"], other, b2)})
+            if i2["T"] * -(-i2["H"] // 128) < 256:
+                sec[-1]["note"] = ("few-token call: split-KV kernel + merge kernel; per-launch events include the "
+                                   "host launch gap, rocprofv3 kernel time is the GPU figure")
             print("bench: %s %.4f ms/call" % (other, t2["ms_per_call"]), file=sys.stderr, flush=True)
         line["secondary"] = sec
     if not args.no_cpu_baseline:
