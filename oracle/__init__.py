@@ -51,6 +51,13 @@ def _load():
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
         ]
+        lib.smla_oracle_forward_ix.restype = ctypes.c_int
+        lib.smla_oracle_forward_ix.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+            ctypes.c_double, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ]
         lib.smla_oracle_threads.restype = ctypes.c_int
         lib.smla_oracle_threads.argtypes = []
         _lib = lib
@@ -65,14 +72,15 @@ def forward(q, kv, topk, sink, scale, tokens=None, *, want_exact=True, want_bf16
     """Evaluate the definition for the given tokens (all tokens when None).
 
     q: uint16 bf16 bits [T, H, 512]; kv: uint16 bf16 bits [num_kv, 512];
-    topk: int32 [T, topk]; sink: float32 [H] or None; scale: float.
+    topk: int32 or int64 [T, topk]; sink: float32 [H] or None; scale: float.
     Returns a dict with ``o`` (float64 [n, H, 512], unrounded), ``o_bf16``
     (uint16 bits [n, H, 512]), ``lse`` (float64 [n, H], natural log) and
     ``n_valid`` (int64 [n]).
     """
     q = np.ascontiguousarray(q, dtype=np.uint16)
     kv = np.ascontiguousarray(kv, dtype=np.uint16)
-    topk = np.ascontiguousarray(topk, dtype=np.int32)
+    topk = np.asarray(topk)
+    topk = np.ascontiguousarray(topk, dtype=np.int64 if topk.dtype == np.int64 else np.int32)
     T, H, d = q.shape
     if d != D or kv.ndim != 2 or (kv.shape[0] > 0 and kv.shape[1] != D):
         raise ValueError("head dim must be 512")
@@ -93,8 +101,8 @@ def forward(q, kv, topk, sink, scale, tokens=None, *, want_exact=True, want_bf16
     ob = np.empty((n, H, D), np.uint16) if want_bf16 else None
     lse = np.empty((n, H), np.float64)
     nv = np.empty((n,), np.int64)
-    rc = _load().smla_oracle_forward(
-        _ptr(q), _ptr(kv) if num_kv > 0 else None, _ptr(topk), _ptr(sink), float(scale),
+    rc = _load().smla_oracle_forward_ix(
+        _ptr(q), _ptr(kv) if num_kv > 0 else None, _ptr(topk), topk.itemsize, _ptr(sink), float(scale),
         T, H, num_kv, topk.shape[1], _ptr(tok), n, _ptr(o), _ptr(ob), _ptr(lse), _ptr(nv), int(threads))
     if rc != 0:
         raise RuntimeError("oracle rejected its arguments (rc=%d)" % rc)

@@ -33,6 +33,10 @@
  *    note on the backward page); with a finite sink, o = 0 and lse = sink.
  *    attn_sink[h] == -inf behaves exactly like having no sink.
  *  - Each valid slot is its own softmax term; a repeated index counts twice.
+ *  - Indices may be int32 or int64; an int64 index is compared as is (the
+ *    DSv4.1-Flash TP4 page's description: int64 slots at or past 2^31 used
+ *    to wrap onto valid rows when cast to int32, and are kept as int64 now),
+ *    so such a slot is simply invalid.
  *  - NaN anywhere in a referenced row or in q propagates to that (t,h).
  *
  * Precision: inputs are bf16 widened exactly; every sum, exp and log is done
@@ -67,8 +71,13 @@ static uint16_t float_to_bf16_rne(float f) {
   return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
 }
 
+/* Index s of a top-k row of 4- or 8-byte signed integers. */
+static int64_t idx_at(const void* row, int idx64, int64_t s) {
+  return idx64 ? ((const int64_t*)row)[s] : (int64_t)((const int32_t*)row)[s];
+}
+
 /* One (t, h) pair, written straight from the definition above. */
-static void one_head(const uint16_t* qrow, const uint16_t* kv, const int32_t* idx_row,
+static void one_head(const uint16_t* qrow, const uint16_t* kv, const void* idx_row, int idx64,
                      int64_t topk, int64_t num_kv, int has_sink, double sink, double scale,
                      double* x /* scratch [topk] */, double* acc /* scratch [D] */,
                      double* o_exact, uint16_t* o_bf16, double* lse_out) {
@@ -76,7 +85,7 @@ static void one_head(const uint16_t* qrow, const uint16_t* kv, const int32_t* id
   /* Pass 1: logits of the valid slots and their maximum. */
   double m = -INFINITY;
   for (int64_t s = 0; s < topk; ++s) {
-    int64_t r = idx_row[s];
+    int64_t r = idx_at(idx_row, idx64, s);
     if (r < 0 || r >= num_kv) continue;
     const uint16_t* krow = kv + r * D;
     double dot = 0.0;
@@ -100,7 +109,7 @@ static void one_head(const uint16_t* qrow, const uint16_t* kv, const int32_t* id
   for (int d = 0; d < D; ++d) acc[d] = 0.0;
   double Z = 0.0;
   for (int64_t s = 0; s < topk; ++s) {
-    int64_t r = idx_row[s];
+    int64_t r = idx_at(idx_row, idx64, s);
     if (r < 0 || r >= num_kv) continue;
     double w = exp(x[s] - m);
     Z += w;
@@ -118,19 +127,22 @@ static void one_head(const uint16_t* qrow, const uint16_t* kv, const int32_t* id
 
 /*
  * q      bf16 bits [T, H, 512]          kv  bf16 bits [num_kv, 512]
- * topk   int32 [T, topk_n]              sink fp32 [H] or NULL
+ * topk   [T, topk_n] of idx_bytes-byte signed integers (4 or 8)
+ * sink   fp32 [H] or NULL
  * tokens int64 [n_tokens] token ids to evaluate, or NULL for 0..T-1
  * o_exact double [n_tokens, H, 512] or NULL;  o_bf16 uint16 [n_tokens, H, 512] or NULL
  * lse    double [n_tokens, H] (required)
  * n_valid int64 [n_tokens] or NULL: number of valid slots of each token
  * nthreads <= 0: OpenMP default.  Returns 0, or -1 on a bad argument.
  */
-int smla_oracle_forward(const uint16_t* q, const uint16_t* kv, const int32_t* topk, const float* sink,
-                        double scale, int64_t T, int64_t H, int64_t num_kv, int64_t topk_n,
-                        const int64_t* tokens, int64_t n_tokens, double* o_exact, uint16_t* o_bf16,
-                        double* lse, int64_t* n_valid, int nthreads) {
+int smla_oracle_forward_ix(const uint16_t* q, const uint16_t* kv, const void* topk, int idx_bytes,
+                           const float* sink, double scale, int64_t T, int64_t H, int64_t num_kv, int64_t topk_n,
+                           const int64_t* tokens, int64_t n_tokens, double* o_exact, uint16_t* o_bf16,
+                           double* lse, int64_t* n_valid, int nthreads) {
   const int D = SMLA_ORACLE_D;
   if (T < 0 || H < 1 || num_kv < 0 || topk_n < 0 || n_tokens < 0 || !lse) return -1;
+  if (idx_bytes != 4 && idx_bytes != 8) return -1;
+  const int idx64 = idx_bytes == 8;
   if (!tokens && n_tokens != T) return -1;
   if (n_tokens > 0 && (!q || !topk || (num_kv > 0 && !kv))) return -1;
   for (int64_t i = 0; tokens && i < n_tokens; ++i)
@@ -153,10 +165,13 @@ int smla_oracle_forward(const uint16_t* q, const uint16_t* kv, const int32_t* to
     for (int64_t i = 0; i < n_tokens; ++i) {
       if (!x || !acc) continue;
       int64_t t = tokens ? tokens[i] : i;
-      const int32_t* idx_row = topk + t * topk_n;
+      const void* idx_row = (const char*)topk + (size_t)(t * topk_n) * (size_t)idx_bytes;
       if (n_valid) {
         int64_t c = 0;
-        for (int64_t s = 0; s < topk_n; ++s) c += (idx_row[s] >= 0 && idx_row[s] < num_kv);
+        for (int64_t s = 0; s < topk_n; ++s) {
+          const int64_t r = idx_at(idx_row, idx64, s);
+          c += (r >= 0 && r < num_kv);
+        }
         n_valid[i] = c;
       }
       for (int64_t h = 0; h < H; ++h) {
@@ -166,7 +181,7 @@ int smla_oracle_forward(const uint16_t* q, const uint16_t* kv, const int32_t* to
           sk = (double)sink[h];
           has_sink = !(sk == -INFINITY);
         }
-        one_head(q + (t * H + h) * D, kv, idx_row, topk_n, num_kv, has_sink, sk, scale, x, acc,
+        one_head(q + (t * H + h) * D, kv, idx_row, idx64, topk_n, num_kv, has_sink, sk, scale, x, acc,
                  o_exact ? o_exact + (i * H + h) * D : NULL, o_bf16 ? o_bf16 + (i * H + h) * D : NULL,
                  lse + i * H + h);
       }
@@ -175,6 +190,15 @@ int smla_oracle_forward(const uint16_t* q, const uint16_t* kv, const int32_t* to
     free(acc);
   }
   return bad ? -2 : 0;
+}
+
+/* int32 indices. */
+int smla_oracle_forward(const uint16_t* q, const uint16_t* kv, const int32_t* topk, const float* sink,
+                        double scale, int64_t T, int64_t H, int64_t num_kv, int64_t topk_n,
+                        const int64_t* tokens, int64_t n_tokens, double* o_exact, uint16_t* o_bf16,
+                        double* lse, int64_t* n_valid, int nthreads) {
+  return smla_oracle_forward_ix(q, kv, topk, 4, sink, scale, T, H, num_kv, topk_n, tokens, n_tokens, o_exact,
+                                o_bf16, lse, n_valid, nthreads);
 }
 
 int smla_oracle_threads(void) {

@@ -282,3 +282,23 @@ def test_nan_in_referenced_row_stays_local():
         refs = victim in set(idx[t].tolist())
         assert np.isnan(r["lse"][t]).all() == refs
         assert (~np.isfinite(r["o"][t])).any() == refs
+
+
+def test_int64_indices_match_brute_force_and_never_wrap():
+    """int64 top-k rows: values at or past 2^31 that an int32 cast would wrap onto valid rows
+    (2^32 + r wraps to r) stay invalid; the result equals brute force on the same rows."""
+    q, kv, idx32, s = random_case(41, T=5, H=3, num_kv=40, topk=20, p_invalid=0.0)
+    idx = idx32.astype(np.int64)
+    rng = np.random.default_rng(42)
+    wrap = rng.random(idx.shape) < 0.3
+    idx[wrap] = idx[wrap] + 2**32          # would alias the same row after a cast to int32
+    idx[0, :3] = [2**31, -(2**40), 2**62]
+    ref = oracle.forward(q, kv, idx, s, 0.07)
+    bo, bl = brute_force(q, kv, idx, s, 0.07)
+    np.testing.assert_allclose(ref["o"], bo, rtol=0, atol=1e-10)
+    np.testing.assert_allclose(ref["lse"], bl, rtol=0, atol=1e-10)
+    # the same as int32 rows with those slots marked -1, bit for bit
+    idx_m = np.where((idx >= 0) & (idx < 40), idx, -1).astype(np.int32)
+    ref32 = oracle.forward(q, kv, idx_m, s, 0.07)
+    assert np.array_equal(ref["o"], ref32["o"]) and np.array_equal(ref["lse"], ref32["lse"])
+    assert np.array_equal(ref["n_valid"], ((idx >= 0) & (idx < 40)).sum(axis=1))
