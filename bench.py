@@ -119,7 +119,7 @@ def cpu_baseline(inp: dict, target_s: float = 10.0):
             "ms_per_call_extrapolated": dt * 1e3 * inp["T"] / len(tokens), "cpu_model": cpu_model()}
 
 
-def measure(name: str, steps: int, warmup: int, cold_steps: int = 0):
+def measure(name: str, steps: int, warmup: int, cold_steps: int = 0, idx64: bool = False):
     import torch
 
     from sparse_attention_top_amd import kernel_name, sparse_mla_prefill, synth
@@ -128,7 +128,7 @@ def measure(name: str, steps: int, warmup: int, cold_steps: int = 0):
     dev = torch.device("cuda:0")
     q = torch.from_numpy(inp["q"].view(np.int16)).view(torch.bfloat16).to(dev)
     kv = torch.from_numpy(inp["kv"].view(np.int16)).view(torch.bfloat16).to(dev)
-    topk = torch.from_numpy(inp["topk"]).to(dev)
+    topk = torch.from_numpy(inp["topk"].astype(np.int64) if idx64 else inp["topk"]).to(dev)
     sink = torch.from_numpy(inp["sink"]).to(dev) if inp["sink"] is not None else None
     out = torch.empty_like(q)
     lse = torch.empty((inp["T"], inp["H"]), dtype=torch.float32, device=dev)
@@ -238,16 +238,20 @@ def main():
           file=sys.stderr, flush=True)
     if not args.no_secondary:
         sec = []
-        for other in ("tp4", "large", "small", "glm", "decode"):
+        for other in ("tp4", "large", "small", "glm", "decode", "tp4:int64"):
             if other == args.workload:
                 continue
-            i2, a2, t2 = measure(other, max(10, args.steps // 2), args.warmup)
+            name2, _, kind = other.partition(":")
+            i2, a2, t2 = measure(name2, max(10, args.steps // 2), args.warmup, idx64=kind == "int64")
             b2 = "mfma" if i2["H"] > 16 else "hbm"
             sec.append({"workload": other, "ms_per_call": t2["ms_per_call"], "kernel_ms_mean": t2["kernel_ms_mean"],
                         "kernel_ms_median": t2["kernel_ms_median"], "kernel_ms_min": t2["kernel_ms_min"],
                         "tflops": a2["flops"] / (t2["ms_per_call"] * 1e-3) / 1e12,
                         "gathered_gbs": a2["gathered_bytes"] / (t2["ms_per_call"] * 1e-3) / 1e9,
-                        "valid_slots": a2["valid_slots"], "roofline": roofline(a2, t2, t2["kernel"], other, b2)})
+                        "valid_slots": a2["valid_slots"],
+                        "roofline": roofline(a2, t2, t2["kernel"], other, b2)})
+            if kind == "int64":
+                sec[-1]["note"] = "int64 top-k rows: index conversion kernel + the int32 path"
             if i2["T"] * -(-i2["H"] // 128) < 256:
                 sec[-1]["note"] = ("few-token call: split-KV kernel + merge kernel; per-launch events include the "
                                    "host launch gap, rocprofv3 kernel time is the GPU figure")

@@ -38,10 +38,12 @@ typedef enum {
   SMLA_OK = 0,
   SMLA_ERR_NULL_POINTER = -1, /* a buffer with nonzero size is NULL                       */
   SMLA_ERR_BAD_SIZE = -2,     /* T < 0, H < 1, num_kv < 0, topk < 0, or a size overflows   */
-  SMLA_ERR_MISALIGNED = -3,   /* q, kv or out not 16-byte aligned; lse, topk, sink not 4   */
+  SMLA_ERR_MISALIGNED = -3,   /* q, kv or out not 16-byte aligned; lse, sink, int32 topk
+                                 not 4; int64 topk not 8                                   */
   SMLA_ERR_BAD_SCALE = -4,    /* scale is NaN or infinite                                  */
   SMLA_ERR_NO_DEVICE = -5,    /* no usable HIP device is current                           */
-  SMLA_ERR_LAUNCH = -6        /* the kernel launch failed (hipGetLastError)                */
+  SMLA_ERR_LAUNCH = -6,       /* the kernel launch failed (hipGetLastError)                */
+  SMLA_ERR_NO_MEMORY = -7     /* sparse_mla_prefill_i64: its index scratch could not be had */
 } smla_status_t;
 
 /*
@@ -86,6 +88,26 @@ typedef enum {
 int sparse_mla_prefill(const void* q, const void* kv, const int32_t* topk_indices, const float* attn_sink,
                        float scale, void* out, float* lse, int64_t T, int64_t H, int64_t num_kv,
                        int64_t topk, void* stream);
+
+/*
+ * sparse_mla_prefill_i64 -- the same operation with int64 top-k rows
+ * (topk_indices: int64 [T, topk], contiguous, 8-byte aligned; every other
+ * argument as above).
+ *
+ * "[Triton/Gluon] [CI] [gfx942] Tuned sparse MLA prefill for DSv4.1-Flash
+ * TP4; fix attn_sink in Triton fallback" (aiter PR #6002), description: int64
+ * slot indices are kept as int64, because a cast to int32 wrapped slots at or
+ * past 2^31 onto valid rows. Here every index is compared as a 64-bit value:
+ * valid iff 0 <= idx < num_kv, anything else (2^32 + r included) is an
+ * invalid slot. A first kernel maps the rows to int32 row numbers (-1 for
+ * invalid) in stream-ordered scratch of 4 * T * topk bytes from the library's
+ * per-device pool (SMLA_ERR_NO_MEMORY if that cannot be had); the forward then
+ * runs as for int32 rows, so results are bitwise those of sparse_mla_prefill
+ * on the equivalent int32 rows.
+ */
+int sparse_mla_prefill_i64(const void* q, const void* kv, const int64_t* topk_indices, const float* attn_sink,
+                           float scale, void* out, float* lse, int64_t T, int64_t H, int64_t num_kv,
+                           int64_t topk, void* stream);
 
 /* Human-readable text for a status code (static storage; never NULL). */
 const char* sparse_mla_status_string(int status);

@@ -27,7 +27,8 @@ def sparse_mla_prefill(q, kv, topk_indices, attn_sink=None, scale=None, out=None
     """Sparse MLA prefill forward; returns ``(out, lse)``.
 
     q: bf16 [T, H, 512]; kv: bf16 [num_kv, 512] (K == V); topk_indices: int32
-    [T, topk] (any value outside [0, num_kv) is an invalid slot); attn_sink:
+    or int64 [T, topk] (any value outside [0, num_kv) is an invalid slot; int64
+    values are compared without narrowing); attn_sink:
     fp32 [H] or None; scale: float (default 1/sqrt(512)); out: optional bf16
     [T, H, 512] buffer; lse: optional fp32 [T, H] buffer. All tensors on the
     same GPU and contiguous. The work is enqueued on the current stream.
@@ -45,7 +46,8 @@ def sparse_mla_prefill(q, kv, topk_indices, attn_sink=None, scale=None, out=None
     _check(kv.dim() == 2 and kv.shape[1] == HEAD_DIM, "kv must be [num_kv, 512], got %s" % (tuple(kv.shape),))
     _check(kv.is_contiguous(), "kv must be contiguous")
     _check(topk_indices.device == dev, "topk_indices must be on %s" % dev)
-    _check(topk_indices.dtype == torch.int32, "topk_indices must be int32, got %s" % topk_indices.dtype)
+    _check(topk_indices.dtype in (torch.int32, torch.int64),
+           "topk_indices must be int32 or int64, got %s" % topk_indices.dtype)
     _check(topk_indices.dim() == 2 and topk_indices.shape[0] == T, "topk_indices must be [T, topk]")
     _check(topk_indices.is_contiguous(), "topk_indices must be contiguous")
     if attn_sink is not None:
@@ -70,7 +72,8 @@ def sparse_mla_prefill(q, kv, topk_indices, attn_sink=None, scale=None, out=None
     lib = _lib.load()
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        rc = lib.sparse_mla_prefill(
+        entry = lib.sparse_mla_prefill if topk_indices.dtype == torch.int32 else lib.sparse_mla_prefill_i64
+        rc = entry(
             q.data_ptr(), kv.data_ptr() if kv.numel() else None, topk_indices.data_ptr() if topk_indices.numel() else None,
             attn_sink.data_ptr() if attn_sink is not None else None, float(scale),
             out.data_ptr(), lse.data_ptr(), T, H, kv.shape[0], topk_indices.shape[1], stream)

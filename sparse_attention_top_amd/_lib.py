@@ -19,6 +19,12 @@ SIGNATURES = {
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,  # T, H, num_kv, topk
         ctypes.c_void_p,  # stream
     ]),
+    "sparse_mla_prefill_i64": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,  # q, kv, topk (int64), sink
+        ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,  # scale, out, lse
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,  # T, H, num_kv, topk
+        ctypes.c_void_p,  # stream
+    ]),
     "sparse_mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "sparse_mla_kernel_name": (ctypes.c_char_p, [ctypes.c_int64, ctypes.c_int64]),
     "sparse_mla_version": (ctypes.c_int, []),
@@ -31,6 +37,7 @@ SMLA_ERR_MISALIGNED = -3
 SMLA_ERR_BAD_SCALE = -4
 SMLA_ERR_NO_DEVICE = -5
 SMLA_ERR_LAUNCH = -6
+SMLA_ERR_NO_MEMORY = -7
 
 _lib = None
 

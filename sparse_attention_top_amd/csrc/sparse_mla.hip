@@ -768,11 +768,11 @@ hipMemPool_t scratch_pool(int dev) {
 
 bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
 
-}  // namespace
 
-extern "C" int sparse_mla_prefill(const void* q, const void* kv, const int32_t* topk_indices, const float* attn_sink,
-                                  float scale, void* out, float* lse, int64_t T, int64_t H, int64_t num_kv,
-                                  int64_t topk, void* stream) {
+// Argument checks shared by the entry points (idx_align: alignment the top-k
+// array needs). Everything but the device query.
+int check_args(const void* q, const void* kv, const void* topk_indices, size_t idx_align, const float* attn_sink,
+               float scale, const void* out, const float* lse, int64_t T, int64_t H, int64_t num_kv, int64_t topk) {
   if (T < 0 || H < 1 || num_kv < 0 || topk < 0) return SMLA_ERR_BAD_SIZE;
   if (T > INT32_MAX || H > INT32_MAX || topk > INT32_MAX) return SMLA_ERR_BAD_SIZE;
   if (!isfinite(scale)) return SMLA_ERR_BAD_SCALE;
@@ -786,14 +786,26 @@ extern "C" int sparse_mla_prefill(const void* q, const void* kv, const int32_t* 
   if (topk > 0 && !topk_indices) return SMLA_ERR_NULL_POINTER;
   if (topk > 0 && num_kv > 0 && !kv) return SMLA_ERR_NULL_POINTER;
   if (!aligned(q, 16) || !aligned(out, 16) || (kv && !aligned(kv, 16))) return SMLA_ERR_MISALIGNED;
-  if (!aligned(lse, 4) || (topk_indices && !aligned(topk_indices, 4)) || (attn_sink && !aligned(attn_sink, 4)))
+  if (!aligned(lse, 4) || (topk_indices && !aligned(topk_indices, idx_align)) || (attn_sink && !aligned(attn_sink, 4)))
     return SMLA_ERR_MISALIGNED;
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+  return SMLA_OK;
+}
+
+int current_device(int* dev) {
+  if (hipGetDevice(dev) != hipSuccess || *dev < 0) {
     (void)hipGetLastError();
     return SMLA_ERR_NO_DEVICE;
   }
+  return SMLA_OK;
+}
 
+// Enqueue the forward for int32 top-k rows (arguments already checked, T > 0).
+int run_prefill(const void* q, const void* kv, const int32_t* topk_indices, const float* attn_sink, float scale,
+                void* out, float* lse, int64_t T, int64_t H, int64_t num_kv, int64_t topk, int dev,
+                hipStream_t s) {
+  const Variant var = pick_variant(H, topk);
+  const int64_t heads_per_wg = (int64_t)16 * var.nw;
+  const int64_t head_groups = (H + heads_per_wg - 1) / heads_per_wg;
   Params p;
   p.q = (const uint16_t*)q;
   p.kv = (const uint16_t*)kv;
@@ -814,7 +826,6 @@ extern "C" int sparse_mla_prefill(const void* q, const void* kv, const int32_t* 
   sa.part_o = nullptr;
   sa.part_ml = nullptr;
   const int64_t units = T * head_groups;
-  hipStream_t s = (hipStream_t)stream;
 
   // Few (token, head group) units leave most CUs idle: split each top-k row
   // over several workgroups, then merge (stream-ordered scratch; if it cannot
@@ -853,15 +864,66 @@ extern "C" int sparse_mla_prefill(const void* q, const void* kv, const int32_t* 
   return err == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
 }
 
+// int64 top-k rows -> int32: a valid index (0 <= v < num_kv) becomes its row
+// number, anything else -1, so an index at or past 2^31 can never alias a row.
+__global__ __launch_bounds__(256) void smla_idx64_kernel(const int64_t* __restrict__ in, int32_t* __restrict__ out,
+                                                         int64_t n, int64_t num_kv) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+    const int64_t v = in[i];
+    out[i] = (v >= 0 && v < num_kv) ? (int32_t)v : -1;
+  }
+}
+
+}  // namespace
+
+extern "C" int sparse_mla_prefill(const void* q, const void* kv, const int32_t* topk_indices, const float* attn_sink,
+                                  float scale, void* out, float* lse, int64_t T, int64_t H, int64_t num_kv,
+                                  int64_t topk, void* stream) {
+  int rc = check_args(q, kv, topk_indices, 4, attn_sink, scale, out, lse, T, H, num_kv, topk);
+  if (rc != SMLA_OK || T == 0) return rc;
+  int dev = -1;
+  if ((rc = current_device(&dev)) != SMLA_OK) return rc;
+  return run_prefill(q, kv, topk_indices, attn_sink, scale, out, lse, T, H, num_kv, topk, dev, (hipStream_t)stream);
+}
+
+extern "C" int sparse_mla_prefill_i64(const void* q, const void* kv, const int64_t* topk_indices,
+                                      const float* attn_sink, float scale, void* out, float* lse, int64_t T,
+                                      int64_t H, int64_t num_kv, int64_t topk, void* stream) {
+  int rc = check_args(q, kv, topk_indices, 8, attn_sink, scale, out, lse, T, H, num_kv, topk);
+  if (rc != SMLA_OK || T == 0) return rc;
+  int dev = -1;
+  if ((rc = current_device(&dev)) != SMLA_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  if (topk == 0) return run_prefill(q, kv, nullptr, attn_sink, scale, out, lse, T, H, num_kv, topk, dev, s);
+  const int64_t n = T * topk;
+  void* ws = nullptr;
+  hipMemPool_t pool = scratch_pool(dev);
+  if (pool == nullptr || hipMallocFromPoolAsync(&ws, (size_t)n * sizeof(int32_t), pool, s) != hipSuccess ||
+      ws == nullptr) {
+    (void)hipGetLastError();
+    return SMLA_ERR_NO_MEMORY;
+  }
+  const int64_t want = (n + 255) / 256;
+  const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(smla_idx64_kernel, dim3(blocks), dim3(256), 0, s, topk_indices, (int32_t*)ws, n, num_kv);
+  rc = hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
+  if (rc == SMLA_OK)
+    rc = run_prefill(q, kv, (const int32_t*)ws, attn_sink, scale, out, lse, T, H, num_kv, topk, dev, s);
+  if (hipFreeAsync(ws, s) != hipSuccess && rc == SMLA_OK) rc = SMLA_ERR_LAUNCH;
+  return rc;
+}
+
 extern "C" const char* sparse_mla_status_string(int status) {
   switch (status) {
     case SMLA_OK: return "ok";
     case SMLA_ERR_NULL_POINTER: return "a required pointer is NULL";
     case SMLA_ERR_BAD_SIZE: return "invalid size (T<0, H<1, num_kv<0, topk<0, or overflow)";
-    case SMLA_ERR_MISALIGNED: return "misaligned pointer (q, kv, out need 16 bytes; lse, topk, sink need 4)";
+    case SMLA_ERR_MISALIGNED: return "misaligned pointer (q, kv, out need 16 bytes; lse, sink and int32 topk 4; int64 topk 8)";
     case SMLA_ERR_BAD_SCALE: return "scale must be finite";
     case SMLA_ERR_NO_DEVICE: return "no usable HIP device";
     case SMLA_ERR_LAUNCH: return "kernel launch failed";
+    case SMLA_ERR_NO_MEMORY: return "device scratch for the int64 index conversion could not be allocated";
     default: return "unknown status";
   }
 }
@@ -871,4 +933,4 @@ extern "C" const char* sparse_mla_kernel_name(int64_t H, int64_t topk) {
   return pick_variant(H, topk).name;
 }
 
-extern "C" int sparse_mla_version(void) { return 101; }
+extern "C" int sparse_mla_version(void) { return 102; }

@@ -23,10 +23,11 @@ def bf16_bits(t: torch.Tensor) -> np.ndarray:
 
 
 def run_gpu(q, kv, topk, sink, scale, out=None, lse=None):
-    """numpy inputs (bf16 bits, int32, fp32) -> (o bits uint16, lse float32), via the C ABI."""
+    """numpy inputs (bf16 bits, int32 or int64 rows, fp32) -> (o bits uint16, lse float32), via the C ABI."""
     qd = to_dev_bf16(q)
     kvd = to_dev_bf16(kv) if kv.shape[0] else torch.empty((0, 512), dtype=torch.bfloat16, device=DEV)
-    td = torch.from_numpy(np.ascontiguousarray(topk, dtype=np.int32)).to(DEV)
+    topk = np.asarray(topk)
+    td = torch.from_numpy(np.ascontiguousarray(topk, dtype=np.int64 if topk.dtype == np.int64 else np.int32)).to(DEV)
     sd = None if sink is None else torch.from_numpy(np.ascontiguousarray(sink, dtype=np.float32)).to(DEV)
     o, l = sparse_mla_prefill(qd, kvd, td, sd, scale, out=out, lse=lse)
     torch.cuda.synchronize()

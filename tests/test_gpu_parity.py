@@ -311,8 +311,8 @@ def test_binding_rejects_bad_inputs():
         sparse_mla_prefill(q, kv.float(), idx)
     with pytest.raises(RuntimeError, match="bfloat16"):
         sparse_mla_prefill(q.half(), kv, idx)
-    with pytest.raises(RuntimeError, match="int32"):
-        sparse_mla_prefill(q, kv, idx.long())
+    with pytest.raises(RuntimeError, match="int32 or int64"):
+        sparse_mla_prefill(q, kv, idx.short())
     with pytest.raises(RuntimeError, match="GPU"):
         sparse_mla_prefill(q.cpu(), kv, idx)
     with pytest.raises(RuntimeError, match="contiguous"):
@@ -361,3 +361,25 @@ def test_decode_workload_full():
     inp = synth.make_inputs("decode")
     o, lse = run_case(inp)
     compare(o, lse, oracle_ref(inp), what="decode")
+
+
+# ---- int64 top-k rows ----
+
+@pytest.mark.parametrize("T,H,topk,num_kv", [(40, 16, 300, 1000), (24, 128, 512, 2000), (3, 16, 1024, 4000)])
+def test_int64_indices_never_wrap(T, H, topk, num_kv):
+    """int64 rows: values 2^32 + r (which an int32 cast would turn into row r), 2^31 and large
+    negatives are invalid; the result equals the oracle and, bitwise, the int32 path on the
+    equivalent rows (invalid -> -1)."""
+    inp = make_random(5000 + T + H, T=T, H=H, num_kv=num_kv, topk=topk, p_invalid=0.1)
+    rng = np.random.default_rng(T * H)
+    idx = inp["topk"].astype(np.int64)
+    wrap = (rng.random(idx.shape) < 0.25) & (idx >= 0)
+    idx[wrap] += 2**32
+    idx[:, 0] = 2**31
+    idx[:, 1] = -(2**40)
+    o64, l64 = run_gpu(inp["q"], inp["kv"], idx, inp["sink"], inp["scale"])
+    ref = oracle_ref(dict(inp, topk=idx))
+    compare(o64, l64, ref, what="int64 T=%d H=%d" % (T, H))
+    idx32 = np.where((idx >= 0) & (idx < num_kv), idx, -1).astype(np.int32)
+    o32, l32 = run_gpu(inp["q"], inp["kv"], idx32, inp["sink"], inp["scale"])
+    assert np.array_equal(o64, o32) and np.array_equal(l64.view(np.uint32), l32.view(np.uint32))
