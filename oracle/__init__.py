@@ -58,6 +58,13 @@ def _load():
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
         ]
+        lib.smla_oracle_forward_kv.restype = ctypes.c_int
+        lib.smla_oracle_forward_kv.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_double, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ]
         lib.smla_oracle_threads.restype = ctypes.c_int
         lib.smla_oracle_threads.argtypes = []
         _lib = lib
@@ -68,17 +75,19 @@ def _ptr(a):
     return None if a is None else a.ctypes.data
 
 
-def forward(q, kv, topk, sink, scale, tokens=None, *, want_exact=True, want_bf16=True, threads=0):
+def forward(q, kv, topk, sink, scale, tokens=None, *, want_exact=True, want_bf16=True, threads=0, kv_scale=None):
     """Evaluate the definition for the given tokens (all tokens when None).
 
-    q: uint16 bf16 bits [T, H, 512]; kv: uint16 bf16 bits [num_kv, 512];
+    q: uint16 bf16 bits [T, H, 512]; kv: uint16 bf16 bits [num_kv, 512], or
+    uint8 OCP FP8 E4M3 codes [num_kv, 512] with ``kv_scale`` (K == V == code * kv_scale);
     topk: int32 or int64 [T, topk]; sink: float32 [H] or None; scale: float.
     Returns a dict with ``o`` (float64 [n, H, 512], unrounded), ``o_bf16``
     (uint16 bits [n, H, 512]), ``lse`` (float64 [n, H], natural log) and
     ``n_valid`` (int64 [n]).
     """
     q = np.ascontiguousarray(q, dtype=np.uint16)
-    kv = np.ascontiguousarray(kv, dtype=np.uint16)
+    kv_fp8 = kv_scale is not None
+    kv = np.ascontiguousarray(kv, dtype=np.uint8 if kv_fp8 else np.uint16)
     topk = np.asarray(topk)
     topk = np.ascontiguousarray(topk, dtype=np.int64 if topk.dtype == np.int64 else np.int32)
     T, H, d = q.shape
@@ -101,8 +110,9 @@ def forward(q, kv, topk, sink, scale, tokens=None, *, want_exact=True, want_bf16
     ob = np.empty((n, H, D), np.uint16) if want_bf16 else None
     lse = np.empty((n, H), np.float64)
     nv = np.empty((n,), np.int64)
-    rc = _load().smla_oracle_forward_ix(
-        _ptr(q), _ptr(kv) if num_kv > 0 else None, _ptr(topk), topk.itemsize, _ptr(sink), float(scale),
+    rc = _load().smla_oracle_forward_kv(
+        _ptr(q), _ptr(kv) if num_kv > 0 else None, int(kv_fp8), float(kv_scale) if kv_fp8 else 1.0,
+        _ptr(topk), topk.itemsize, _ptr(sink), float(scale),
         T, H, num_kv, topk.shape[1], _ptr(tok), n, _ptr(o), _ptr(ob), _ptr(lse), _ptr(nv), int(threads))
     if rc != 0:
         raise RuntimeError("oracle rejected its arguments (rc=%d)" % rc)

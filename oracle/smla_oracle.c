@@ -39,6 +39,13 @@
  *    so such a slot is simply invalid.
  *  - NaN anywhere in a referenced row or in q propagates to that (t,h).
  *
+ * KV pools may also hold OCP FP8 E4M3 ("e4m3fn") codes with one fp32 dequant
+ * scale for the whole pool (the forward pages only mention fp8 caches, as a
+ * type the Triton path rejected; reading: K == V == code value * kv_scale).
+ * Each code is decoded exactly from the format's definition: sign bit,
+ * 4-bit exponent with bias 7, 3-bit mantissa; exponent 0 is subnormal
+ * (m/8 * 2^-6); exponent 15 with mantissa 7 is NaN; there is no infinity.
+ *
  * Precision: inputs are bf16 widened exactly; every sum, exp and log is done
  * in double. o is returned both unrounded (double) and rounded to bf16
  * (double -> float -> bf16, each round to nearest even).
@@ -71,13 +78,27 @@ static uint16_t float_to_bf16_rne(float f) {
   return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
 }
 
+/* One OCP FP8 E4M3 code, exactly. */
+static double e4m3_to_double(uint8_t c) {
+  const int sgn = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return NAN;
+  const double v = e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sgn ? -v : v;
+}
+
+/* Element d of pool row r: bf16 bits, or an fp8 code times kv_scale. */
+static double kv_at(const void* kv, int kv_fp8, double kv_scale, int64_t r, int d) {
+  if (kv_fp8) return e4m3_to_double(((const uint8_t*)kv)[r * SMLA_ORACLE_D + d]) * kv_scale;
+  return bf16_to_double(((const uint16_t*)kv)[r * SMLA_ORACLE_D + d]);
+}
+
 /* Index s of a top-k row of 4- or 8-byte signed integers. */
 static int64_t idx_at(const void* row, int idx64, int64_t s) {
   return idx64 ? ((const int64_t*)row)[s] : (int64_t)((const int32_t*)row)[s];
 }
 
 /* One (t, h) pair, written straight from the definition above. */
-static void one_head(const uint16_t* qrow, const uint16_t* kv, const void* idx_row, int idx64,
+static void one_head(const uint16_t* qrow, const void* kv, int kv_fp8, double kv_scale, const void* idx_row, int idx64,
                      int64_t topk, int64_t num_kv, int has_sink, double sink, double scale,
                      double* x /* scratch [topk] */, double* acc /* scratch [D] */,
                      double* o_exact, uint16_t* o_bf16, double* lse_out) {
@@ -87,9 +108,8 @@ static void one_head(const uint16_t* qrow, const uint16_t* kv, const void* idx_r
   for (int64_t s = 0; s < topk; ++s) {
     int64_t r = idx_at(idx_row, idx64, s);
     if (r < 0 || r >= num_kv) continue;
-    const uint16_t* krow = kv + r * D;
     double dot = 0.0;
-    for (int d = 0; d < D; ++d) dot += bf16_to_double(qrow[d]) * bf16_to_double(krow[d]);
+    for (int d = 0; d < D; ++d) dot += bf16_to_double(qrow[d]) * kv_at(kv, kv_fp8, kv_scale, r, d);
     double xs = scale * dot;
     x[s] = xs;
     if (!(xs <= m)) m = xs; /* a NaN logit makes m NaN */
@@ -113,8 +133,7 @@ static void one_head(const uint16_t* qrow, const uint16_t* kv, const void* idx_r
     if (r < 0 || r >= num_kv) continue;
     double w = exp(x[s] - m);
     Z += w;
-    const uint16_t* vrow = kv + r * D;
-    for (int d = 0; d < D; ++d) acc[d] += w * bf16_to_double(vrow[d]);
+    for (int d = 0; d < D; ++d) acc[d] += w * kv_at(kv, kv_fp8, kv_scale, r, d);
   }
   if (has_sink) Z += exp(sink - m);
   for (int d = 0; d < D; ++d) {
@@ -135,10 +154,10 @@ static void one_head(const uint16_t* qrow, const uint16_t* kv, const void* idx_r
  * n_valid int64 [n_tokens] or NULL: number of valid slots of each token
  * nthreads <= 0: OpenMP default.  Returns 0, or -1 on a bad argument.
  */
-int smla_oracle_forward_ix(const uint16_t* q, const uint16_t* kv, const void* topk, int idx_bytes,
-                           const float* sink, double scale, int64_t T, int64_t H, int64_t num_kv, int64_t topk_n,
-                           const int64_t* tokens, int64_t n_tokens, double* o_exact, uint16_t* o_bf16,
-                           double* lse, int64_t* n_valid, int nthreads) {
+int smla_oracle_forward_kv(const uint16_t* q, const void* kv, int kv_fp8, double kv_scale, const void* topk,
+                           int idx_bytes, const float* sink, double scale, int64_t T, int64_t H, int64_t num_kv,
+                           int64_t topk_n, const int64_t* tokens, int64_t n_tokens, double* o_exact,
+                           uint16_t* o_bf16, double* lse, int64_t* n_valid, int nthreads) {
   const int D = SMLA_ORACLE_D;
   if (T < 0 || H < 1 || num_kv < 0 || topk_n < 0 || n_tokens < 0 || !lse) return -1;
   if (idx_bytes != 4 && idx_bytes != 8) return -1;
@@ -181,7 +200,8 @@ int smla_oracle_forward_ix(const uint16_t* q, const uint16_t* kv, const void* to
           sk = (double)sink[h];
           has_sink = !(sk == -INFINITY);
         }
-        one_head(q + (t * H + h) * D, kv, idx_row, idx64, topk_n, num_kv, has_sink, sk, scale, x, acc,
+        one_head(q + (t * H + h) * D, kv, kv_fp8, kv_scale, idx_row, idx64, topk_n, num_kv, has_sink, sk, scale, x,
+                 acc,
                  o_exact ? o_exact + (i * H + h) * D : NULL, o_bf16 ? o_bf16 + (i * H + h) * D : NULL,
                  lse + i * H + h);
       }
@@ -190,6 +210,15 @@ int smla_oracle_forward_ix(const uint16_t* q, const uint16_t* kv, const void* to
     free(acc);
   }
   return bad ? -2 : 0;
+}
+
+/* bf16 pool, int32 or int64 indices. */
+int smla_oracle_forward_ix(const uint16_t* q, const uint16_t* kv, const void* topk, int idx_bytes,
+                           const float* sink, double scale, int64_t T, int64_t H, int64_t num_kv, int64_t topk_n,
+                           const int64_t* tokens, int64_t n_tokens, double* o_exact, uint16_t* o_bf16,
+                           double* lse, int64_t* n_valid, int nthreads) {
+  return smla_oracle_forward_kv(q, kv, 0, 1.0, topk, idx_bytes, sink, scale, T, H, num_kv, topk_n, tokens, n_tokens,
+                                o_exact, o_bf16, lse, n_valid, nthreads);
 }
 
 /* int32 indices. */

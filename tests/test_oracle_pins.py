@@ -302,3 +302,82 @@ def test_int64_indices_match_brute_force_and_never_wrap():
     ref32 = oracle.forward(q, kv, idx_m, s, 0.07)
     assert np.array_equal(ref["o"], ref32["o"]) and np.array_equal(ref["lse"], ref32["lse"])
     assert np.array_equal(ref["n_valid"], ((idx >= 0) & (idx < 40)).sum(axis=1))
+
+
+# ---- fp8 (OCP E4M3) pools with one dequant scale ----
+
+def fp8_decode_torch(codes):
+    """Library decode of OCP FP8 E4M3 codes (torch's float8_e4m3fn), float64."""
+    return torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def brute_force_f64pool(q, pool, idx, sink, scale):
+    """brute_force() on a float64 pool (dense masked attention by library routines)."""
+    T, H, _ = q.shape
+    num_kv = pool.shape[0]
+    K = torch.from_numpy(np.vstack([pool, np.zeros((1, D))]))
+    o = np.zeros((T, H, D))
+    lse = np.full((T, H), -np.inf)
+    for t in range(T):
+        valid = np.zeros(num_kv + 1, bool)
+        r = idx[t].astype(np.int64)
+        valid[r[(r >= 0) & (r < num_kv)]] = True
+        mask = np.where(valid, 0.0, -np.inf)[None, :].repeat(H, 0)
+        if sink is not None:
+            mask[:, num_kv] = sink.astype(np.float64)
+        Q = torch.from_numpy(f32(q[t]))[:, None, :]
+        logits = scale * (f32(q[t]) @ K.numpy().T) + mask
+        out = torch.nn.functional.scaled_dot_product_attention(
+            Q, K[None].expand(H, -1, -1), K[None].expand(H, -1, -1),
+            attn_mask=torch.from_numpy(mask)[:, None, :], scale=scale).numpy()[:, 0, :]
+        for h in range(H):
+            if np.isfinite(mask[h]).any():
+                o[t, h] = out[h]
+                lse[t, h] = scipy.special.logsumexp(logits[h])
+    return o, lse
+
+
+def test_fp8_decode_matches_library_for_every_code():
+    """A single valid slot and q = 0 return the row itself: every non-NaN code, times the scale,
+    must equal torch's own decode of the format (subnormals, both zeros, the largest values)."""
+    codes = np.arange(256, dtype=np.uint8)
+    codes = np.where((codes & 0x7F) == 0x7F, 0, codes)  # NaN codes are covered by the NaN test
+    pool = np.vstack([np.concatenate([codes, codes[::-1]])[None, :], np.full((1, D), 0x38, np.uint8)])
+    q = np.zeros((1, 2, D), np.uint16)
+    idx = np.array([[0, -1]], np.int32)
+    for kv_scale in (1.0, 0.375, 2.0 ** -9):
+        ref = oracle.forward(q, pool, idx, None, 0.1, kv_scale=kv_scale)
+        want = fp8_decode_torch(pool[0]) * kv_scale
+        assert np.array_equal(ref["o"][0, 0], want) and np.array_equal(ref["o"][0, 1], want)
+        assert np.all(ref["lse"] == 0.0)
+
+
+@pytest.mark.parametrize("seed,sink", [(51, True), (52, False)])
+def test_fp8_pool_matches_brute_force(seed, sink):
+    q, _, idx, s = random_case(seed, T=5, H=4, num_kv=40, topk=24, sink=sink)
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, (40, D)).astype(np.uint8)
+    codes = np.where((codes & 0x7F) == 0x7F, 0x3A, codes)  # no NaN codes here
+    kv_scale = 0.0625
+    ref = oracle.forward(q, codes, idx, s, 0.05, kv_scale=kv_scale)
+    bo, bl = brute_force_f64pool(q, fp8_decode_torch(codes) * kv_scale, idx, s, 0.05)
+    np.testing.assert_allclose(ref["o"], bo, rtol=0, atol=1e-10)
+    np.testing.assert_allclose(ref["lse"], bl, rtol=0, atol=1e-10)
+
+
+def test_fp8_nan_codes_stay_local():
+    """A NaN code (0x7F or 0xFF) in a referenced row makes that token NaN; in an unreferenced row it
+    changes nothing."""
+    q, _, idx, s = random_case(53, T=4, H=3, num_kv=30, topk=10, p_invalid=0.0)
+    rng = np.random.default_rng(53)
+    codes = rng.integers(0, 0x70, (30, D)).astype(np.uint8)
+    base = oracle.forward(q, codes, idx, s, 0.05, kv_scale=0.5)
+    unused = np.setdiff1d(np.arange(30), idx.ravel())
+    poisoned = codes.copy()
+    poisoned[unused, 5] = 0x7F
+    r_used = idx[2, 3]
+    poisoned[r_used, 7] = 0xFF
+    ref = oracle.forward(q, poisoned, idx, s, 0.05, kv_scale=0.5)
+    hit = np.array([(idx[t] == r_used).any() for t in range(4)])
+    assert np.all(np.isnan(ref["o"][hit])) and np.all(np.isnan(ref["lse"][hit]))
+    assert np.array_equal(ref["o"][~hit], base["o"][~hit]) and np.array_equal(ref["lse"][~hit], base["lse"][~hit])
