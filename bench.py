@@ -33,7 +33,8 @@ def algorithmic(inp: dict) -> dict:
     T, H, k = inp["T"], inp["H"], inp["topk_n"]
     nvalid = int(((inp["topk"] >= 0) & (inp["topk"] < inp["num_kv"])).sum())
     flops = 4.0 * H * D * nvalid  # S = QK^T and O = PV, 2 flop per MAC each
-    gathered = 1024.0 * nvalid  # one 1 KiB row per valid slot (K == V)
+    row = 512.0 if inp.get("kv_scale") is not None else 1024.0  # fp8 or bf16 pool row
+    gathered = row * nvalid  # one pool row per valid slot (K == V)
     io = T * H * 1024.0 * 2 + T * H * 4.0 + T * k * 4.0  # q + o + lse + indices
     return {"valid_slots": nvalid, "flops": flops, "gathered_bytes": gathered, "bytes": gathered + io}
 
@@ -103,14 +104,14 @@ def cpu_baseline(inp: dict, target_s: float = 10.0):
     tokens = np.linspace(0, T - 1, n).round().astype(np.int64)
     t0 = time.perf_counter()
     oracle.forward(inp["q"], inp["kv"], inp["topk"], inp["sink"], inp["scale"], tokens=tokens,
-                   want_exact=False, want_bf16=True)
+                   want_exact=False, want_bf16=True, kv_scale=inp.get("kv_scale"))
     dt = time.perf_counter() - t0
     if dt < target_s / 4 and n < T:  # grow the sample toward the target wall time
         n = int(min(T, n * max(1.0, target_s / max(dt, 1e-3))))
         tokens = np.linspace(0, T - 1, n).round().astype(np.int64)
         t0 = time.perf_counter()
         oracle.forward(inp["q"], inp["kv"], inp["topk"], inp["sink"], inp["scale"], tokens=tokens,
-                       want_exact=False, want_bf16=True)
+                       want_exact=False, want_bf16=True, kv_scale=inp.get("kv_scale"))
         dt = time.perf_counter() - t0
     nv = int(((inp["topk"][tokens] >= 0) & (inp["topk"][tokens] < inp["num_kv"])).sum())
     flops = 4.0 * inp["H"] * D * nv
@@ -127,7 +128,11 @@ def measure(name: str, steps: int, warmup: int, cold_steps: int = 0, idx64: bool
     inp = synth.make_inputs(name)
     dev = torch.device("cuda:0")
     q = torch.from_numpy(inp["q"].view(np.int16)).view(torch.bfloat16).to(dev)
-    kv = torch.from_numpy(inp["kv"].view(np.int16)).view(torch.bfloat16).to(dev)
+    kv_scale = inp.get("kv_scale")
+    if kv_scale is not None:  # OCP FP8 E4M3 codes
+        kv = torch.from_numpy(inp["kv"]).to(dev).view(torch.float8_e4m3fn)
+    else:
+        kv = torch.from_numpy(inp["kv"].view(np.int16)).view(torch.bfloat16).to(dev)
     topk = torch.from_numpy(inp["topk"].astype(np.int64) if idx64 else inp["topk"]).to(dev)
     sink = torch.from_numpy(inp["sink"]).to(dev) if inp["sink"] is not None else None
     out = torch.empty_like(q)
@@ -135,7 +140,7 @@ def measure(name: str, steps: int, warmup: int, cold_steps: int = 0, idx64: bool
     stream = torch.cuda.current_stream(dev)
 
     def run():
-        sparse_mla_prefill(q, kv, topk, sink, inp["scale"], out=out, lse=lse)
+        sparse_mla_prefill(q, kv, topk, sink, inp["scale"], out=out, lse=lse, kv_scale=kv_scale)
 
     wall, st = time_gpu(run, steps, warmup, stream)
     alg = algorithmic(inp)
@@ -168,7 +173,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="wide", choices=["tiny", "small", "tp4", "wide", "large", "glm", "decode"])
+    ap.add_argument("--workload", default="wide", choices=["tiny", "small", "tp4", "wide", "large", "glm", "decode",
+                                                          "tp4_fp8", "wide_fp8", "glm_fp8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timing of the main workload")
@@ -210,6 +216,8 @@ def main():
     else:
         metric, value, unit = "sparse MLA prefill fwd gathered-KV GB/s (H=%d)" % inp["H"], gbs, "GB/s"
     cfg = inp["config"]
+    if inp.get("kv_scale") is not None:
+        metric = metric + " [fp8 pool]"
     line = {
         "metric": metric,
         "value": value,
@@ -238,7 +246,7 @@ def main():
           file=sys.stderr, flush=True)
     if not args.no_secondary:
         sec = []
-        for other in ("tp4", "large", "small", "glm", "decode", "tp4:int64"):
+        for other in ("tp4", "large", "small", "glm", "decode", "tp4:int64", "tp4_fp8", "glm_fp8", "wide_fp8"):
             if other == args.workload:
                 continue
             name2, _, kind = other.partition(":")

@@ -90,6 +90,24 @@ int sparse_mla_prefill(const void* q, const void* kv, const int32_t* topk_indice
                        int64_t topk, void* stream);
 
 /*
+ * sparse_mla_prefill_fp8 -- the same operation on a pool of OCP FP8 E4M3
+ * ("e4m3fn") codes: kv is uint8 [num_kv, 512], contiguous, 16-byte aligned,
+ * and K == V == code value * kv_scale (one fp32 dequant scale for the pool;
+ * any finite value). Codes decode exactly (exponent bias 7, subnormals at
+ * exponent 0, NaN at S.1111.111, no infinity); a NaN code in a referenced row
+ * propagates to that (t,h) like a NaN in a bf16 row. Every other argument as
+ * for sparse_mla_prefill (int32 rows). The forward pages only mention fp8
+ * caches, as a type their Triton path could not take ("[Triton/Gluon] [CI]
+ * [gfx942] Tuned sparse MLA prefill for DSv4.1-Flash TP4; fix attn_sink in
+ * Triton fallback" (aiter PR #6002), description and review); the gather
+ * moves half the bytes of a bf16 pool. SMLA_ERR_BAD_SCALE if kv_scale or
+ * scale * kv_scale is not finite.
+ */
+int sparse_mla_prefill_fp8(const void* q, const void* kv, float kv_scale, const int32_t* topk_indices,
+                           const float* attn_sink, float scale, void* out, float* lse, int64_t T, int64_t H,
+                           int64_t num_kv, int64_t topk, void* stream);
+
+/*
  * sparse_mla_prefill_i64 -- the same operation with int64 top-k rows
  * (topk_indices: int64 [T, topk], contiguous, 8-byte aligned; every other
  * argument as above).

@@ -23,13 +23,15 @@ def _check(cond: bool, msg: str):
         raise RuntimeError(msg)
 
 
-def sparse_mla_prefill(q, kv, topk_indices, attn_sink=None, scale=None, out=None, lse=None):
+def sparse_mla_prefill(q, kv, topk_indices, attn_sink=None, scale=None, out=None, lse=None, kv_scale=None):
     """Sparse MLA prefill forward; returns ``(out, lse)``.
 
     q: bf16 [T, H, 512]; kv: bf16 [num_kv, 512] (K == V); topk_indices: int32
     or int64 [T, topk] (any value outside [0, num_kv) is an invalid slot; int64
     values are compared without narrowing); attn_sink:
-    fp32 [H] or None; scale: float (default 1/sqrt(512)); out: optional bf16
+    fp32 [H] or None; scale: float (default 1/sqrt(512)); kv may instead be a
+    float8_e4m3fn [num_kv, 512] pool with its dequant scale ``kv_scale`` (K == V ==
+    code * kv_scale; int32 rows only); out: optional bf16
     [T, H, 512] buffer; lse: optional fp32 [T, H] buffer. All tensors on the
     same GPU and contiguous. The work is enqueued on the current stream.
     """
@@ -42,7 +44,10 @@ def sparse_mla_prefill(q, kv, topk_indices, attn_sink=None, scale=None, out=None
     _check(q.is_contiguous(), "q must be contiguous")
     T, H, _ = q.shape
     _check(kv.device == dev, "kv must be on %s, got %s" % (dev, kv.device))
-    _check(kv.dtype == q.dtype, "kv dtype mismatch: kv is %s, q is %s" % (kv.dtype, q.dtype))
+    fp8 = kv.dtype == torch.float8_e4m3fn
+    _check(kv.dtype == q.dtype or fp8,
+           "kv dtype mismatch: kv is %s, q is %s (or float8_e4m3fn with kv_scale)" % (kv.dtype, q.dtype))
+    _check(fp8 == (kv_scale is not None), "kv_scale goes with a float8_e4m3fn pool, and only with one")
     _check(kv.dim() == 2 and kv.shape[1] == HEAD_DIM, "kv must be [num_kv, 512], got %s" % (tuple(kv.shape),))
     _check(kv.is_contiguous(), "kv must be contiguous")
     _check(topk_indices.device == dev, "topk_indices must be on %s" % dev)
@@ -72,11 +77,18 @@ def sparse_mla_prefill(q, kv, topk_indices, attn_sink=None, scale=None, out=None
     lib = _lib.load()
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        entry = lib.sparse_mla_prefill if topk_indices.dtype == torch.int32 else lib.sparse_mla_prefill_i64
-        rc = entry(
-            q.data_ptr(), kv.data_ptr() if kv.numel() else None, topk_indices.data_ptr() if topk_indices.numel() else None,
-            attn_sink.data_ptr() if attn_sink is not None else None, float(scale),
-            out.data_ptr(), lse.data_ptr(), T, H, kv.shape[0], topk_indices.shape[1], stream)
+        kvp = kv.data_ptr() if kv.numel() else None
+        tkp = topk_indices.data_ptr() if topk_indices.numel() else None
+        skp = attn_sink.data_ptr() if attn_sink is not None else None
+        if fp8:
+            _check(topk_indices.dtype == torch.int32, "a float8_e4m3fn pool takes int32 topk_indices")
+            rc = lib.sparse_mla_prefill_fp8(q.data_ptr(), kvp, float(kv_scale), tkp, skp, float(scale),
+                                            out.data_ptr(), lse.data_ptr(), T, H, kv.shape[0], topk_indices.shape[1],
+                                            stream)
+        else:
+            entry = lib.sparse_mla_prefill if topk_indices.dtype == torch.int32 else lib.sparse_mla_prefill_i64
+            rc = entry(q.data_ptr(), kvp, tkp, skp, float(scale), out.data_ptr(), lse.data_ptr(), T, H, kv.shape[0],
+                       topk_indices.shape[1], stream)
     if rc != 0:
         raise RuntimeError("sparse_mla_prefill failed: %s (status %d)" % (_lib.status_string(rc), rc))
     return out, lse

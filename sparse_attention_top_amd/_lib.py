@@ -19,6 +19,12 @@ SIGNATURES = {
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,  # T, H, num_kv, topk
         ctypes.c_void_p,  # stream
     ]),
+    "sparse_mla_prefill_fp8": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,  # q, kv, kv_scale, topk, sink
+        ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,  # scale, out, lse
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,  # T, H, num_kv, topk
+        ctypes.c_void_p,  # stream
+    ]),
     "sparse_mla_prefill_i64": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,  # q, kv, topk (int64), sink
         ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,  # scale, out, lse

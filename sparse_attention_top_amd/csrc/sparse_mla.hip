@@ -36,6 +36,7 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "sparse_mla.h"
 
@@ -71,7 +72,8 @@ struct Params {
   uint32_t nkv;  // min(num_kv, 2^31): slot valid iff (uint32)idx < nkv
   int topk_n;
   int head_groups;
-  float scale_log2;  // scale * log2(e)
+  float scale_log2;  // scale * log2(e) (times the pool's dequant scale for fp8 pools)
+  float out_scale;   // fp8 pools: the dequant scale, applied to o at the end
 };
 
 // Split over the top-k row (few tokens): split `sp` of a row covers raw
@@ -118,6 +120,22 @@ template <int OFF>
 __device__ __forceinline__ u32x2 ds_read_tr16_b64(uint32_t addr) {
   u32x2 r;
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ u32x2 ds_read_b64(uint32_t addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+// gfx950 transposing read of 8-bit elements: in each 16-lane group, lane li
+// fetches 8 bytes at its address and receives byte (li % 8) of the fetches of
+// lanes 2m + li / 8, m = 0..7 -- with lane 2m + h addressing columns 8h..8h+7 of
+// row m, lane li gets column li of the group's 8 rows.
+template <int OFF>
+__device__ __forceinline__ u32x2 ds_read_tr8_b64(uint32_t addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
   return r;
 }
 template <int N, typename T>
@@ -327,6 +345,51 @@ struct TileIssue {
   __device__ __forceinline__ int count() const { return active ? min(RPW, max(0, cnt - r0)) : 0; }
 };
 
+// The gather of one tile of an fp8 pool (512-byte rows). The tile's LDS
+// layout is slab-major: block k (1 KiB) holds d = 32k .. 32k+31 of all 32 rows,
+// as two 16-byte chunks per row with chunk j of row r at 16 (r + 32 j). One
+// LDS-DMA instruction fills one block (lane L fetches row L % 32, chunk L / 32),
+// so a tile takes 16 instructions; wave w fills blocks [w SPW, (w+1) SPW). Rows
+// past the tile's count are zero-filled.
+template <int NW>
+struct TileIssue8 {
+  static constexpr int SPW = 16 / NW;
+  const uint8_t* kv;
+  uint32_t tile;
+  int k0;
+  int idx;  // list entry of row lane % 32
+  bool act, valid;
+
+  __device__ __forceinline__ void init(const int32_t* list, int i, int n, bool act_, uint32_t buf, const uint8_t* kv_,
+                                       int lane, int w) {
+    kv = kv_;
+    act = act_;
+    tile = buf;
+    k0 = w * SPW;
+    const int cnt = act ? tile_rows(i, n) : 0;
+    valid = act && (lane & 31) < cnt;
+    int e = 0;
+    if (valid) e = list[i * kBK + (lane & 31)];
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(e));
+    idx = e;
+  }
+  template <int S>
+  __device__ __forceinline__ void slab(int lane) const {
+    if (!act) return;
+    const int k = k0 + S;
+    const uint32_t dst = tile + (uint32_t)k * 1024;
+    if (valid) {
+      const uint8_t* src = kv + (size_t)(uint32_t)idx * kD + 32 * k + 16 * (lane >> 5);
+      __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(uintptr_t)dst, 16, 0, 0);
+    } else {
+      *(LDS_AS u32x4*)(uintptr_t)(dst + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ __forceinline__ void all(int lane) const {
+    static_for<0, SPW>([&](auto sc) { slab<decltype(sc)::value>(lane); });
+  }
+};
+
 // Max over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48).
 __device__ __forceinline__ float row4_max(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -475,6 +538,101 @@ __device__ __forceinline__ void tile_pv(uint32_t vrow, const bf16x8& pk, f32x4 (
   });
 }
 
+// Eight OCP FP8 E4M3 codes -> eight bf16 (exact: every code is a bf16 value).
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(const u32x2& v) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(v[0], false);
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(v[0], true);
+  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(v[1], false);
+  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(v[1], true);
+  const bf16x8 r = bf16x8{(__bf16)a[0], (__bf16)a[1], (__bf16)b[0], (__bf16)b[1],
+                          (__bf16)c[0], (__bf16)c[1], (__bf16)d[0], (__bf16)d[1]};
+  return __builtin_bit_cast(u32x4, r);
+}
+
+// The MFMAs here are inline asm, so the compiler inserts none of the wait
+// states an MFMA needs after a VALU instruction wrote one of its source VGPRs
+// (two on CDNA3/4; four are given). Taking the converted fragments as in/out
+// operands pins the conversion above the nops and the MFMA below them.
+__device__ __forceinline__ void valu_to_mfma(u32x4& a, u32x4& b) {
+  asm volatile("s_nop 3" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void valu_to_mfma(u32x4& a) { asm volatile("s_nop 3" : "+v"(a)); }
+
+// S^T = K Q^T from an fp8 tile: the K fragment of half sh and k-step k
+// (lane: row 16 sh + li, d = 32k + 8g .. +8) is 8 bytes at kaddr + 1024 k + 256 sh,
+// kaddr = tile + 16 (li + 32 (g / 2)) + 8 (g % 2); converted to bf16 before the MFMA.
+template <int KPF>
+__device__ __forceinline__ void tile_s8(uint32_t kaddr, const bf16x8 (&qf)[16], f32x4 (&s)[2]) {
+  constexpr int KST = KPF + 1;
+  f32x4 sp[2];
+  u32x2 kf[KST][2];
+  auto kread = [&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    kf[k % KST][0] = ds_read_b64<1024 * k>(kaddr);
+    kf[k % KST][1] = ds_read_b64<1024 * k + 256>(kaddr);
+  };
+  static_for<0, KPF>([&](auto kc) { kread(kc); });
+  static_for<0, 16>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    if constexpr (k + KPF < 16) kread(Int<k + KPF>{});
+    constexpr int younger = 2 * (15 - k < KPF ? 15 - k : KPF);
+    lds_wait<younger>(kf[k % KST][0], kf[k % KST][1]);
+    u32x4 a0 = fp8x8_to_bf16(kf[k % KST][0]);
+    u32x4 a1 = fp8x8_to_bf16(kf[k % KST][1]);
+    valu_to_mfma(a0, a1);
+    if constexpr (k == 0) {
+      mfma_s_first(sp[0], a0, __builtin_bit_cast(u32x4, qf[k]));
+      mfma_s_first(sp[1], a1, __builtin_bit_cast(u32x4, qf[k]));
+    } else {
+      mfma_s(sp[0], a0, __builtin_bit_cast(u32x4, qf[k]));
+      mfma_s(sp[1], a1, __builtin_bit_cast(u32x4, qf[k]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");  // MFMA write -> VALU read distance
+#pragma unroll
+  for (int sh = 0; sh < 2; ++sh) {
+    asm volatile("" : "+v"(sp[sh]));
+    s[sh] = sp[sh];
+  }
+}
+
+// V^T fragment base of an fp8 tile. The P fragment (the B operand, built from
+// the S^T accumulator layout) holds slots 4g .. 4g+3 then 16+4g .. 16+4g+3, so
+// the lanes of group g fetch rows R(m) = 4g + m (m < 4) and 16 + 4g + m - 4
+// (m >= 4), m = li / 2, bytes 8 (li % 2) of the d-tile's 16-column chunk; the
+// transposing read then hands lane (g, li) those 8 slots at d = 16 dt + li.
+__device__ __forceinline__ uint32_t v8_frag_addr(uint32_t tile, int g, int li) {
+  const int m = li >> 1;
+  const int row = 4 * g + m + (m >= 4 ? 12 : 0);
+  return opaque(tile + 16 * row + 8 * (li & 1));
+}
+
+// O^T += V^T P^T from an fp8 tile: the V^T fragment of d-tile dt is one
+// transposing 8-bit read at vaddr + 1024 (dt / 2) + 512 (dt % 2).
+__device__ __forceinline__ void tile_pv8(uint32_t vaddr, const bf16x8& pk, f32x4 (&acc)[32]) {
+  asm volatile("s_nop 4" ::: "memory");  // P written by VALU, read by MFMA below
+  constexpr int VPF = 6;
+  constexpr int VST = VPF + 1;
+  u32x2 vf[VST];
+  auto vread = [&](auto dc) {
+    constexpr int dt = decltype(dc)::value;
+    vf[dt % VST] = ds_read_tr8_b64<1024 * (dt / 2) + 512 * (dt % 2)>(vaddr);
+  };
+  static_for<0, VPF>([&](auto dc) { vread(dc); });
+  static_for<0, 32>([&](auto dc) {
+    constexpr int dt = decltype(dc)::value;
+    if constexpr (dt + VPF < 32) vread(Int<dt + VPF>{});
+    constexpr int younger = 31 - dt < VPF ? 31 - dt : VPF;
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(vf[dt % VST]) : "n"(younger));
+    u32x4 a = fp8x8_to_bf16(vf[dt % VST]);
+    valu_to_mfma(a);
+    mfma_acc(acc[dt], __builtin_bit_cast(bf16x8, a), pk);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
 // Sink and normalisation of one head: o = acc * oscale, lse in natural log.
 // With no mass on any valid slot, o = 0 and lse is the sink itself (or -inf).
 struct HeadEnd {
@@ -505,7 +663,7 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[16], const Params& p, int t,
 // One workgroup per (token, group of 16 NW heads). Iteration j computes tile j
 // from ring buffer j % NBUF while tiles j+1 .. j+NBUF-1 land; the rows of tile
 // j+NBUF-1 are issued in one burst before P.V(j).
-template <int NW, int NBUF, bool SPLIT>
+template <int NW, int NBUF, bool SPLIT, bool FP8>
 __device__ __forceinline__ void smla_fwd_body(const Params& p, const SplitArgs& sa) {
   static_assert(NBUF >= 2 && NBUF <= 4, "ring of 2 to 4 tiles");
   static_assert(NBUF * kBK >= NW * 16, "the output staging needs 16 LDS rows per wave");
@@ -542,10 +700,13 @@ __device__ __forceinline__ void smla_fwd_body(const Params& p, const SplitArgs& 
     const int ntiles = (n + kBK - 1) / kBK;
     if (ntiles == 0) continue;
 
+    using Issue = typename std::conditional<FP8, TileIssue8<NW>, TileIssue<NW>>::type;
+    using Elem = typename std::conditional<FP8, uint8_t, uint16_t>::type;
+    const Elem* kvp = (const Elem*)p.kv;
 #pragma unroll
     for (int i = 0; i < AHEAD; ++i) {
-      TileIssue<NW> is;
-      is.init(sm.list, i, n, i < ntiles, lds_addr(&sm.tile[i][0][0]), p.kv, lane, w);
+      Issue is;
+      is.init(sm.list, i, n, i < ntiles, lds_addr(&sm.tile[i][0][0]), kvp, lane, w);
       is.all(lane);
     }
 
@@ -553,18 +714,19 @@ __device__ __forceinline__ void smla_fwd_body(const Params& p, const SplitArgs& 
       int after = 0;  // this wave's gather loads issued after tile j's
 #pragma unroll
       for (int i = 1; i < AHEAD; ++i)
-        if (j + i < ntiles) after += tile_dma<NW>(j + i, n, w);
+        if (j + i < ntiles) after += FP8 ? TileIssue8<NW>::SPW : tile_dma<NW>(j + i, n, w);
       wait_vmcnt_le(after);
       if constexpr (NW > 1) lds_barrier();
-      TileIssue<NW> is;
-      is.init(sm.list, j + AHEAD, n, j + AHEAD < ntiles, lds_addr(&sm.tile[(j + AHEAD) % NBUF][0][0]), p.kv, lane,
-              w);
+      Issue is;
+      is.init(sm.list, j + AHEAD, n, j + AHEAD < ntiles, lds_addr(&sm.tile[(j + AHEAD) % NBUF][0][0]), kvp, lane, w);
       const uint32_t tb = lds_addr(&sm.tile[j % NBUF][0][0]);
       f32x4 s[2];
-      tile_s<2, 2>(k_frag_addr(tb, g, li), qf, s);
+      if constexpr (FP8) tile_s8<2>(opaque(tb + 16 * (li + 32 * (g >> 1)) + 8 * (g & 1)), qf, s);
+      else tile_s<2, 2>(k_frag_addr(tb, g, li), qf, s);
       tile_softmax(s, tile_rows(j, n), p.scale_log2, g, m_ref, l_part, acc, pk);
       is.all(lane);
-      tile_pv(v_frag_addr(tb, g, li), pk, acc);
+      if constexpr (FP8) tile_pv8(v8_frag_addr(tb, g, li), pk, acc);
+      else tile_pv(v_frag_addr(tb, g, li), pk, acc);
     }
   }
 
@@ -593,7 +755,8 @@ __device__ __forceinline__ void smla_fwd_body(const Params& p, const SplitArgs& 
   if constexpr (NW > 1) lds_barrier();  // all waves are done with the tiles
   const uint32_t ob = lds_addr(&sm.tile[0][0][0]) + (uint32_t)w * 16 * kRowStride;
   mfma_agpr_drain(acc);
-  const HeadEnd he = head_end(l_part, m_ref, sk, has_sink, sink_l2);
+  HeadEnd he = head_end(l_part, m_ref, sk, has_sink, sink_l2);
+  if constexpr (FP8) he.oscale *= p.out_scale;  // V == code * dequant scale
   if (g == 0 && head < p.H) p.lse[(size_t)t * p.H + head] = he.lse;
   // lane (g, li) holds o[head li][16 dt + 4g .. +4): write it to LDS row li
 #pragma unroll
@@ -614,14 +777,26 @@ __device__ __forceinline__ void smla_fwd_body(const Params& p, const SplitArgs& 
 
 template <int NW, int NBUF>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void smla_fwd_kernel(const Params p) {
-  smla_fwd_body<NW, NBUF, false>(p, SplitArgs{});
+  smla_fwd_body<NW, NBUF, false, false>(p, SplitArgs{});
 }
 
 // One workgroup per (token, head group, split of the top-k row); writes partial results.
 template <int NW, int NBUF>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void smla_fwd_split_kernel(
     const Params p, const SplitArgs sa) {
-  smla_fwd_body<NW, NBUF, true>(p, sa);
+  smla_fwd_body<NW, NBUF, true, false>(p, sa);
+}
+
+// The same two kernels for a pool of OCP FP8 E4M3 codes.
+template <int NW, int NBUF>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void smla_fwd_fp8_kernel(
+    const Params p) {
+  smla_fwd_body<NW, NBUF, false, true>(p, SplitArgs{});
+}
+template <int NW, int NBUF>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void smla_fwd_fp8_split_kernel(
+    const Params p, const SplitArgs sa) {
+  smla_fwd_body<NW, NBUF, true, true>(p, sa);
 }
 
 // Merge of the splits of one (token, head), one wave each: lane s < nsplit
@@ -678,7 +853,7 @@ __global__ __launch_bounds__(256) void smla_merge_kernel(const Params p, const S
   const float mf = has_sink ? __builtin_fmaxf(mv, sink_l2) : mv;
   const float a = __builtin_amdgcn_exp2f(mv - mf);
   const float lf = lsum * a + (has_sink ? __builtin_amdgcn_exp2f(sink_l2 - mf) : 0.f);
-  const float oscale = a / lf;
+  const float oscale = a / lf * p.out_scale;
   o0 *= oscale;
   o1 *= oscale;
   *(bf16x8*)dst = bf16x8{(__bf16)o0[0], (__bf16)o0[1], (__bf16)o0[2], (__bf16)o0[3],
@@ -701,10 +876,15 @@ Variant pick_variant(int64_t H, int64_t topk) {
   return {8, "smla_fwd_kernel<8, 4>"};
 }
 
-template <int NW, int NBUF, bool SPLIT>
+template <int NW, int NBUF, bool SPLIT, bool FP8>
 hipError_t launch(const Params& p, const SplitArgs& sa, int blocks, hipStream_t stream) {
-  if constexpr (SPLIT) {
+  if constexpr (SPLIT && FP8) {
+    hipLaunchKernelGGL((smla_fwd_fp8_split_kernel<NW, NBUF>), dim3(blocks), dim3(NW * 64), 0, stream, p, sa);
+  } else if constexpr (SPLIT) {
     hipLaunchKernelGGL((smla_fwd_split_kernel<NW, NBUF>), dim3(blocks), dim3(NW * 64), 0, stream, p, sa);
+  } else if constexpr (FP8) {
+    (void)sa;
+    hipLaunchKernelGGL((smla_fwd_fp8_kernel<NW, NBUF>), dim3(blocks), dim3(NW * 64), 0, stream, p);
   } else {
     (void)sa;
     hipLaunchKernelGGL((smla_fwd_kernel<NW, NBUF>), dim3(blocks), dim3(NW * 64), 0, stream, p);
@@ -712,12 +892,12 @@ hipError_t launch(const Params& p, const SplitArgs& sa, int blocks, hipStream_t 
   return hipGetLastError();
 }
 
-template <bool SPLIT>
+template <bool SPLIT, bool FP8>
 hipError_t launch_variant(int nw, const Params& p, const SplitArgs& sa, int blocks, hipStream_t s) {
-  if (nw == 1) return launch<1, 2, SPLIT>(p, sa, blocks, s);
-  if (nw == 2) return launch<2, 2, SPLIT>(p, sa, blocks, s);
-  if (nw == 4) return launch<4, 2, SPLIT>(p, sa, blocks, s);
-  return launch<8, 4, SPLIT>(p, sa, blocks, s);
+  if (nw == 1) return launch<1, 2, SPLIT, FP8>(p, sa, blocks, s);
+  if (nw == 2) return launch<2, 2, SPLIT, FP8>(p, sa, blocks, s);
+  if (nw == 4) return launch<4, 2, SPLIT, FP8>(p, sa, blocks, s);
+  return launch<8, 4, SPLIT, FP8>(p, sa, blocks, s);
 }
 
 // Compute units of a device (cached; 0 if unknown).
@@ -802,7 +982,7 @@ int current_device(int* dev) {
 // Enqueue the forward for int32 top-k rows (arguments already checked, T > 0).
 int run_prefill(const void* q, const void* kv, const int32_t* topk_indices, const float* attn_sink, float scale,
                 void* out, float* lse, int64_t T, int64_t H, int64_t num_kv, int64_t topk, int dev,
-                hipStream_t s) {
+                hipStream_t s, bool fp8 = false, float kv_scale = 1.f) {
   const Variant var = pick_variant(H, topk);
   const int64_t heads_per_wg = (int64_t)16 * var.nw;
   const int64_t head_groups = (H + heads_per_wg - 1) / heads_per_wg;
@@ -819,7 +999,8 @@ int run_prefill(const void* q, const void* kv, const int32_t* topk_indices, cons
   if (topk == 0 || !kv) p.nkv = 0;
   p.topk_n = (int)topk;
   p.head_groups = (int)head_groups;
-  p.scale_log2 = scale * kLog2e;
+  p.scale_log2 = scale * (fp8 ? kv_scale : 1.f) * kLog2e;
+  p.out_scale = fp8 ? kv_scale : 1.f;
   SplitArgs sa;
   sa.nsplit = 1;
   sa.split_len = (int)topk;
@@ -849,7 +1030,8 @@ int run_prefill(const void* q, const void* kv, const int32_t* topk_indices, cons
         sa.split_len = (int)len;
         sa.part_o = (float*)ws;
         sa.part_ml = (float*)((char*)ws + bytes_o);
-        hipError_t err = launch_variant<true>(var.nw, p, sa, (int)(units * ns), s);
+        hipError_t err = fp8 ? launch_variant<true, true>(var.nw, p, sa, (int)(units * ns), s)
+                             : launch_variant<true, false>(var.nw, p, sa, (int)(units * ns), s);
         if (err == hipSuccess) {
           hipLaunchKernelGGL(smla_merge_kernel, dim3((unsigned)((T * H + 3) / 4)), dim3(256), 0, s, p, sa, 16 * var.nw);
           err = hipGetLastError();
@@ -860,7 +1042,8 @@ int run_prefill(const void* q, const void* kv, const int32_t* topk_indices, cons
       (void)hipGetLastError();
     }
   }
-  const hipError_t err = launch_variant<false>(var.nw, p, sa, (int)units, s);
+  const hipError_t err = fp8 ? launch_variant<false, true>(var.nw, p, sa, (int)units, s)
+                            : launch_variant<false, false>(var.nw, p, sa, (int)units, s);
   return err == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
 }
 
@@ -885,6 +1068,19 @@ extern "C" int sparse_mla_prefill(const void* q, const void* kv, const int32_t* 
   int dev = -1;
   if ((rc = current_device(&dev)) != SMLA_OK) return rc;
   return run_prefill(q, kv, topk_indices, attn_sink, scale, out, lse, T, H, num_kv, topk, dev, (hipStream_t)stream);
+}
+
+extern "C" int sparse_mla_prefill_fp8(const void* q, const void* kv, float kv_scale, const int32_t* topk_indices,
+                                      const float* attn_sink, float scale, void* out, float* lse, int64_t T,
+                                      int64_t H, int64_t num_kv, int64_t topk, void* stream) {
+  int rc = check_args(q, kv, topk_indices, 4, attn_sink, scale, out, lse, T, H, num_kv, topk);
+  if (rc != SMLA_OK) return rc;
+  if (!isfinite(kv_scale) || !isfinite(scale * kv_scale)) return SMLA_ERR_BAD_SCALE;
+  if (T == 0) return SMLA_OK;
+  int dev = -1;
+  if ((rc = current_device(&dev)) != SMLA_OK) return rc;
+  return run_prefill(q, kv, topk_indices, attn_sink, scale, out, lse, T, H, num_kv, topk, dev, (hipStream_t)stream,
+                     true, kv_scale);
 }
 
 extern "C" int sparse_mla_prefill_i64(const void* q, const void* kv, const int64_t* topk_indices,

@@ -32,7 +32,10 @@ distinct earlier positions ``< t-W+1`` (all when at most ``P``, else a seeded
 
 ``q``, ``kv`` are N(0,1) fp32 rounded to bf16 (round to nearest, ties to even)
 and returned as their raw ``uint16`` bit patterns; ``attn_sink`` is N(0,1)
-fp32. The draw order is fixed: q, kv (the sequence's rows, for ``paged``),
+fp32. With ``kv_fp8`` the same kv draw is stored as OCP FP8 E4M3 codes
+(``uint8``) of ``x / kv_scale``, ``kv_scale = max|x| / 448`` (round to nearest
+even, by torch's float8_e4m3fn conversion), and ``kv_scale`` is returned.
+The draw order is fixed: q, kv (the sequence's rows, for ``paged``),
 sink, then (``paged``) the page placement, then per-token choices in token
 order, then the drop mask.
 """
@@ -65,6 +68,7 @@ class Config:
     nan_unused: bool = False
     layout: str = "pool"  # "pool" (window + compressed pool) or "paged"
     tail: int = 0         # keep only the last `tail` tokens' q and top-k rows (decode-sized calls)
+    kv_fp8: bool = False  # pool as OCP FP8 E4M3 codes with one dequant scale
     pool_rows: int = 0    # paged: rows in the whole pool
     page: int = 64        # paged: rows per page
 
@@ -92,6 +96,19 @@ CONFIGS = {
     "decode": Config("decode", T=16384, H=16, topk=640, window=128, pool_slots=512, compression=4, seed=103,
                      tail=16),
 }
+# the same draws with the pool stored as fp8 codes
+for _name in ("tiny", "tp4", "wide", "glm"):
+    CONFIGS[_name + "_fp8"] = dataclasses.replace(CONFIGS[_name], name=_name + "_fp8", kv_fp8=True)
+
+
+def to_fp8_codes(x: np.ndarray):
+    """fp32 values -> (OCP FP8 E4M3 codes of x / s, s) with s = max|x| / 448."""
+    import torch
+
+    amax = float(np.max(np.abs(x))) if x.size else 0.0
+    s = np.float32(amax / 448.0) if amax > 0 else np.float32(1.0)
+    codes = torch.from_numpy(np.ascontiguousarray(x / s, dtype=np.float32)).to(torch.float8_e4m3fn)
+    return codes.view(torch.uint8).numpy(), float(s)
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -164,8 +181,13 @@ def make_inputs(cfg: Config | str, *, T: int | None = None) -> dict:
     T_, H = cfg.T, cfg.H
     num_kv = cfg.num_kv
     q = f32_to_bf16_bits(rng.standard_normal((T_, H, D), dtype=np.float32))
+    kv_scale = None
     if cfg.layout == "paged":
-        seq = f32_to_bf16_bits(rng.standard_normal((T_, D), dtype=np.float32))
+        seqf = rng.standard_normal((T_, D), dtype=np.float32)
+        if cfg.kv_fp8:
+            seq, kv_scale = to_fp8_codes(seqf)
+        else:
+            seq = f32_to_bf16_bits(seqf)
         sink = rng.standard_normal(H, dtype=np.float32) if cfg.sink else None
         n_pages = -(-T_ // cfg.page)
         if n_pages * cfg.page > num_kv:
@@ -173,11 +195,15 @@ def make_inputs(cfg: Config | str, *, T: int | None = None) -> dict:
         slots = rng.permutation(num_kv // cfg.page)[:n_pages].astype(np.int64)
         p_ = np.arange(T_, dtype=np.int64)
         row_of = slots[p_ // cfg.page] * cfg.page + p_ % cfg.page
-        kv = np.zeros((num_kv, D), dtype=np.uint16)  # untouched pages stay unallocated
+        kv = np.zeros((num_kv, D), dtype=np.uint8 if cfg.kv_fp8 else np.uint16)  # untouched pages stay unallocated
         kv[row_of] = seq
         topk = build_topk_paged(rng, T_, cfg.topk, cfg.window, cfg.pool_slots, row_of)
     else:
-        kv = f32_to_bf16_bits(rng.standard_normal((num_kv, D), dtype=np.float32))
+        kvf = rng.standard_normal((num_kv, D), dtype=np.float32)
+        if cfg.kv_fp8:
+            kv, kv_scale = to_fp8_codes(kvf)
+        else:
+            kv = f32_to_bf16_bits(kvf)
         sink = rng.standard_normal(H, dtype=np.float32) if cfg.sink else None
         topk = build_topk(rng, T_, cfg.topk, cfg.window, cfg.pool_slots, cfg.compression)
     if cfg.drop_p > 0.0:
@@ -194,7 +220,7 @@ def make_inputs(cfg: Config | str, *, T: int | None = None) -> dict:
         valid = topk[(topk >= 0) & (topk < num_kv)]
         used[valid] = True
         n_unused = int((~used).sum())
-        kv[~used] = BF16_NAN
+        kv[~used] = 0x7F if cfg.kv_fp8 else BF16_NAN
     return {
         "config": cfg,
         "q": q,
@@ -207,6 +233,7 @@ def make_inputs(cfg: Config | str, *, T: int | None = None) -> dict:
         "num_kv": num_kv,
         "topk_n": cfg.topk,
         "n_unused_nan_rows": n_unused,
+        "kv_scale": kv_scale,
     }
 
 

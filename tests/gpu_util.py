@@ -22,20 +22,23 @@ def bf16_bits(t: torch.Tensor) -> np.ndarray:
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def run_gpu(q, kv, topk, sink, scale, out=None, lse=None):
+def run_gpu(q, kv, topk, sink, scale, out=None, lse=None, kv_scale=None):
     """numpy inputs (bf16 bits, int32 or int64 rows, fp32) -> (o bits uint16, lse float32), via the C ABI."""
     qd = to_dev_bf16(q)
-    kvd = to_dev_bf16(kv) if kv.shape[0] else torch.empty((0, 512), dtype=torch.bfloat16, device=DEV)
+    if kv_scale is not None:  # OCP FP8 E4M3 codes
+        kvd = torch.from_numpy(np.ascontiguousarray(kv, dtype=np.uint8)).to(DEV).view(torch.float8_e4m3fn)
+    else:
+        kvd = to_dev_bf16(kv) if kv.shape[0] else torch.empty((0, 512), dtype=torch.bfloat16, device=DEV)
     topk = np.asarray(topk)
     td = torch.from_numpy(np.ascontiguousarray(topk, dtype=np.int64 if topk.dtype == np.int64 else np.int32)).to(DEV)
     sd = None if sink is None else torch.from_numpy(np.ascontiguousarray(sink, dtype=np.float32)).to(DEV)
-    o, l = sparse_mla_prefill(qd, kvd, td, sd, scale, out=out, lse=lse)
+    o, l = sparse_mla_prefill(qd, kvd, td, sd, scale, out=out, lse=lse, kv_scale=kv_scale)
     torch.cuda.synchronize()
     return bf16_bits(o), l.cpu().numpy()
 
 
 def run_case(inp):
-    return run_gpu(inp["q"], inp["kv"], inp["topk"], inp["sink"], inp["scale"])
+    return run_gpu(inp["q"], inp["kv"], inp["topk"], inp["sink"], inp["scale"], kv_scale=inp.get("kv_scale"))
 
 
 def compare(o_bits, lse, ref, tokens=None, what=""):
@@ -67,4 +70,5 @@ def compare(o_bits, lse, ref, tokens=None, what=""):
 
 
 def oracle_ref(inp, tokens=None):
-    return oracle.forward(inp["q"], inp["kv"], inp["topk"], inp["sink"], inp["scale"], tokens=tokens)
+    return oracle.forward(inp["q"], inp["kv"], inp["topk"], inp["sink"], inp["scale"], tokens=tokens,
+                          kv_scale=inp.get("kv_scale"))

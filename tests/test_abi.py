@@ -98,6 +98,23 @@ def test_int64_entry_argument_errors(kw, rc):
     assert call64(**kw) == rc
 
 
+def call8(q=0x1000, kv=0x2000, kv_scale=0.5, topk=0x3000, sink=None, scale=0.0441, out=0x4000, lse=0x5000,
+          T=4, H=8, num_kv=16, k=8):
+    return _lib.load().sparse_mla_prefill_fp8(q, kv, kv_scale, topk, sink, scale, out, lse, T, H, num_kv, k, None)
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(kv_scale=float("nan")), _lib.SMLA_ERR_BAD_SCALE),
+    (dict(kv_scale=float("inf")), _lib.SMLA_ERR_BAD_SCALE),
+    (dict(kv_scale=1e30, scale=1e30), _lib.SMLA_ERR_BAD_SCALE),  # the product overflows
+    (dict(kv=0x2008), _lib.SMLA_ERR_MISALIGNED),
+    (dict(topk=None), _lib.SMLA_ERR_NULL_POINTER),
+    (dict(H=0), _lib.SMLA_ERR_BAD_SIZE),
+])
+def test_fp8_entry_argument_errors(kw, rc):
+    assert call8(**kw) == rc
+
+
 def test_empty_sequence_is_ok_without_a_device():
     assert call(T=0, q=None, out=None, lse=None, topk=None, kv=None) == _lib.SMLA_OK
 

@@ -383,3 +383,54 @@ def test_int64_indices_never_wrap(T, H, topk, num_kv):
     idx32 = np.where((idx >= 0) & (idx < num_kv), idx, -1).astype(np.int32)
     o32, l32 = run_gpu(inp["q"], inp["kv"], idx32, inp["sink"], inp["scale"])
     assert np.array_equal(o64, o32) and np.array_equal(l64.view(np.uint32), l32.view(np.uint32))
+
+
+# ---- fp8 (OCP E4M3) pools ----
+
+@pytest.mark.parametrize("name,T", [("tiny_fp8", None), ("tp4_fp8", 768), ("wide_fp8", 384), ("glm_fp8", 512)])
+def test_fp8_pool_truncated_all_tokens(name, T):
+    inp = synth.make_inputs(name, T=T)
+    o, lse = run_case(inp)
+    stats = compare(o, lse, oracle_ref(inp), what="%s T=%s" % (name, inp["T"]))
+    print(name, inp["T"], stats)
+
+
+@pytest.mark.parametrize("name,k", [("tp4_fp8", 32), ("glm_fp8", 16)])
+def test_fp8_pool_full_size_sampled(name, k):
+    inp, o, lse = full_case(name)
+    tok = sample_tokens(inp["topk"], inp["num_kv"], k, seed=9)
+    compare(o, lse, oracle_ref(inp, tokens=tok), tokens=tok, what="%s full" % name)
+
+
+def make_random_fp8(seed, T, H, num_kv, topk, p_invalid=0.15, sink=True, kv_scale=0.03):
+    rng = np.random.default_rng(seed)
+    inp = make_random(seed, T=T, H=H, num_kv=num_kv, topk=topk, p_invalid=p_invalid, sink=sink)
+    codes = rng.integers(0, 256, (num_kv, 512)).astype(np.uint8)
+    codes = np.where((codes & 0x7F) == 0x7F, 0x30, codes)  # NaN codes only where a test puts them
+    return dict(inp, kv=codes, kv_scale=kv_scale)
+
+
+@pytest.mark.parametrize("T,H,topk,num_kv", [(20, 16, 300, 900), (16, 128, 200, 600), (3, 16, 1024, 3000),
+                                             (2, 128, 777, 2000), (9, 40, 96, 300)])
+def test_fp8_pool_random(T, H, topk, num_kv):
+    """Random rows and every code value (subnormals, both signs, the largest); few-token shapes
+    take the split path."""
+    inp = make_random_fp8(6000 + T + H, T, H, num_kv, topk)
+    o, lse = run_case(inp)
+    compare(o, lse, oracle_ref(inp), what="fp8 T=%d H=%d topk=%d" % (T, H, topk))
+
+
+def test_fp8_nan_code_stays_local_and_invalid_rows():
+    inp = make_random_fp8(6100, T=12, H=16, num_kv=400, topk=64, p_invalid=0.1)
+    idx = inp["topk"]
+    idx[0, :] = -1                                   # no valid slot
+    unused = np.setdiff1d(np.arange(400), idx.ravel())
+    inp["kv"][unused[:5], 3] = 0x7F                   # NaN codes in unreferenced rows: no effect
+    r = idx[5][idx[5] >= 0][0]
+    inp["kv"][r, 100] = 0xFF                          # NaN code in a referenced row
+    o, lse = run_case(inp)
+    compare(o, lse, oracle_ref(inp), what="fp8 NaN")
+    hit = np.array([(idx[t] == r).any() for t in range(12)])
+    of = synth.bf16_bits_to_f32(o)
+    assert np.all(np.isnan(of[hit])) and np.all(np.isfinite(of[~hit]))
+    assert np.all(of[0] == 0.0) and np.array_equal(lse[0], inp["sink"])

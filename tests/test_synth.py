@@ -81,6 +81,21 @@ def test_paged_layout_counts_and_structure():
     assert np.all(kv[untouched] == 0)
 
 
+def test_fp8_pool_draw():
+    """The fp8 configs keep the bf16 configs' draws: same q and rows; the pool is the same kv draw
+    as OCP FP8 E4M3 codes of x / s (s = max|x| / 448), within fp8 rounding of the bf16 values."""
+    import torch
+
+    a, b = synth.make_inputs("tiny"), synth.make_inputs("tiny_fp8")
+    assert b["kv"].dtype == np.uint8 and b["kv_scale"] > 0
+    assert np.array_equal(a["q"], b["q"]) and np.array_equal(a["topk"], b["topk"])
+    dec = torch.from_numpy(b["kv"]).view(torch.float8_e4m3fn).double().numpy() * b["kv_scale"]
+    x = synth.bf16_bits_to_f32(a["kv"]).astype(np.float64)
+    assert np.all(np.abs(dec - x) <= 2.0 ** -4 * np.abs(x) + 2.0 ** -9 * b["kv_scale"] + 2.0 ** -8 * np.abs(x))
+    g = synth.make_inputs("glm_fp8", T=300)
+    assert g["kv"].dtype == np.uint8 and g["kv"].shape == (2_200_000, 512)
+
+
 def test_deterministic_and_seeded():
     a = synth.make_inputs("tiny")
     b = synth.make_inputs("tiny")
