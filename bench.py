@@ -146,7 +146,7 @@ def measure(name: str, steps: int, warmup: int, cold_steps: int = 0, idx64: bool
     alg = algorithmic(inp)
     t = {"wall_s": wall, "ms_per_call": wall * 1e3 / steps, "kernel_ms_mean": st["mean"],
          "kernel_ms_median": st["median"], "kernel_ms_min": st["min"],
-         "kernel": kernel_name(inp["H"], inp["topk_n"])}
+         "kernel": kernel_name(inp["H"], inp["topk_n"], kv_scale is not None)}
     if cold_steps:
         # cold caches: overwrite 512 MiB (more than the 256 MB MALL plus 8 x 4 MB of L2) before each launch
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)

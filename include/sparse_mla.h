@@ -131,11 +131,13 @@ int sparse_mla_prefill_i64(const void* q, const void* kv, const int64_t* topk_in
 const char* sparse_mla_status_string(int status);
 
 /*
- * Name of the kernel that sparse_mla_prefill launches for H heads and top-k
- * rows of `topk` entries (static storage, as it appears in profiler traces),
- * or NULL when H < 1 or topk < 0. Pure host function: no device access.
+ * Name of the kernel that sparse_mla_prefill (kv_fp8 == 0) or
+ * sparse_mla_prefill_fp8 (kv_fp8 != 0) launches for H heads and top-k rows of
+ * `topk` entries when the call is not split over the top-k row (static
+ * storage, as it appears in profiler traces), or NULL when H < 1 or topk < 0.
+ * Pure host function: no device access.
  */
-const char* sparse_mla_kernel_name(int64_t H, int64_t topk);
+const char* sparse_mla_kernel_name(int64_t H, int64_t topk, int kv_fp8);
 
 /* Library version, major * 10000 + minor * 100 + patch. */
 int sparse_mla_version(void);

@@ -94,10 +94,10 @@ def sparse_mla_prefill(q, kv, topk_indices, attn_sink=None, scale=None, out=None
     return out, lse
 
 
-def kernel_name(H: int, topk: int) -> str:
+def kernel_name(H: int, topk: int, kv_fp8: bool = False) -> str:
     """Name of the kernel launched for H heads and top-k rows of `topk` entries
-    (as profilers show it)."""
-    name = _lib.load().sparse_mla_kernel_name(int(H), int(topk))
+    over a bf16 pool, or an fp8 one with kv_fp8 (as profilers show it)."""
+    name = _lib.load().sparse_mla_kernel_name(int(H), int(topk), int(bool(kv_fp8)))
     if name is None:
         raise ValueError("need H >= 1 and topk >= 0")
     return name.decode()

@@ -32,7 +32,7 @@ SIGNATURES = {
         ctypes.c_void_p,  # stream
     ]),
     "sparse_mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
-    "sparse_mla_kernel_name": (ctypes.c_char_p, [ctypes.c_int64, ctypes.c_int64]),
+    "sparse_mla_kernel_name": (ctypes.c_char_p, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int]),
     "sparse_mla_version": (ctypes.c_int, []),
 }
 

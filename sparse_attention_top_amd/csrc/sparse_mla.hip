@@ -87,11 +87,21 @@ struct SplitArgs {
   float* part_ml;
 };
 
-template <int NW, int NBUF>
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(LDS_AS const void*)p; }
+
+// LDS of one workgroup: the compacted top-k list and one byte area that holds,
+// in turn, the per-wave counts of the compaction, the ring of NBUF gathered
+// tiles (bf16 rows at pitch kRowStride, or 16 KiB fp8 slab tiles), and at the
+// end the output staging (16 rows of pitch kRowStride per wave).
+template <int NW, int NBUF, bool FP8>
 struct Smem {
-  uint8_t tile[NBUF][kBK][kRowStride];
+  static constexpr int kTileBytes = FP8 ? kBK * kD : kBK * kRowStride;
+  static constexpr int kStageBytes = NW * 16 * kRowStride;
+  static constexpr int kAreaBytes = NBUF * kTileBytes > kStageBytes ? NBUF * kTileBytes : kStageBytes;
+  uint8_t area[kAreaBytes];
   int32_t list[kListCap];
-  int32_t wcount[kListCap / (NW * 64)][NW];
+  __device__ __forceinline__ uint32_t tile(int b) { return lds_addr(area + b * kTileBytes); }
+  __device__ __forceinline__ int32_t& wcount(int c, int w) { return ((int32_t*)area)[c * NW + w]; }
 };
 
 // Optimisation barrier on a per-tile base address: keeps loop strength
@@ -208,13 +218,19 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(LDS_AS const void*)p; }
 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Wait until at most n of this wave's vector-memory operations are
 // outstanding (n rounded down to an encodable step; waiting more is safe).
 __device__ __forceinline__ void wait_vmcnt_le(int n) {
+  if (n < 16) {  // exact below 16
+    static_for<0, 16>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      if (n == k) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(k) : "memory");
+    });
+    return;
+  }
   if (n >= 48) asm volatile("s_waitcnt vmcnt(48)" ::: "memory");
   else if (n >= 32) asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
   else if (n >= 24) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
@@ -244,10 +260,12 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
 
 // Compact the valid entries of trow[0, len) into sm.list (order kept), with
 // one round of loads and two workgroup barriers. Returns the count (uniform
-// across the workgroup).
-template <int NW, int NBUF>
-__device__ __forceinline__ int compact_segment(const int32_t* __restrict__ trow, int len, uint32_t nkv, Smem<NW, NBUF>& sm,
-                               int lane, int w) {
+// across the workgroup). The per-wave counts live in the tile area, which
+// holds no tile then; the closing barrier keeps them until every wave has
+// read them.
+template <int NW, typename SM>
+__device__ __forceinline__ int compact_segment(const int32_t* __restrict__ trow, int len, uint32_t nkv, SM& sm, int lane,
+                                               int w) {
   constexpr int CH = NW * 64;              // entries per chunk (one per thread)
   constexpr int MAXC = kListCap / CH;      // chunks per segment
   int raw[MAXC];
@@ -270,7 +288,7 @@ __device__ __forceinline__ int compact_segment(const int32_t* __restrict__ trow,
   } else {
     if (lane == 0) {
 #pragma unroll
-      for (int c = 0; c < MAXC; ++c) sm.wcount[c][w] = __popcll(bal[c]);
+      for (int c = 0; c < MAXC; ++c) sm.wcount(c, w) = __popcll(bal[c]);
     }
     lds_barrier();
     int base = 0;
@@ -279,7 +297,7 @@ __device__ __forceinline__ int compact_segment(const int32_t* __restrict__ trow,
       int off = 0, tot = 0;
 #pragma unroll
       for (int i = 0; i < NW; ++i) {
-        const int ci = __builtin_amdgcn_readfirstlane(sm.wcount[c][i]);
+        const int ci = __builtin_amdgcn_readfirstlane(sm.wcount(c, i));
         off += (i < w) ? ci : 0;
         tot += ci;
       }
@@ -538,16 +556,21 @@ __device__ __forceinline__ void tile_pv(uint32_t vrow, const bf16x8& pk, f32x4 (
   });
 }
 
-// Eight OCP FP8 E4M3 codes -> eight bf16 (exact: every code is a bf16 value).
+// Two OCP FP8 E4M3 codes (bytes 2 HI .. 2 HI + 1 of x) -> two bf16 (exact:
+// every code is a bf16 value; the two NaN codes stay NaN). gfx950's packed
+// scaled conversion with scale 1, issued as asm: the compiler's lowering of its
+// builtin keeps only the first element of the pair.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16(uint32_t x) {
+  uint32_t r;
+  if constexpr (HI) asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0 op_sel:[1,0,0]" : "=v"(r) : "v"(x));
+  else asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0" : "=v"(r) : "v"(x));
+  return r;
+}
+// Eight codes (little-endian bytes of v) -> eight bf16 in the same order.
 __device__ __forceinline__ u32x4 fp8x8_to_bf16(const u32x2& v) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(v[0], false);
-  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(v[0], true);
-  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(v[1], false);
-  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(v[1], true);
-  const bf16x8 r = bf16x8{(__bf16)a[0], (__bf16)a[1], (__bf16)b[0], (__bf16)b[1],
-                          (__bf16)c[0], (__bf16)c[1], (__bf16)d[0], (__bf16)d[1]};
-  return __builtin_bit_cast(u32x4, r);
+  return u32x4{fp8x2_to_bf16<false>(v[0]), fp8x2_to_bf16<true>(v[0]), fp8x2_to_bf16<false>(v[1]),
+               fp8x2_to_bf16<true>(v[1])};
 }
 
 // The MFMAs here are inline asm, so the compiler inserts none of the wait
@@ -665,10 +688,9 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[16], const Params& p, int t,
 // j+NBUF-1 are issued in one burst before P.V(j).
 template <int NW, int NBUF, bool SPLIT, bool FP8>
 __device__ __forceinline__ void smla_fwd_body(const Params& p, const SplitArgs& sa) {
-  static_assert(NBUF >= 2 && NBUF <= 4, "ring of 2 to 4 tiles");
-  static_assert(NBUF * kBK >= NW * 16, "the output staging needs 16 LDS rows per wave");
+  static_assert(NBUF >= 2 && NBUF <= 8, "ring of 2 to 8 tiles");
   constexpr int AHEAD = NBUF - 1;  // tiles gathered ahead of the one being computed
-  __shared__ __attribute__((aligned(16))) Smem<NW, NBUF> sm;
+  __shared__ __attribute__((aligned(16))) Smem<NW, NBUF, FP8> sm;
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -696,7 +718,7 @@ __device__ __forceinline__ void smla_fwd_body(const Params& p, const SplitArgs& 
   const int32_t* trow = p.topk + (size_t)t * p.topk_n;
   for (int seg0 = row_begin; seg0 < row_end; seg0 += kListCap) {
     if (seg0 > row_begin && NW > 1) lds_barrier();  // previous segment's list and tiles fully consumed
-    const int n = compact_segment<NW, NBUF>(trow + seg0, min(kListCap, row_end - seg0), p.nkv, sm, lane, w);
+    const int n = compact_segment<NW>(trow + seg0, min(kListCap, row_end - seg0), p.nkv, sm, lane, w);
     const int ntiles = (n + kBK - 1) / kBK;
     if (ntiles == 0) continue;
 
@@ -706,7 +728,7 @@ __device__ __forceinline__ void smla_fwd_body(const Params& p, const SplitArgs& 
 #pragma unroll
     for (int i = 0; i < AHEAD; ++i) {
       Issue is;
-      is.init(sm.list, i, n, i < ntiles, lds_addr(&sm.tile[i][0][0]), kvp, lane, w);
+      is.init(sm.list, i, n, i < ntiles, sm.tile(i), kvp, lane, w);
       is.all(lane);
     }
 
@@ -718,8 +740,8 @@ __device__ __forceinline__ void smla_fwd_body(const Params& p, const SplitArgs& 
       wait_vmcnt_le(after);
       if constexpr (NW > 1) lds_barrier();
       Issue is;
-      is.init(sm.list, j + AHEAD, n, j + AHEAD < ntiles, lds_addr(&sm.tile[(j + AHEAD) % NBUF][0][0]), kvp, lane, w);
-      const uint32_t tb = lds_addr(&sm.tile[j % NBUF][0][0]);
+      is.init(sm.list, j + AHEAD, n, j + AHEAD < ntiles, sm.tile((j + AHEAD) % NBUF), kvp, lane, w);
+      const uint32_t tb = sm.tile(j % NBUF);
       f32x4 s[2];
       if constexpr (FP8) tile_s8<2>(opaque(tb + 16 * (li + 32 * (g >> 1)) + 8 * (g & 1)), qf, s);
       else tile_s<2, 2>(k_frag_addr(tb, g, li), qf, s);
@@ -753,7 +775,7 @@ __device__ __forceinline__ void smla_fwd_body(const Params& p, const SplitArgs& 
   const bool has_sink = !(sk == -INFINITY);
   const float sink_l2 = sk * kLog2e;
   if constexpr (NW > 1) lds_barrier();  // all waves are done with the tiles
-  const uint32_t ob = lds_addr(&sm.tile[0][0][0]) + (uint32_t)w * 16 * kRowStride;
+  const uint32_t ob = sm.tile(0) + (uint32_t)w * 16 * kRowStride;
   mfma_agpr_drain(acc);
   HeadEnd he = head_end(l_part, m_ref, sk, has_sink, sink_l2);
   if constexpr (FP8) he.oscale *= p.out_scale;  // V == code * dequant scale
@@ -863,17 +885,21 @@ __global__ __launch_bounds__(256) void smla_merge_kernel(const Params p, const S
 
 struct Variant {
   int nw;
-  const char* name;
+  const char* name;      // bf16 pool
+  const char* name_fp8;  // fp8 pool
 };
 
-// One wave per 16 heads. H <= 64: 1 to 4 waves per workgroup, two workgroups
-// per CU. Wider: 8 waves (128 heads) per workgroup, one per CU.
+// One wave per 16 heads: 1, 2 or 4 waves per workgroup up to 64 heads, 8 waves
+// (128 heads) wider. The ring depth is NBUF below: bf16 tiles (33 KiB) take
+// 2 per workgroup up to 4 waves (two workgroups per CU) and 4 at 8 waves (one
+// per CU); fp8 tiles (16 KiB) take as many as fit in the output staging area,
+// and at one wave four workgroups share a CU.
 Variant pick_variant(int64_t H, int64_t topk) {
   (void)topk;
-  if (H <= 16) return {1, "smla_fwd_kernel<1, 2>"};
-  if (H <= 32) return {2, "smla_fwd_kernel<2, 2>"};
-  if (H <= 64) return {4, "smla_fwd_kernel<4, 2>"};
-  return {8, "smla_fwd_kernel<8, 4>"};
+  if (H <= 16) return {1, "smla_fwd_kernel<1, 2>", "smla_fwd_fp8_kernel<1, 2>"};
+  if (H <= 32) return {2, "smla_fwd_kernel<2, 2>", "smla_fwd_fp8_kernel<2, 2>"};
+  if (H <= 64) return {4, "smla_fwd_kernel<4, 2>", "smla_fwd_fp8_kernel<4, 4>"};
+  return {8, "smla_fwd_kernel<8, 4>", "smla_fwd_fp8_kernel<8, 8>"};
 }
 
 template <int NW, int NBUF, bool SPLIT, bool FP8>
@@ -896,8 +922,8 @@ template <bool SPLIT, bool FP8>
 hipError_t launch_variant(int nw, const Params& p, const SplitArgs& sa, int blocks, hipStream_t s) {
   if (nw == 1) return launch<1, 2, SPLIT, FP8>(p, sa, blocks, s);
   if (nw == 2) return launch<2, 2, SPLIT, FP8>(p, sa, blocks, s);
-  if (nw == 4) return launch<4, 2, SPLIT, FP8>(p, sa, blocks, s);
-  return launch<8, 4, SPLIT, FP8>(p, sa, blocks, s);
+  if (nw == 4) return launch<4, FP8 ? 4 : 2, SPLIT, FP8>(p, sa, blocks, s);
+  return launch<8, FP8 ? 8 : 4, SPLIT, FP8>(p, sa, blocks, s);
 }
 
 // Compute units of a device (cached; 0 if unknown).
@@ -1124,9 +1150,10 @@ extern "C" const char* sparse_mla_status_string(int status) {
   }
 }
 
-extern "C" const char* sparse_mla_kernel_name(int64_t H, int64_t topk) {
+extern "C" const char* sparse_mla_kernel_name(int64_t H, int64_t topk, int kv_fp8) {
   if (H < 1 || topk < 0) return nullptr;
-  return pick_variant(H, topk).name;
+  const Variant v = pick_variant(H, topk);
+  return kv_fp8 ? v.name_fp8 : v.name;
 }
 
 extern "C" int sparse_mla_version(void) { return 102; }

@@ -49,11 +49,13 @@ def test_status_strings_and_version():
 
 def test_kernel_names():
     lib = _lib.load()
-    assert lib.sparse_mla_kernel_name(0, 64) is None
-    assert lib.sparse_mla_kernel_name(8, -1) is None
-    assert lib.sparse_mla_kernel_name(8, 64) == lib.sparse_mla_kernel_name(16, 64)
-    assert lib.sparse_mla_kernel_name(64, 512).startswith(b"smla_fwd_kernel")
-    assert lib.sparse_mla_kernel_name(128, 2048).startswith(b"smla_fwd_kernel")
+    assert lib.sparse_mla_kernel_name(0, 64, 0) is None
+    assert lib.sparse_mla_kernel_name(8, -1, 1) is None
+    assert lib.sparse_mla_kernel_name(8, 64, 0) == lib.sparse_mla_kernel_name(16, 64, 0)
+    assert lib.sparse_mla_kernel_name(64, 512, 0).startswith(b"smla_fwd_kernel<")
+    assert lib.sparse_mla_kernel_name(128, 2048, 0).startswith(b"smla_fwd_kernel<")
+    assert lib.sparse_mla_kernel_name(16, 2048, 1).startswith(b"smla_fwd_fp8_kernel<1,")
+    assert lib.sparse_mla_kernel_name(128, 512, 1).startswith(b"smla_fwd_fp8_kernel<8,")
 
 
 @pytest.mark.parametrize("kw,rc", [
