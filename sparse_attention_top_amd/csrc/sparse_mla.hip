@@ -92,15 +92,26 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(
 // LDS of one workgroup: the compacted top-k list and one byte area that holds,
 // in turn, the per-wave counts of the compaction, the ring of NBUF gathered
 // tiles (bf16 rows at pitch kRowStride, or 16 KiB fp8 slab tiles), and at the
-// end the output staging (16 rows of pitch kRowStride per wave).
+// end the output staging (16 rows of pitch kRowStride per wave). With an fp8
+// pool and eight waves (kConv), two bf16 tiles precede the ring: the waves
+// dequantise each gathered tile once into one of them and compute from it.
 template <int NW, int NBUF, bool FP8>
 struct Smem {
-  static constexpr int kTileBytes = FP8 ? kBK * kD : kBK * kRowStride;
+  static constexpr bool kConv = FP8 && NW == 8;
+  static constexpr int kBf16Tile = kBK * kRowStride;
+  static constexpr int kTileBytes = FP8 ? kBK * kD : kBf16Tile;
+  static constexpr int kRingOff = kConv ? 2 * kBf16Tile : 0;
+  static constexpr int kRingEnd = kRingOff + NBUF * kTileBytes;
   static constexpr int kStageBytes = NW * 16 * kRowStride;
-  static constexpr int kAreaBytes = NBUF * kTileBytes > kStageBytes ? NBUF * kTileBytes : kStageBytes;
+  static constexpr int kAreaBytes = kRingEnd > kStageBytes ? kRingEnd : kStageBytes;
   uint8_t area[kAreaBytes];
   int32_t list[kListCap];
-  __device__ __forceinline__ uint32_t tile(int b) { return lds_addr(area + b * kTileBytes); }
+  // gather ring slot b
+  __device__ __forceinline__ uint32_t tile(int b) { return lds_addr(area + kRingOff + b * kTileBytes); }
+  // dequantised bf16 tile b (kConv only)
+  __device__ __forceinline__ uint32_t ctile(int b) { return lds_addr(area + b * kBf16Tile); }
+  // output staging base
+  __device__ __forceinline__ uint32_t stage() { return lds_addr(area); }
   __device__ __forceinline__ int32_t& wcount(int c, int w) { return ((int32_t*)area)[c * NW + w]; }
 };
 
@@ -363,45 +374,56 @@ struct TileIssue {
   __device__ __forceinline__ int count() const { return active ? min(RPW, max(0, cnt - r0)) : 0; }
 };
 
+// A pointer that is the same in every lane, kept in scalar registers (a
+// vector copy would be spilled in the tile loop, and its reload would wait
+// for every gather in flight: scratch loads share the gathers' counter).
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return (const T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// A row of zero codes: lanes whose row is past a tile's count gather from it.
+__device__ __attribute__((aligned(64))) const uint8_t kZeroRow8[kD] = {};
+
 // The gather of one tile of an fp8 pool (512-byte rows). The tile's LDS
 // layout is slab-major: block k (1 KiB) holds d = 32k .. 32k+31 of all 32 rows,
 // as two 16-byte chunks per row with chunk j of row r at 16 (r + 32 j). One
 // LDS-DMA instruction fills one block (lane L fetches row L % 32, chunk L / 32),
 // so a tile takes 16 instructions; wave w fills blocks [w SPW, (w+1) SPW). Rows
-// past the tile's count are zero-filled.
+// past the tile's count are gathered from kZeroRow8.
 template <int NW>
 struct TileIssue8 {
   static constexpr int SPW = 16 / NW;
-  const uint8_t* kv;
-  uint32_t tile;
-  int k0;
-  int idx;  // list entry of row lane % 32
-  bool act, valid;
+  const uint8_t* src;  // this lane's bytes of its row in the wave's first slab
+  uint32_t dst0;       // the wave's first slab in the target buffer
+  bool act;
 
-  __device__ __forceinline__ void init(const int32_t* list, int i, int n, bool act_, uint32_t buf, const uint8_t* kv_,
+  // The list entry is read with a raw LDS read (see ds_read_b128): read by a
+  // compiled load, the compiler may first wait for every gather in flight,
+  // not knowing that none of them writes the list.
+  __device__ __forceinline__ void init(const int32_t* list, int i, int n, bool act_, uint32_t buf, const uint8_t* kv,
                                        int lane, int w) {
-    kv = kv_;
     act = act_;
-    tile = buf;
-    k0 = w * SPW;
+    const int k0 = w * SPW;
+    dst0 = buf + (uint32_t)k0 * 1024;
     const int cnt = act ? tile_rows(i, n) : 0;
-    valid = act && (lane & 31) < cnt;
-    int e = 0;
-    if (valid) e = list[i * kBK + (lane & 31)];
+    const bool valid = act && (lane & 31) < cnt;
+    uint32_t e = 0;
+    if (valid) {
+      asm volatile("ds_read_b32 %0, %1" : "=v"(e) : "v"(lds_addr(list + i * kBK + (lane & 31))));
+    }
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(e));
-    idx = e;
+    const uint8_t* row = valid ? uniform_ptr(kv) + ((uint64_t)e << 9) : uniform_ptr(kZeroRow8);
+    src = row + (32 * k0 + 16 * (lane >> 5));
   }
   template <int S>
   __device__ __forceinline__ void slab(int lane) const {
+    (void)lane;
     if (!act) return;
-    const int k = k0 + S;
-    const uint32_t dst = tile + (uint32_t)k * 1024;
-    if (valid) {
-      const uint8_t* src = kv + (size_t)(uint32_t)idx * kD + 32 * k + 16 * (lane >> 5);
-      __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(uintptr_t)dst, 16, 0, 0);
-    } else {
-      *(LDS_AS u32x4*)(uintptr_t)(dst + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
-    }
+    __builtin_amdgcn_global_load_lds(src + 32 * S, (LDS_AS void*)(uintptr_t)(dst0 + S * 1024), 16, 0, 0);
   }
   __device__ __forceinline__ void all(int lane) const {
     static_for<0, SPW>([&](auto sc) { slab<decltype(sc)::value>(lane); });
@@ -573,10 +595,11 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16(const u32x2& v) {
                fp8x2_to_bf16<true>(v[1])};
 }
 
-// The MFMAs here are inline asm, so the compiler inserts none of the wait
-// states an MFMA needs after a VALU instruction wrote one of its source VGPRs
-// (two on CDNA3/4; four are given). Taking the converted fragments as in/out
-// operands pins the conversion above the nops and the MFMA below them.
+// The conversions and MFMAs here are inline asm, so the compiler inserts none
+// of the wait states between an asm VALU write of a VGPR and its reader (an
+// MFMA source needs two on CDNA3/4; four are given). Taking the converted
+// values as in/out operands pins the conversion above the nops and the reader
+// below them.
 __device__ __forceinline__ void valu_to_mfma(u32x4& a, u32x4& b) {
   asm volatile("s_nop 3" : "+v"(a), "+v"(b));
 }
@@ -656,6 +679,33 @@ __device__ __forceinline__ void tile_pv8(uint32_t vaddr, const bf16x8& pk, f32x4
   });
 }
 
+// Dequantisation of wave w's slabs of an fp8 tile (slab-major at src) into a
+// bf16 tile at dst (rows at pitch kRowStride): lane L converts the 16 codes of
+// row L % 32, d = 32 k + 16 (L / 32) .. +16 of each slab k it gathered. The
+// reads are raw LDS reads (see ds_read_b128); the store half waits for them.
+template <int NW>
+struct SlabCodes {
+  static constexpr int SPW = 16 / NW;
+  u32x4 v[SPW];
+  __device__ __forceinline__ void load(uint32_t src, int lane, int w) {
+    const uint32_t a = opaque(src + (uint32_t)(w * SPW * 1024 + 16 * lane));
+    static_for<0, SPW>([&](auto sc) { v[decltype(sc)::value] = ds_read_b128<1024 * decltype(sc)::value>(a); });
+  }
+  __device__ __forceinline__ void store(uint32_t dst, int lane, int w) {
+    static_for<0, SPW>([&](auto sc) { asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v[decltype(sc)::value])); });
+    const uint32_t out = dst + (uint32_t)(lane & 31) * kRowStride + 32 * (lane >> 5);
+    static_for<0, SPW>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      const int k = w * SPW + s;
+      u32x4 lo = fp8x8_to_bf16(u32x2{v[s][0], v[s][1]});
+      u32x4 hi = fp8x8_to_bf16(u32x2{v[s][2], v[s][3]});
+      valu_to_mfma(lo, hi);  // the asm conversions' results are read by the stores below
+      *(LDS_AS u32x4*)(uintptr_t)(out + 64 * k) = lo;
+      *(LDS_AS u32x4*)(uintptr_t)(out + 64 * k + 16) = hi;
+    });
+  }
+};
+
 // Sink and normalisation of one head: o = acc * oscale, lse in natural log.
 // With no mass on any valid slot, o = 0 and lse is the sink itself (or -inf).
 struct HeadEnd {
@@ -690,7 +740,8 @@ template <int NW, int NBUF, bool SPLIT, bool FP8>
 __device__ __forceinline__ void smla_fwd_body(const Params& p, const SplitArgs& sa) {
   static_assert(NBUF >= 2 && NBUF <= 8, "ring of 2 to 8 tiles");
   constexpr int AHEAD = NBUF - 1;  // tiles gathered ahead of the one being computed
-  __shared__ __attribute__((aligned(16))) Smem<NW, NBUF, FP8> sm;
+  using SM = Smem<NW, NBUF, FP8>;
+  __shared__ __attribute__((aligned(16))) SM sm;
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -725,6 +776,45 @@ __device__ __forceinline__ void smla_fwd_body(const Params& p, const SplitArgs& 
     using Issue = typename std::conditional<FP8, TileIssue8<NW>, TileIssue<NW>>::type;
     using Elem = typename std::conditional<FP8, uint8_t, uint16_t>::type;
     const Elem* kvp = (const Elem*)p.kv;
+    if constexpr (SM::kConv) {
+      // Tile j: gathered into ring slot j % NBUF (NBUF tiles ahead), each wave
+      // dequantises its own slabs into bf16 tile j % 2 one iteration ahead,
+      // and all waves compute from that.
+      constexpr int SPW = TileIssue8<NW>::SPW;
+#pragma unroll
+      for (int i = 0; i < NBUF; ++i) {
+        Issue is;
+        is.init(sm.list, i, n, i < ntiles, sm.tile(i), kvp, lane, w);
+        is.all(lane);
+      }
+      int after0 = 0;
+#pragma unroll
+      for (int i = 1; i < NBUF; ++i) after0 += i < ntiles ? SPW : 0;
+      wait_vmcnt_le(after0);
+      SlabCodes<NW> codes;
+      codes.load(sm.tile(0), lane, w);
+      codes.store(sm.ctile(0), lane, w);
+      for (int j = 0; j < ntiles; ++j) {
+        lds_barrier();  // tile j dequantised by every wave; bf16 tile (j + 1) % 2 no longer read
+        Issue is;
+        is.init(sm.list, j + NBUF, n, j + NBUF < ntiles, sm.tile(j % NBUF), kvp, lane, w);
+        is.all(lane);
+        const uint32_t tb = sm.ctile(j & 1);
+        f32x4 s[2];
+        tile_s<2, 2>(k_frag_addr(tb, g, li), qf, s);
+        tile_softmax(s, tile_rows(j, n), p.scale_log2, g, m_ref, l_part, acc, pk);
+        if (j + 1 < ntiles) {
+          int after = 0;  // this wave's gather loads issued after tile j+1's
+#pragma unroll
+          for (int i = 2; i <= NBUF; ++i) after += j + i < ntiles ? SPW : 0;
+          wait_vmcnt_le(after);
+          codes.load(sm.tile((j + 1) % NBUF), lane, w);
+          codes.store(sm.ctile((j + 1) & 1), lane, w);
+        }
+        tile_pv(v_frag_addr(tb, g, li), pk, acc);
+      }
+      continue;
+    }
 #pragma unroll
     for (int i = 0; i < AHEAD; ++i) {
       Issue is;
@@ -775,7 +865,7 @@ __device__ __forceinline__ void smla_fwd_body(const Params& p, const SplitArgs& 
   const bool has_sink = !(sk == -INFINITY);
   const float sink_l2 = sk * kLog2e;
   if constexpr (NW > 1) lds_barrier();  // all waves are done with the tiles
-  const uint32_t ob = sm.tile(0) + (uint32_t)w * 16 * kRowStride;
+  const uint32_t ob = sm.stage() + (uint32_t)w * 16 * kRowStride;
   mfma_agpr_drain(acc);
   HeadEnd he = head_end(l_part, m_ref, sk, has_sink, sink_l2);
   if constexpr (FP8) he.oscale *= p.out_scale;  // V == code * dequant scale
@@ -892,14 +982,15 @@ struct Variant {
 // One wave per 16 heads: 1, 2 or 4 waves per workgroup up to 64 heads, 8 waves
 // (128 heads) wider. The ring depth is NBUF below: bf16 tiles (33 KiB) take
 // 2 per workgroup up to 4 waves (two workgroups per CU) and 4 at 8 waves (one
-// per CU); fp8 tiles (16 KiB) take as many as fit in the output staging area,
-// and at one wave four workgroups share a CU.
+// per CU). fp8 tiles (16 KiB): 2 at one wave (four workgroups per CU) and two
+// waves, 4 at four waves (in the output staging area's room), and 4 at eight
+// waves, beside the two bf16 tiles they are dequantised into.
 Variant pick_variant(int64_t H, int64_t topk) {
   (void)topk;
   if (H <= 16) return {1, "smla_fwd_kernel<1, 2>", "smla_fwd_fp8_kernel<1, 2>"};
   if (H <= 32) return {2, "smla_fwd_kernel<2, 2>", "smla_fwd_fp8_kernel<2, 2>"};
   if (H <= 64) return {4, "smla_fwd_kernel<4, 2>", "smla_fwd_fp8_kernel<4, 4>"};
-  return {8, "smla_fwd_kernel<8, 4>", "smla_fwd_fp8_kernel<8, 8>"};
+  return {8, "smla_fwd_kernel<8, 4>", "smla_fwd_fp8_kernel<8, 4>"};
 }
 
 template <int NW, int NBUF, bool SPLIT, bool FP8>
@@ -923,7 +1014,7 @@ hipError_t launch_variant(int nw, const Params& p, const SplitArgs& sa, int bloc
   if (nw == 1) return launch<1, 2, SPLIT, FP8>(p, sa, blocks, s);
   if (nw == 2) return launch<2, 2, SPLIT, FP8>(p, sa, blocks, s);
   if (nw == 4) return launch<4, FP8 ? 4 : 2, SPLIT, FP8>(p, sa, blocks, s);
-  return launch<8, FP8 ? 8 : 4, SPLIT, FP8>(p, sa, blocks, s);
+  return launch<8, 4, SPLIT, FP8>(p, sa, blocks, s);
 }
 
 // Compute units of a device (cached; 0 if unknown).
