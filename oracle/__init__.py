@@ -1,14 +1,15 @@
-"""CPU oracle for the sparse MLA prefill forward -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for the sparse MLA prefill forward and backward -- TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package. It shares no code with the HIP library
 (``sparse_attention_top_amd``) and neither imports the other; the seeded input
 generator is the only module both sides use.
 
-The arithmetic lives in ``smla_oracle.c`` (plain C, double precision, one
-sequential loop per token and head); this module only compiles it with gcc and
-marshals numpy arrays through ctypes. The definition it follows, with every
-reading of the pages it takes, is in that file's header comment.
+The arithmetic lives in ``smla_oracle.c`` (forward) and ``smla_oracle_bwd.c``
+(backward): plain C, double precision, sequential loops per token and head.
+This module only compiles them with gcc and marshals numpy arrays through
+ctypes. The definitions they follow, with every reading of the pages they take,
+are in the files' header comments.
 """
 
 from __future__ import annotations
@@ -20,7 +21,7 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "smla_oracle.c")
+_SRC = [os.path.join(_HERE, "smla_oracle.c"), os.path.join(_HERE, "smla_oracle_bwd.c")]
 _LIB = os.path.join(_HERE, "libsmla_oracle.so")
 D = 512
 
@@ -32,7 +33,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra",
-               "-o", tmp, _SRC, "-lm"]
+               "-o", tmp, *_SRC, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB
@@ -63,6 +64,13 @@ def _load():
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_int,
             ctypes.c_void_p, ctypes.c_double, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ]
+        lib.smla_oracle_backward.restype = ctypes.c_int
+        lib.smla_oracle_backward.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
         ]
         lib.smla_oracle_threads.restype = ctypes.c_int
@@ -117,6 +125,54 @@ def forward(q, kv, topk, sink, scale, tokens=None, *, want_exact=True, want_bf16
     if rc != 0:
         raise RuntimeError("oracle rejected its arguments (rc=%d)" % rc)
     return {"o": o, "o_bf16": ob, "lse": lse, "n_valid": nv}
+
+
+def _bf16_to_f64(bits):
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(
+        np.float64)
+
+
+def backward(q, kv, dout, o, lse, topk, sink, scale, tokens=None, rows=None, *, want_dq=True, want_dkv=True,
+             threads=0):
+    """Gradients of the forward, written out from its definition.
+
+    q, dout: uint16 bf16 bits [T, H, 512]; kv: uint16 bf16 bits [num_kv, 512];
+    o: the forward's output, uint16 bf16 bits or float64 [T, H, 512]; lse: float32
+    or float64 [T, H] (sink-inclusive, natural log); topk: int32 [T, topk];
+    sink: float32 [H] or None; scale: float. ``tokens`` selects the tokens whose
+    dq is evaluated (all when None); ``rows`` the pool rows whose dkv is (all
+    when None). Returns a dict with ``dq`` (float64 [n_tokens, H, 512]),
+    ``dkv`` (float64 [n_rows, 512]) and ``d_sink`` (float64 [H], or None without
+    a sink).
+    """
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    dout = np.ascontiguousarray(dout, dtype=np.uint16)
+    kv = np.ascontiguousarray(kv, dtype=np.uint16)
+    o = np.asarray(o)
+    o = _bf16_to_f64(o) if o.dtype == np.uint16 else np.ascontiguousarray(o, dtype=np.float64)
+    lse = np.ascontiguousarray(lse, dtype=np.float64)
+    topk = np.ascontiguousarray(topk, dtype=np.int32)
+    T, H, d = q.shape
+    num_kv = kv.shape[0]
+    if d != D or dout.shape != q.shape or o.shape != q.shape or lse.shape != (T, H):
+        raise ValueError("shapes")
+    if topk.ndim != 2 or topk.shape[0] != T:
+        raise ValueError("topk must be [T, topk]")
+    if sink is not None:
+        sink = np.ascontiguousarray(sink, dtype=np.float32)
+    tok = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int64)
+    n_tok = T if tok is None else tok.size
+    rws = np.arange(num_kv, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    dq = np.empty((n_tok, H, D), np.float64) if want_dq else None
+    dkv = np.empty((rws.size, D), np.float64) if want_dkv else None
+    ds = np.empty((H,), np.float64)
+    rc = _load().smla_oracle_backward(
+        _ptr(q), _ptr(kv) if num_kv > 0 else None, _ptr(dout), _ptr(o), _ptr(lse), _ptr(topk), _ptr(sink),
+        float(scale), T, H, num_kv, topk.shape[1], _ptr(tok), n_tok, _ptr(dq), _ptr(rws), rws.size, _ptr(dkv),
+        _ptr(ds), int(threads))
+    if rc != 0:
+        raise RuntimeError("oracle rejected its arguments (rc=%d)" % rc)
+    return {"dq": dq, "dkv": dkv, "d_sink": ds if sink is not None else None}
 
 
 def threads() -> int:
