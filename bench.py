@@ -41,7 +41,8 @@ def algorithmic(inp: dict) -> dict:
 
 def source_digest() -> str:
     h = hashlib.sha256()
-    for rel in ("sparse_attention_top_amd/csrc/sparse_mla.hip", "include/sparse_mla.h"):
+    for rel in ("sparse_attention_top_amd/csrc/smla_common.h", "sparse_attention_top_amd/csrc/sparse_mla.hip",
+                "include/sparse_mla.h"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

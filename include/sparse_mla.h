@@ -127,6 +127,38 @@ int sparse_mla_prefill_i64(const void* q, const void* kv, const int64_t* topk_in
                            float scale, void* out, float* lse, int64_t T, int64_t H, int64_t num_kv,
                            int64_t topk, void* stream);
 
+/*
+ * sparse_mla_backward -- gradients of sparse_mla_prefill ("[Triton/Gluon]
+ * [GFX950][DSV4] Sparse MLA training backward" (aiter PR #4766), sections
+ * "Contract" and "Structure"). With x_s = scale q[t,h] . kv[r_s] over the
+ * valid slots s of token t (r_s its row, validity as in the forward),
+ * P_s = exp(x_s - lse[t,h]) and delta = sum_d o[t,h,d] dout[t,h,d]:
+ *   dS_s = P_s (dout[t,h] . kv[r_s] - delta)
+ *   dq[t,h] = scale sum_s dS_s kv[r_s]
+ *   dkv[r]  = sum over (t, h, s) with r_s == r of scale dS_s q[t,h] + P_s dout[t,h]
+ *   d_sink[h] = -sum_t exp(attn_sink[h] - lse[t,h]) delta        (K == V)
+ *
+ * q, dout, o   bf16 [T, H, 512], contiguous, 16-byte aligned (o and lse
+ *              are the forward's outputs; lse is sink-inclusive, natural log)
+ * kv           bf16 [num_kv, 512], contiguous, 16-byte aligned
+ * lse          fp32 [T, H]
+ * topk_indices int32 [T, topk]; slots outside [0, num_kv) are invalid
+ * attn_sink    fp32 [H] or NULL; d_sink is required with it, ignored without
+ * dq           bf16 [T, H, 512] out;  dkv bf16 [num_kv, 512] out (rows no slot
+ *              holds are written 0);  d_sink fp32 [H] out
+ * H <= 128 (SMLA_ERR_BAD_SIZE above), num_kv < 2^31, T * round_up(topk, 32) < 2^31.
+ *
+ * Enqueued on `stream`. dkv is deterministic: each row sums its contributors
+ * in (token, slot) order, with no atomics. The call takes stream-ordered
+ * scratch from the library's per-device pool (the same pool as the forward's
+ * split path) and returns it before the call's work ends: about
+ * T * round_up(topk, 32) * (4 H + 1040) bytes (wide shape T=4096, H=128,
+ * topk=512: 3.2 GB); SMLA_ERR_NO_MEMORY if it cannot be had, before any launch.
+ */
+int sparse_mla_backward(const void* q, const void* kv, const void* dout, const void* o, const float* lse,
+                        const int32_t* topk_indices, const float* attn_sink, float scale, void* dq, void* dkv,
+                        float* d_sink, int64_t T, int64_t H, int64_t num_kv, int64_t topk, void* stream);
+
 /* Human-readable text for a status code (static storage; never NULL). */
 const char* sparse_mla_status_string(int status);
 

@@ -71,7 +71,7 @@ def _load():
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
         ]
         lib.smla_oracle_threads.restype = ctypes.c_int
         lib.smla_oracle_threads.argtypes = []
@@ -133,7 +133,7 @@ def _bf16_to_f64(bits):
 
 
 def backward(q, kv, dout, o, lse, topk, sink, scale, tokens=None, rows=None, *, want_dq=True, want_dkv=True,
-             threads=0):
+             want_mag=False, threads=0):
     """Gradients of the forward, written out from its definition.
 
     q, dout: uint16 bf16 bits [T, H, 512]; kv: uint16 bf16 bits [num_kv, 512];
@@ -143,7 +143,8 @@ def backward(q, kv, dout, o, lse, topk, sink, scale, tokens=None, rows=None, *, 
     dq is evaluated (all when None); ``rows`` the pool rows whose dkv is (all
     when None). Returns a dict with ``dq`` (float64 [n_tokens, H, 512]),
     ``dkv`` (float64 [n_rows, 512]) and ``d_sink`` (float64 [H], or None without
-    a sink).
+    a sink); with ``want_mag``, also ``dq_mag``, ``dkv_mag`` and ``d_sink_mag``:
+    per element, the sum of the absolute values of the terms added into it.
     """
     q = np.ascontiguousarray(q, dtype=np.uint16)
     dout = np.ascontiguousarray(dout, dtype=np.uint16)
@@ -166,13 +167,19 @@ def backward(q, kv, dout, o, lse, topk, sink, scale, tokens=None, rows=None, *, 
     dq = np.empty((n_tok, H, D), np.float64) if want_dq else None
     dkv = np.empty((rws.size, D), np.float64) if want_dkv else None
     ds = np.empty((H,), np.float64)
+    dqm = np.empty_like(dq) if (want_mag and dq is not None) else None
+    dkvm = np.empty_like(dkv) if (want_mag and dkv is not None) else None
+    dsm = np.empty((H,), np.float64) if want_mag else None
     rc = _load().smla_oracle_backward(
         _ptr(q), _ptr(kv) if num_kv > 0 else None, _ptr(dout), _ptr(o), _ptr(lse), _ptr(topk), _ptr(sink),
         float(scale), T, H, num_kv, topk.shape[1], _ptr(tok), n_tok, _ptr(dq), _ptr(rws), rws.size, _ptr(dkv),
-        _ptr(ds), int(threads))
+        _ptr(ds), _ptr(dqm), _ptr(dkvm), _ptr(dsm), int(threads))
     if rc != 0:
         raise RuntimeError("oracle rejected its arguments (rc=%d)" % rc)
-    return {"dq": dq, "dkv": dkv, "d_sink": ds if sink is not None else None}
+    out = {"dq": dq, "dkv": dkv, "d_sink": ds if sink is not None else None}
+    if want_mag:
+        out.update(dq_mag=dqm, dkv_mag=dkvm, d_sink_mag=dsm if sink is not None else None)
+    return out
 
 
 def threads() -> int:

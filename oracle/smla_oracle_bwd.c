@@ -37,6 +37,11 @@
  * dq is evaluated per (t, h) for a list of tokens; dkv for a list of rows,
  * each row scanning every (t, s) for the slots that hold it (plain, and
  * independent of how any index is built); d_sink over all tokens.
+ *
+ * Optionally, for each output element, the sum of the absolute values of the
+ * terms added into it (dq_mag, dkv_mag, dsink_mag): the scale of the rounding
+ * error of any evaluation that rounds its terms (a test tolerance derives
+ * from it); it does not enter the gradients.
  */
 #include <math.h>
 #include <stdint.h>
@@ -81,7 +86,8 @@ static void bw_dots(const uint16_t* qrow, const uint16_t* dorow, const uint16_t*
 int smla_oracle_backward(const uint16_t* q, const uint16_t* kv, const uint16_t* dout, const double* o,
                          const double* lse, const int32_t* topk, const float* sink, double scale, int64_t T, int64_t H,
                          int64_t num_kv, int64_t topk_n, const int64_t* tokens, int64_t n_tokens, double* dq,
-                         const int64_t* rows, int64_t n_rows, double* dkv, double* d_sink, int nthreads) {
+                         const int64_t* rows, int64_t n_rows, double* dkv, double* d_sink, double* dq_mag,
+                         double* dkv_mag, double* dsink_mag, int nthreads) {
   const int D = BWD_D;
   if (T < 0 || H < 1 || num_kv < 0 || topk_n < 0 || n_tokens < 0 || n_rows < 0) return -1;
   if (T > 0 && (!q || !dout || !o || !lse || (topk_n > 0 && !topk))) return -1;
@@ -114,7 +120,10 @@ int smla_oracle_backward(const uint16_t* q, const uint16_t* kv, const uint16_t* 
       const int64_t t = tokens ? tokens[i] : i;
       for (int64_t h = 0; h < H; ++h) {
         double* g = dq + (i * H + h) * D;
+        double* gm = dq_mag ? dq_mag + (i * H + h) * D : NULL;
         for (int d = 0; d < D; ++d) g[d] = 0.0;
+        if (gm)
+          for (int d = 0; d < D; ++d) gm[d] = 0.0;
         const uint16_t* qrow = q + (t * H + h) * D;
         const uint16_t* dorow = dout + (t * H + h) * D;
         for (int64_t s = 0; s < topk_n; ++s) {
@@ -126,6 +135,8 @@ int smla_oracle_backward(const uint16_t* q, const uint16_t* kv, const uint16_t* 
           const double p = exp(x - lse[t * H + h]);
           const double ds = p * (dp - delta[t * H + h]);
           for (int d = 0; d < D; ++d) g[d] += scale * ds * bw_bf16(kvrow[d]);
+          if (gm)
+            for (int d = 0; d < D; ++d) gm[d] += fabs(scale * ds * bw_bf16(kvrow[d]));
         }
       }
     }
@@ -137,7 +148,10 @@ int smla_oracle_backward(const uint16_t* q, const uint16_t* kv, const uint16_t* 
     for (int64_t i = 0; i < n_rows; ++i) {
       const int64_t r = rows[i];
       double* g = dkv + i * D;
+      double* gm = dkv_mag ? dkv_mag + i * D : NULL;
       for (int d = 0; d < D; ++d) g[d] = 0.0;
+      if (gm)
+        for (int d = 0; d < D; ++d) gm[d] = 0.0;
       const uint16_t* kvrow = kv + r * D;
       for (int64_t t = 0; t < T; ++t) {
         for (int64_t s = 0; s < topk_n; ++s) {
@@ -150,6 +164,8 @@ int smla_oracle_backward(const uint16_t* q, const uint16_t* kv, const uint16_t* 
             const double p = exp(x - lse[t * H + h]);
             const double ds = p * (dp - delta[t * H + h]);
             for (int d = 0; d < D; ++d) g[d] += scale * ds * bw_bf16(qrow[d]) + p * bw_bf16(dorow[d]);
+            if (gm)
+              for (int d = 0; d < D; ++d) gm[d] += fabs(scale * ds * bw_bf16(qrow[d])) + fabs(p * bw_bf16(dorow[d]));
           }
         }
       }
@@ -159,11 +175,15 @@ int smla_oracle_backward(const uint16_t* q, const uint16_t* kv, const uint16_t* 
   /* d_sink */
   if (d_sink) {
     for (int64_t h = 0; h < H; ++h) {
-      double acc = 0.0;
+      double acc = 0.0, mag = 0.0;
       const double sk = sink ? (double)sink[h] : -INFINITY;
       if (sk != -INFINITY)
-        for (int64_t t = 0; t < T; ++t) acc -= exp(sk - lse[t * H + h]) * delta[t * H + h];
+        for (int64_t t = 0; t < T; ++t) {
+          acc -= exp(sk - lse[t * H + h]) * delta[t * H + h];
+          mag += fabs(exp(sk - lse[t * H + h]) * delta[t * H + h]);
+        }
       d_sink[h] = acc;
+      if (dsink_mag) dsink_mag[h] = mag;
     }
   }
   free(delta);

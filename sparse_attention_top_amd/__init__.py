@@ -1,6 +1,6 @@
-"""Sparse MLA prefill forward (DeepSeek-V4) for MI355X / gfx950.
+"""Sparse MLA prefill forward and backward (DeepSeek-V4) for MI355X / gfx950.
 
-``sparse_mla_prefill`` marshals torch tensors to the C ABI of
+``sparse_mla_prefill`` and ``sparse_mla_backward`` marshal torch tensors to the C ABI of
 ``libsparse_mla.so`` (declared in ``include/sparse_mla.h``); every step of the
 computation runs in the HIP kernels. torch provides device memory and the
 current stream only.
@@ -15,7 +15,7 @@ from . import _lib
 HEAD_DIM = 512
 DEFAULT_SCALE = 1.0 / math.sqrt(HEAD_DIM)
 
-__all__ = ["sparse_mla_prefill", "kernel_name", "HEAD_DIM", "DEFAULT_SCALE"]
+__all__ = ["sparse_mla_prefill", "sparse_mla_backward", "kernel_name", "HEAD_DIM", "DEFAULT_SCALE"]
 
 
 def _check(cond: bool, msg: str):
@@ -92,6 +92,57 @@ def sparse_mla_prefill(q, kv, topk_indices, attn_sink=None, scale=None, out=None
     if rc != 0:
         raise RuntimeError("sparse_mla_prefill failed: %s (status %d)" % (_lib.status_string(rc), rc))
     return out, lse
+
+
+def sparse_mla_backward(q, kv, dout, o, lse, topk_indices, attn_sink=None, scale=None):
+    """Gradients of ``sparse_mla_prefill``; returns ``(dq, dkv, d_sink)``.
+
+    q, dout, o: bf16 [T, H, 512] (o and lse are the forward's outputs, lse
+    sink-inclusive fp32 [T, H]); kv: bf16 [num_kv, 512]; topk_indices: int32
+    [T, topk]; attn_sink: fp32 [H] or None (then d_sink is None); scale: float
+    (default 1/sqrt(512)). H <= 128. dq and dkv come back bf16, d_sink fp32.
+    All tensors on the same GPU and contiguous; enqueued on the current stream.
+    """
+    import torch
+
+    _check(q.is_cuda, "q must be a GPU tensor (got %s)" % q.device)
+    dev = q.device
+    _check(q.dtype == torch.bfloat16, "q must be bfloat16, got %s" % q.dtype)
+    _check(q.dim() == 3 and q.shape[2] == HEAD_DIM, "q must be [T, H, 512], got %s" % (tuple(q.shape),))
+    T, H, _ = q.shape
+    for name, x in (("dout", dout), ("o", o)):
+        _check(x.device == dev and x.dtype == torch.bfloat16 and x.shape == q.shape,
+               "%s must be bfloat16 %s on %s" % (name, tuple(q.shape), dev))
+    _check(kv.device == dev and kv.dtype == torch.bfloat16, "kv must be bfloat16 on %s" % dev)
+    _check(kv.dim() == 2 and kv.shape[1] == HEAD_DIM, "kv must be [num_kv, 512], got %s" % (tuple(kv.shape),))
+    _check(lse.device == dev and lse.dtype == torch.float32 and tuple(lse.shape) == (T, H),
+           "lse must be float32 [T, H] on q's device")
+    _check(topk_indices.device == dev and topk_indices.dtype == torch.int32, "topk_indices must be int32 on %s" % dev)
+    _check(topk_indices.dim() == 2 and topk_indices.shape[0] == T, "topk_indices must be [T, topk]")
+    if attn_sink is not None:
+        _check(attn_sink.device == dev and attn_sink.dtype == torch.float32 and tuple(attn_sink.shape) == (H,),
+               "attn_sink must be float32 [H] on q's device")
+    for name, x in (("q", q), ("kv", kv), ("dout", dout), ("o", o), ("lse", lse), ("topk_indices", topk_indices)):
+        _check(x.is_contiguous(), "%s must be contiguous" % name)
+    if attn_sink is not None:
+        _check(attn_sink.is_contiguous(), "attn_sink must be contiguous")
+    if scale is None:
+        scale = DEFAULT_SCALE
+    dq = torch.empty_like(q)
+    dkv = torch.empty_like(kv)
+    d_sink = torch.empty((H,), dtype=torch.float32, device=dev) if attn_sink is not None else None
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib.sparse_mla_backward(
+            q.data_ptr(), kv.data_ptr() if kv.numel() else None, dout.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            topk_indices.data_ptr() if topk_indices.numel() else None,
+            attn_sink.data_ptr() if attn_sink is not None else None, float(scale),
+            dq.data_ptr(), dkv.data_ptr() if dkv.numel() else None,
+            d_sink.data_ptr() if d_sink is not None else None, T, H, kv.shape[0], topk_indices.shape[1], stream)
+    if rc != 0:
+        raise RuntimeError("sparse_mla_backward failed: %s (status %d)" % (_lib.status_string(rc), rc))
+    return dq, dkv, d_sink
 
 
 def kernel_name(H: int, topk: int, kv_fp8: bool = False) -> str:

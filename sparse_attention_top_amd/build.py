@@ -12,7 +12,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "sparse_mla.hip")
+SRC = [os.path.join(PKG, "csrc", "sparse_mla.hip"), os.path.join(PKG, "csrc", "sparse_mla_bwd.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsparse_mla.so")
 ARCH = "gfx950"
@@ -34,7 +34,7 @@ FLAGS = [
 
 def build(resource_usage: bool = False) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-o", tmp, SRC]
+    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-o", tmp, *SRC]
     if resource_usage:
         cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
     proc = subprocess.run(cmd, capture_output=True, text=True)

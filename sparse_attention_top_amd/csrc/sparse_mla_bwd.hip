@@ -1,0 +1,588 @@
+// Sparse MLA backward (DeepSeek-V4) for MI355X / gfx950 (CDNA4).
+//
+// Operation: "[Triton/Gluon] [GFX950][DSV4] Sparse MLA training backward"
+// (aiter PR #4766), sections "Contract" and "Structure": from q, kv, dO, the
+// forward's o and sink-inclusive lse, the top-k rows and the optional sink,
+// compute dq, dkv and d_sink. With x_s = scale q . kv[r_s] over the valid
+// slots s of token t, P_s = exp(x_s - lse) and delta = rowsum(o * dO):
+//   dS_s = P_s (dO . kv[r_s] - delta)
+//   dq   = scale sum_s dS_s kv[r_s]
+//   dkv[r] = sum over slots holding r of (scale dS_s q + P_s dO), over all heads
+//   d_sink = -sum_t exp(sink - lse) delta
+//
+// Phases (each a kernel; scratch from the library's per-device pool):
+//   B1 smla_bwd_dq_kernel      one workgroup per (token, group of 16 NW heads):
+//      the forward's compaction and LDS-DMA tile gather; one read of each K
+//      fragment feeds the S and dP MFMAs; P and dS in fp32; dQ^T += K^T dS^T
+//      from the same tile; writes dq, P and scale dS (bf16, [T][H][TP], TP =
+//      top-k rounded up to 32, compacted positions), the row key and entry id
+//      of every compacted position, and the sink partials.
+//   B2 smla_bwd_interm_kernel  one workgroup per (token, 128 columns of d): the
+//      per-slot dkv contribution interm[t][j] = [scale dS ; P]^T [q ; dO], one
+//      MFMA contraction over heads (both terms side by side along K).
+//   B3 a stable radix sort of (row key, entry id) (hipcub) and the start of
+//      each row's run: the scatter inverted, so each row gathers its own
+//      contributors in a fixed order (deterministic, no atomics).
+//   B4 smla_bwd_dkv_kernel     one wave per pool row: fp32 sum of its interm
+//      rows, bf16 store (rows nobody references get 0).
+//   B5 smla_bwd_dsink_kernel   fixed-order sum of the sink partials.
+
+#include <hipcub/hipcub.hpp>
+
+#include "smla_common.h"
+
+namespace {
+
+using namespace smla_host;
+
+constexpr int kBwdMaxH = 128;  // heads handled by the interm contraction (2 x 128 rows of K)
+constexpr int kIDC = 128;      // d columns per interm workgroup
+
+// A zero row for padded heads (interm staging gathers them from here).
+__device__ __attribute__((aligned(256))) const uint16_t kZeroRowBf16[kD] = {};
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* kv;
+  const uint16_t* dout;
+  const uint16_t* o;
+  const float* lse;
+  const int32_t* topk;
+  const float* sink;
+  uint16_t* dq;
+  uint16_t* pbuf;   // P, [T][H][TP] bf16
+  uint16_t* dsbuf;  // scale dS, [T][H][TP] bf16
+  uint32_t* ckey;   // [T][TP]: pool row of compacted position j, or the sentinel
+  uint32_t* cval;   // [T][TP]: entry id t TP + j
+  int32_t* ncount;  // [T]: compacted positions used (a multiple of 32)
+  float* dsink_part;  // [T][H]: exp(sink - lse) delta
+  int T;
+  int H;
+  int topk_n;
+  int TP;
+  int head_groups;
+  uint32_t nkv;      // slot valid iff (uint32)idx < nkv
+  uint32_t sentinel;  // row key of unused positions (== nkv)
+  float scale;
+  float scale_log2;
+};
+
+template <int NW, int NBUF>
+struct BwdSmem {
+  static constexpr int kTileBytes = kBK * kRowStride;
+  static constexpr int kStageBytes = NW * 16 * kRowStride;
+  static constexpr int kAreaBytes = NBUF * kTileBytes > kStageBytes ? NBUF * kTileBytes : kStageBytes;
+  uint8_t area[kAreaBytes];
+  int32_t list[kListCap];
+  __device__ __forceinline__ uint32_t tile(int b) { return lds_addr(area + b * kTileBytes); }
+  __device__ __forceinline__ uint32_t stage() { return lds_addr(area); }
+  __device__ __forceinline__ int32_t& wcount(int c, int w) { return ((int32_t*)area)[c * NW + w]; }
+};
+
+// Fragments of a [T, H, 512] bf16 tensor in the B-operand layout of
+// S^T = K X^T: lane (g, li) holds x[t, head, 32k + 8g .. +8) (zero past H).
+__device__ __forceinline__ void load_frag(bf16x8 (&f)[16], const uint16_t* x, int t, int H, int head, int g) {
+  if (head < H) {
+    const bf16x8* src = (const bf16x8*)(x + ((size_t)t * H + head) * kD + 8 * g);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) f[k] = src[4 * k];
+  } else {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) f[k] = bf16x8{};
+  }
+}
+
+// S^T = K Q^T and dP^T = K dO^T from one read of each K fragment: four
+// independent MFMA chains (two halves of 16 slots, two products).
+template <int KPF>
+__device__ __forceinline__ void tile_sdp(uint32_t krow, const bf16x8 (&qf)[16], const bf16x8 (&df)[16], f32x4 (&s)[2],
+                                         f32x4 (&dp)[2]) {
+  constexpr int KST = KPF + 1;
+  f32x4 acc[2][2][1];  // [S or dP][half][1]
+  u32x4 kf[KST][2];
+  auto kread = [&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    kf[k % KST][0] = ds_read_b128<64 * k>(krow);
+    kf[k % KST][1] = ds_read_b128<16 * kRowStride + 64 * k>(krow);
+  };
+  static_for<0, KPF>([&](auto kc) { kread(kc); });
+  static_for<0, 16>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    if constexpr (k + KPF < 16) kread(Int<k + KPF>{});
+    constexpr int younger = 2 * (15 - k < KPF ? 15 - k : KPF);
+    lds_wait<younger>(kf[k % KST][0], kf[k % KST][1]);
+#pragma unroll
+    for (int sh = 0; sh < 2; ++sh) {
+      if constexpr (k == 0) {
+        mfma_s_first(acc[0][sh][0], kf[k % KST][sh], __builtin_bit_cast(u32x4, qf[k]));
+        mfma_s_first(acc[1][sh][0], kf[k % KST][sh], __builtin_bit_cast(u32x4, df[k]));
+      } else {
+        mfma_s(acc[0][sh][0], kf[k % KST][sh], __builtin_bit_cast(u32x4, qf[k]));
+        mfma_s(acc[1][sh][0], kf[k % KST][sh], __builtin_bit_cast(u32x4, df[k]));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  mfma_vgpr_drain2<1>(acc);
+#pragma unroll
+  for (int sh = 0; sh < 2; ++sh) {
+    s[sh] = acc[0][sh][0];
+    dp[sh] = acc[1][sh][0];
+  }
+}
+
+// ---- B1: dq, P, scale dS, compacted row keys, sink partials ----
+template <int NW, int NBUF>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) void smla_bwd_dq_kernel(
+    const BwdParams p) {
+  constexpr int AHEAD = NBUF - 1;
+  __shared__ __attribute__((aligned(16))) BwdSmem<NW, NBUF> sm;
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int li = lane & 15;
+  const int vb = xcd_remap(blockIdx.x, gridDim.x);
+  const int t = p.T - 1 - vb / p.head_groups;
+  const int hg = vb % p.head_groups;
+  const int head_base = (hg * NW + w) * 16;
+  const int head = head_base + li;
+  const bool hv = head < p.H;
+
+  bf16x8 qf[16], df[16];
+  load_frag(qf, p.q, t, p.H, head, g);
+  load_frag(df, p.dout, t, p.H, head, g);
+  float delta;
+  {
+    bf16x8 of[16];
+    load_frag(of, p.o, t, p.H, head, g);
+    float part = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part += (float)of[k][e] * (float)df[k][e];
+    delta = row4_sum(part);  // the four 16-lane groups hold the four quarters of d
+  }
+  const float lse_v = hv ? p.lse[(size_t)t * p.H + head] : 0.f;
+  const float lse_l2 = lse_v * kLog2e;
+  if (p.sink != nullptr && hv && g == 0) {
+    const float sk = p.sink[head];
+    p.dsink_part[(size_t)t * p.H + head] = (sk == -INFINITY) ? 0.f : __expf(sk - lse_v) * delta;
+  }
+
+  f32x4 acc[32];
+#pragma unroll
+  for (int dt = 0; dt < 32; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 pk;
+
+  const int32_t* trow = p.topk + (size_t)t * p.topk_n;
+  const uint16_t* kvp = p.kv;
+  const size_t prow = ((size_t)t * p.H + head) * p.TP;  // this lane's P / dS row
+  int jbase = 0;  // compacted position of the segment's first entry (a multiple of 32)
+  for (int seg0 = 0; seg0 < p.topk_n; seg0 += kListCap) {
+    if (seg0 > 0 && NW > 1) lds_barrier();  // previous segment's list and tiles fully consumed
+    const int n = compact_segment<NW>(trow + seg0, min(kListCap, p.topk_n - seg0), p.nkv, sm, lane, w);
+    const int npos = (n + kBK - 1) / kBK * kBK;
+    if (hg == 0) {
+      for (int i = threadIdx.x; i < npos; i += NW * 64) {
+        const size_t e = (size_t)t * p.TP + jbase + i;
+        p.ckey[e] = i < n ? (uint32_t)sm.list[i] : p.sentinel;
+        p.cval[e] = (uint32_t)e;
+      }
+    }
+    const int ntiles = npos / kBK;
+    if (ntiles == 0) continue;
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) {
+      TileIssue<NW> is;
+      is.init(sm.list, i, n, i < ntiles, sm.tile(i), kvp, lane, w);
+      is.all(lane);
+    }
+    for (int j = 0; j < ntiles; ++j) {
+      int after = 0;  // this wave's gather loads issued after tile j's (stores in between only add to the wait)
+#pragma unroll
+      for (int i = 1; i < AHEAD; ++i)
+        if (j + i < ntiles) after += tile_dma<NW>(j + i, n, w);
+      wait_vmcnt_le(after);
+      if constexpr (NW > 1) lds_barrier();
+      TileIssue<NW> is;
+      is.init(sm.list, j + AHEAD, n, j + AHEAD < ntiles, sm.tile((j + AHEAD) % NBUF), kvp, lane, w);
+      const uint32_t tb = sm.tile(j % NBUF);
+      f32x4 s[2], dp[2];
+      tile_sdp<2>(k_frag_addr(tb, g, li), qf, df, s, dp);
+      const int cnt = tile_rows(j, n);
+      bf16x4 pst[2], dst[2];
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int slot = sh * 16 + 4 * g + i;
+          const float pr = slot < cnt ? __builtin_amdgcn_exp2f(s[sh][i] * p.scale_log2 - lse_l2) : 0.f;
+          const float ds = pr * (dp[sh][i] - delta);
+          pk[sh * 4 + i] = (__bf16)ds;
+          pst[sh][i] = (__bf16)pr;
+          dst[sh][i] = (__bf16)(ds * p.scale);
+        }
+      if (hv) {
+        const size_t o0 = prow + jbase + j * kBK + 4 * g;
+        *(bf16x4*)(p.pbuf + o0) = pst[0];
+        *(bf16x4*)(p.pbuf + o0 + 16) = pst[1];
+        *(bf16x4*)(p.dsbuf + o0) = dst[0];
+        *(bf16x4*)(p.dsbuf + o0 + 16) = dst[1];
+      }
+      is.all(lane);
+      tile_pv(v_frag_addr(tb, g, li), pk, acc);  // dQ^T += K^T dS^T (V == K)
+    }
+    jbase += npos;
+  }
+  if (hg == 0) {
+    for (int i = jbase + threadIdx.x; i < p.TP; i += NW * 64) {
+      const size_t e = (size_t)t * p.TP + i;
+      p.ckey[e] = p.sentinel;
+      p.cval[e] = (uint32_t)e;
+    }
+    if (threadIdx.x == 0) p.ncount[t] = jbase;
+  }
+
+  // dq = scale acc, staged through LDS for whole-row stores (as the forward's o)
+  if constexpr (NW > 1) lds_barrier();
+  const uint32_t ob = sm.stage() + (uint32_t)w * 16 * kRowStride;
+  mfma_agpr_drain(acc);
+#pragma unroll
+  for (int dt = 0; dt < 32; ++dt) {
+    const f32x4 v = acc[dt] * p.scale;
+    const bf16x4 v4 = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+    *(LDS_AS bf16x4*)(uintptr_t)(ob + li * kRowStride + 32 * dt + 8 * g) = v4;
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int hr = head_base + r;
+    const u32x4 val = *(LDS_AS const u32x4*)(uintptr_t)(ob + r * kRowStride + 16 * lane);
+    if (hr < p.H) *(u32x4*)(p.dq + ((size_t)t * p.H + hr) * kD + 8 * lane) = val;
+  }
+}
+
+// ---- B2: interm[t][j][d] = sum_h scale dS[t][h][j] q[t][h][d] + P[t][h][j] dO[t][h][d] ----
+// One workgroup of 8 waves per (token, 128 columns of d); wave w owns 16
+// columns. C^T[d][j] = X^T[d][k] Y[k][j] with k running over the 2 Hp rows
+// [q ; dO] (X, staged [k][128 d], 256 B rows) and [scale dS ; P] (Y, staged
+// per 32-position tile, [k][32 j], 64 B rows), Hp = H rounded up to 16, rows
+// of padded heads zero. Both MFMA operands come from transposing LDS reads:
+// lane (g, li) takes rows k0 + 4g .. +3 and k0 + 16 + 4g .. +3 at one column,
+// the same rows for both, so the K order matches.
+struct InterParams {
+  const uint16_t* q;
+  const uint16_t* dout;
+  const uint16_t* pbuf;
+  const uint16_t* dsbuf;
+  const int32_t* ncount;
+  uint16_t* interm;  // [T][TP][512]
+  int T;
+  int H;
+  int Hp;
+  int TP;
+};
+
+struct InterSmem {
+  uint8_t x[2 * kBwdMaxH][kIDC * 2];  // [q ; dO] rows, 256 B each
+  uint8_t y[2][2 * kBwdMaxH][64];     // [scale dS ; P] rows of a 32-position tile, double-buffered
+};
+
+// Stage the [q ; dO] column block: row k = 4i + L/16, bytes 16 (L % 16); wave w issues i = w, w + 8, ...
+__device__ __forceinline__ void interm_stage_x(const InterParams& p, InterSmem& sm, int t, int d0, int lane, int w) {
+  const int rows = 2 * p.Hp;
+  const uint16_t* zero = uniform_ptr(kZeroRowBf16);
+  for (int i = w; i * 4 < rows; i += 8) {
+    const int k = 4 * i + (lane >> 4);
+    const int h = k < p.Hp ? k : k - p.Hp;
+    const uint16_t* base = k < p.Hp ? p.q : p.dout;
+    const uint16_t* src = h < p.H ? base + ((size_t)t * p.H + h) * kD + d0 + 8 * (lane & 15) : zero + 8 * (lane & 15);
+    __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(uintptr_t)lds_addr(&sm.x[4 * i][0]), 16, 0, 0);
+  }
+}
+// Stage tile jt of [scale dS ; P]: row k = 16i + L/4, bytes 16 (L % 4).
+__device__ __forceinline__ void interm_stage_y(const InterParams& p, InterSmem& sm, int buf, int t, int jt, int lane,
+                                               int w) {
+  const int rows = 2 * p.Hp;
+  const uint16_t* zero = uniform_ptr(kZeroRowBf16);
+  for (int i = w; i * 16 < rows; i += 8) {
+    const int k = 16 * i + (lane >> 2);
+    const int h = k < p.Hp ? k : k - p.Hp;
+    const uint16_t* base = k < p.Hp ? p.dsbuf : p.pbuf;
+    const uint16_t* src = h < p.H ? base + ((size_t)t * p.H + h) * p.TP + jt * kBK + 8 * (lane & 3) : zero + 8 * (lane & 3);
+    __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(uintptr_t)lds_addr(&sm.y[buf][16 * i][0]), 16, 0, 0);
+  }
+}
+
+__global__ __launch_bounds__(512) void smla_bwd_interm_kernel(const InterParams p) {
+  __shared__ __attribute__((aligned(16))) InterSmem sm;
+  const int t = blockIdx.x;
+  const int d0 = blockIdx.y * kIDC;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int li = lane & 15;
+  const int npos = p.ncount[t];
+  const int ntl = npos / kBK;
+  if (ntl == 0) return;
+  const int ksteps = (2 * p.Hp) / 32;
+
+  interm_stage_x(p, sm, t, d0, lane, w);
+  interm_stage_y(p, sm, 0, t, 0, lane, w);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  lds_barrier();
+
+  // lane's rows in a 32-row k step: 4g + li/4 (and + 16); column chunk 8 (li & 3) bytes
+  const uint32_t xr = lds_addr(&sm.x[0][0]) + (uint32_t)(4 * g + (li >> 2)) * (kIDC * 2) + 32 * w + 8 * (li & 3);
+  for (int it = 0; it < ntl; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < ntl) interm_stage_y(p, sm, buf ^ 1, t, it + 1, lane, w);
+    const uint32_t yr = lds_addr(&sm.y[buf][0][0]) + (uint32_t)(4 * g + (li >> 2)) * 64 + 8 * (li & 3);
+    f32x4 c[2][1];
+    for (int ks = 0; ks < ksteps; ++ks) {
+      const uint32_t xa = opaque(xr + (uint32_t)ks * 32 * (kIDC * 2));
+      const uint32_t ya = opaque(yr + (uint32_t)ks * 32 * 64);
+      u32x2 a0 = ds_read_tr16_b64<0>(xa);
+      u32x2 a1 = ds_read_tr16_b64<16 * kIDC * 2>(xa);
+      u32x2 b00 = ds_read_tr16_b64<0>(ya);
+      u32x2 b01 = ds_read_tr16_b64<16 * 64>(ya);
+      u32x2 b10 = ds_read_tr16_b64<32>(ya);
+      u32x2 b11 = ds_read_tr16_b64<16 * 64 + 32>(ya);
+      lds_wait6<0>(a0, a1, b00, b01, b10, b11);
+      const u32x4 a = u32x4{a0[0], a0[1], a1[0], a1[1]};
+      const u32x4 b0 = u32x4{b00[0], b00[1], b01[0], b01[1]};
+      const u32x4 b1 = u32x4{b10[0], b10[1], b11[0], b11[1]};
+      if (ks == 0) {
+        mfma_s_first(c[0][0], a, b0);
+        mfma_s_first(c[1][0], a, b1);
+      } else {
+        mfma_s(c[0][0], a, b0);
+        mfma_s(c[1][0], a, b1);
+      }
+    }
+    mfma_vgpr_drain<1>(c);
+    // lane holds C^T[d = 16 w + 4 g + i][j = 16 jt + li]
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt) {
+      const int j = it * kBK + 16 * jt + li;
+      const bf16x4 v = bf16x4{(__bf16)c[jt][0][0], (__bf16)c[jt][0][1], (__bf16)c[jt][0][2], (__bf16)c[jt][0][3]};
+      *(bf16x4*)(p.interm + ((size_t)t * p.TP + j) * kD + d0 + 16 * w + 4 * g) = v;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // next tile's rows landed (this wave's)
+    lds_barrier();                                      // ... every wave's; this tile no longer read
+  }
+}
+
+// ---- B3: start of each row's run in the sorted keys (lower bound) ----
+__global__ __launch_bounds__(256) void smla_bwd_rowstart_kernel(const uint32_t* __restrict__ skey, uint32_t n,
+                                                                uint32_t nrows, uint32_t* __restrict__ row_start) {
+  const uint32_t r = blockIdx.x * 256 + threadIdx.x;
+  if (r > nrows) return;
+  uint32_t lo = 0, hi = n;
+  while (lo < hi) {
+    const uint32_t mid = lo + (hi - lo) / 2;
+    if (skey[mid] < r) lo = mid + 1;
+    else hi = mid;
+  }
+  row_start[r] = lo;
+}
+
+// ---- B4: dkv[r] = sum of the interm rows of r's contributors (fp32), bf16 ----
+__global__ __launch_bounds__(256) void smla_bwd_dkv_kernel(const uint32_t* __restrict__ row_start,
+                                                           const uint32_t* __restrict__ sval,
+                                                           const uint16_t* __restrict__ interm, uint16_t* __restrict__ dkv,
+                                                           int64_t num_kv) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= num_kv) return;
+  const uint32_t e0 = row_start[r], e1 = row_start[r + 1];
+  float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  uint32_t e = e0;
+  for (; e + 4 <= e1; e += 4) {
+    u32x4 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = *(const u32x4*)(interm + (size_t)sval[e + u] * kD + 8 * lane);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bf16x8 v = __builtin_bit_cast(bf16x8, x[u]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a[i] += (float)v[i];
+    }
+  }
+  for (; e < e1; ++e) {
+    const bf16x8 v = __builtin_bit_cast(bf16x8, *(const u32x4*)(interm + (size_t)sval[e] * kD + 8 * lane));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] += (float)v[i];
+  }
+  const bf16x8 o = bf16x8{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3],
+                          (__bf16)a[4], (__bf16)a[5], (__bf16)a[6], (__bf16)a[7]};
+  *(bf16x8*)(dkv + r * kD + 8 * lane) = o;
+}
+
+// ---- B5: d_sink[h] = -sum_t part[t][h], in a fixed order ----
+__global__ __launch_bounds__(256) void smla_bwd_dsink_kernel(const float* __restrict__ part, int T, int H,
+                                                             float* __restrict__ d_sink) {
+  __shared__ float red[256];
+  const int h = blockIdx.x;
+  float acc = 0.f;
+  for (int t = threadIdx.x; t < T; t += 256) acc += part[(size_t)t * H + h];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) d_sink[h] = -red[0];
+}
+
+// Zero fill (rows of dkv when nothing is gathered; d_sink without tokens).
+__global__ __launch_bounds__(256) void smla_zero_kernel(uint32_t* __restrict__ p, int64_t n_words) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n_words; i += stride) p[i] = 0u;
+}
+
+int bwd_nw(int64_t H) { return H <= 16 ? 1 : (H <= 32 ? 2 : 4); }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" int sparse_mla_backward(const void* q, const void* kv, const void* dout, const void* o, const float* lse,
+                                   const int32_t* topk_indices, const float* attn_sink, float scale, void* dq,
+                                   void* dkv, float* d_sink, int64_t T, int64_t H, int64_t num_kv, int64_t topk,
+                                   void* stream) {
+  if (T < 0 || H < 1 || num_kv < 0 || topk < 0) return SMLA_ERR_BAD_SIZE;
+  if (H > kBwdMaxH || T > INT32_MAX || topk > INT32_MAX || num_kv >= ((int64_t)1 << 31)) return SMLA_ERR_BAD_SIZE;
+  if (!isfinite(scale)) return SMLA_ERR_BAD_SCALE;
+  const int64_t TP = (topk + kBK - 1) / kBK * kBK;
+  if (T * TP >= ((int64_t)1 << 31)) return SMLA_ERR_BAD_SIZE;
+  if (T > 0 && (!q || !dout || !o || !lse || !dq)) return SMLA_ERR_NULL_POINTER;
+  if (T > 0 && topk > 0 && !topk_indices) return SMLA_ERR_NULL_POINTER;
+  if (num_kv > 0 && (!kv || !dkv)) return SMLA_ERR_NULL_POINTER;
+  if (attn_sink && !d_sink) return SMLA_ERR_NULL_POINTER;
+  if (!aligned(q, 16) || !aligned(dout, 16) || !aligned(o, 16) || !aligned(dq, 16) || (kv && !aligned(kv, 16)) ||
+      (dkv && !aligned(dkv, 16)))
+    return SMLA_ERR_MISALIGNED;
+  if (!aligned(lse, 4) || (topk_indices && !aligned(topk_indices, 4)) || (attn_sink && !aligned(attn_sink, 4)) ||
+      (d_sink && !aligned(d_sink, 4)))
+    return SMLA_ERR_MISALIGNED;
+  int dev = 0;
+  if (current_device(&dev) != SMLA_OK) return SMLA_ERR_NO_DEVICE;
+  hipStream_t s = (hipStream_t)stream;
+
+  if (T == 0 || TP == 0) {
+    // No slot at all: every gradient is zero (with a sink, each token's o is 0,
+    // so delta and the sink gradient are 0 too).
+    if (num_kv > 0) hipLaunchKernelGGL(smla_zero_kernel, dim3(1024), dim3(256), 0, s, (uint32_t*)dkv, num_kv * kD / 2);
+    if (T > 0) hipLaunchKernelGGL(smla_zero_kernel, dim3(1024), dim3(256), 0, s, (uint32_t*)dq, T * H * kD / 2);
+    if (attn_sink) hipLaunchKernelGGL(smla_zero_kernel, dim3(1), dim3(256), 0, s, (uint32_t*)d_sink, H);
+    return hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
+  }
+
+  const int nw = bwd_nw(H);
+  const int64_t heads_per_wg = 16 * nw;
+  const int64_t head_groups = (H + heads_per_wg - 1) / heads_per_wg;
+  const int64_t N = T * TP;
+  const int Hp = (int)((H + 15) / 16 * 16);
+
+  const uint32_t nkv = kv ? (uint32_t)num_kv : 0u;
+  int end_bit = 1;  // the sort looks at the bits the keys use (rows < nkv, the sentinel nkv)
+  while (end_bit < 32 && ((uint64_t)1 << end_bit) <= (uint64_t)nkv) ++end_bit;
+
+  // scratch layout
+  size_t sort_bytes = 0;
+  {
+    const hipError_t e = hipcub::DeviceRadixSort::SortPairs(nullptr, sort_bytes, (const uint32_t*)nullptr,
+                                                            (uint32_t*)nullptr, (const uint32_t*)nullptr,
+                                                            (uint32_t*)nullptr, (int)N, 0, end_bit, s);
+    if (e != hipSuccess) return SMLA_ERR_LAUNCH;
+  }
+  const size_t A = 256;
+  size_t off = 0;
+  const size_t o_p = off;      off = align_up(off + (size_t)T * H * TP * 2, A);
+  const size_t o_ds = off;     off = align_up(off + (size_t)T * H * TP * 2, A);
+  const size_t o_ck = off;     off = align_up(off + (size_t)N * 4, A);
+  const size_t o_cv = off;     off = align_up(off + (size_t)N * 4, A);
+  const size_t o_sk = off;     off = align_up(off + (size_t)N * 4, A);
+  const size_t o_sv = off;     off = align_up(off + (size_t)N * 4, A);
+  const size_t o_nc = off;     off = align_up(off + (size_t)T * 4, A);
+  const size_t o_dsp = off;    off = align_up(off + (size_t)T * H * 4, A);
+  const size_t o_rs = off;     off = align_up(off + (size_t)(num_kv + 1) * 4, A);
+  const size_t o_it = off;     off = align_up(off + (size_t)N * kD * 2, A);
+  const size_t o_tmp = off;    off = align_up(off + sort_bytes, A);
+  void* ws = nullptr;
+  hipMemPool_t pool = scratch_pool(dev);
+  if (pool == nullptr || hipMallocFromPoolAsync(&ws, off, pool, s) != hipSuccess || ws == nullptr) {
+    (void)hipGetLastError();
+    return SMLA_ERR_NO_MEMORY;
+  }
+  char* b = (char*)ws;
+
+  BwdParams bp;
+  bp.q = (const uint16_t*)q;
+  bp.kv = (const uint16_t*)kv;
+  bp.dout = (const uint16_t*)dout;
+  bp.o = (const uint16_t*)o;
+  bp.lse = lse;
+  bp.topk = topk_indices;
+  bp.sink = attn_sink;
+  bp.dq = (uint16_t*)dq;
+  bp.pbuf = (uint16_t*)(b + o_p);
+  bp.dsbuf = (uint16_t*)(b + o_ds);
+  bp.ckey = (uint32_t*)(b + o_ck);
+  bp.cval = (uint32_t*)(b + o_cv);
+  bp.ncount = (int32_t*)(b + o_nc);
+  bp.dsink_part = (float*)(b + o_dsp);
+  bp.T = (int)T;
+  bp.H = (int)H;
+  bp.topk_n = (int)topk;
+  bp.TP = (int)TP;
+  bp.head_groups = (int)head_groups;
+  bp.nkv = nkv;
+  bp.sentinel = nkv;
+  bp.scale = scale;
+  bp.scale_log2 = scale * kLog2e;
+
+  const unsigned g1 = (unsigned)(T * head_groups);
+  if (nw == 1) hipLaunchKernelGGL((smla_bwd_dq_kernel<1, 2>), dim3(g1), dim3(64), 0, s, bp);
+  else if (nw == 2) hipLaunchKernelGGL((smla_bwd_dq_kernel<2, 2>), dim3(g1), dim3(128), 0, s, bp);
+  else hipLaunchKernelGGL((smla_bwd_dq_kernel<4, 2>), dim3(g1), dim3(256), 0, s, bp);
+  hipError_t err = hipGetLastError();
+
+  if (err == hipSuccess) {
+    InterParams ip;
+    ip.q = (const uint16_t*)q;
+    ip.dout = (const uint16_t*)dout;
+    ip.pbuf = bp.pbuf;
+    ip.dsbuf = bp.dsbuf;
+    ip.ncount = bp.ncount;
+    ip.interm = (uint16_t*)(b + o_it);
+    ip.T = (int)T;
+    ip.H = (int)H;
+    ip.Hp = Hp;
+    ip.TP = (int)TP;
+    hipLaunchKernelGGL(smla_bwd_interm_kernel, dim3((unsigned)T, kD / kIDC), dim3(512), 0, s, ip);
+    err = hipGetLastError();
+  }
+  if (err == hipSuccess && num_kv > 0) {
+    size_t tb = sort_bytes;
+    err = hipcub::DeviceRadixSort::SortPairs((void*)(b + o_tmp), tb, bp.ckey, (uint32_t*)(b + o_sk), bp.cval,
+                                             (uint32_t*)(b + o_sv), (int)N, 0, end_bit, s);
+  }
+  if (err == hipSuccess && num_kv > 0) {
+    hipLaunchKernelGGL(smla_bwd_rowstart_kernel, dim3((unsigned)((num_kv + 1 + 255) / 256)), dim3(256), 0, s,
+                       (const uint32_t*)(b + o_sk), (uint32_t)N, (uint32_t)num_kv, (uint32_t*)(b + o_rs));
+    hipLaunchKernelGGL(smla_bwd_dkv_kernel, dim3((unsigned)((num_kv + 3) / 4)), dim3(256), 0, s,
+                       (const uint32_t*)(b + o_rs), (const uint32_t*)(b + o_sv), (const uint16_t*)(b + o_it),
+                       (uint16_t*)dkv, num_kv);
+    err = hipGetLastError();
+  }
+  if (err == hipSuccess && attn_sink) {
+    hipLaunchKernelGGL(smla_bwd_dsink_kernel, dim3((unsigned)H), dim3(256), 0, s, (const float*)(b + o_dsp), (int)T,
+                       (int)H, d_sink);
+    err = hipGetLastError();
+  }
+  const hipError_t ferr = hipFreeAsync(ws, s);
+  return (err == hipSuccess && ferr == hipSuccess) ? SMLA_OK : SMLA_ERR_LAUNCH;
+}

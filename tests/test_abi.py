@@ -117,6 +117,36 @@ def test_fp8_entry_argument_errors(kw, rc):
     assert call8(**kw) == rc
 
 
+def callbwd(q=0x1000, kv=0x2000, dout=0x3000, o=0x4000, lse=0x5000, topk=0x6000, sink=None, scale=0.0441,
+            dq=0x7000, dkv=0x8000, d_sink=None, T=4, H=8, num_kv=16, k=8):
+    return _lib.load().sparse_mla_backward(q, kv, dout, o, lse, topk, sink, scale, dq, dkv, d_sink, T, H, num_kv, k,
+                                           None)
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(T=-1), _lib.SMLA_ERR_BAD_SIZE),
+    (dict(H=0), _lib.SMLA_ERR_BAD_SIZE),
+    (dict(H=129), _lib.SMLA_ERR_BAD_SIZE),  # the backward handles up to 128 heads
+    (dict(num_kv=2**31), _lib.SMLA_ERR_BAD_SIZE),
+    (dict(T=2**26, k=64), _lib.SMLA_ERR_BAD_SIZE),  # T * round_up(topk, 32) >= 2^31
+    (dict(scale=float("nan")), _lib.SMLA_ERR_BAD_SCALE),
+    (dict(q=None), _lib.SMLA_ERR_NULL_POINTER),
+    (dict(dout=None), _lib.SMLA_ERR_NULL_POINTER),
+    (dict(o=None), _lib.SMLA_ERR_NULL_POINTER),
+    (dict(lse=None), _lib.SMLA_ERR_NULL_POINTER),
+    (dict(dq=None), _lib.SMLA_ERR_NULL_POINTER),
+    (dict(dkv=None), _lib.SMLA_ERR_NULL_POINTER),
+    (dict(topk=None), _lib.SMLA_ERR_NULL_POINTER),
+    (dict(sink=0x9000), _lib.SMLA_ERR_NULL_POINTER),  # a sink needs d_sink
+    (dict(dq=0x7008), _lib.SMLA_ERR_MISALIGNED),
+    (dict(dkv=0x8004), _lib.SMLA_ERR_MISALIGNED),
+    (dict(lse=0x5002), _lib.SMLA_ERR_MISALIGNED),
+    (dict(sink=0x9000, d_sink=0xA001), _lib.SMLA_ERR_MISALIGNED),
+])
+def test_backward_argument_errors(kw, rc):
+    assert callbwd(**kw) == rc
+
+
 def test_empty_sequence_is_ok_without_a_device():
     assert call(T=0, q=None, out=None, lse=None, topk=None, kv=None) == _lib.SMLA_OK
 

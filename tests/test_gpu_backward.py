@@ -1,0 +1,163 @@
+"""Backward parity: the HIP path (through the C ABI) against the backward oracle.
+
+Both sides get the same inputs: q, kv, top-k rows, sink, a seeded dO, and the
+forward's o (bf16) and lse (fp32) as the GPU forward produced them.
+
+Tolerance, from the arithmetic: every term of a gradient element passes
+through bf16 at most three times on the GPU (P and scale dS enter their MFMAs
+in bf16; a slot's dkv contribution is stored in bf16; dq and dkv are stored in
+bf16), each a relative error of at most 2^-9, while the fp32 parts are ~2^-24.
+So |d| <= 6 * 2^-9 * mag + 1e-6 * max(mag) elementwise, mag being the sum of
+the absolute values of the element's terms (the oracle reports it), and the
+cosine similarity of each tensor with the oracle's must be >= 0.9999 (the
+pages' backward checks cos > 0.999). NaN patterns must match.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_top_amd import sparse_mla_backward, synth
+
+from gpu_util import DEV, bf16_bits, run_gpu, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+G_MAG = 6 * 2.0**-9
+G_COS = 0.9999
+
+
+def bf16(x):
+    return synth.f32_to_bf16_bits(np.asarray(x, np.float32))
+
+
+def f64(bits):
+    return synth.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def check_grad(got, ref, mag, what):
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    nan_ref = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan_ref), "%s: NaN pattern differs" % what
+    g, r, m = got[~nan_ref], ref[~nan_ref], mag[~nan_ref]
+    if r.size == 0:
+        return
+    err = np.abs(g - r)
+    bound = G_MAG * m + 1e-6 * float(m.max())
+    bad = err > bound
+    worst = int(np.argmax(err / np.maximum(bound, 1e-300)))
+    assert not bad.any(), "%s: %d of %d out of tolerance (worst: err %.3g, mag %.3g, ref %.3g)" % (
+        what, int(bad.sum()), r.size, float(err[worst]), float(m[worst]), float(r[worst]))
+    nr, ng = np.linalg.norm(r), np.linalg.norm(g)
+    if nr > 0:
+        cos = float(np.dot(g, r) / (nr * ng))
+        assert cos >= G_COS, "%s: cosine %.6f" % (what, cos)
+    else:
+        assert np.all(g == 0), "%s: reference is zero, got nonzero" % what
+
+
+def run_backward(q, kv, dout, o_bits, lse, topk, sink, scale):
+    qd, dd, od = to_dev_bf16(q), to_dev_bf16(dout), to_dev_bf16(o_bits)
+    kvd = to_dev_bf16(kv) if kv.shape[0] else torch.empty((0, 512), dtype=torch.bfloat16, device=DEV)
+    ld = torch.from_numpy(np.ascontiguousarray(lse, dtype=np.float32)).to(DEV)
+    td = torch.from_numpy(np.ascontiguousarray(topk, dtype=np.int32)).to(DEV)
+    sd = None if sink is None else torch.from_numpy(np.ascontiguousarray(sink, dtype=np.float32)).to(DEV)
+    dq, dkv, ds = sparse_mla_backward(qd, kvd, dd, od, ld, td, sd, scale)
+    torch.cuda.synchronize()
+    return (f64(bf16_bits(dq)), f64(bf16_bits(dkv)) if kv.shape[0] else np.zeros((0, 512)),
+            None if ds is None else ds.cpu().numpy().astype(np.float64))
+
+
+def full_case(q, kv, topk, sink, scale, seed, what, tokens=None, rows=None):
+    """GPU forward, then GPU backward and oracle backward on the same inputs; compare."""
+    print("backward case %s: T=%d H=%d topk=%d num_kv=%d sink=%s" % (
+        what, q.shape[0], q.shape[1], topk.shape[1], kv.shape[0], sink is not None), flush=True)
+    rng = np.random.default_rng(seed)
+    dout = bf16(rng.standard_normal(q.shape))
+    o_bits, lse = run_gpu(q, kv, topk, sink, scale)
+    dq, dkv, ds = run_backward(q, kv, dout, o_bits, lse, topk, sink, scale)
+    ref = oracle.backward(q, kv, dout, o_bits, lse, topk, sink, scale, tokens=tokens, rows=rows, want_mag=True)
+    check_grad(dq if tokens is None else dq[tokens], ref["dq"], ref["dq_mag"], what + " dq")
+    check_grad(dkv if rows is None else dkv[rows], ref["dkv"], ref["dkv_mag"], what + " dkv")
+    if sink is not None:
+        check_grad(ds, ref["d_sink"], ref["d_sink_mag"], what + " d_sink")
+    else:
+        assert ds is None
+    return dq, dkv, ds
+
+
+def random_case(seed, T, H, topk, num_kv, p_invalid=0.2, sink=True, dup=False):
+    rng = np.random.default_rng(seed)
+    q = bf16(rng.standard_normal((T, H, 512)))
+    kv = bf16(rng.standard_normal((num_kv, 512)))
+    idx = np.empty((T, topk), np.int32)
+    for t in range(T):
+        rows = rng.choice(num_kv, topk, replace=dup or topk > num_kv).astype(np.int64)
+        bad = rng.random(topk) < p_invalid
+        rows[bad] = rng.choice(np.array([-1, num_kv, num_kv + 5, -(2**31), 2**31 - 1], np.int64), bad.sum())
+        idx[t] = rows.astype(np.int32)
+    s = rng.standard_normal(H).astype(np.float32) if sink else None
+    return q, kv, idx, s
+
+
+def test_backward_tiny_config():
+    inp = synth.make_inputs("tiny")
+    full_case(inp["q"], inp["kv"], inp["topk"], inp["sink"], inp["scale"], 1, "tiny")
+
+
+@pytest.mark.parametrize("H,topk,sink,dup", [(128, 96, True, False), (64, 40, False, True), (100, 70, True, False),
+                                             (8, 40, True, False), (24, 33, False, False), (16, 5, True, True)])
+def test_backward_random(H, topk, sink, dup):
+    q, kv, idx, s = random_case(H * 7 + topk, T=40, H=H, topk=topk, num_kv=300, sink=sink, dup=dup)
+    full_case(q, kv, idx, s, synth.DEFAULT_SCALE, H + topk, "random H=%d topk=%d" % (H, topk))
+
+
+def test_backward_multi_segment_row():
+    """Rows longer than one 2048-entry compaction segment."""
+    q, kv, idx, s = random_case(5, T=6, H=16, topk=2500, num_kv=3000, p_invalid=0.3)
+    full_case(q, kv, idx, s, synth.DEFAULT_SCALE, 6, "topk 2500")
+
+
+def test_backward_all_invalid_and_heavy_rows():
+    """Tokens with no valid slot, and a row every token references many times."""
+    q, kv, idx, s = random_case(9, T=32, H=16, topk=64, num_kv=200, p_invalid=0.1)
+    idx[3] = -1
+    idx[17] = 200
+    idx[:, 5:12] = 7  # row 7: seven slots per token
+    full_case(q, kv, idx, s, 0.07, 10, "invalid + heavy rows")
+
+
+def test_backward_empty_topk_and_zero_tokens():
+    q, kv, idx, s = random_case(11, T=8, H=16, topk=4, num_kv=50)
+    idx0 = np.zeros((8, 0), np.int32)
+    dq, dkv, ds = full_case(q, kv, idx0, s, synth.DEFAULT_SCALE, 12, "topk 0")
+    assert np.all(dq == 0) and np.all(dkv == 0) and np.all(ds == 0)
+    q0 = np.zeros((0, 16, 512), np.uint16)
+    dq, dkv, ds = run_backward(q0, kv, q0, q0, np.zeros((0, 16), np.float32), np.zeros((0, 4), np.int32), s,
+                               synth.DEFAULT_SCALE)
+    assert dq.shape == (0, 16, 512) and np.all(dkv == 0) and np.all(ds == 0)
+
+
+def test_backward_is_deterministic():
+    q, kv, idx, s = random_case(13, T=64, H=128, topk=128, num_kv=400, dup=True)
+    rng = np.random.default_rng(14)
+    dout = bf16(rng.standard_normal(q.shape))
+    o_bits, lse = run_gpu(q, kv, idx, s, synth.DEFAULT_SCALE)
+    a = run_backward(q, kv, dout, o_bits, lse, idx, s, synth.DEFAULT_SCALE)
+    b = run_backward(q, kv, dout, o_bits, lse, idx, s, synth.DEFAULT_SCALE)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_backward_wide_full_size_sampled():
+    """The wide workload (T=4096, H=128, topk=512) at full size: dq of sampled
+    tokens, dkv of sampled rows (window rows and heavily shared pool rows), and
+    d_sink over all tokens, against the oracle."""
+    inp = synth.make_inputs("wide")
+    T = inp["T"]
+    tokens = np.linspace(0, T - 1, 24).astype(np.int64)
+    num_kv = inp["kv"].shape[0]
+    rows = np.array([0, 1, T // 2, T - 1, T, T + 1, T + 300, num_kv - 1], np.int64)
+    full_case(inp["q"], inp["kv"], inp["topk"], inp["sink"], inp["scale"], 15, "wide sampled", tokens=tokens,
+              rows=rows)

@@ -158,6 +158,24 @@ def test_unreferenced_rows_and_linearity_in_dout():
         assert np.array_equal(r2[k], 2.0 * r1[k]), k
 
 
+def test_magnitudes_bound_the_gradients():
+    """|gradient| <= sum of |terms|, with equality where every term has one sign
+    (P dO terms of a row held by one slot of one head: H = 1, one token)."""
+    q, kv, dout, idx, s = case(51, num_kv=30)
+    f = oracle.forward(q, kv, idx, s, 0.2)
+    r = oracle.backward(q, kv, dout, f["o"], f["lse"], idx, s, 0.2, want_mag=True)
+    for k in ("dq", "dkv", "d_sink"):
+        assert np.all(np.abs(r[k]) <= r[k + "_mag"] * (1 + 1e-12) + 1e-300), k
+    plain = oracle.backward(q, kv, dout, f["o"], f["lse"], idx, s, 0.2)
+    for k in ("dq", "dkv", "d_sink"):
+        assert np.array_equal(plain[k], r[k]), k
+    q1, kv1, dout1, idx1, _ = case(52, T=1, H=1, topk=4, p_invalid=0.0)
+    idx1[0] = [3, -1, -1, -1]
+    f1 = oracle.forward(q1, kv1, idx1, None, 0.2)
+    r1 = oracle.backward(q1, kv1, dout1, f1["o"], f1["lse"], idx1, None, 0.2, want_mag=True)
+    np.testing.assert_allclose(r1["dkv_mag"][3], np.abs(r1["dkv"][3]), rtol=1e-15)
+
+
 def test_selected_tokens_and_rows_match_full_evaluation():
     q, kv, dout, idx, s = case(41, T=7, num_kv=30)
     f = oracle.forward(q, kv, idx, s, 0.2)
