@@ -158,6 +158,44 @@ def measure(name: str, steps: int, warmup: int, cold_steps: int = 0, idx64: bool
     return inp, alg, t
 
 
+def measure_bwd(name: str, steps: int, warmup: int):
+    """The backward on a workload: dO ~ N(0, 1) from a seeded device generator,
+    o and lse from one forward call, then `steps` timed backward calls."""
+    import torch
+
+    from sparse_attention_top_amd import sparse_mla_backward, sparse_mla_prefill, synth
+
+    inp = synth.make_inputs(name)
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(inp["q"].view(np.int16)).view(torch.bfloat16).to(dev)
+    kv = torch.from_numpy(inp["kv"].view(np.int16)).view(torch.bfloat16).to(dev)
+    topk = torch.from_numpy(inp["topk"]).to(dev)
+    sink = torch.from_numpy(inp["sink"]).to(dev) if inp["sink"] is not None else None
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(inp["config"].seed + 1000)
+    dout = torch.randn(q.shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    o, lse = sparse_mla_prefill(q, kv, topk, sink, inp["scale"])
+    stream = torch.cuda.current_stream(dev)
+
+    def run():
+        sparse_mla_backward(q, kv, dout, o, lse, topk, sink, inp["scale"])
+
+    wall, st = time_gpu(run, steps, warmup, stream)
+    nvalid = int(((inp["topk"] >= 0) & (inp["topk"] < inp["num_kv"])).sum())
+    ms = st["mean"]
+    flops_valid = 10.0 * inp["H"] * D * nvalid  # S, dP, dQ and the two dkv terms per valid (slot, head)
+    flops_pages = 10.0 * inp["T"] * inp["H"] * inp["topk_n"] * D  # the backward page's TFLOPS convention
+    return {"workload": "bwd:" + name, "ms_per_call": wall * 1e3 / steps, "kernel_ms_mean": ms,
+            "kernel_ms_median": st["median"], "kernel_ms_min": st["min"],
+            "tflops_pages_formula": flops_pages / (ms * 1e-3) / 1e12,
+            "tflops_valid": flops_valid / (ms * 1e-3) / 1e12, "valid_slots": nvalid,
+            "roofline": {"bound": "mfma", "achieved": flops_valid / (ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": flops_valid / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                         "traffic": None, "kernel": "backward (five phases)"},
+            "note": "per-call time of the whole backward (dq, dkv, d_sink: five kernels and the sort); "
+                    "TFLOPS as the backward page counts them, 10 T H topk 512 / t, and on valid slots"}
+
+
 def roofline(alg, t, kernel, workload, bound):
     if bound == "mfma":
         achieved = alg["flops"] / (t["kernel_ms_mean"] * 1e-3) / 1e12
@@ -179,6 +217,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timing of the main workload")
+    ap.add_argument("--bwd", action="store_true",
+                    help="only time the backward on --workload and print its line (for profiling)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -205,6 +245,12 @@ def main():
         return
 
     from sparse_attention_top_amd import synth
+
+    if args.bwd:
+        print("bench: backward on %s, %d warmup + %d timed steps" % (args.workload, args.warmup, args.steps),
+              file=sys.stderr, flush=True)
+        print(json.dumps(measure_bwd(args.workload, args.steps, args.warmup)))
+        return
 
     print("bench: workload %s, %d warmup + %d timed steps" % (args.workload, args.warmup, args.steps),
           file=sys.stderr, flush=True)
@@ -265,6 +311,12 @@ def main():
                 sec[-1]["note"] = ("few-token call: split-KV kernel + merge kernel; per-launch events include the "
                                    "host launch gap, rocprofv3 kernel time is the GPU figure")
             print("bench: %s %.4f ms/call" % (other, t2["ms_per_call"]), file=sys.stderr, flush=True)
+        for name in ("wide",):
+            b = measure_bwd(name, max(10, args.steps // 2), args.warmup)
+            sec.append(b)
+            print("bench: bwd:%s %.4f ms/call, %.1f TFLOPS (page formula)" % (name, b["kernel_ms_mean"],
+                                                                             b["tflops_pages_formula"]),
+                  file=sys.stderr, flush=True)
         line["secondary"] = sec
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a token sample", file=sys.stderr, flush=True)
