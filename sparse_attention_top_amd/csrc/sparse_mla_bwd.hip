@@ -17,9 +17,9 @@
 //      from the same tile; writes dq, P and scale dS (bf16, [T][H][TP], TP =
 //      top-k rounded up to 32, compacted positions), the row key and entry id
 //      of every compacted position, and the sink partials.
-//   B2 smla_bwd_interm_kernel  one workgroup per (token, 128 columns of d): the
-//      per-slot dkv contribution interm[t][j] = [scale dS ; P]^T [q ; dO], one
-//      MFMA contraction over heads (both terms side by side along K).
+//   B2 smla_bwd_interm_kernel  one workgroup per token: the per-slot dkv
+//      contribution interm[t][j] = [scale dS ; P]^T [q ; dO], one MFMA
+//      contraction over heads (both terms side by side along K).
 //   B3 a stable radix sort of (row key, entry id) (hipcub) and the start of
 //      each row's run: the scatter inverted, so each row gathers its own
 //      contributors in a fixed order (deterministic, no atomics).
@@ -36,7 +36,6 @@ namespace {
 using namespace smla_host;
 
 constexpr int kBwdMaxH = 128;  // heads handled by the interm contraction (2 x 128 rows of K)
-constexpr int kIDC = 128;      // d columns per interm workgroup
 
 // A zero row for padded heads (interm staging gathers them from here).
 __device__ __attribute__((aligned(256))) const uint16_t kZeroRowBf16[kD] = {};
@@ -264,13 +263,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
 }
 
 // ---- B2: interm[t][j][d] = sum_h scale dS[t][h][j] q[t][h][d] + P[t][h][j] dO[t][h][d] ----
-// One workgroup of 8 waves per (token, 128 columns of d); wave w owns 16
-// columns. C^T[d][j] = X^T[d][k] Y[k][j] with k running over the 2 Hp rows
-// [q ; dO] (X, staged [k][128 d], 256 B rows) and [scale dS ; P] (Y, staged
-// per 32-position tile, [k][32 j], 64 B rows), Hp = H rounded up to 16, rows
-// of padded heads zero. Both MFMA operands come from transposing LDS reads:
-// lane (g, li) takes rows k0 + 4g .. +3 and k0 + 16 + 4g .. +3 at one column,
-// the same rows for both, so the K order matches.
+// One workgroup of 8 waves per token; wave w owns the 64 columns d = 64 w ..
+// 64 w + 63 (four 16-column d-tiles). C^T[d][j] = X^T[d][k] Y[k][j], k running
+// over the 2 Hp rows of X = [q ; dO] and of Y = [scale dS ; P] (Hp = H rounded
+// up to 16; rows of padded heads are zero), KS = 2 Hp / 32 MFMA k-steps. A wave's
+// X^T fragments (4 KS of them) do not depend on j: they are read once per token,
+// from [q ; dO] staged a quarter of d (128 columns) at a time, and stay in
+// registers. Y is staged per 32-position tile (double-buffered, the next tile's
+// LDS-DMA in flight during the current one). Both operands come from
+// transposing LDS reads that give lane (g, li) rows k0 + 4g .. +3 and
+// k0 + 16 + 4g .. +3 at one column, the same rows for both, so the K order
+// matches.
 struct InterParams {
   const uint16_t* q;
   const uint16_t* dout;
@@ -285,25 +288,25 @@ struct InterParams {
 };
 
 struct InterSmem {
-  uint8_t x[2 * kBwdMaxH][kIDC * 2];  // [q ; dO] rows, 256 B each
-  uint8_t y[2][2 * kBwdMaxH][64];     // [scale dS ; P] rows of a 32-position tile, double-buffered
+  uint8_t x[2][2 * kBwdMaxH][256];  // [q ; dO] rows, 128 columns of d, double-buffered
+  uint8_t y[2][2 * kBwdMaxH][64];   // [scale dS ; P] rows of a 32-position tile, double-buffered
 };
 
-// Stage the [q ; dO] column block: row k = 4i + L/16, bytes 16 (L % 16); wave w issues i = w, w + 8, ...
-__device__ __forceinline__ void interm_stage_x(const InterParams& p, InterSmem& sm, int t, int d0, int lane, int w) {
+// Stage quarter qd of [q ; dO] (columns 128 qd ..): row k = 4i + L/16, bytes 16 (L % 16); wave w issues i = w, w + 8, ...
+__device__ __forceinline__ void interm_stage_x(const InterParams& p, uint8_t (*x)[256], int t, int qd, int lane, int w) {
   const int rows = 2 * p.Hp;
   const uint16_t* zero = uniform_ptr(kZeroRowBf16);
   for (int i = w; i * 4 < rows; i += 8) {
     const int k = 4 * i + (lane >> 4);
     const int h = k < p.Hp ? k : k - p.Hp;
     const uint16_t* base = k < p.Hp ? p.q : p.dout;
-    const uint16_t* src = h < p.H ? base + ((size_t)t * p.H + h) * kD + d0 + 8 * (lane & 15) : zero + 8 * (lane & 15);
-    __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(uintptr_t)lds_addr(&sm.x[4 * i][0]), 16, 0, 0);
+    const uint16_t* src =
+        h < p.H ? base + ((size_t)t * p.H + h) * kD + 128 * qd + 8 * (lane & 15) : zero + 8 * (lane & 15);
+    __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(uintptr_t)lds_addr(&x[4 * i][0]), 16, 0, 0);
   }
 }
 // Stage tile jt of [scale dS ; P]: row k = 16i + L/4, bytes 16 (L % 4).
-__device__ __forceinline__ void interm_stage_y(const InterParams& p, InterSmem& sm, int buf, int t, int jt, int lane,
-                                               int w) {
+__device__ __forceinline__ void interm_stage_y(const InterParams& p, uint8_t (*y)[64], int t, int jt, int lane, int w) {
   const int rows = 2 * p.Hp;
   const uint16_t* zero = uniform_ptr(kZeroRowBf16);
   for (int i = w; i * 16 < rows; i += 8) {
@@ -311,66 +314,96 @@ __device__ __forceinline__ void interm_stage_y(const InterParams& p, InterSmem& 
     const int h = k < p.Hp ? k : k - p.Hp;
     const uint16_t* base = k < p.Hp ? p.dsbuf : p.pbuf;
     const uint16_t* src = h < p.H ? base + ((size_t)t * p.H + h) * p.TP + jt * kBK + 8 * (lane & 3) : zero + 8 * (lane & 3);
-    __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(uintptr_t)lds_addr(&sm.y[buf][16 * i][0]), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(uintptr_t)lds_addr(&y[16 * i][0]), 16, 0, 0);
   }
 }
 
-__global__ __launch_bounds__(512) void smla_bwd_interm_kernel(const InterParams p) {
+template <int KS>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void smla_bwd_interm_kernel(
+    const InterParams p) {
   __shared__ __attribute__((aligned(16))) InterSmem sm;
   const int t = blockIdx.x;
-  const int d0 = blockIdx.y * kIDC;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
   const int li = lane & 15;
-  const int npos = p.ncount[t];
-  const int ntl = npos / kBK;
+  const int ntl = p.ncount[t] / kBK;
   if (ntl == 0) return;
-  const int ksteps = (2 * p.Hp) / 32;
 
-  interm_stage_x(p, sm, t, d0, lane, w);
-  interm_stage_y(p, sm, 0, t, 0, lane, w);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  lds_barrier();
+  interm_stage_y(p, sm.y[0], t, 0, lane, w);
+  interm_stage_x(p, sm.x[0], t, 0, lane, w);
+  // lane's row in a 32-row k step (4g + li/4, and + 16) and its 8-byte column chunk
+  const uint32_t lrow = (uint32_t)(4 * g + (li >> 2));
+  u32x4 af[KS][4];
+  static_for<0, 4>([&](auto qc) {
+    constexpr int qd = decltype(qc)::value;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // quarter qd (and Y tile 0) landed, this wave's part
+    lds_barrier();                                      // ... every wave's; quarter qd - 1 no longer read
+    if constexpr (qd + 1 < 4) interm_stage_x(p, sm.x[(qd + 1) & 1], t, qd + 1, lane, w);
+    if (w / 2 == qd) {
+      const uint32_t xb = opaque(lds_addr(&sm.x[qd & 1][0][0]) + lrow * 256 + 128 * (w & 1) + 8 * (li & 3));
+      static_for<0, KS>([&](auto kc) {
+        constexpr int ks = decltype(kc)::value;
+        static_for<0, 4>([&](auto dc) {
+          constexpr int dt = decltype(dc)::value;
+          u32x2 a0 = ds_read_tr16_b64<ks * 32 * 256 + 32 * dt>(xb);
+          u32x2 a1 = ds_read_tr16_b64<ks * 32 * 256 + 16 * 256 + 32 * dt>(xb);
+          lds_wait<0>(a0, a1);
+          af[ks][dt] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+        });
+      });
+    }
+  });
 
-  // lane's rows in a 32-row k step: 4g + li/4 (and + 16); column chunk 8 (li & 3) bytes
-  const uint32_t xr = lds_addr(&sm.x[0][0]) + (uint32_t)(4 * g + (li >> 2)) * (kIDC * 2) + 32 * w + 8 * (li & 3);
   for (int it = 0; it < ntl; ++it) {
     const int buf = it & 1;
-    if (it + 1 < ntl) interm_stage_y(p, sm, buf ^ 1, t, it + 1, lane, w);
-    const uint32_t yr = lds_addr(&sm.y[buf][0][0]) + (uint32_t)(4 * g + (li >> 2)) * 64 + 8 * (li & 3);
-    f32x4 c[2][1];
-    for (int ks = 0; ks < ksteps; ++ks) {
-      const uint32_t xa = opaque(xr + (uint32_t)ks * 32 * (kIDC * 2));
-      const uint32_t ya = opaque(yr + (uint32_t)ks * 32 * 64);
-      u32x2 a0 = ds_read_tr16_b64<0>(xa);
-      u32x2 a1 = ds_read_tr16_b64<16 * kIDC * 2>(xa);
-      u32x2 b00 = ds_read_tr16_b64<0>(ya);
-      u32x2 b01 = ds_read_tr16_b64<16 * 64>(ya);
-      u32x2 b10 = ds_read_tr16_b64<32>(ya);
-      u32x2 b11 = ds_read_tr16_b64<16 * 64 + 32>(ya);
-      lds_wait6<0>(a0, a1, b00, b01, b10, b11);
-      const u32x4 a = u32x4{a0[0], a0[1], a1[0], a1[1]};
-      const u32x4 b0 = u32x4{b00[0], b00[1], b01[0], b01[1]};
-      const u32x4 b1 = u32x4{b10[0], b10[1], b11[0], b11[1]};
-      if (ks == 0) {
-        mfma_s_first(c[0][0], a, b0);
-        mfma_s_first(c[1][0], a, b1);
-      } else {
-        mfma_s(c[0][0], a, b0);
-        mfma_s(c[1][0], a, b1);
-      }
-    }
-    mfma_vgpr_drain<1>(c);
-    // lane holds C^T[d = 16 w + 4 g + i][j = 16 jt + li]
+    if (it + 1 < ntl) interm_stage_y(p, sm.y[buf ^ 1], t, it + 1, lane, w);
+    const uint32_t yb = opaque(lds_addr(&sm.y[buf][0][0]) + lrow * 64 + 8 * (li & 3));
+    f32x4 c[4][2];
+    u32x2 bf[2][2][2];  // [k-step parity][jt][half]
+    auto bread = [&](auto kc) {
+      constexpr int ks = decltype(kc)::value;
+      static_for<0, 2>([&](auto jc) {
+        constexpr int jt = decltype(jc)::value;
+        bf[ks & 1][jt][0] = ds_read_tr16_b64<ks * 32 * 64 + 32 * jt>(yb);
+        bf[ks & 1][jt][1] = ds_read_tr16_b64<ks * 32 * 64 + 16 * 64 + 32 * jt>(yb);
+      });
+    };
+    bread(Int<0>{});
+    static_for<0, KS>([&](auto kc) {
+      constexpr int ks = decltype(kc)::value;
+      if constexpr (ks + 1 < KS) bread(Int<ks + 1>{});
+      constexpr int younger = ks + 1 < KS ? 4 : 0;
+      asm volatile("s_waitcnt lgkmcnt(%4)"
+                   : "+v"(bf[ks & 1][0][0]), "+v"(bf[ks & 1][0][1]), "+v"(bf[ks & 1][1][0]), "+v"(bf[ks & 1][1][1])
+                   : "n"(younger));
+      static_for<0, 2>([&](auto jc) {
+        constexpr int jt = decltype(jc)::value;
+        const u32x4 b = u32x4{bf[ks & 1][jt][0][0], bf[ks & 1][jt][0][1], bf[ks & 1][jt][1][0], bf[ks & 1][jt][1][1]};
+        static_for<0, 4>([&](auto dc) {
+          constexpr int dt = decltype(dc)::value;
+          if constexpr (ks == 0) mfma_s_first(c[dt][jt], af[ks][dt], b);
+          else mfma_s(c[dt][jt], af[ks][dt], b);
+        });
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");  // MFMA write -> VALU read distance
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) asm volatile("" : "+v"(c[dt][jt]));
+    // lane holds C^T[d = 64 w + 16 dt + 4 g + i][j = 32 it + 16 jt + li]: 8 stores
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt) {
-      const int j = it * kBK + 16 * jt + li;
-      const bf16x4 v = bf16x4{(__bf16)c[jt][0][0], (__bf16)c[jt][0][1], (__bf16)c[jt][0][2], (__bf16)c[jt][0][3]};
-      *(bf16x4*)(p.interm + ((size_t)t * p.TP + j) * kD + d0 + 16 * w + 4 * g) = v;
+      uint16_t* row = p.interm + ((size_t)t * p.TP + it * kBK + 16 * jt + li) * kD + 64 * w + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        *(bf16x4*)(row + 16 * dt) =
+            bf16x4{(__bf16)c[dt][jt][0], (__bf16)c[dt][jt][1], (__bf16)c[dt][jt][2], (__bf16)c[dt][jt][3]};
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // next tile's rows landed (this wave's)
-    lds_barrier();                                      // ... every wave's; this tile no longer read
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // the next tile's rows landed (only the 8 stores may be younger)
+    lds_barrier();                                     // ... every wave's; this tile no longer read
   }
 }
 
@@ -562,7 +595,17 @@ extern "C" int sparse_mla_backward(const void* q, const void* kv, const void* do
     ip.H = (int)H;
     ip.Hp = Hp;
     ip.TP = (int)TP;
-    hipLaunchKernelGGL(smla_bwd_interm_kernel, dim3((unsigned)T, kD / kIDC), dim3(512), 0, s, ip);
+    const dim3 grid((unsigned)T);
+    switch (Hp / 16) {
+      case 1: hipLaunchKernelGGL(smla_bwd_interm_kernel<1>, grid, dim3(512), 0, s, ip); break;
+      case 2: hipLaunchKernelGGL(smla_bwd_interm_kernel<2>, grid, dim3(512), 0, s, ip); break;
+      case 3: hipLaunchKernelGGL(smla_bwd_interm_kernel<3>, grid, dim3(512), 0, s, ip); break;
+      case 4: hipLaunchKernelGGL(smla_bwd_interm_kernel<4>, grid, dim3(512), 0, s, ip); break;
+      case 5: hipLaunchKernelGGL(smla_bwd_interm_kernel<5>, grid, dim3(512), 0, s, ip); break;
+      case 6: hipLaunchKernelGGL(smla_bwd_interm_kernel<6>, grid, dim3(512), 0, s, ip); break;
+      case 7: hipLaunchKernelGGL(smla_bwd_interm_kernel<7>, grid, dim3(512), 0, s, ip); break;
+      default: hipLaunchKernelGGL(smla_bwd_interm_kernel<8>, grid, dim3(512), 0, s, ip); break;
+    }
     err = hipGetLastError();
   }
   if (err == hipSuccess && num_kv > 0) {
