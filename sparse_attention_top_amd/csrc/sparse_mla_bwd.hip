@@ -23,8 +23,10 @@
 //   B3 a stable radix sort of (row key, entry id) (hipcub) and the start of
 //      each row's run: the scatter inverted, so each row gathers its own
 //      contributors in a fixed order (deterministic, no atomics).
-//   B4 smla_bwd_dkv_kernel     one wave per pool row: fp32 sum of its interm
-//      rows, bf16 store (rows nobody references get 0).
+//   B4 smla_bwd_dkv_chunk_kernel / smla_bwd_dkv_fix_kernel: fixed 64-entry
+//      chunks of the sorted entries, one wave each, sum the interm rows of
+//      each row's contributors (fp32); rows spanning chunks are finished from
+//      per-chunk partials in chunk order; rows nobody references get 0.
 //   B5 smla_bwd_dsink_kernel   fixed-order sum of the sink partials.
 
 #include <hipcub/hipcub.hpp>
@@ -422,35 +424,95 @@ __global__ __launch_bounds__(256) void smla_bwd_rowstart_kernel(const uint32_t* 
 }
 
 // ---- B4: dkv[r] = sum of the interm rows of r's contributors (fp32), bf16 ----
-__global__ __launch_bounds__(256) void smla_bwd_dkv_kernel(const uint32_t* __restrict__ row_start,
-                                                           const uint32_t* __restrict__ sval,
-                                                           const uint16_t* __restrict__ interm, uint16_t* __restrict__ dkv,
-                                                           int64_t num_kv) {
+// The sorted entries are cut into chunks of kChunk; one wave per chunk sums
+// each run of equal keys inside it (lane L: d = 8L .. 8L+7). A run that is a
+// whole row is stored to dkv at once; the run at a chunk's start that belongs
+// to a row begun in an earlier chunk goes to head[chunk], the run at its end
+// that continues past it to tail[chunk] (fp32). B4b then finishes every row
+// that spans chunks c0 .. c1 as tail[c0] + head[c0 + 1] + ... + head[c1], in
+// that order, and zero-fills rows no slot holds. The order of every sum is
+// fixed by the sort, so dkv is deterministic.
+constexpr int kChunk = 64;
+
+__device__ __forceinline__ void dkv_flush(const float (&a)[8], uint32_t r, uint32_t s0, uint32_t s1,
+                                          const uint32_t* __restrict__ row_start, uint16_t* __restrict__ dkv,
+                                          float* __restrict__ head, float* __restrict__ tail, uint32_t c, int lane) {
+  const bool before = row_start[r] < s0;
+  const bool after = row_start[r + 1] > s1;
+  if (!before && !after) {
+    *(bf16x8*)(dkv + (size_t)r * kD + 8 * lane) = bf16x8{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3],
+                                                         (__bf16)a[4], (__bf16)a[5], (__bf16)a[6], (__bf16)a[7]};
+  } else {
+    float* dst = (before ? head : tail) + (size_t)c * kD + 8 * lane;
+    *(f32x4*)dst = f32x4{a[0], a[1], a[2], a[3]};
+    *(f32x4*)(dst + 4) = f32x4{a[4], a[5], a[6], a[7]};
+  }
+}
+
+__global__ __launch_bounds__(256) void smla_bwd_dkv_chunk_kernel(const uint32_t* __restrict__ skey,
+                                                                 const uint32_t* __restrict__ sval,
+                                                                 const uint32_t* __restrict__ row_start,
+                                                                 const uint16_t* __restrict__ interm,
+                                                                 uint16_t* __restrict__ dkv, float* __restrict__ head,
+                                                                 float* __restrict__ tail, uint32_t num_kv) {
   const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= num_kv) return;
-  const uint32_t e0 = row_start[r], e1 = row_start[r + 1];
+  const uint32_t c = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const uint32_t nv = row_start[num_kv];  // entries with a valid key
+  const uint32_t e0 = c * kChunk;
+  if (e0 >= nv) return;
+  const uint32_t e1 = min(e0 + (uint32_t)kChunk, nv);
   float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  uint32_t e = e0;
-  for (; e + 4 <= e1; e += 4) {
+  uint32_t cur = skey[e0], seg = e0;
+  for (uint32_t e = e0; e < e1; e += 4) {
     u32x4 x[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) x[u] = *(const u32x4*)(interm + (size_t)sval[e + u] * kD + 8 * lane);
+    uint32_t rk[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
+      const uint32_t ee = e + u < e1 ? e + u : e1 - 1;  // in range; the extra loads are not used
+      rk[u] = skey[ee];
+      x[u] = *(const u32x4*)(interm + (size_t)sval[ee] * kD + 8 * lane);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (e + u >= e1) break;
+      if (rk[u] != cur) {
+        dkv_flush(a, cur, seg, e + u, row_start, dkv, head, tail, c, lane);
+        cur = rk[u];
+        seg = e + u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i] = 0.f;
+      }
       const bf16x8 v = __builtin_bit_cast(bf16x8, x[u]);
 #pragma unroll
       for (int i = 0; i < 8; ++i) a[i] += (float)v[i];
     }
   }
-  for (; e < e1; ++e) {
-    const bf16x8 v = __builtin_bit_cast(bf16x8, *(const u32x4*)(interm + (size_t)sval[e] * kD + 8 * lane));
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] += (float)v[i];
+  dkv_flush(a, cur, seg, e1, row_start, dkv, head, tail, c, lane);
+}
+
+__global__ __launch_bounds__(256) void smla_bwd_dkv_fix_kernel(const uint32_t* __restrict__ row_start,
+                                                               const float* __restrict__ head,
+                                                               const float* __restrict__ tail, uint16_t* __restrict__ dkv,
+                                                               int64_t num_kv) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= num_kv) return;
+  const uint32_t s0 = row_start[r], s1 = row_start[r + 1];
+  uint16_t* dst = dkv + r * kD + 8 * lane;
+  if (s0 == s1) {
+    *(u32x4*)dst = u32x4{0u, 0u, 0u, 0u};
+    return;
   }
-  const bf16x8 o = bf16x8{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3],
-                          (__bf16)a[4], (__bf16)a[5], (__bf16)a[6], (__bf16)a[7]};
-  *(bf16x8*)(dkv + r * kD + 8 * lane) = o;
+  const uint32_t c0 = s0 / kChunk, c1 = (s1 - 1) / kChunk;
+  if (c0 == c1) return;  // the chunk pass stored it
+  f32x4 lo = *(const f32x4*)(tail + (size_t)c0 * kD + 8 * lane);
+  f32x4 hi = *(const f32x4*)(tail + (size_t)c0 * kD + 8 * lane + 4);
+  for (uint32_t c = c0 + 1; c <= c1; ++c) {
+    lo += *(const f32x4*)(head + (size_t)c * kD + 8 * lane);
+    hi += *(const f32x4*)(head + (size_t)c * kD + 8 * lane + 4);
+  }
+  *(bf16x8*)dst = bf16x8{(__bf16)lo[0], (__bf16)lo[1], (__bf16)lo[2], (__bf16)lo[3],
+                         (__bf16)hi[0], (__bf16)hi[1], (__bf16)hi[2], (__bf16)hi[3]};
 }
 
 // ---- B5: d_sink[h] = -sum_t part[t][h], in a fixed order ----
@@ -543,6 +605,9 @@ extern "C" int sparse_mla_backward(const void* q, const void* kv, const void* do
   const size_t o_dsp = off;    off = align_up(off + (size_t)T * H * 4, A);
   const size_t o_rs = off;     off = align_up(off + (size_t)(num_kv + 1) * 4, A);
   const size_t o_it = off;     off = align_up(off + (size_t)N * kD * 2, A);
+  const size_t nch = (size_t)(N + kChunk - 1) / kChunk;
+  const size_t o_hd = off;     off = align_up(off + nch * kD * 4, A);
+  const size_t o_tl = off;     off = align_up(off + nch * kD * 4, A);
   const size_t o_tmp = off;    off = align_up(off + sort_bytes, A);
   void* ws = nullptr;
   hipMemPool_t pool = scratch_pool(dev);
@@ -616,9 +681,13 @@ extern "C" int sparse_mla_backward(const void* q, const void* kv, const void* do
   if (err == hipSuccess && num_kv > 0) {
     hipLaunchKernelGGL(smla_bwd_rowstart_kernel, dim3((unsigned)((num_kv + 1 + 255) / 256)), dim3(256), 0, s,
                        (const uint32_t*)(b + o_sk), (uint32_t)N, (uint32_t)num_kv, (uint32_t*)(b + o_rs));
-    hipLaunchKernelGGL(smla_bwd_dkv_kernel, dim3((unsigned)((num_kv + 3) / 4)), dim3(256), 0, s,
-                       (const uint32_t*)(b + o_rs), (const uint32_t*)(b + o_sv), (const uint16_t*)(b + o_it),
-                       (uint16_t*)dkv, num_kv);
+    hipLaunchKernelGGL(smla_bwd_dkv_chunk_kernel, dim3((unsigned)((nch + 3) / 4)), dim3(256), 0, s,
+                       (const uint32_t*)(b + o_sk), (const uint32_t*)(b + o_sv), (const uint32_t*)(b + o_rs),
+                       (const uint16_t*)(b + o_it), (uint16_t*)dkv, (float*)(b + o_hd), (float*)(b + o_tl),
+                       (uint32_t)num_kv);
+    hipLaunchKernelGGL(smla_bwd_dkv_fix_kernel, dim3((unsigned)((num_kv + 3) / 4)), dim3(256), 0, s,
+                       (const uint32_t*)(b + o_rs), (const float*)(b + o_hd), (const float*)(b + o_tl), (uint16_t*)dkv,
+                       num_kv);
     err = hipGetLastError();
   }
   if (err == hipSuccess && attn_sink) {
