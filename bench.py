@@ -213,7 +213,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="wide", choices=["tiny", "small", "tp4", "wide", "large", "glm", "decode",
-                                                          "tp4_fp8", "wide_fp8", "glm_fp8"])
+                                                          "tp4_fp8", "wide_fp8", "glm_fp8", "wide_k1024", "long"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timing of the main workload")
@@ -311,7 +311,7 @@ def main():
                 sec[-1]["note"] = ("few-token call: split-KV kernel + merge kernel; per-launch events include the "
                                    "host launch gap, rocprofv3 kernel time is the GPU figure")
             print("bench: %s %.4f ms/call" % (other, t2["ms_per_call"]), file=sys.stderr, flush=True)
-        for name in ("wide",):
+        for name in ("wide", "wide_k1024", "long", "tp4"):
             b = measure_bwd(name, max(10, args.steps // 2), args.warmup)
             sec.append(b)
             print("bench: bwd:%s %.4f ms/call, %.1f TFLOPS (page formula)" % (name, b["kernel_ms_mean"],

@@ -89,6 +89,9 @@ CONFIGS = {
     "tp4": Config("tp4", T=16384, H=16, topk=640, window=128, pool_slots=512, compression=4, seed=103),
     "wide": Config("wide", T=4096, H=128, topk=512, window=128, pool_slots=384, compression=4, seed=104),
     "large": Config("large", T=8192, H=128, topk=1024, window=256, pool_slots=768, compression=8, seed=105),
+    # the backward page's other two benchmark shapes (T=4096 / topk=1024 / Kv=5120 and T=8192 / topk=512 / Kv=9216)
+    "wide_k1024": Config("wide_k1024", T=4096, H=128, topk=1024, window=128, pool_slots=896, compression=4, seed=107),
+    "long": Config("long", T=8192, H=128, topk=512, window=128, pool_slots=384, compression=8, seed=108),
     # GLM-shaped prefill on a server-sized paged pool (2.2 M rows = 2.1 GiB)
     "glm": Config("glm", T=16384, H=16, topk=2048, window=128, pool_slots=1920, compression=1, seed=106,
                   sink=False, layout="paged", pool_rows=2_200_000, page=64),

@@ -161,3 +161,17 @@ def test_backward_wide_full_size_sampled():
     rows = np.array([0, 1, T // 2, T - 1, T, T + 1, T + 300, num_kv - 1], np.int64)
     full_case(inp["q"], inp["kv"], inp["topk"], inp["sink"], inp["scale"], 15, "wide sampled", tokens=tokens,
               rows=rows)
+
+
+@pytest.mark.parametrize("name", ["long", "tp4"])
+def test_backward_full_size_sampled(name):
+    """The backward page's T=8192 shape (H=128, topk=512, 9216 pool rows) and the
+    16-head tp4 shape at full size: sampled tokens' dq, window and pool rows' dkv,
+    d_sink over all tokens."""
+    inp = synth.make_inputs(name)
+    T = inp["T"]
+    num_kv = inp["kv"].shape[0]
+    tokens = np.linspace(0, T - 1, 16).astype(np.int64)
+    rows = np.array([0, T // 3, T - 1, T, T + 7, (T + num_kv) // 2, num_kv - 1], np.int64)
+    full_case(inp["q"], inp["kv"], inp["topk"], inp["sink"], inp["scale"], 17, name + " sampled", tokens=tokens,
+              rows=rows)
