@@ -175,3 +175,34 @@ def test_backward_full_size_sampled(name):
     rows = np.array([0, T // 3, T - 1, T, T + 7, (T + num_kv) // 2, num_kv - 1], np.int64)
     full_case(inp["q"], inp["kv"], inp["topk"], inp["sink"], inp["scale"], 17, name + " sampled", tokens=tokens,
               rows=rows)
+
+
+def test_backward_one_head_and_minus_inf_sinks():
+    q, kv, idx, _ = random_case(21, T=24, H=1, topk=48, num_kv=120)
+    full_case(q, kv, idx, np.array([0.3], np.float32), 0.1, 22, "H=1")
+    q, kv, idx, s = random_case(23, T=24, H=40, topk=48, num_kv=120)
+    s[::3] = -np.inf  # those heads behave as if they had no sink: d_sink 0
+    _, _, ds = full_case(q, kv, idx, s, synth.DEFAULT_SCALE, 24, "-inf sinks")
+    assert np.all(ds[::3] == 0.0)
+
+
+def test_backward_nan_rows():
+    """NaN in a referenced row reaches exactly what the oracle says (the NaN
+    pattern must match); NaN in rows no slot holds changes nothing at all."""
+    q, kv, idx, s = random_case(25, T=32, H=16, topk=40, num_kv=200)
+    referenced = np.unique(idx[(idx >= 0) & (idx < 200)])
+    unref = np.setdiff1d(np.arange(200), referenced)
+    assert unref.size > 0
+    rng = np.random.default_rng(26)
+    dout = bf16(rng.standard_normal(q.shape))
+    o_bits, lse = run_gpu(q, kv, idx, s, synth.DEFAULT_SCALE)
+    clean = run_backward(q, kv, dout, o_bits, lse, idx, s, synth.DEFAULT_SCALE)
+    poisoned = kv.copy()
+    poisoned[unref] = synth.BF16_NAN
+    dirty = run_backward(q, poisoned, dout, o_bits, lse, idx, s, synth.DEFAULT_SCALE)
+    for a, b in zip(clean, dirty):
+        assert np.array_equal(a, b)
+    assert np.all(clean[1][unref] == 0.0)
+    kv_nan = kv.copy()
+    kv_nan[referenced[0], 7] = synth.BF16_NAN
+    full_case(q, kv_nan, idx, s, synth.DEFAULT_SCALE, 27, "NaN in a referenced row")
