@@ -289,9 +289,25 @@ struct InterParams {
   int TP;
 };
 
-struct InterSmem {
-  uint8_t x[2][2 * kBwdMaxH][256];  // [q ; dO] rows, 128 columns of d, double-buffered
-  uint8_t y[2][2 * kBwdMaxH][64];   // [scale dS ; P] rows of a 32-position tile, double-buffered
+// LDS of the interm kernel, sized for its 32 KS rows of [q ; dO] and [scale dS ; P],
+// and the staging of one 32-position output tile (32 rows of kRowStride) for
+// whole-row stores: in the [q ; dO] buffers once the fragments are read, or in
+// an area of its own when those are smaller.
+template <bool OWN>
+struct InterStage {  // the staging area of its own
+  uint8_t o[kBK * kRowStride];
+  __device__ __forceinline__ const void* own() const { return o; }
+};
+template <>
+struct InterStage<false> {  // empty: the staging reuses the [q ; dO] buffers
+  __device__ __forceinline__ const void* own() const { return nullptr; }
+};
+template <int KS>
+struct InterSmem : InterStage<(2 * 32 * KS * 256 < kBK * kRowStride)> {
+  static constexpr bool kOwnStage = 2 * 32 * KS * 256 < kBK * kRowStride;
+  uint8_t x[2][32 * KS][256];  // [q ; dO] rows, 128 columns of d, double-buffered
+  uint8_t y[2][32 * KS][64];   // [scale dS ; P] rows of a 32-position tile, double-buffered
+  __device__ __forceinline__ uint32_t stage() { return lds_addr(kOwnStage ? this->own() : &x[0][0][0]); }
 };
 
 // Stage quarter qd of [q ; dO] (columns 128 qd ..): row k = 4i + L/16, bytes 16 (L % 16); wave w issues i = w, w + 8, ...
@@ -323,7 +339,7 @@ __device__ __forceinline__ void interm_stage_y(const InterParams& p, uint8_t (*y
 template <int KS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void smla_bwd_interm_kernel(
     const InterParams p) {
-  __shared__ __attribute__((aligned(16))) InterSmem sm;
+  __shared__ __attribute__((aligned(16))) InterSmem<KS> sm;
   const int t = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -356,6 +372,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
       });
     }
   });
+  lds_barrier();  // every wave holds its fragments: the [q ; dO] buffers may now take the output staging
 
   for (int it = 0; it < ntl; ++it) {
     const int buf = it & 1;
@@ -395,17 +412,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt) asm volatile("" : "+v"(c[dt][jt]));
-    // lane holds C^T[d = 64 w + 16 dt + 4 g + i][j = 32 it + 16 jt + li]: 8 stores
+    // lane holds C^T[d = 64 w + 16 dt + 4 g + i][j = 16 jt + li] of this tile: staged as rows j
+    const uint32_t ob = sm.stage();
 #pragma unroll
-    for (int jt = 0; jt < 2; ++jt) {
-      uint16_t* row = p.interm + ((size_t)t * p.TP + it * kBK + 16 * jt + li) * kD + 64 * w + 4 * g;
+    for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
-        *(bf16x4*)(row + 16 * dt) =
+        *(LDS_AS bf16x4*)(uintptr_t)(ob + (16 * jt + li) * kRowStride + 2 * (64 * w + 16 * dt + 4 * g)) =
             bf16x4{(__bf16)c[dt][jt][0], (__bf16)c[dt][jt][1], (__bf16)c[dt][jt][2], (__bf16)c[dt][jt][3]};
+    lds_barrier();  // the tile is staged; no wave reads this Y tile any more
+    // wave w stores rows 4 w .. 4 w + 3, one whole 1 KiB row per instruction
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = 4 * w + r;
+      const u32x4 v = *(LDS_AS const u32x4*)(uintptr_t)(ob + j * kRowStride + 16 * lane);
+      *(u32x4*)(p.interm + ((size_t)t * p.TP + it * kBK + j) * kD + 8 * lane) = v;
     }
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // the next tile's rows landed (only the 8 stores may be younger)
-    lds_barrier();                                     // ... every wave's; this tile no longer read
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // the next tile's rows landed (only the 4 stores may be younger)
+    lds_barrier();                                     // ... every wave's; the staging is free again
   }
 }
 
