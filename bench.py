@@ -96,7 +96,7 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(inp: dict, target_s: float = 10.0):
+def cpu_baseline(inp: dict, target_s: float = 15.0):
     """The oracle, untuned, on the host cores over an evenly spaced token sample."""
     import oracle
 
