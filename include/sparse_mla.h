@@ -152,8 +152,9 @@ int sparse_mla_prefill_i64(const void* q, const void* kv, const int64_t* topk_in
  * in (token, slot) order, with no atomics. The call takes stream-ordered
  * scratch from the library's per-device pool (the same pool as the forward's
  * split path) and returns it before the call's work ends: about
- * T * round_up(topk, 32) * (4 H + 1040) bytes (wide shape T=4096, H=128,
- * topk=512: 3.2 GB); SMLA_ERR_NO_MEMORY if it cannot be had, before any launch.
+ * T * round_up(topk, 32) * (4 H + 1104) bytes plus the sort's workspace (wide
+ * shape T=4096, H=128, topk=512: 3.4 GB); SMLA_ERR_NO_MEMORY if it cannot be
+ * had, before any launch.
  */
 int sparse_mla_backward(const void* q, const void* kv, const void* dout, const void* o, const float* lse,
                         const int32_t* topk_indices, const float* attn_sink, float scale, void* dq, void* dkv,
