@@ -154,7 +154,9 @@ int sparse_mla_prefill_i64(const void* q, const void* kv, const int64_t* topk_in
  * split path) and returns it before the call's work ends: about
  * T * round_up(topk, 32) * (4 H + 1104) bytes plus the sort's workspace (wide
  * shape T=4096, H=128, topk=512: 3.4 GB); SMLA_ERR_NO_MEMORY if it cannot be
- * had, before any launch.
+ * had, before any launch. The inverted index is a library radix sort that
+ * clears its counters with hipMemsetAsync: do not capture this call into a
+ * HIP graph.
  */
 int sparse_mla_backward(const void* q, const void* kv, const void* dout, const void* o, const float* lse,
                         const int32_t* topk_indices, const float* attn_sink, float scale, void* dq, void* dkv,
