@@ -534,22 +534,25 @@ __global__ __launch_bounds__(256) void smla_merge_kernel(const Params p, const S
 
 struct Variant {
   int nw;
-  const char* name;      // bf16 pool
-  const char* name_fp8;  // fp8 pool
+  const char* name;
 };
 
-// One wave per 16 heads: 1, 2 or 4 waves per workgroup up to 64 heads, 8 waves
-// (128 heads) wider. The ring depth is NBUF below: bf16 tiles (33 KiB) take
-// 2 per workgroup up to 4 waves (two workgroups per CU) and 4 at 8 waves (one
-// per CU). fp8 tiles (16 KiB): 2 at one wave (four workgroups per CU) and two
-// waves, 4 at four waves (in the output staging area's room), and 4 at eight
-// waves, beside the two bf16 tiles they are dequantised into.
-Variant pick_variant(int64_t H, int64_t topk) {
+// One wave per 16 heads. The ring depth is NBUF below. A bf16 tile takes
+// 33 KiB: workgroups of 1, 2 or 4 waves with 2 tiles, two per CU; wider heads
+// are cut into groups of 64, so that two 4-wave workgroups share a CU and one
+// hides the other's gather waits, softmax, barriers and finalisation (each row
+// is then gathered once per group; the second gather mostly hits L2). An fp8
+// tile takes 16 KiB: 2 at one wave (four workgroups per CU) and two waves, 4 at
+// four waves (in the output staging area's room); above 64 heads one 8-wave
+// workgroup of 128 heads with 4 tiles, dequantised once into two shared bf16
+// tiles, so that the conversion is not repeated per head group.
+Variant pick_variant(int64_t H, int64_t topk, bool fp8) {
   (void)topk;
-  if (H <= 16) return {1, "smla_fwd_kernel<1, 2>", "smla_fwd_fp8_kernel<1, 2>"};
-  if (H <= 32) return {2, "smla_fwd_kernel<2, 2>", "smla_fwd_fp8_kernel<2, 2>"};
-  if (H <= 64) return {4, "smla_fwd_kernel<4, 2>", "smla_fwd_fp8_kernel<4, 4>"};
-  return {8, "smla_fwd_kernel<8, 4>", "smla_fwd_fp8_kernel<8, 4>"};
+  if (H <= 16) return {1, fp8 ? "smla_fwd_fp8_kernel<1, 2>" : "smla_fwd_kernel<1, 2>"};
+  if (H <= 32) return {2, fp8 ? "smla_fwd_fp8_kernel<2, 2>" : "smla_fwd_kernel<2, 2>"};
+  if (!fp8) return {4, "smla_fwd_kernel<4, 2>"};
+  if (H <= 64) return {4, "smla_fwd_fp8_kernel<4, 4>"};
+  return {8, "smla_fwd_fp8_kernel<8, 4>"};
 }
 
 template <int NW, int NBUF, bool SPLIT, bool FP8>
@@ -573,7 +576,8 @@ hipError_t launch_variant(int nw, const Params& p, const SplitArgs& sa, int bloc
   if (nw == 1) return launch<1, 2, SPLIT, FP8>(p, sa, blocks, s);
   if (nw == 2) return launch<2, 2, SPLIT, FP8>(p, sa, blocks, s);
   if (nw == 4) return launch<4, FP8 ? 4 : 2, SPLIT, FP8>(p, sa, blocks, s);
-  return launch<8, 4, SPLIT, FP8>(p, sa, blocks, s);
+  if constexpr (FP8) return launch<8, 4, SPLIT, FP8>(p, sa, blocks, s);
+  return hipErrorInvalidValue;  // bf16 pools use at most 4 waves per workgroup
 }
 
 // A split covers at least this many top-k positions (two full tiles); a row
@@ -586,12 +590,13 @@ constexpr int kMaxSplit = 64;
 // Argument checks shared by the entry points (idx_align: alignment the top-k
 // array needs). Everything but the device query.
 int check_args(const void* q, const void* kv, const void* topk_indices, size_t idx_align, const float* attn_sink,
-               float scale, const void* out, const float* lse, int64_t T, int64_t H, int64_t num_kv, int64_t topk) {
+               float scale, const void* out, const float* lse, int64_t T, int64_t H, int64_t num_kv, int64_t topk,
+               bool fp8) {
   if (T < 0 || H < 1 || num_kv < 0 || topk < 0) return SMLA_ERR_BAD_SIZE;
   if (T > INT32_MAX || H > INT32_MAX || topk > INT32_MAX) return SMLA_ERR_BAD_SIZE;
   if (!isfinite(scale)) return SMLA_ERR_BAD_SCALE;
   if (T == 0) return SMLA_OK;
-  const Variant var = pick_variant(H, topk);
+  const Variant var = pick_variant(H, topk, fp8);
   const int64_t heads_per_wg = (int64_t)16 * var.nw;
   const int64_t head_groups = (H + heads_per_wg - 1) / heads_per_wg;
   if (T * head_groups > INT32_MAX) return SMLA_ERR_BAD_SIZE;
@@ -609,7 +614,7 @@ int check_args(const void* q, const void* kv, const void* topk_indices, size_t i
 int run_prefill(const void* q, const void* kv, const int32_t* topk_indices, const float* attn_sink, float scale,
                 void* out, float* lse, int64_t T, int64_t H, int64_t num_kv, int64_t topk, int dev,
                 hipStream_t s, bool fp8 = false, float kv_scale = 1.f) {
-  const Variant var = pick_variant(H, topk);
+  const Variant var = pick_variant(H, topk, fp8);
   const int64_t heads_per_wg = (int64_t)16 * var.nw;
   const int64_t head_groups = (H + heads_per_wg - 1) / heads_per_wg;
   Params p;
@@ -689,7 +694,7 @@ __global__ __launch_bounds__(256) void smla_idx64_kernel(const int64_t* __restri
 extern "C" int sparse_mla_prefill(const void* q, const void* kv, const int32_t* topk_indices, const float* attn_sink,
                                   float scale, void* out, float* lse, int64_t T, int64_t H, int64_t num_kv,
                                   int64_t topk, void* stream) {
-  int rc = check_args(q, kv, topk_indices, 4, attn_sink, scale, out, lse, T, H, num_kv, topk);
+  int rc = check_args(q, kv, topk_indices, 4, attn_sink, scale, out, lse, T, H, num_kv, topk, false);
   if (rc != SMLA_OK || T == 0) return rc;
   int dev = -1;
   if ((rc = current_device(&dev)) != SMLA_OK) return rc;
@@ -699,7 +704,7 @@ extern "C" int sparse_mla_prefill(const void* q, const void* kv, const int32_t* 
 extern "C" int sparse_mla_prefill_fp8(const void* q, const void* kv, float kv_scale, const int32_t* topk_indices,
                                       const float* attn_sink, float scale, void* out, float* lse, int64_t T,
                                       int64_t H, int64_t num_kv, int64_t topk, void* stream) {
-  int rc = check_args(q, kv, topk_indices, 4, attn_sink, scale, out, lse, T, H, num_kv, topk);
+  int rc = check_args(q, kv, topk_indices, 4, attn_sink, scale, out, lse, T, H, num_kv, topk, true);
   if (rc != SMLA_OK) return rc;
   if (!isfinite(kv_scale) || !isfinite(scale * kv_scale)) return SMLA_ERR_BAD_SCALE;
   if (T == 0) return SMLA_OK;
@@ -712,7 +717,7 @@ extern "C" int sparse_mla_prefill_fp8(const void* q, const void* kv, float kv_sc
 extern "C" int sparse_mla_prefill_i64(const void* q, const void* kv, const int64_t* topk_indices,
                                       const float* attn_sink, float scale, void* out, float* lse, int64_t T,
                                       int64_t H, int64_t num_kv, int64_t topk, void* stream) {
-  int rc = check_args(q, kv, topk_indices, 8, attn_sink, scale, out, lse, T, H, num_kv, topk);
+  int rc = check_args(q, kv, topk_indices, 8, attn_sink, scale, out, lse, T, H, num_kv, topk, false);
   if (rc != SMLA_OK || T == 0) return rc;
   int dev = -1;
   if ((rc = current_device(&dev)) != SMLA_OK) return rc;
@@ -752,8 +757,7 @@ extern "C" const char* sparse_mla_status_string(int status) {
 
 extern "C" const char* sparse_mla_kernel_name(int64_t H, int64_t topk, int kv_fp8) {
   if (H < 1 || topk < 0) return nullptr;
-  const Variant v = pick_variant(H, topk);
-  return kv_fp8 ? v.name_fp8 : v.name;
+  return pick_variant(H, topk, kv_fp8 != 0).name;
 }
 
 extern "C" int sparse_mla_version(void) { return 102; }

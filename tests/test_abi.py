@@ -53,7 +53,7 @@ def test_kernel_names():
     assert lib.sparse_mla_kernel_name(8, -1, 1) is None
     assert lib.sparse_mla_kernel_name(8, 64, 0) == lib.sparse_mla_kernel_name(16, 64, 0)
     assert lib.sparse_mla_kernel_name(64, 512, 0).startswith(b"smla_fwd_kernel<")
-    assert lib.sparse_mla_kernel_name(128, 2048, 0).startswith(b"smla_fwd_kernel<")
+    assert lib.sparse_mla_kernel_name(128, 2048, 0) == b"smla_fwd_kernel<4, 2>"  # two 64-head groups
     assert lib.sparse_mla_kernel_name(16, 2048, 1).startswith(b"smla_fwd_fp8_kernel<1,")
     assert lib.sparse_mla_kernel_name(128, 512, 1).startswith(b"smla_fwd_fp8_kernel<8,")
 
