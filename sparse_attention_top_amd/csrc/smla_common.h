@@ -235,22 +235,41 @@ __device__ __forceinline__ int compact_segment(const int32_t* __restrict__ trow,
 
 __device__ __forceinline__ int tile_rows(int i, int n) { return min(kBK, n - i * kBK); }
 
-// Number of LDS-DMA loads wave w issues for tile i.
+// A pointer that is the same in every lane, kept in scalar registers (a
+// vector copy would be spilled in the tile loop, and its reload would wait
+// for every gather in flight: scratch loads share the gathers' counter).
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return (const T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// One zero row of the pool: rows past a tile's count are gathered from here,
+// and padded rows of other staged operands too.
+__device__ __attribute__((aligned(256))) const uint16_t kZeroRowBf16[kD] = {};
+
+// Number of LDS-DMA loads wave w issues for tile i: every row of an existing
+// tile is gathered (past the count from the zero row).
 template <int NW>
 __device__ __forceinline__ int tile_dma(int i, int n, int w) {
-  constexpr int RPW = kBK / NW;
-  return min(RPW, max(0, tile_rows(i, n) - w * RPW));
+  (void)w;
+  return tile_rows(i, n) > 0 ? kBK / NW : 0;
 }
 
 // The gather of one tile into an LDS ring buffer: one LDS-DMA instruction per
-// row (lane L moves bytes [16 L, 16 L + 16) of the 1 KiB row); rows past the
-// tile's count are zero-filled. Wave w moves rows [w RPW, (w+1) RPW).
+// row (lane L moves bytes [16 L, 16 L + 16) of the 1 KiB row). Rows past the
+// tile's count come from the zero row, so that stale LDS never meets a zero
+// probability (0 * NaN) and the issue has no branch per row (a uniform select
+// of the source). Wave w moves rows [w RPW, (w+1) RPW).
 template <int NW>
 struct TileIssue {
   static constexpr int RPW = kBK / NW;
-  const uint16_t* kv;
+  const uint16_t* kv;    // pool, in scalar registers
+  const uint16_t* zero;  // zero row, in scalar registers
   uint32_t dst0;  // LDS address of this wave's first row in the target buffer
-  int cnt;        // valid rows in the tile (rows >= cnt are zero-filled)
+  int cnt;        // valid rows in the tile
   int r0;         // first row of this wave
   int my;         // lane L < RPW: list entry of row r0 + L
   bool active;
@@ -258,7 +277,8 @@ struct TileIssue {
   // Tile i of the n-entry LDS list `list`, into the ring buffer at LDS address buf.
   __device__ __forceinline__ void init(const int32_t* list, int i, int n, bool act, uint32_t buf, const uint16_t* kv_,
                                        int lane, int w) {
-    kv = kv_;
+    kv = uniform_ptr(kv_);
+    zero = uniform_ptr(kZeroRowBf16);
     active = act;
     r0 = w * RPW;
     cnt = act ? tile_rows(i, n) : 0;
@@ -270,33 +290,19 @@ struct TileIssue {
   }
   template <int RR>
   __device__ __forceinline__ void row(int lane) const {
-    if (!active) return;
     const uint32_t dst = dst0 + RR * kRowStride;
-    if (r0 + RR < cnt) {
-      const int idx = __builtin_amdgcn_readlane(my, RR);
-      const uint16_t* src = kv + (size_t)(uint32_t)idx * kD + 8 * lane;
-      __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(uintptr_t)dst, 16, 0, 0);
-    } else {
-      *(LDS_AS u32x4*)(uintptr_t)(dst + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
-    }
+    const int idx = __builtin_amdgcn_readlane(my, RR);
+    const uint16_t* src = (r0 + RR < cnt) ? kv + (size_t)(uint32_t)idx * kD : zero;
+    __builtin_amdgcn_global_load_lds(src + 8 * lane, (LDS_AS void*)(uintptr_t)dst, 16, 0, 0);
   }
   __device__ __forceinline__ void all(int lane) const {
+    if (!active) return;
     static_for<0, RPW>([&](auto rc) { row<decltype(rc)::value>(lane); });
   }
   // LDS-DMA instructions all() issues
-  __device__ __forceinline__ int count() const { return active ? min(RPW, max(0, cnt - r0)) : 0; }
+  __device__ __forceinline__ int count() const { return active ? RPW : 0; }
 };
 
-// A pointer that is the same in every lane, kept in scalar registers (a
-// vector copy would be spilled in the tile loop, and its reload would wait
-// for every gather in flight: scratch loads share the gathers' counter).
-template <typename T>
-__device__ __forceinline__ const T* uniform_ptr(const T* p) {
-  const uint64_t a = (uint64_t)(uintptr_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  return (const T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
-}
 
 // Max over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48).
 __device__ __forceinline__ float row4_max(float x) {

@@ -39,9 +39,6 @@ using namespace smla_host;
 
 constexpr int kBwdMaxH = 128;  // heads handled by the interm contraction (2 x 128 rows of K)
 
-// A zero row for padded heads (interm staging gathers them from here).
-__device__ __attribute__((aligned(256))) const uint16_t kZeroRowBf16[kD] = {};
-
 struct BwdParams {
   const uint16_t* q;
   const uint16_t* kv;
