@@ -28,8 +28,8 @@
 //   6. the sink is folded into the max and the denominator at the end, o is
 //      rounded to bf16 and lse converted back to natural log.
 //
-// Invalid (tail) rows of a partial tile are zero-filled in LDS and their
-// logits forced to -inf, so stale LDS contents never reach the output.
+// Invalid (tail) rows of a partial tile are gathered from a zero row and
+// their logits forced to -inf, so stale LDS contents never reach the output.
 
 
 #include <type_traits>
