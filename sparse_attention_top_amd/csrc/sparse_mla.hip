@@ -291,11 +291,13 @@ __device__ __forceinline__ HeadEnd head_end(float l_part, float m_ref, float sin
 }
 
 __device__ __forceinline__ void load_q(bf16x8 (&qf)[16], const Params& p, int t, int head, int g) {
-  // Q^T fragments (MFMA B operand of S^T = K Q^T): lane holds q[t, head, 32k + 8g .. +8)
+  // Q^T fragments (MFMA B operand of S^T = K Q^T): lane holds q[t, head, 32k + 8g .. +8).
+  // q is read once: non-temporal loads leave the caches to the pool rows the
+  // gathers reuse (2% at H = 128, where q and o stream 1 KiB per head).
   if (head < p.H) {
     const bf16x8* src = (const bf16x8*)(p.q + ((size_t)t * p.H + head) * kD + 8 * g);
 #pragma unroll
-    for (int k = 0; k < 16; ++k) qf[k] = src[4 * k];
+    for (int k = 0; k < 16; ++k) qf[k] = __builtin_nontemporal_load(src + 4 * k);
   } else {
 #pragma unroll
     for (int k = 0; k < 16; ++k) qf[k] = bf16x8{};
@@ -448,12 +450,12 @@ __device__ __forceinline__ void smla_fwd_body(const Params& p, const SplitArgs& 
     *(LDS_AS bf16x4*)(uintptr_t)(ob + li * kRowStride + 32 * dt + 8 * g) = ob4;
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  // row r of this wave's 16: lane L stores bytes [16 L, 16 L + 16)
+  // row r of this wave's 16: lane L stores bytes [16 L, 16 L + 16) (non-temporal, like the q loads)
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int hr = head_base + r;
     const u32x4 val = *(LDS_AS const u32x4*)(uintptr_t)(ob + r * kRowStride + 16 * lane);
-    if (hr < p.H) *(u32x4*)(p.out + ((size_t)t * p.H + hr) * kD + 8 * lane) = val;
+    if (hr < p.H) __builtin_nontemporal_store(val, (u32x4*)(p.out + ((size_t)t * p.H + hr) * kD + 8 * lane));
   }
 }
 
