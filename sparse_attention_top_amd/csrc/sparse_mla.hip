@@ -84,6 +84,14 @@ struct Smem {
   static constexpr int kAreaBytes = kRingEnd > kStageBytes ? kRingEnd : kStageBytes;
   uint8_t area[kAreaBytes];
   int32_t list[kListCap];
+  // D-split P.V (four waves, bf16 pool): each wave's P tile in its MFMA
+  // B-operand layout (16 bytes per lane), and per head a factor: the rescale
+  // of the tile (1 when the reference max stayed), at the end the output scale.
+  static constexpr bool kDs = !FP8 && NW == 4;
+  static constexpr int kPBytes = kDs ? NW * 64 * 16 : 16;
+  static constexpr int kFBytes = kDs ? 16 * NW * 4 : 16;
+  uint8_t pbuf[kPBytes];
+  float fac[kFBytes / 4];
   // gather ring slot b
   __device__ __forceinline__ uint32_t tile(int b) { return lds_addr(area + kRingOff + b * kTileBytes); }
   // dequantised bf16 tile b (kConv only)
@@ -304,6 +312,116 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[16], const Params& p, int t,
   }
 }
 
+// ---- D-split P.V (four waves, 64 heads, bf16 pool) ----
+// The wave that owns 16 heads computes their S and softmax, then publishes P
+// (its B-operand fragment) and the per-head rescale factor in LDS; after a
+// barrier every wave accumulates O^T for all 64 heads over its own 128 columns
+// of d. Each V^T fragment read then feeds four MFMAs (one per head group)
+// instead of one, so a tile's P.V reads 12 KiB of LDS per wave instead of 32.
+
+// Online softmax of one tile as in tile_softmax, but the rescale factor of
+// what earlier tiles accumulated is returned (1 when the reference max stays)
+// instead of being applied: the accumulators of these heads are spread over
+// all waves.
+__device__ __forceinline__ float tile_softmax_ds(const f32x4 (&s)[2], int cnt, float scale_log2, int g, float& m_ref,
+                                                 float& l_part, bf16x8& pk) {
+  float x[2][4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int slot = sh * 16 + 4 * g + i;
+      const float xv = slot < cnt ? s[sh][i] * scale_log2 : -INFINITY;
+      x[sh][i] = xv;
+      mx = __builtin_fmaxf(mx, xv);
+    }
+  mx = row4_max(mx);
+  float alpha = 1.f;
+  if (__ballot(mx > m_ref + kLazyTau) != 0ull) {
+    const float m_new = __builtin_fmaxf(m_ref, mx);
+    // a head whose reference is still -inf has nothing accumulated (alpha 0 keeps it 0)
+    if (__ballot(m_ref != -INFINITY) != 0ull) alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+    l_part *= alpha;
+    m_ref = m_new;
+  }
+  const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
+  float ls = 0.f;
+#pragma unroll
+  for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pv = __builtin_amdgcn_exp2f(x[sh][i] - mu);
+      ls += pv;
+      pk[sh * 4 + i] = (__bf16)pv;
+    }
+  l_part += ls;
+  return alpha;
+}
+
+// Scale accumulator group o (8 d-tiles of one head group) by f, in place in
+// the AGPRs, one register at a time.
+__device__ __forceinline__ void scale_acc8(f32x4 (&acc)[32], int o, float f) {
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float e = acc[8 * o + dt][i];
+      float tmp;
+      asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                   : "+a"(e), "=&v"(tmp)
+                   : "v"(f));
+      acc[8 * o + dt][i] = e;
+    }
+}
+
+// Apply the four head groups' published factors (lane li reads the factors
+// of heads li, 16 + li, 32 + li, 48 + li); a group whose factors are all 1 is
+// skipped.
+__device__ __forceinline__ void apply_factors(f32x4 (&acc)[32], uint32_t fac_addr) {
+  u32x4 f = ds_read_b128<0>(fac_addr);
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f));
+#pragma unroll
+  for (int o = 0; o < 4; ++o) {
+    const float fo = __uint_as_float(f[o]);
+    if (__ballot(fo != 1.f) != 0ull) scale_acc8(acc, o, fo);
+  }
+}
+
+// O^T[128 w + 16 dt .. +16][heads 16 o + li] += V^T P_o^T for the wave's eight
+// d-tiles and the four published P fragments. vrow: v_frag_addr of the tile
+// plus the wave's 256-byte column offset; pbase: this lane's 16 bytes of head
+// group 0's fragment (group o at + 1024 o).
+__device__ __forceinline__ void tile_pv_ds(uint32_t vrow, uint32_t pbase, f32x4 (&acc)[32]) {
+  asm volatile("s_nop 4" ::: "memory");  // accumulators rescaled by VALU, read by the MFMAs below
+  constexpr int VPF = 3;
+  constexpr int VST = VPF + 1;
+  u32x4 pf[4];
+  u32x2 vf[VST][2];
+  static_for<0, 4>([&](auto oc) {
+    constexpr int o = decltype(oc)::value;
+    pf[o] = ds_read_b128<1024 * o>(pbase);
+  });
+  auto vread = [&](auto dc) {
+    constexpr int dt = decltype(dc)::value;
+    vf[dt % VST][0] = ds_read_tr16_b64<32 * dt>(vrow);
+    vf[dt % VST][1] = ds_read_tr16_b64<16 * kRowStride + 32 * dt>(vrow);
+  };
+  static_for<0, VPF>([&](auto dc) { vread(dc); });
+  static_for<0, 8>([&](auto dc) {
+    constexpr int dt = decltype(dc)::value;
+    if constexpr (dt + VPF < 8) vread(Int<dt + VPF>{});
+    constexpr int younger = 2 * (7 - dt < VPF ? 7 - dt : VPF);
+    if constexpr (dt == 0) lds_wait6<younger>(vf[0][0], vf[0][1], pf[0], pf[1], pf[2], pf[3]);
+    else lds_wait<younger>(vf[dt % VST][0], vf[dt % VST][1]);
+    const bf16x8 a = __builtin_bit_cast(
+        bf16x8, u32x4{vf[dt % VST][0][0], vf[dt % VST][0][1], vf[dt % VST][1][0], vf[dt % VST][1][1]});
+#pragma unroll
+    for (int o = 0; o < 4; ++o) mfma_acc(acc[8 * o + dt], a, __builtin_bit_cast(bf16x8, pf[o]));
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
 // ---------------------------------------------------------------------------
 // One workgroup per (token, group of 16 NW heads). Iteration j computes tile j
 // from ring buffer j % NBUF while tiles j+1 .. j+NBUF-1 land; the rows of tile
@@ -329,6 +447,14 @@ __device__ __forceinline__ void smla_fwd_body(const Params& p, const SplitArgs& 
   const int head = head_base + li;
   const int row_begin = SPLIT ? min(p.topk_n, sp * sa.split_len) : 0;
   const int row_end = SPLIT ? min(p.topk_n, row_begin + sa.split_len) : p.topk_n;
+
+  // D-split P.V: acc[8 o + dt] holds O^T[128 w + 16 dt + 4 g .. +4][head 16 o + li] of the
+  // workgroup's 64 heads; otherwise acc[dt] holds O^T[16 dt + 4 g .. +4][head].
+  constexpr bool DS = SM::kDs && !SPLIT;
+  const uint32_t pb_rd = lds_addr(sm.pbuf) + 16 * lane;       // P fragments, head group 0 (+1024 o)
+  const uint32_t pb_own = pb_rd + 1024 * w;                   // this wave's P fragment
+  const uint32_t fac_rd = lds_addr(sm.fac) + 16 * li;         // factors of heads li, 16 + li, 32 + li, 48 + li
+  const uint32_t fac_own = lds_addr(sm.fac) + 16 * li + 4 * w;  // this lane's head
 
   f32x4 acc[32];
 #pragma unroll
@@ -405,6 +531,19 @@ __device__ __forceinline__ void smla_fwd_body(const Params& p, const SplitArgs& 
       is.init(sm.list, j + AHEAD, n, j + AHEAD < ntiles, sm.tile((j + AHEAD) % NBUF), kvp, lane, w);
       const uint32_t tb = sm.tile(j % NBUF);
       f32x4 s[2];
+      if constexpr (DS) {
+        // S and softmax of this wave's heads; P and the rescale factor go to
+        // LDS (the previous tile's were consumed before the barrier above)
+        tile_s<2, 2>(k_frag_addr(tb, g, li), qf, s);
+        const float alpha = tile_softmax_ds(s, tile_rows(j, n), p.scale_log2, g, m_ref, l_part, pk);
+        *(LDS_AS bf16x8*)(uintptr_t)(pb_own) = pk;
+        if (g == 0) *(LDS_AS float*)(uintptr_t)(fac_own) = alpha;
+        lds_barrier();  // every wave's P and factors visible
+        is.all(lane);
+        apply_factors(acc, fac_rd);
+        tile_pv_ds(v_frag_addr(tb, g, li) + 256 * w, pb_rd, acc);
+        continue;
+      }
       if constexpr (FP8) tile_s8<2>(opaque(tb + 16 * (li + 32 * (g >> 1)) + 8 * (g & 1)), qf, s);
       else tile_s<2, 2>(k_frag_addr(tb, g, li), qf, s);
       tile_softmax(s, tile_rows(j, n), p.scale_log2, g, m_ref, l_part, acc, pk);
@@ -442,14 +581,35 @@ __device__ __forceinline__ void smla_fwd_body(const Params& p, const SplitArgs& 
   HeadEnd he = head_end(l_part, m_ref, sk, has_sink, sink_l2);
   if constexpr (FP8) he.oscale *= p.out_scale;  // V == code * dequant scale
   if (g == 0 && head < p.H) p.lse[(size_t)t * p.H + head] = he.lse;
-  // lane (g, li) holds o[head li][16 dt + 4g .. +4): write it to LDS row li
+  if constexpr (DS) {
+    // every wave scales its columns of all 64 heads by the owners' output scales
+    if (g == 0) *(LDS_AS float*)(uintptr_t)(fac_own) = he.oscale;
+    lds_barrier();
+    u32x4 f = ds_read_b128<0>(fac_rd);
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f));
+    const uint32_t st = sm.stage() + 256 * w + 8 * g;  // row 16 o + li, bytes 2 (128 w + 16 dt + 4 g)
 #pragma unroll
-  for (int dt = 0; dt < 32; ++dt) {
-    const f32x4 o = acc[dt] * he.oscale;
-    const bf16x4 ob4 = bf16x4{(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
-    *(LDS_AS bf16x4*)(uintptr_t)(ob + li * kRowStride + 32 * dt + 8 * g) = ob4;
+    for (int o = 0; o < 4; ++o) {
+      const float fo = __uint_as_float(f[o]);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const f32x4 v = acc[8 * o + dt] * fo;
+        const bf16x4 v4 = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+        *(LDS_AS bf16x4*)(uintptr_t)(st + (16 * o + li) * kRowStride + 32 * dt) = v4;
+      }
+    }
+    lds_barrier();  // the rows of every head staged
   }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if constexpr (!DS) {
+    // lane (g, li) holds o[head li][16 dt + 4g .. +4): write it to LDS row li
+#pragma unroll
+    for (int dt = 0; dt < 32; ++dt) {
+      const f32x4 o = acc[dt] * he.oscale;
+      const bf16x4 ob4 = bf16x4{(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+      *(LDS_AS bf16x4*)(uintptr_t)(ob + li * kRowStride + 32 * dt + 8 * g) = ob4;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
   // row r of this wave's 16: lane L stores bytes [16 L, 16 L + 16) (non-temporal, like the q loads)
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
