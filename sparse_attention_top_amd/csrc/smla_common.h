@@ -266,38 +266,43 @@ __device__ __forceinline__ int tile_dma(int i, int n, int w) {
 template <int NW>
 struct TileIssue {
   static constexpr int RPW = kBK / NW;
-  const uint16_t* kv;    // pool, in scalar registers
-  const uint16_t* zero;  // zero row, in scalar registers
-  uint32_t dst0;  // LDS address of this wave's first row in the target buffer
-  int cnt;        // valid rows in the tile
-  int r0;         // first row of this wave
-  int my;         // lane L < RPW: list entry of row r0 + L
+  const uint16_t* kv;  // pool, in scalar registers
+  uint32_t dst0;       // LDS address of this wave's first row in the target buffer
+  int my;              // lane L < RPW: list entry of row r0 + L, or -1 past the tile's count
   bool active;
 
   // Tile i of the n-entry LDS list `list`, into the ring buffer at LDS address buf.
   __device__ __forceinline__ void init(const int32_t* list, int i, int n, bool act, uint32_t buf, const uint16_t* kv_,
                                        int lane, int w) {
     kv = uniform_ptr(kv_);
-    zero = uniform_ptr(kZeroRowBf16);
     active = act;
-    r0 = w * RPW;
-    cnt = act ? tile_rows(i, n) : 0;
+    const int r0 = w * RPW;
+    const int cnt = act ? tile_rows(i, n) : 0;
     dst0 = buf + r0 * kRowStride;
-    int e = 0;
+    int e = -1;
     if (act && lane < RPW && r0 + lane < cnt) e = list[i * kBK + r0 + lane];
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(e));
     my = e;
   }
-  template <int RR>
-  __device__ __forceinline__ void row(int lane) const {
-    const uint32_t dst = dst0 + RR * kRowStride;
-    const int idx = __builtin_amdgcn_readlane(my, RR);
-    const uint16_t* src = (r0 + RR < cnt) ? kv + (size_t)(uint32_t)idx * kD : zero;
-    __builtin_amdgcn_global_load_lds(src + 8 * lane, (LDS_AS void*)(uintptr_t)dst, 16, 0, 0);
-  }
+  // Lane L < RPW forms the 64-bit source address of row r0 + L once (vector
+  // ops); each row then costs two lane reads, the LDS base and the load.
   __device__ __forceinline__ void all(int lane) const {
     if (!active) return;
-    static_for<0, RPW>([&](auto rc) { row<decltype(rc)::value>(lane); });
+    const uint16_t* src = my >= 0 ? kv + (size_t)(uint32_t)my * kD : kZeroRowBf16;
+    const uint64_t a = (uint64_t)(uintptr_t)src;
+    const uint32_t alo = (uint32_t)a, ahi = (uint32_t)(a >> 32);
+    uint64_t ra[RPW];  // all lane reads first: no read-to-load wait per row
+    static_for<0, RPW>([&](auto rc) {
+      constexpr int RR = decltype(rc)::value;
+      const uint32_t rlo = (uint32_t)__builtin_amdgcn_readlane(alo, RR);
+      const uint32_t rhi = (uint32_t)__builtin_amdgcn_readlane(ahi, RR);
+      ra[RR] = ((uint64_t)rhi << 32) | rlo;
+    });
+    static_for<0, RPW>([&](auto rc) {
+      constexpr int RR = decltype(rc)::value;
+      const uint16_t* rs = (const uint16_t*)(uintptr_t)ra[RR];
+      __builtin_amdgcn_global_load_lds(rs + 8 * lane, (LDS_AS void*)(uintptr_t)(dst0 + RR * kRowStride), 16, 0, 0);
+    });
   }
   // LDS-DMA instructions all() issues
   __device__ __forceinline__ int count() const { return active ? RPW : 0; }
