@@ -73,8 +73,21 @@ struct SplitArgs {
 // end the output staging (16 rows of pitch kRowStride per wave). With an fp8
 // pool and eight waves (kConv), two bf16 tiles precede the ring: the waves
 // dequantise each gathered tile once into one of them and compute from it.
+// D-split P.V exchange (four waves, bf16 pool): each wave's P tile in its MFMA
+// B-operand layout (16 bytes per lane), and per head a factor: the rescale of
+// the tile (1 when the reference max stayed), at the end the output scale.
+// Empty otherwise, so that the other variants keep their LDS size (the
+// one-wave fp8 workgroup fits four per CU at exactly 40 KiB).
+template <bool DS>
+struct DsExchange {};
+template <>
+struct DsExchange<true> {
+  uint8_t pbuf[4 * 64 * 16];
+  float fac[16 * 4];
+};
+
 template <int NW, int NBUF, bool FP8>
-struct Smem {
+struct Smem : DsExchange<!FP8 && NW == 4> {
   static constexpr bool kConv = FP8 && NW == 8;
   static constexpr int kBf16Tile = kBK * kRowStride;
   static constexpr int kTileBytes = FP8 ? kBK * kD : kBf16Tile;
@@ -84,14 +97,7 @@ struct Smem {
   static constexpr int kAreaBytes = kRingEnd > kStageBytes ? kRingEnd : kStageBytes;
   uint8_t area[kAreaBytes];
   int32_t list[kListCap];
-  // D-split P.V (four waves, bf16 pool): each wave's P tile in its MFMA
-  // B-operand layout (16 bytes per lane), and per head a factor: the rescale
-  // of the tile (1 when the reference max stayed), at the end the output scale.
   static constexpr bool kDs = !FP8 && NW == 4;
-  static constexpr int kPBytes = kDs ? NW * 64 * 16 : 16;
-  static constexpr int kFBytes = kDs ? 16 * NW * 4 : 16;
-  uint8_t pbuf[kPBytes];
-  float fac[kFBytes / 4];
   // gather ring slot b
   __device__ __forceinline__ uint32_t tile(int b) { return lds_addr(area + kRingOff + b * kTileBytes); }
   // dequantised bf16 tile b (kConv only)
@@ -451,10 +457,13 @@ __device__ __forceinline__ void smla_fwd_body(const Params& p, const SplitArgs& 
   // D-split P.V: acc[8 o + dt] holds O^T[128 w + 16 dt + 4 g .. +4][head 16 o + li] of the
   // workgroup's 64 heads; otherwise acc[dt] holds O^T[16 dt + 4 g .. +4][head].
   constexpr bool DS = SM::kDs && !SPLIT;
-  const uint32_t pb_rd = lds_addr(sm.pbuf) + 16 * lane;       // P fragments, head group 0 (+1024 o)
-  const uint32_t pb_own = pb_rd + 1024 * w;                   // this wave's P fragment
-  const uint32_t fac_rd = lds_addr(sm.fac) + 16 * li;         // factors of heads li, 16 + li, 32 + li, 48 + li
-  const uint32_t fac_own = lds_addr(sm.fac) + 16 * li + 4 * w;  // this lane's head
+  uint32_t pb_rd = 0, pb_own = 0, fac_rd = 0, fac_own = 0;
+  if constexpr (SM::kDs) {
+    pb_rd = lds_addr(sm.pbuf) + 16 * lane;          // P fragments, head group 0 (+1024 o)
+    pb_own = pb_rd + 1024 * w;                      // this wave's P fragment
+    fac_rd = lds_addr(sm.fac) + 16 * li;            // factors of heads li, 16 + li, 32 + li, 48 + li
+    fac_own = lds_addr(sm.fac) + 16 * li + 4 * w;   // this lane's head
+  }
 
   f32x4 acc[32];
 #pragma unroll
