@@ -187,11 +187,11 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
 // across the workgroup). The per-wave counts live in the tile area, which
 // holds no tile then; the closing barrier keeps them until every wave has
 // read them.
-template <int NW, typename SM>
+template <int NW, typename SM, int CAP = kListCap>
 __device__ __forceinline__ int compact_segment(const int32_t* __restrict__ trow, int len, uint32_t nkv, SM& sm, int lane,
                                                int w) {
   constexpr int CH = NW * 64;              // entries per chunk (one per thread)
-  constexpr int MAXC = kListCap / CH;      // chunks per segment
+  constexpr int MAXC = CAP / CH;           // chunks per segment (len <= CAP)
   int raw[MAXC];
 #pragma unroll
   for (int c = 0; c < MAXC; ++c) {
@@ -263,9 +263,9 @@ __device__ __forceinline__ int tile_dma(int i, int n, int w) {
 // tile's count come from the zero row, so that stale LDS never meets a zero
 // probability (0 * NaN) and the issue has no branch per row (a uniform select
 // of the source). Wave w moves rows [w RPW, (w+1) RPW).
-template <int NW>
+template <int NW, int BK = kBK>
 struct TileIssue {
-  static constexpr int RPW = kBK / NW;
+  static constexpr int RPW = BK / NW;
   const uint16_t* kv;  // pool, in scalar registers
   uint32_t dst0;       // LDS address of this wave's first row in the target buffer
   int my;              // lane L < RPW: list entry of row r0 + L, or -1 past the tile's count
@@ -277,10 +277,10 @@ struct TileIssue {
     kv = uniform_ptr(kv_);
     active = act;
     const int r0 = w * RPW;
-    const int cnt = act ? tile_rows(i, n) : 0;
+    const int cnt = act ? min(BK, n - i * BK) : 0;
     dst0 = buf + r0 * kRowStride;
     int e = -1;
-    if (act && lane < RPW && r0 + lane < cnt) e = list[i * kBK + r0 + lane];
+    if (act && lane < RPW && r0 + lane < cnt) e = list[i * BK + r0 + lane];
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(e));
     my = e;
   }

@@ -652,6 +652,202 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   smla_fwd_body<NW, NBUF, true, true>(p, sa);
 }
 
+// ---------------------------------------------------------------------------
+// H <= 16, bf16 pool: 16-row tiles, one wave of 16 heads per workgroup. A
+// 32-row ring of two tiles takes 74 KiB, so only two one-wave workgroups fit
+// a CU and two of its four SIMDs hold a wave; with 16-row tiles the ring of
+// NBUF tiles and a list of CAP entries take 38 KiB (NBUF 2, CAP 1024: four
+// per CU, one wave per SIMD) or 19 KiB (NBUF 1, CAP 512: eight per CU, two
+// waves per SIMD). S^T is one 16-row half of the 32-row form; P.V uses the
+// 16x16x16 MFMA, whose A operand is one transposing read and whose B operand
+// is the four P values the S^T accumulator layout leaves in each lane.
+constexpr int kBK16 = 16;
+
+template <int NBUF, int CAP>
+struct Smem16 {
+  static constexpr int kTileBytes = kBK16 * kRowStride;
+  static constexpr int kRing = NBUF * kTileBytes;
+  static constexpr int kStage = 16 * kRowStride;
+  static constexpr int kAreaBytes = kRing > kStage ? kRing : kStage;
+  uint8_t area[kAreaBytes];
+  int32_t list[CAP];
+  __device__ __forceinline__ uint32_t tile(int b) { return lds_addr(area + b * kTileBytes); }
+  __device__ __forceinline__ uint32_t stage() { return lds_addr(area); }
+};
+
+// S^T = K Q^T for a 16-row tile: s holds S^T[slot 4g + i][head li]. Four
+// independent MFMA chains (k mod 4), summed at the end.
+template <int KPF>
+__device__ __forceinline__ void tile_s16(uint32_t krow, const bf16x8 (&qf)[16], f32x4& s) {
+  constexpr int KST = KPF + 1;
+  f32x4 sp[4];
+  u32x4 kf[KST];
+  auto kread = [&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    kf[k % KST] = ds_read_b128<64 * k>(krow);
+  };
+  static_for<0, KPF>([&](auto kc) { kread(kc); });
+  static_for<0, 16>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    if constexpr (k + KPF < 16) kread(Int<k + KPF>{});
+    constexpr int younger = 15 - k < KPF ? 15 - k : KPF;
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(kf[k % KST]) : "n"(younger));
+    if constexpr (k < 4) mfma_s_first(sp[k & 3], kf[k % KST], __builtin_bit_cast(u32x4, qf[k]));
+    else mfma_s(sp[k & 3], kf[k % KST], __builtin_bit_cast(u32x4, qf[k]));
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");  // MFMA write -> VALU read distance
+  asm volatile("" : "+v"(sp[0]), "+v"(sp[1]), "+v"(sp[2]), "+v"(sp[3]));
+  s = (sp[0] + sp[1]) + (sp[2] + sp[3]);
+}
+
+// Online softmax of a 16-row tile (as tile_softmax, four slots per lane).
+__device__ __forceinline__ void tile_softmax16(const f32x4& s, int cnt, float scale_log2, int g, float& m_ref,
+                                               float& l_part, f32x4 (&acc)[32], bf16x4& pk) {
+  float x[4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float xv = 4 * g + i < cnt ? s[i] * scale_log2 : -INFINITY;
+    x[i] = xv;
+    mx = __builtin_fmaxf(mx, xv);
+  }
+  mx = row4_max(mx);
+  if (__ballot(mx > m_ref + kLazyTau) != 0ull) {
+    const float m_new = __builtin_fmaxf(m_ref, mx);
+    if (__ballot(m_ref != -INFINITY) != 0ull) {
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      l_part *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float e = acc[dt][i];
+          float tmp;
+          asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                       : "+a"(e), "=&v"(tmp)
+                       : "v"(alpha));
+          acc[dt][i] = e;
+        }
+    }
+    m_ref = m_new;
+  }
+  const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
+  float ls = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float pv = __builtin_amdgcn_exp2f(x[i] - mu);
+    ls += pv;
+    pk[i] = (__bf16)pv;
+  }
+  l_part += ls;
+}
+
+__device__ __forceinline__ void mfma16_acc(f32x4& c, const u32x2& a, const u32x2& b) {
+  asm volatile("v_mfma_f32_16x16x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
+// O^T += V^T P^T for a 16-row tile: per d-tile one transposing read gives
+// lane (g, li) V[4g .. 4g+3][16 dt + li], the A operand of the 16x16x16 MFMA.
+__device__ __forceinline__ void tile_pv16(uint32_t vrow, const bf16x4& pk, f32x4 (&acc)[32]) {
+  asm volatile("s_nop 4" ::: "memory");  // P written by VALU, read by MFMA below
+  constexpr int VPF = 6;
+  constexpr int VST = VPF + 1;
+  const u32x2 pb = __builtin_bit_cast(u32x2, pk);
+  u32x2 vf[VST];
+  auto vread = [&](auto dc) {
+    constexpr int dt = decltype(dc)::value;
+    vf[dt % VST] = ds_read_tr16_b64<32 * dt>(vrow);
+  };
+  static_for<0, VPF>([&](auto dc) { vread(dc); });
+  static_for<0, 32>([&](auto dc) {
+    constexpr int dt = decltype(dc)::value;
+    if constexpr (dt + VPF < 32) vread(Int<dt + VPF>{});
+    constexpr int younger = 31 - dt < VPF ? 31 - dt : VPF;
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(vf[dt % VST]) : "n"(younger));
+    mfma16_acc(acc[dt], vf[dt % VST], pb);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
+// One workgroup (one wave) per token. Tile j+NBUF-1 is gathered at the top of
+// iteration j (its ring slot was last read in iteration j-1, whose reads have
+// completed), then the wave waits for tile j and computes it.
+template <int NBUF, int CAP>
+__device__ __forceinline__ void smla_fwd16_body(const Params& p) {
+  static_assert(NBUF == 1 || NBUF == 2, "ring of one or two 16-row tiles");
+  constexpr int AHEAD = NBUF - 1;
+  using SM = Smem16<NBUF, CAP>;
+  __shared__ __attribute__((aligned(16))) SM sm;
+
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const int li = lane & 15;
+  const int t = p.T - 1 - xcd_remap(blockIdx.x, gridDim.x);  // latest (heaviest) tokens first
+  const int head = li;
+
+  f32x4 acc[32];
+#pragma unroll
+  for (int dt = 0; dt < 32; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY, l_part = 0.f;
+  bf16x8 qf[16];
+  load_q(qf, p, t, head, g);
+  bf16x4 pk;
+
+  const int32_t* trow = p.topk + (size_t)t * p.topk_n;
+  const uint16_t* kvp = p.kv;
+  using Issue = TileIssue<1, kBK16>;
+  for (int seg0 = 0; seg0 < p.topk_n; seg0 += CAP) {
+    const int n = compact_segment<1, SM, CAP>(trow + seg0, min(CAP, p.topk_n - seg0), p.nkv, sm, lane, 0);
+    const int ntiles = (n + kBK16 - 1) / kBK16;
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) {
+      Issue is;
+      is.init(sm.list, i, n, i < ntiles, sm.tile(i), kvp, lane, 0);
+      is.all(lane);
+    }
+    for (int j = 0; j < ntiles; ++j) {
+      Issue is;
+      const bool ahead = j + AHEAD < ntiles;
+      is.init(sm.list, j + AHEAD, n, ahead, sm.tile((j + AHEAD) % NBUF), kvp, lane, 0);
+      is.all(lane);
+      wait_vmcnt_le(AHEAD > 0 && ahead ? kBK16 : 0);  // tile j landed (tile j + AHEAD may be in flight)
+      const uint32_t tb = sm.tile(j % NBUF);
+      f32x4 sv;
+      tile_s16<3>(k_frag_addr(tb, g, li), qf, sv);
+      tile_softmax16(sv, min(kBK16, n - j * kBK16), p.scale_log2, g, m_ref, l_part, acc, pk);
+      tile_pv16(v_frag_addr(tb, g, li), pk, acc);
+    }
+  }
+
+  // finalise: fold the sink, normalise, stage 16 rows, store whole rows
+  const float sk = (p.sink != nullptr && head < p.H) ? p.sink[head] : -INFINITY;
+  const bool has_sink = !(sk == -INFINITY);
+  const float sink_l2 = sk * kLog2e;
+  const uint32_t ob = sm.stage();
+  mfma_agpr_drain(acc);
+  const HeadEnd he = head_end(l_part, m_ref, sk, has_sink, sink_l2);
+  if (g == 0 && head < p.H) p.lse[(size_t)t * p.H + head] = he.lse;
+#pragma unroll
+  for (int dt = 0; dt < 32; ++dt) {
+    const f32x4 o = acc[dt] * he.oscale;
+    const bf16x4 ob4 = bf16x4{(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+    *(LDS_AS bf16x4*)(uintptr_t)(ob + li * kRowStride + 32 * dt + 8 * g) = ob4;
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const u32x4 val = *(LDS_AS const u32x4*)(uintptr_t)(ob + r * kRowStride + 16 * lane);
+    if (r < p.H) __builtin_nontemporal_store(val, (u32x4*)(p.out + ((size_t)t * p.H + r) * kD + 8 * lane));
+  }
+}
+
+template <int NBUF, int CAP>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NBUF == 1 ? 2 : 1))) void smla_fwd16_kernel(
+    const Params p) {
+  smla_fwd16_body<NBUF, CAP>(p);
+}
+
 // Merge of the splits of one (token, head), one wave each: lane s < nsplit
 // reads split s's reference max m_s and sum l_s; with Mv the largest m_s, the
 // splits are weighted by c_s = 2^(m_s - Mv) (0 for a split that saw no valid
@@ -717,9 +913,17 @@ struct Variant {
 // four waves (in the output staging area's room); above 64 heads one 8-wave
 // workgroup of 128 heads with 4 tiles, dequantised once into two shared bf16
 // tiles, so that the conversion is not repeated per head group.
+// 16-row variant for H <= 16 and a bf16 pool (single pass): ring depth and list capacity.
+#ifndef SMLA_R16_NBUF
+#define SMLA_R16_NBUF 1
+#endif
+constexpr int kR16Nbuf = SMLA_R16_NBUF;
+constexpr int kR16Cap = kR16Nbuf == 1 ? 512 : 1024;
+
 Variant pick_variant(int64_t H, int64_t topk, bool fp8) {
   (void)topk;
-  if (H <= 16) return {1, fp8 ? "smla_fwd_fp8_kernel<1, 2>" : "smla_fwd_kernel<1, 2>"};
+  if (H <= 16 && !fp8) return {1, kR16Nbuf == 1 ? "smla_fwd16_kernel<1, 512>" : "smla_fwd16_kernel<2, 1024>"};
+  if (H <= 16) return {1, "smla_fwd_fp8_kernel<1, 2>"};
   if (H <= 32) return {2, fp8 ? "smla_fwd_fp8_kernel<2, 2>" : "smla_fwd_kernel<2, 2>"};
   if (!fp8) return {4, "smla_fwd_kernel<4, 2>"};
   if (H <= 64) return {4, "smla_fwd_fp8_kernel<4, 4>"};
@@ -843,6 +1047,10 @@ int run_prefill(const void* q, const void* kv, const int32_t* topk_indices, cons
       }
       (void)hipGetLastError();
     }
+  }
+  if (!fp8 && H <= 16) {
+    hipLaunchKernelGGL((smla_fwd16_kernel<kR16Nbuf, kR16Cap>), dim3((unsigned)units), dim3(64), 0, s, p);
+    return hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
   }
   const hipError_t err = fp8 ? launch_variant<false, true>(var.nw, p, sa, (int)units, s)
                             : launch_variant<false, false>(var.nw, p, sa, (int)units, s);

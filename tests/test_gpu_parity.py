@@ -112,6 +112,17 @@ def test_head_counts(H):
     compare(o, lse, oracle_ref(inp), what="H=%d" % H)
 
 
+@pytest.mark.parametrize("topk,num_kv,p_invalid", [(15, 40, 0.0), (16, 40, 0.0), (17, 40, 0.0), (512, 900, 0.0),
+                                                   (513, 900, 0.0), (1039, 2000, 0.0), (1100, 2000, 0.5)])
+def test_h16_tile_and_segment_edges(topk, num_kv, p_invalid):
+    """H <= 16 runs 16-row tiles from 512-entry compaction segments: counts one short of, at and one past a tile and
+    a segment, a row of two segments plus a partial tile, and one where half the slots are invalid (segments whose
+    valid counts are not multiples of 16)."""
+    inp = make_random(2500 + topk, T=5, H=16, num_kv=num_kv, topk=topk, p_invalid=p_invalid)
+    o, lse = run_case(inp)
+    compare(o, lse, oracle_ref(inp), what="H=16 topk=%d" % topk)
+
+
 @pytest.mark.parametrize("topk,num_kv", [(1, 50), (31, 40), (33, 100), (2048, 3000), (2500, 4000), (4500, 6000)])
 def test_topk_extremes(topk, num_kv):
     """Single slots, tile-boundary counts and rows longer than one compaction segment."""
