@@ -663,9 +663,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 // is the four P values the S^T accumulator layout leaves in each lane.
 constexpr int kBK16 = 16;
 
-template <int NBUF, int CAP>
+template <int NBUF, int CAP, bool FP8 = false>
 struct Smem16 {
-  static constexpr int kTileBytes = kBK16 * kRowStride;
+  static constexpr int kTileBytes = FP8 ? kBK16 * kD : kBK16 * kRowStride;
   static constexpr int kRing = NBUF * kTileBytes;
   static constexpr int kStage = 16 * kRowStride;
   static constexpr int kAreaBytes = kRing > kStage ? kRing : kStage;
@@ -770,14 +770,113 @@ __device__ __forceinline__ void tile_pv16(uint32_t vrow, const bf16x4& pk, f32x4
   });
 }
 
+// ---- 16-row tiles of an fp8 pool ----
+// Tile layout, slab-major: block k (512 bytes) holds d = 32k .. 32k+31 of the 16
+// rows as two 16-byte chunks per row, chunk j of row r at 16 (r + 16 j). One
+// LDS-DMA instruction fills blocks 2m and 2m+1 (lane L: row L % 16, chunk
+// (L / 16) % 2 of block 2m + L / 32, written at byte 16 L), so a tile takes 8
+// instructions; rows past the tile's count come from a zero row.
+struct TileIssue8r16 {
+  const uint8_t* src;  // this lane's bytes of its row in blocks 0 and 1
+  uint32_t dst0;
+  bool act;
+  __device__ __forceinline__ void init(const int32_t* list, int i, int n, bool act_, uint32_t buf, const uint8_t* kv,
+                                       int lane, int w) {
+    (void)w;
+    act = act_;
+    dst0 = buf;
+    const int cnt = act ? min(kBK16, n - i * kBK16) : 0;
+    const int row = lane & 15;
+    const bool valid = act && row < cnt;
+    uint32_t e = 0;
+    if (valid) asm volatile("ds_read_b32 %0, %1" : "=v"(e) : "v"(lds_addr(list + i * kBK16 + row)));
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(e));
+    const uint8_t* base = valid ? uniform_ptr(kv) + ((uint64_t)e << 9) : uniform_ptr(kZeroRow8);
+    src = base + 32 * (lane >> 5) + 16 * ((lane >> 4) & 1);
+  }
+  __device__ __forceinline__ void all(int lane) const {
+    (void)lane;
+    if (!act) return;
+    static_for<0, 8>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      __builtin_amdgcn_global_load_lds(src + 64 * m, (LDS_AS void*)(uintptr_t)(dst0 + 1024 * m), 16, 0, 0);
+    });
+  }
+};
+
+// S^T = K Q^T for a 16-row fp8 tile: the K fragment of k-step k (lane: row li,
+// d = 32k + 8g .. +8) is 8 bytes at kaddr + 512 k, kaddr = tile + 16 (li + 16 (g / 2))
+// + 8 (g % 2), converted to bf16 before the MFMA. Four chains (k mod 4).
+template <int KPF>
+__device__ __forceinline__ void tile_s8r16(uint32_t kaddr, const bf16x8 (&qf)[16], f32x4& s) {
+  constexpr int KST = KPF + 1;
+  f32x4 sp[4];
+  u32x2 kf[KST];
+  auto kread = [&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    kf[k % KST] = ds_read_b64<512 * k>(kaddr);
+  };
+  static_for<0, KPF>([&](auto kc) { kread(kc); });
+  static_for<0, 16>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    if constexpr (k + KPF < 16) kread(Int<k + KPF>{});
+    constexpr int younger = 15 - k < KPF ? 15 - k : KPF;
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(kf[k % KST]) : "n"(younger));
+    u32x4 a = fp8x8_to_bf16(kf[k % KST]);
+    valu_to_mfma(a);
+    if constexpr (k < 4) mfma_s_first(sp[k & 3], a, __builtin_bit_cast(u32x4, qf[k]));
+    else mfma_s(sp[k & 3], a, __builtin_bit_cast(u32x4, qf[k]));
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");  // MFMA write -> VALU read distance
+  asm volatile("" : "+v"(sp[0]), "+v"(sp[1]), "+v"(sp[2]), "+v"(sp[3]));
+  s = (sp[0] + sp[1]) + (sp[2] + sp[3]);
+}
+
+// V^T fragment base of a 16-row fp8 tile for the 16x16x16 MFMA: lane
+// (g, li) must end up with V[4g .. 4g+3][16 dt + li]. In the transposing 8-bit
+// read, lane li of a 16-lane group receives byte li % 8 of the fetches of
+// lanes 2m + li / 8 (m = 0..7); lane 2m + h therefore fetches row 4g + (m % 4)
+// at columns 8h .. 8h+7 of the d-tile, and the low four bytes received are
+// slots 4g .. 4g+3 (the high four repeat them and are not used).
+__device__ __forceinline__ uint32_t v8r16_frag_addr(uint32_t tile, int g, int li) {
+  const int m = li >> 1;
+  return opaque(tile + 16 * (4 * g + (m & 3)) + 8 * (li & 1));
+}
+
+// O^T += V^T P^T for a 16-row fp8 tile: d-tile dt is one transposing read at
+// vaddr + 512 (dt / 2) + 256 (dt % 2), four codes converted to bf16.
+__device__ __forceinline__ void tile_pv8r16(uint32_t vaddr, const bf16x4& pk, f32x4 (&acc)[32]) {
+  asm volatile("s_nop 4" ::: "memory");  // P written by VALU, read by MFMA below
+  constexpr int VPF = 6;
+  constexpr int VST = VPF + 1;
+  const u32x2 pb = __builtin_bit_cast(u32x2, pk);
+  u32x2 vf[VST];
+  auto vread = [&](auto dc) {
+    constexpr int dt = decltype(dc)::value;
+    vf[dt % VST] = ds_read_tr8_b64<512 * (dt / 2) + 256 * (dt % 2)>(vaddr);
+  };
+  static_for<0, VPF>([&](auto dc) { vread(dc); });
+  static_for<0, 32>([&](auto dc) {
+    constexpr int dt = decltype(dc)::value;
+    if constexpr (dt + VPF < 32) vread(Int<dt + VPF>{});
+    constexpr int younger = 31 - dt < VPF ? 31 - dt : VPF;
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(vf[dt % VST]) : "n"(younger));
+    u32x2 a = u32x2{fp8x2_to_bf16<false>(vf[dt % VST][0]), fp8x2_to_bf16<true>(vf[dt % VST][0])};
+    asm volatile("s_nop 3" : "+v"(a));  // asm conversion (VALU) -> MFMA source
+    mfma16_acc(acc[dt], a, pb);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
 // One workgroup (one wave) per token. Tile j+NBUF-1 is gathered at the top of
 // iteration j (its ring slot was last read in iteration j-1, whose reads have
 // completed), then the wave waits for tile j and computes it.
-template <int NBUF, int CAP>
+template <int NBUF, int CAP, bool FP8>
 __device__ __forceinline__ void smla_fwd16_body(const Params& p) {
   static_assert(NBUF == 1 || NBUF == 2, "ring of one or two 16-row tiles");
   constexpr int AHEAD = NBUF - 1;
-  using SM = Smem16<NBUF, CAP>;
+  using SM = Smem16<NBUF, CAP, FP8>;
   __shared__ __attribute__((aligned(16))) SM sm;
 
   const int lane = threadIdx.x & 63;
@@ -795,8 +894,10 @@ __device__ __forceinline__ void smla_fwd16_body(const Params& p) {
   bf16x4 pk;
 
   const int32_t* trow = p.topk + (size_t)t * p.topk_n;
-  const uint16_t* kvp = p.kv;
-  using Issue = TileIssue<1, kBK16>;
+  using Issue = typename std::conditional<FP8, TileIssue8r16, TileIssue<1, kBK16>>::type;
+  using Elem = typename std::conditional<FP8, uint8_t, uint16_t>::type;
+  const Elem* kvp = (const Elem*)p.kv;
+  constexpr int kDma = FP8 ? 8 : kBK16;  // LDS-DMA instructions per tile
   for (int seg0 = 0; seg0 < p.topk_n; seg0 += CAP) {
     const int n = compact_segment<1, SM, CAP>(trow + seg0, min(CAP, p.topk_n - seg0), p.nkv, sm, lane, 0);
     const int ntiles = (n + kBK16 - 1) / kBK16;
@@ -811,12 +912,14 @@ __device__ __forceinline__ void smla_fwd16_body(const Params& p) {
       const bool ahead = j + AHEAD < ntiles;
       is.init(sm.list, j + AHEAD, n, ahead, sm.tile((j + AHEAD) % NBUF), kvp, lane, 0);
       is.all(lane);
-      wait_vmcnt_le(AHEAD > 0 && ahead ? kBK16 : 0);  // tile j landed (tile j + AHEAD may be in flight)
+      wait_vmcnt_le(AHEAD > 0 && ahead ? kDma : 0);  // tile j landed (tile j + AHEAD may be in flight)
       const uint32_t tb = sm.tile(j % NBUF);
       f32x4 sv;
-      tile_s16<3>(k_frag_addr(tb, g, li), qf, sv);
+      if constexpr (FP8) tile_s8r16<3>(opaque(tb + 16 * (li + 16 * (g >> 1)) + 8 * (g & 1)), qf, sv);
+      else tile_s16<3>(k_frag_addr(tb, g, li), qf, sv);
       tile_softmax16(sv, min(kBK16, n - j * kBK16), p.scale_log2, g, m_ref, l_part, acc, pk);
-      tile_pv16(v_frag_addr(tb, g, li), pk, acc);
+      if constexpr (FP8) tile_pv8r16(v8r16_frag_addr(tb, g, li), pk, acc);
+      else tile_pv16(v_frag_addr(tb, g, li), pk, acc);
     }
   }
 
@@ -826,7 +929,8 @@ __device__ __forceinline__ void smla_fwd16_body(const Params& p) {
   const float sink_l2 = sk * kLog2e;
   const uint32_t ob = sm.stage();
   mfma_agpr_drain(acc);
-  const HeadEnd he = head_end(l_part, m_ref, sk, has_sink, sink_l2);
+  HeadEnd he = head_end(l_part, m_ref, sk, has_sink, sink_l2);
+  if constexpr (FP8) he.oscale *= p.out_scale;  // V == code * dequant scale
   if (g == 0 && head < p.H) p.lse[(size_t)t * p.H + head] = he.lse;
 #pragma unroll
   for (int dt = 0; dt < 32; ++dt) {
@@ -845,7 +949,14 @@ __device__ __forceinline__ void smla_fwd16_body(const Params& p) {
 template <int NBUF, int CAP>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NBUF == 1 ? 2 : 1))) void smla_fwd16_kernel(
     const Params p) {
-  smla_fwd16_body<NBUF, CAP>(p);
+  smla_fwd16_body<NBUF, CAP, false>(p);
+}
+
+// The same for a pool of OCP FP8 E4M3 codes: 8 KiB tiles, so a ring of two
+// still fits the 16.5 KiB output staging area (19 KiB of LDS, eight per CU).
+template <int NBUF, int CAP>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void smla_fwd16_fp8_kernel(const Params p) {
+  smla_fwd16_body<NBUF, CAP, true>(p);
 }
 
 // Merge of the splits of one (token, head), one wave each: lane s < nsplit
@@ -922,7 +1033,7 @@ constexpr int kR16Cap = 512;
 Variant pick_variant(int64_t H, int64_t topk, bool fp8) {
   (void)topk;
   if (H <= 16 && !fp8) return {1, "smla_fwd16_kernel<1, 512>"};
-  if (H <= 16) return {1, "smla_fwd_fp8_kernel<1, 2>"};
+  if (H <= 16) return {1, "smla_fwd16_fp8_kernel<2, 512>"};
   if (H <= 32) return {2, fp8 ? "smla_fwd_fp8_kernel<2, 2>" : "smla_fwd_kernel<2, 2>"};
   if (!fp8) return {4, "smla_fwd_kernel<4, 2>"};
   if (H <= 64) return {4, "smla_fwd_fp8_kernel<4, 4>"};
@@ -1047,8 +1158,9 @@ int run_prefill(const void* q, const void* kv, const int32_t* topk_indices, cons
       (void)hipGetLastError();
     }
   }
-  if (!fp8 && H <= 16) {
-    hipLaunchKernelGGL((smla_fwd16_kernel<kR16Nbuf, kR16Cap>), dim3((unsigned)units), dim3(64), 0, s, p);
+  if (H <= 16) {
+    if (fp8) hipLaunchKernelGGL((smla_fwd16_fp8_kernel<2, 512>), dim3((unsigned)units), dim3(64), 0, s, p);
+    else hipLaunchKernelGGL((smla_fwd16_kernel<kR16Nbuf, kR16Cap>), dim3((unsigned)units), dim3(64), 0, s, p);
     return hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
   }
   const hipError_t err = fp8 ? launch_variant<false, true>(var.nw, p, sa, (int)units, s)
