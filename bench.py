@@ -148,6 +148,13 @@ def measure(name: str, steps: int, warmup: int, cold_steps: int = 0, idx64: bool
     t = {"wall_s": wall, "ms_per_call": wall * 1e3 / steps, "kernel_ms_mean": st["mean"],
          "kernel_ms_median": st["median"], "kernel_ms_min": st["min"],
          "kernel": kernel_name(inp["H"], inp["topk_n"], kv_scale is not None)}
+    # few (token, head group) units: the library splits each top-k row and merges (the split path's kernels)
+    H, fp8 = inp["H"], kv_scale is not None
+    nw = 1 if H <= 16 else 2 if H <= 32 else (8 if fp8 and H > 64 else 4)
+    units = inp["T"] * -(-H // (16 * nw))
+    if units < torch.cuda.get_device_properties(dev).multi_processor_count and inp["topk_n"] >= 128:
+        t["kernel"] = "smla_fwd%s_split_kernel<%d, %d> + smla_merge_kernel" % ("_fp8" if fp8 else "", nw,
+                                                                              4 if fp8 and nw >= 4 else 2)
     if cold_steps:
         # cold caches: overwrite 512 MiB (more than the 256 MB MALL plus 8 x 4 MB of L2) before each launch
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
