@@ -112,13 +112,17 @@ def test_head_counts(H):
     compare(o, lse, oracle_ref(inp), what="H=%d" % H)
 
 
-@pytest.mark.parametrize("topk,num_kv,p_invalid", [(15, 40, 0.0), (16, 40, 0.0), (17, 40, 0.0), (512, 900, 0.0),
-                                                   (513, 900, 0.0), (1039, 2000, 0.0), (1100, 2000, 0.5)])
+H16_EDGES = [(15, 40, 0.0), (16, 40, 0.0), (17, 40, 0.0), (512, 900, 0.0), (513, 900, 0.0), (1039, 2000, 0.0),
+             (1100, 2000, 0.5)]
+
+
+@pytest.mark.parametrize("topk,num_kv,p_invalid", H16_EDGES)
 def test_h16_tile_and_segment_edges(topk, num_kv, p_invalid):
     """H <= 16 runs 16-row tiles from 512-entry compaction segments: counts one short of, at and one past a tile and
     a segment, a row of two segments plus a partial tile, and one where half the slots are invalid (segments whose
-    valid counts are not multiples of 16)."""
-    inp = make_random(2500 + topk, T=5, H=16, num_kv=num_kv, topk=topk, p_invalid=p_invalid)
+    valid counts are not multiples of 16). 300 tokens: more (token, head group) units than the MI355X's 256 CUs, so
+    every row takes the single-pass 16-row kernel, not the split path."""
+    inp = make_random(2500 + topk, T=300, H=16, num_kv=num_kv, topk=topk, p_invalid=p_invalid)
     o, lse = run_case(inp)
     compare(o, lse, oracle_ref(inp), what="H=16 topk=%d" % topk)
 
@@ -429,6 +433,15 @@ def test_fp8_pool_random(T, H, topk, num_kv):
     inp = make_random_fp8(6000 + T + H, T, H, num_kv, topk)
     o, lse = run_case(inp)
     compare(o, lse, oracle_ref(inp), what="fp8 T=%d H=%d topk=%d" % (T, H, topk))
+
+
+@pytest.mark.parametrize("topk,num_kv,p_invalid", H16_EDGES)
+def test_fp8_h16_tile_and_segment_edges(topk, num_kv, p_invalid):
+    """The fp8 16-row kernel (8 KiB slab tiles, 512-entry segments) at the same tile and segment edges, single pass
+    (300 tokens)."""
+    inp = make_random_fp8(7500 + topk, 300, 16, num_kv, topk, p_invalid=p_invalid)
+    o, lse = run_case(inp)
+    compare(o, lse, oracle_ref(inp), what="fp8 H=16 topk=%d" % topk)
 
 
 def test_fp8_nan_code_stays_local_and_invalid_rows():
