@@ -196,11 +196,13 @@ def test_single_valid_slot_is_exact_gather():
         assert np.array_equal(o[t], np.broadcast_to(inp["kv"][rows[t]], (16, 512)))
 
 
+@pytest.mark.parametrize("name,T", [("large", 600), ("tp4", 300)])
 @pytest.mark.parametrize("sink", [False, True])
-def test_zero_query_counts_exact_valid_slots(sink):
+def test_zero_query_counts_exact_valid_slots(sink, name, T):
     """q = 0 makes every logit 0, so lse = ln(n) (or ln(n + e^sink)): the count n of
-    gathered slots is pinned exactly (neighbouring counts differ by > 9e-4)."""
-    inp = synth.make_inputs("large", T=600)
+    gathered slots is pinned exactly (neighbouring counts differ by > 9e-4), on the
+    H = 128 D-split kernel and the H = 16 16-row kernel."""
+    inp = synth.make_inputs(name, T=T)
     inp["q"][:] = 0
     if not sink:
         inp["sink"] = None
