@@ -816,16 +816,28 @@ __device__ __forceinline__ void tile_s8r16(uint32_t kaddr, const bf16x8 (&qf)[16
     constexpr int k = decltype(kc)::value;
     kf[k % KST] = ds_read_b64<512 * k>(kaddr);
   };
+  // k-step k's fragment is converted during step k - 1, so that the asm
+  // conversions (VALU) sit several instructions before their MFMA reader;
+  // only the last step's reader needs explicit wait states.
   static_for<0, KPF>([&](auto kc) { kread(kc); });
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(kf[0]) : "n"(KPF - 1));
+  u32x4 acur = fp8x8_to_bf16(kf[0]);
+  asm volatile("" : "+v"(acur));  // converted above step 0's reads and conversion
   static_for<0, 16>([&](auto kc) {
     constexpr int k = decltype(kc)::value;
     if constexpr (k + KPF < 16) kread(Int<k + KPF>{});
-    constexpr int younger = 15 - k < KPF ? 15 - k : KPF;
-    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(kf[k % KST]) : "n"(younger));
-    u32x4 a = fp8x8_to_bf16(kf[k % KST]);
-    valu_to_mfma(a);
-    if constexpr (k < 4) mfma_s_first(sp[k & 3], a, __builtin_bit_cast(u32x4, qf[k]));
-    else mfma_s(sp[k & 3], a, __builtin_bit_cast(u32x4, qf[k]));
+    u32x4 anext;
+    if constexpr (k + 1 < 16) {
+      constexpr int younger = 14 - k < KPF - 1 ? 14 - k : KPF - 1;  // reads issued after step k+1's
+      asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(kf[(k + 1) % KST]) : "n"(younger));
+      anext = fp8x8_to_bf16(kf[(k + 1) % KST]);
+      asm volatile("" : "+v"(anext));  // the conversion stays above this step's MFMA
+    } else {
+      valu_to_mfma(acur);  // no conversion between the last one and its reader
+    }
+    if constexpr (k < 4) mfma_s_first(sp[k & 3], acur, __builtin_bit_cast(u32x4, qf[k]));
+    else mfma_s(sp[k & 3], acur, __builtin_bit_cast(u32x4, qf[k]));
+    if constexpr (k + 1 < 16) acur = anext;
     __builtin_amdgcn_sched_barrier(0);
   });
   asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");  // MFMA write -> VALU read distance
@@ -856,15 +868,25 @@ __device__ __forceinline__ void tile_pv8r16(uint32_t vaddr, const bf16x4& pk, f3
     constexpr int dt = decltype(dc)::value;
     vf[dt % VST] = ds_read_tr8_b64<512 * (dt / 2) + 256 * (dt % 2)>(vaddr);
   };
+  // d-tile dt's fragment is converted during d-tile dt - 1 (see tile_s8r16)
   static_for<0, VPF>([&](auto dc) { vread(dc); });
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(vf[0]) : "n"(VPF - 1));
+  u32x2 acur = u32x2{fp8x2_to_bf16<false>(vf[0][0]), fp8x2_to_bf16<true>(vf[0][0])};
+  asm volatile("" : "+v"(acur));
   static_for<0, 32>([&](auto dc) {
     constexpr int dt = decltype(dc)::value;
     if constexpr (dt + VPF < 32) vread(Int<dt + VPF>{});
-    constexpr int younger = 31 - dt < VPF ? 31 - dt : VPF;
-    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(vf[dt % VST]) : "n"(younger));
-    u32x2 a = u32x2{fp8x2_to_bf16<false>(vf[dt % VST][0]), fp8x2_to_bf16<true>(vf[dt % VST][0])};
-    asm volatile("s_nop 3" : "+v"(a));  // asm conversion (VALU) -> MFMA source
-    mfma16_acc(acc[dt], a, pb);
+    u32x2 anext;
+    if constexpr (dt + 1 < 32) {
+      constexpr int younger = 30 - dt < VPF - 1 ? 30 - dt : VPF - 1;  // reads issued after d-tile dt+1's
+      asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(vf[(dt + 1) % VST]) : "n"(younger));
+      anext = u32x2{fp8x2_to_bf16<false>(vf[(dt + 1) % VST][0]), fp8x2_to_bf16<true>(vf[(dt + 1) % VST][0])};
+      asm volatile("" : "+v"(anext));  // the conversion stays above this d-tile's MFMA
+    } else {
+      asm volatile("s_nop 3" : "+v"(acur));  // no conversion between the last one and its reader
+    }
+    mfma16_acc(acc[dt], acur, pb);
+    if constexpr (dt + 1 < 32) acur = anext;
     __builtin_amdgcn_sched_barrier(0);
   });
 }
