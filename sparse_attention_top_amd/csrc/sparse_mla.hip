@@ -14,17 +14,19 @@
 //      the output (the fix described on "[Triton/Gluon] [CI] [gfx942] Tuned
 //      sparse MLA prefill for DSv4.1-Flash TP4; fix attn_sink in Triton
 //      fallback" (aiter PR #6002), description);
-//   2. tiles of 32 valid rows are gathered global->LDS with the CDNA4
-//      LDS-DMA load (one wave instruction moves one whole 1 KiB row), into a
-//      ring of NBUF buffers, so that one gather serves every head of the token
-//      and both contractions;
+//   2. tiles of 32 valid rows (16 at H <= 16) are gathered global->LDS with
+//      the CDNA4 LDS-DMA load (one wave instruction moves one whole 1 KiB row),
+//      into a ring of NBUF buffers, so that one gather serves every head of the
+//      workgroup and both contractions;
 //   3. S^T = K Q^T on bf16 MFMA (16x16x32, fp32 accumulate), K read from LDS;
 //   4. online softmax in base 2 (scale * log2 e folded into one multiply),
 //      with lazy rescaling: the reference max only moves when a tile's max
 //      exceeds it by more than 2^8, which is exact because the final
 //      normalisation uses the same reference;
 //   5. O^T += V^T P^T on bf16 MFMA, V read from the same LDS tile with the
-//      gfx950 transposing LDS load, P rounded to bf16;
+//      gfx950 transposing LDS load, P rounded to bf16 (at four waves each wave
+//      accumulates its 128 columns of d for all 64 heads from the P tiles the
+//      waves publish in LDS);
 //   6. the sink is folded into the max and the denominator at the end, o is
 //      rounded to bf16 and lse converted back to natural log.
 //
@@ -1037,15 +1039,17 @@ struct Variant {
   const char* name;
 };
 
-// One wave per 16 heads. The ring depth is NBUF below. A bf16 tile takes
-// 33 KiB: workgroups of 1, 2 or 4 waves with 2 tiles, two per CU; wider heads
-// are cut into groups of 64, so that two 4-wave workgroups share a CU and one
-// hides the other's gather waits, softmax, barriers and finalisation (each row
-// is then gathered once per group; the second gather mostly hits L2). An fp8
-// tile takes 16 KiB: 2 at one wave (four workgroups per CU) and two waves, 4 at
-// four waves (in the output staging area's room); above 64 heads one 8-wave
-// workgroup of 128 heads with 4 tiles, dequantised once into two shared bf16
-// tiles, so that the conversion is not repeated per head group.
+// One wave per 16 heads. Up to 16 heads the single pass runs the 16-row
+// kernels (one wave, 19 KiB of LDS, eight workgroups per CU); the 32-row
+// one-wave form serves only the few-token split path. A 32-row bf16 tile takes
+// 33 KiB: workgroups of 2 or 4 waves with 2 tiles, two per CU; wider heads are
+// cut into groups of 64, so that two 4-wave D-split workgroups share a CU and
+// one hides the other's gather waits, softmax, barriers and finalisation (each
+// row is then gathered once per group; the second gather mostly hits L2). A
+// 32-row fp8 tile takes 16 KiB: 2 at two waves, 4 at four waves (in the output
+// staging area's room); above 64 heads one 8-wave workgroup of 128 heads with
+// 4 tiles, dequantised once into two shared bf16 tiles, so that the conversion
+// is not repeated per head group.
 // 16-row variant for H <= 16 and a bf16 pool (single pass): one tile and a
 // 512-entry list, eight workgroups per CU (a ring of two tiles with a
 // 1024-entry list fits four per CU and measured 1.3x slower).
@@ -1080,7 +1084,11 @@ hipError_t launch(const Params& p, const SplitArgs& sa, int blocks, hipStream_t 
 
 template <bool SPLIT, bool FP8>
 hipError_t launch_variant(int nw, const Params& p, const SplitArgs& sa, int blocks, hipStream_t s) {
-  if (nw == 1) return launch<1, 2, SPLIT, FP8>(p, sa, blocks, s);
+  if (nw == 1) {
+    // the single pass at H <= 16 runs the 16-row kernels (run_prefill)
+    if constexpr (SPLIT) return launch<1, 2, SPLIT, FP8>(p, sa, blocks, s);
+    return hipErrorInvalidValue;
+  }
   if (nw == 2) return launch<2, 2, SPLIT, FP8>(p, sa, blocks, s);
   if (nw == 4) return launch<4, FP8 ? 4 : 2, SPLIT, FP8>(p, sa, blocks, s);
   if constexpr (FP8) return launch<8, 4, SPLIT, FP8>(p, sa, blocks, s);
