@@ -258,11 +258,12 @@ __device__ __forceinline__ int tile_dma(int i, int n, int w) {
   return tile_rows(i, n) > 0 ? kBK / NW : 0;
 }
 
-// The gather of one tile into an LDS ring buffer: one LDS-DMA instruction per
-// row (lane L moves bytes [16 L, 16 L + 16) of the 1 KiB row). Rows past the
-// tile's count come from the zero row, so that stale LDS never meets a zero
-// probability (0 * NaN) and the issue has no branch per row (a uniform select
-// of the source). Wave w moves rows [w RPW, (w+1) RPW).
+// The gather of one tile of BK rows into an LDS ring buffer: one LDS-DMA
+// instruction per row (lane L moves bytes [16 L, 16 L + 16) of the 1 KiB
+// row). Rows past the tile's count come from the zero row, so that stale LDS
+// never meets a zero probability (0 * NaN) and the issue has no branch per row
+// (lane r picks row r's source, pool row or zero row, once per tile). Wave w
+// moves rows [w RPW, (w+1) RPW).
 template <int NW, int BK = kBK>
 struct TileIssue {
   static constexpr int RPW = BK / NW;
