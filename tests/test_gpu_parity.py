@@ -265,9 +265,13 @@ def test_head_independence():
         assert np.max(np.abs(l1[:, 0] - l[:, h])) <= 1e-3
 
 
-def test_large_logits_stay_finite():
-    inp = make_random(14, T=16, H=16, num_kv=200, topk=64)
-    inp["q"] = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(inp["q"]) * 100.0)
+@pytest.mark.parametrize("H,T,topk,mult", [(16, 16, 64, 100.0), (128, 260, 200, 100.0), (128, 260, 200, 10.0)])
+def test_large_logits_stay_finite(H, T, topk, mult):
+    """Logits of spread 10 to 100 move the lazy reference max across tiles, so earlier tiles' sums are rescaled: in
+    the 16-row kernel in place, in the H = 128 D-split kernel by factors the owner waves publish to every wave
+    (260 tokens: single pass, 7 tiles per row)."""
+    inp = make_random(14, T=T, H=H, num_kv=400, topk=topk)
+    inp["q"] = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(inp["q"]) * mult)
     o, l = run_case(inp)
     assert np.all(np.isfinite(synth.bf16_bits_to_f32(o))) and np.all(np.isfinite(l))
     compare(o, l, oracle_ref(inp), what="large logits")
