@@ -285,9 +285,12 @@ def test_any_finite_scale(scale):
     compare(o, l, oracle_ref(inp), what="scale=%g" % scale)
 
 
-def test_nan_in_referenced_row_stays_local():
-    inp = synth.make_inputs("tp4", T=300)
-    victim = 250  # a token row inside the windows of tokens 250..299 only
+@pytest.mark.parametrize("name", ["tp4", "wide"])
+def test_nan_in_referenced_row_stays_local(name):
+    """A NaN in one referenced row reaches exactly the tokens that reference it (all their heads), on the 16-row
+    kernel (tp4) and the D-split kernel (wide: the NaN enters S and P.V in every wave of both head groups)."""
+    inp = synth.make_inputs(name, T=300)
+    victim = 250  # a token row inside the windows of tokens 250..299 only (windows of at least 50 tokens)
     inp["kv"][victim, 7] = synth.BF16_NAN
     o, l = run_case(inp)
     refs = np.array([victim in set(r.tolist()) for r in inp["topk"]])
