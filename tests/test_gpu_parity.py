@@ -135,8 +135,9 @@ def test_topk_extremes(topk, num_kv):
     compare(o, lse, oracle_ref(inp), what="topk=%d" % topk)
 
 
-def test_permutation_invariance():
-    inp = synth.make_inputs("wide", T=160)
+@pytest.mark.parametrize("name,T", [("wide", 160), ("tp4", 300)])
+def test_permutation_invariance(name, T):
+    inp = synth.make_inputs(name, T=T)
     rng = np.random.default_rng(3)
     perm = np.stack([rng.permutation(inp["topk_n"]) for _ in range(inp["T"])])
     inp_p = dict(inp, topk=np.take_along_axis(inp["topk"], perm, axis=1))
@@ -185,15 +186,17 @@ def test_zero_sequence():
     assert o.shape == (0, 16, 512) and l.shape == (0, 16)
 
 
-def test_single_valid_slot_is_exact_gather():
-    inp = make_random(8, T=40, H=16, num_kv=500, topk=64, sink=False)
+@pytest.mark.parametrize("H", [16, 128])
+def test_single_valid_slot_is_exact_gather(H):
+    """One valid slot: P = 1 exactly, so o is the gathered row bit for bit (16-row and D-split kernels)."""
+    inp = make_random(8, T=40, H=H, num_kv=500, topk=64, sink=False)
     rng = np.random.default_rng(9)
     rows = rng.choice(500, 40, replace=False)
     inp["topk"][:] = -1
     inp["topk"][np.arange(40), rng.integers(0, 64, 40)] = rows
     o, l = run_case(inp)
     for t in range(40):
-        assert np.array_equal(o[t], np.broadcast_to(inp["kv"][rows[t]], (16, 512)))
+        assert np.array_equal(o[t], np.broadcast_to(inp["kv"][rows[t]], (H, 512)))
 
 
 @pytest.mark.parametrize("name,T", [("large", 600), ("tp4", 300)])
@@ -215,12 +218,13 @@ def test_zero_query_counts_exact_valid_slots(sink, name, T):
     assert np.max(np.abs(l - expect)) < 2e-4
 
 
-def test_poisoned_unused_rows_and_out_of_range_slots():
+@pytest.mark.parametrize("H", [16, 128])
+def test_poisoned_unused_rows_and_out_of_range_slots(H):
     """Rows no valid slot references (row 0 included, and the row just past
     num_kv inside the same allocation) are filled with NaN/Inf, and invalid
     slots take -2, INT32_MIN, num_kv, num_kv+1, INT32_MAX: bitwise the same
-    output as the clean run with -1."""
-    inp = make_random(10, T=32, H=16, num_kv=400, topk=96, p_invalid=0.0)
+    output as the clean run with -1 (16-row and D-split kernels)."""
+    inp = make_random(10, T=32, H=H, num_kv=400, topk=96, p_invalid=0.0)
     rng = np.random.default_rng(11)
     inp["topk"][inp["topk"] == 0] = 1  # row 0 unreferenced
     inp["topk"] = np.where(inp["topk"] == 1, -1, inp["topk"]).astype(np.int32)
