@@ -546,12 +546,17 @@ __device__ __forceinline__ void smla_fwd_body(const Params& p, const SplitArgs& 
         // S and softmax of this wave's heads; P and the rescale factor go to
         // LDS (the previous tile's were consumed before the barrier above)
         tile_s<2, 2>(k_frag_addr(tb, g, li), qf, s);
+        // The softmax, the P exchange and the gather issue run at raised wave
+        // priority, so that they pass ahead of the other workgroup's MFMA-bound
+        // wave on this SIMD and the workgroup reaches its barrier sooner (1-2%).
+        asm volatile("s_setprio 2" ::: "memory");
         const float alpha = tile_softmax_ds(s, tile_rows(j, n), p.scale_log2, g, m_ref, l_part, pk);
         *(LDS_AS bf16x8*)(uintptr_t)(pb_own) = pk;
         if (g == 0) *(LDS_AS float*)(uintptr_t)(fac_own) = alpha;
         lds_barrier();  // every wave's P and factors visible
         is.all(lane);
         apply_factors(acc, fac_rd);
+        asm volatile("s_setprio 0" ::: "memory");
         tile_pv_ds(v_frag_addr(tb, g, li) + 256 * w, pb_rd, acc);
         continue;
       }
