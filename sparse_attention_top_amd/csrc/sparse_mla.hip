@@ -97,8 +97,12 @@ struct Smem : DsExchange<!FP8 && NW == 4> {
   static constexpr int kRingEnd = kRingOff + NBUF * kTileBytes;
   static constexpr int kStageBytes = NW * 16 * kRowStride;
   static constexpr int kAreaBytes = kRingEnd > kStageBytes ? kRingEnd : kStageBytes;
+  // list entries per compaction segment: 1024 in the four-wave bf16 workgroup
+  // (four top-k values per thread instead of eight: fewer registers live in
+  // the prologue, 11 -> 4 spilled, and 4 KiB less LDS), 2048 otherwise
+  static constexpr int kCap = (!FP8 && NW == 4) ? 1024 : kListCap;
   uint8_t area[kAreaBytes];
-  int32_t list[kListCap];
+  int32_t list[kCap];
   static constexpr bool kDs = !FP8 && NW == 4;
   // gather ring slot b
   __device__ __forceinline__ uint32_t tile(int b) { return lds_addr(area + kRingOff + b * kTileBytes); }
@@ -476,9 +480,9 @@ __device__ __forceinline__ void smla_fwd_body(const Params& p, const SplitArgs& 
   bf16x8 pk;
 
   const int32_t* trow = p.topk + (size_t)t * p.topk_n;
-  for (int seg0 = row_begin; seg0 < row_end; seg0 += kListCap) {
+  for (int seg0 = row_begin; seg0 < row_end; seg0 += SM::kCap) {
     if (seg0 > row_begin && NW > 1) lds_barrier();  // previous segment's list and tiles fully consumed
-    const int n = compact_segment<NW>(trow + seg0, min(kListCap, row_end - seg0), p.nkv, sm, lane, w);
+    const int n = compact_segment<NW, SM, SM::kCap>(trow + seg0, min(SM::kCap, row_end - seg0), p.nkv, sm, lane, w);
     const int ntiles = (n + kBK - 1) / kBK;
     if (ntiles == 0) continue;
 

@@ -127,6 +127,15 @@ def test_h16_tile_and_segment_edges(topk, num_kv, p_invalid):
     compare(o, lse, oracle_ref(inp), what="H=16 topk=%d" % topk)
 
 
+def test_h128_rows_over_several_segments():
+    """The H = 128 D-split workgroup compacts rows in 1024-entry segments: rows of 1500 entries (two segments, the
+    second partial) on the single pass (300 tokens x 2 head groups), compared on sampled tokens."""
+    inp = make_random(2600, T=300, H=128, num_kv=2000, topk=1500, p_invalid=0.3)
+    o, lse = run_case(inp)
+    tok = np.arange(0, 300, 15)
+    compare(o, lse, oracle_ref(inp, tokens=tok), tokens=tok, what="H=128 topk=1500")
+
+
 @pytest.mark.parametrize("topk,num_kv", [(1, 50), (31, 40), (33, 100), (2048, 3000), (2500, 4000), (4500, 6000)])
 def test_topk_extremes(topk, num_kv):
     """Single slots, tile-boundary counts and rows longer than one compaction segment."""
