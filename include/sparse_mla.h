@@ -43,8 +43,15 @@ typedef enum {
   SMLA_ERR_BAD_SCALE = -4,    /* scale is NaN or infinite                                  */
   SMLA_ERR_NO_DEVICE = -5,    /* no usable HIP device is current                           */
   SMLA_ERR_LAUNCH = -6,       /* the kernel launch failed (hipGetLastError)                */
-  SMLA_ERR_NO_MEMORY = -7     /* sparse_mla_prefill_i64: its index scratch could not be had */
+  SMLA_ERR_NO_MEMORY = -7,    /* device scratch could not be had (int64 rows, backward, or
+                                 the no-allocation entry point's array)                    */
+  SMLA_ERR_SCRATCH_LIMIT = -8 /* sparse_mla_prefill_noalloc: the call's split partials do not
+                                 fit SPARSE_MLA_NOALLOC_SCRATCH_BYTES                      */
 } smla_status_t;
+
+/* Size of the device array that sparse_mla_prefill_noalloc keeps its split
+ * partials in (64 MiB per device that calls it). */
+#define SPARSE_MLA_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 /*
  * sparse_mla_prefill -- enqueue the forward on `stream` and return.
@@ -88,6 +95,30 @@ typedef enum {
 int sparse_mla_prefill(const void* q, const void* kv, const int32_t* topk_indices, const float* attn_sink,
                        float scale, void* out, float* lse, int64_t T, int64_t H, int64_t num_kv,
                        int64_t topk, void* stream);
+
+/*
+ * sparse_mla_prefill_noalloc -- sparse_mla_prefill for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Same arguments, same kernels, same results
+ * bit for bit (the same split decision is taken), but the call itself never
+ * calls hipMalloc, hipFree or an allocating routine.
+ *
+ * Where sparse_mla_prefill would split each top-k row (few (token, head group)
+ * units, rows of >= 128 entries), the partial results go to one static device
+ * array of SPARSE_MLA_NOALLOC_SCRATCH_BYTES per device instead of the pool; it
+ * is reserved when the library's code is first loaded on that device and held
+ * until the process ends. A call whose partials need more than that returns
+ * SMLA_ERR_SCRATCH_LIMIT before anything is enqueued (2056 bytes per (unit,
+ * split, head): e.g. 16 tokens at H = 16 or H = 128 fit, 100 tokens at H = 128
+ * with 512-entry rows do not). Every partial a call reads is written by the same
+ * call, so the array needs no clearing; but all calls on one device share it,
+ * so two calls whose execution overlaps on one device (different streams, or
+ * host threads) race on it and must be ordered by the caller. Calls that do
+ * not split use no scratch at all.
+ */
+int sparse_mla_prefill_noalloc(const void* q, const void* kv, const int32_t* topk_indices, const float* attn_sink,
+                               float scale, void* out, float* lse, int64_t T, int64_t H, int64_t num_kv,
+                               int64_t topk, void* stream);
 
 /*
  * sparse_mla_prefill_fp8 -- the same operation on a pool of OCP FP8 E4M3

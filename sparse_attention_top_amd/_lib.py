@@ -19,6 +19,12 @@ SIGNATURES = {
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,  # T, H, num_kv, topk
         ctypes.c_void_p,  # stream
     ]),
+    "sparse_mla_prefill_noalloc": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,  # q, kv, topk, sink
+        ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,  # scale, out, lse
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,  # T, H, num_kv, topk
+        ctypes.c_void_p,  # stream
+    ]),
     "sparse_mla_prefill_fp8": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,  # q, kv, kv_scale, topk, sink
         ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,  # scale, out, lse
@@ -51,6 +57,7 @@ SMLA_ERR_BAD_SCALE = -4
 SMLA_ERR_NO_DEVICE = -5
 SMLA_ERR_LAUNCH = -6
 SMLA_ERR_NO_MEMORY = -7
+SMLA_ERR_SCRATCH_LIMIT = -8
 
 _lib = None
 

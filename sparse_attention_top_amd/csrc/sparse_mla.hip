@@ -1135,9 +1135,12 @@ int check_args(const void* q, const void* kv, const void* topk_indices, size_t i
 }
 
 // Enqueue the forward for int32 top-k rows (arguments already checked, T > 0).
+// fixed_ws / fixed_cap: caller-provided scratch for the split path's partials
+// (the entry point that allocates nothing); NULL takes them from the pool.
 int run_prefill(const void* q, const void* kv, const int32_t* topk_indices, const float* attn_sink, float scale,
                 void* out, float* lse, int64_t T, int64_t H, int64_t num_kv, int64_t topk, int dev,
-                hipStream_t s, bool fp8 = false, float kv_scale = 1.f) {
+                hipStream_t s, bool fp8 = false, float kv_scale = 1.f, void* fixed_ws = nullptr,
+                size_t fixed_cap = 0) {
   const Variant var = pick_variant(H, topk, fp8);
   const int64_t heads_per_wg = (int64_t)16 * var.nw;
   const int64_t head_groups = (H + heads_per_wg - 1) / heads_per_wg;
@@ -1179,8 +1182,15 @@ int run_prefill(const void* q, const void* kv, const int32_t* topk_indices, cons
       const size_t bytes_o = (size_t)parts * kD * sizeof(float);
       const size_t bytes = bytes_o + (size_t)parts * 2 * sizeof(float);
       void* ws = nullptr;
-      hipMemPool_t pool = scratch_pool(dev);
-      if (pool != nullptr && hipMallocFromPoolAsync(&ws, bytes, pool, s) == hipSuccess && ws != nullptr) {
+      const bool pooled = fixed_ws == nullptr;
+      if (!pooled) {
+        if (bytes > fixed_cap) return SMLA_ERR_SCRATCH_LIMIT;  // nothing enqueued
+        ws = fixed_ws;
+      } else {
+        hipMemPool_t pool = scratch_pool(dev);
+        if (pool == nullptr || hipMallocFromPoolAsync(&ws, bytes, pool, s) != hipSuccess) ws = nullptr;
+      }
+      if (ws != nullptr) {
         sa.nsplit = (int)ns;
         sa.split_len = (int)len;
         sa.part_o = (float*)ws;
@@ -1191,7 +1201,7 @@ int run_prefill(const void* q, const void* kv, const int32_t* topk_indices, cons
           hipLaunchKernelGGL(smla_merge_kernel, dim3((unsigned)((T * H + 3) / 4)), dim3(256), 0, s, p, sa, 16 * var.nw);
           err = hipGetLastError();
         }
-        const hipError_t ferr = hipFreeAsync(ws, s);
+        const hipError_t ferr = pooled ? hipFreeAsync(ws, s) : hipSuccess;
         return (err == hipSuccess && ferr == hipSuccess) ? SMLA_OK : SMLA_ERR_LAUNCH;
       }
       (void)hipGetLastError();
@@ -1220,6 +1230,32 @@ __global__ __launch_bounds__(256) void smla_idx64_kernel(const int64_t* __restri
 
 }  // namespace
 
+// ---- scratch of sparse_mla_prefill_noalloc ----
+// The split path's partial results for callers that cannot allocate: one
+// array per device, held from the library's first use on that device until
+// the process ends. Host code never passes `scratch` itself to a kernel (on
+// the host the name is only a stand-in for the symbol): it uses the device
+// address looked up once per device with that device current.
+constexpr size_t kNoAllocScratchBytes = (size_t)SPARSE_MLA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+static int noalloc_scratch(int dev, void** ptr) {
+  static std::mutex mu;
+  static void* addr[64];
+  if (dev < 0 || dev >= 64) return SMLA_ERR_NO_DEVICE;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return SMLA_ERR_NO_MEMORY;
+    }
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return SMLA_OK;
+}
+
 extern "C" int sparse_mla_prefill(const void* q, const void* kv, const int32_t* topk_indices, const float* attn_sink,
                                   float scale, void* out, float* lse, int64_t T, int64_t H, int64_t num_kv,
                                   int64_t topk, void* stream) {
@@ -1228,6 +1264,19 @@ extern "C" int sparse_mla_prefill(const void* q, const void* kv, const int32_t* 
   int dev = -1;
   if ((rc = current_device(&dev)) != SMLA_OK) return rc;
   return run_prefill(q, kv, topk_indices, attn_sink, scale, out, lse, T, H, num_kv, topk, dev, (hipStream_t)stream);
+}
+
+extern "C" int sparse_mla_prefill_noalloc(const void* q, const void* kv, const int32_t* topk_indices,
+                                          const float* attn_sink, float scale, void* out, float* lse, int64_t T,
+                                          int64_t H, int64_t num_kv, int64_t topk, void* stream) {
+  int rc = check_args(q, kv, topk_indices, 4, attn_sink, scale, out, lse, T, H, num_kv, topk, false);
+  if (rc != SMLA_OK || T == 0) return rc;
+  int dev = -1;
+  if ((rc = current_device(&dev)) != SMLA_OK) return rc;
+  void* ws = nullptr;
+  if ((rc = noalloc_scratch(dev, &ws)) != SMLA_OK) return rc;
+  return run_prefill(q, kv, topk_indices, attn_sink, scale, out, lse, T, H, num_kv, topk, dev, (hipStream_t)stream,
+                     false, 1.f, ws, kNoAllocScratchBytes);
 }
 
 extern "C" int sparse_mla_prefill_fp8(const void* q, const void* kv, float kv_scale, const int32_t* topk_indices,
@@ -1279,7 +1328,10 @@ extern "C" const char* sparse_mla_status_string(int status) {
     case SMLA_ERR_BAD_SCALE: return "scale must be finite";
     case SMLA_ERR_NO_DEVICE: return "no usable HIP device";
     case SMLA_ERR_LAUNCH: return "kernel launch failed";
-    case SMLA_ERR_NO_MEMORY: return "device scratch for the int64 index conversion could not be allocated";
+    case SMLA_ERR_NO_MEMORY: return "device scratch could not be had (int64 index conversion, backward, or the no-allocation array)";
+    case SMLA_ERR_SCRATCH_LIMIT:
+      return "the call's split partials need more than the no-allocation scratch holds "
+             "(SPARSE_MLA_NOALLOC_SCRATCH_BYTES); use sparse_mla_prefill";
     default: return "unknown status";
   }
 }

@@ -41,7 +41,7 @@ def call(q=0x1000, kv=0x2000, topk=0x3000, sink=None, scale=0.0441, out=0x4000, 
 
 def test_status_strings_and_version():
     lib = _lib.load()
-    for rc in range(-7, 1):
+    for rc in range(-8, 1):
         assert _lib.status_string(rc)
     assert _lib.status_string(17) == "unknown status"
     assert lib.sparse_mla_version() >= 100
@@ -83,6 +83,24 @@ def test_kernel_names():
 ])
 def test_argument_errors_return_before_any_launch(kw, rc):
     assert call(**kw) == rc
+
+
+def call_noalloc(q=0x1000, kv=0x2000, topk=0x3000, sink=None, scale=0.0441, out=0x4000, lse=0x5000,
+                 T=4, H=8, num_kv=16, k=8):
+    return _lib.load().sparse_mla_prefill_noalloc(q, kv, topk, sink, scale, out, lse, T, H, num_kv, k, None)
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(T=-1), _lib.SMLA_ERR_BAD_SIZE),
+    (dict(H=0), _lib.SMLA_ERR_BAD_SIZE),
+    (dict(scale=float("nan")), _lib.SMLA_ERR_BAD_SCALE),
+    (dict(q=None), _lib.SMLA_ERR_NULL_POINTER),
+    (dict(topk=None), _lib.SMLA_ERR_NULL_POINTER),
+    (dict(out=0x4002), _lib.SMLA_ERR_MISALIGNED),
+])
+def test_noalloc_entry_argument_errors(kw, rc):
+    assert call_noalloc(**kw) == rc
+    assert call_noalloc(T=0, q=None, out=None, lse=None, topk=None, kv=None) == _lib.SMLA_OK
 
 
 def call64(q=0x1000, kv=0x2000, topk=0x3000, sink=None, scale=0.0441, out=0x4000, lse=0x5000,
