@@ -182,22 +182,35 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
   return ((p / kXcdChunk) * kNumXcd + x) * kXcdChunk + (p % kXcdChunk);
 }
 
-// Compact the valid entries of trow[0, len) into sm.list (order kept), with
-// one round of loads and two workgroup barriers. Returns the count (uniform
-// across the workgroup). The per-wave counts live in the tile area, which
-// holds no tile then; the closing barrier keeps them until every wave has
-// read them.
-template <int NW, typename SM, int CAP = kListCap>
-__device__ __forceinline__ int compact_segment(const int32_t* __restrict__ trow, int len, uint32_t nkv, SM& sm, int lane,
-                                               int w) {
-  constexpr int CH = NW * 64;              // entries per chunk (one per thread)
-  constexpr int MAXC = CAP / CH;           // chunks per segment (len <= CAP)
+// The two halves of compact_segment: the loads of the segment's entries (one
+// per thread per chunk), and the compaction proper. A caller may issue other
+// loads in between: memory loads complete in issue order, so loads issued
+// before the entries would hold the compaction up until they land.
+template <int NW, int CAP>
+struct SegmentRaw {
+  static constexpr int CH = NW * 64;     // entries per chunk (one per thread)
+  static constexpr int MAXC = CAP / CH;  // chunks per segment (len <= CAP)
+  int raw[MAXC];
+};
+// The loads take no branch (positions past len read entry len - 1 and are
+// dropped by compact_finish), so that no wait for them is forced at a join;
+// trow must hold at least one entry.
+template <int NW, int CAP>
+__device__ __forceinline__ void compact_load(SegmentRaw<NW, CAP>& r, const int32_t* __restrict__ trow, int len, int lane,
+                                             int w) {
+#pragma unroll
+  for (int c = 0; c < SegmentRaw<NW, CAP>::MAXC; ++c) {
+    const int pos = c * SegmentRaw<NW, CAP>::CH + w * 64 + lane;
+    r.raw[c] = trow[max(min(pos, len - 1), 0)];
+  }
+}
+template <int NW, typename SM, int CAP>
+__device__ __forceinline__ int compact_finish(const SegmentRaw<NW, CAP>& rr, int len, uint32_t nkv, SM& sm, int lane,
+                                              int w) {
+  constexpr int MAXC = SegmentRaw<NW, CAP>::MAXC;
   int raw[MAXC];
 #pragma unroll
-  for (int c = 0; c < MAXC; ++c) {
-    const int pos = c * CH + w * 64 + lane;
-    raw[c] = pos < len ? trow[pos] : -1;
-  }
+  for (int c = 0; c < MAXC; ++c) raw[c] = (c * SegmentRaw<NW, CAP>::CH + w * 64 + lane) < len ? rr.raw[c] : -1;
   uint64_t bal[MAXC];
 #pragma unroll
   for (int c = 0; c < MAXC; ++c) bal[c] = __ballot((uint32_t)raw[c] < nkv);
@@ -231,6 +244,18 @@ __device__ __forceinline__ int compact_segment(const int32_t* __restrict__ trow,
     lds_barrier();
     return __builtin_amdgcn_readfirstlane(base);
   }
+}
+// Compact the valid entries of trow[0, len) into sm.list (order kept), with
+// one round of loads and two workgroup barriers. Returns the count (uniform
+// across the workgroup). The per-wave counts live in the tile area, which
+// holds no tile then; the closing barrier keeps them until every wave has
+// read them.
+template <int NW, typename SM, int CAP = kListCap>
+__device__ __forceinline__ int compact_segment(const int32_t* __restrict__ trow, int len, uint32_t nkv, SM& sm, int lane,
+                                               int w) {
+  SegmentRaw<NW, CAP> r;
+  compact_load(r, trow, len, lane, w);
+  return compact_finish<NW>(r, len, nkv, sm, lane, w);
 }
 
 __device__ __forceinline__ int tile_rows(int i, int n) { return min(kBK, n - i * kBK); }

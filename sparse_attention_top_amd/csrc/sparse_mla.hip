@@ -324,6 +324,14 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[16], const Params& p, int t,
   }
 }
 
+// As load_q with no branch: a head past H loads head H - 1 (its results are
+// never stored), so no wait for q is forced where control flow joins.
+__device__ __forceinline__ void load_q_any(bf16x8 (&qf)[16], const Params& p, int t, int head, int g) {
+  const bf16x8* src = (const bf16x8*)(p.q + ((size_t)t * p.H + min(head, p.H - 1)) * kD + 8 * g);
+#pragma unroll
+  for (int k = 0; k < 16; ++k) qf[k] = __builtin_nontemporal_load(src + 4 * k);
+}
+
 // ---- D-split P.V (four waves, 64 heads, bf16 pool) ----
 // The wave that owns 16 heads computes their S and softmax, then publishes P
 // (its B-operand fragment) and the per-head rescale factor in LDS; after a
@@ -661,6 +669,630 @@ template <int NW, int NBUF>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void smla_fwd_fp8_split_kernel(
     const Params p, const SplitArgs sa) {
   smla_fwd_body<NW, NBUF, true, true>(p, sa);
+}
+
+// ---------------------------------------------------------------------------
+// H > 64, bf16 pool, single pass: one four-wave workgroup per (token, group of
+// 128 heads), one workgroup per CU (one wave per SIMD, up to 512 registers).
+//
+// Each wave owns 32 heads for S (Q^T of 32 heads in 128 VGPRs), so one K
+// fragment read from LDS feeds two MFMAs; P of every head goes through LDS and
+// each wave accumulates O^T for its 128 columns of d over all 128 heads (256
+// AGPRs), so one V^T fragment read feeds eight MFMAs. Each row is gathered once
+// per token (not once per 64-head group).
+//
+// With one wave per SIMD nothing else hides a wave's own latencies, so each
+// tile is software-pipelined by hand: phase X accumulates P.V(j) and runs the
+// softmax of tile j+1 between its MFMAs (publishing P(j+1)); after one barrier,
+// phase Y computes S(j+2) and issues the rows of tile j+3 between its MFMAs. A
+// 16x16x32 MFMA keeps the matrix pipe busy for about 16 cycles, during which
+// the wave can issue about two other instructions, so the softmax is kept to
+// about 80 instructions per tile: the reference max moves (a cross-lane
+// reduction and rescale factors published for all waves) only when a lane's
+// tile max passes its threshold, which after the first tile is rare. Tiles are
+// gathered three ahead into a ring of four (also the 128-row output staging).
+
+// The O^T accumulators of this kernel are kept by hand in the AGPR file:
+// acc(o, dt) (head block o, d-tile dt) is a[32 o + 4 dt .. +3]. With all 256
+// AGPRs holding live accumulators, the register allocator has no free AGPR for
+// the copies it makes at loop joins and spills; here the compiler allocates
+// no AGPR of its own (the kernel's VGPR demand stays below 256, so nothing is
+// spilled into AGPRs), and one empty asm claims the whole file so the kernel's
+// register allocation covers it.
+#include "smla_acc128.h"
+
+__device__ __forceinline__ void acc128_claim_and_zero() {
+  asm volatile(SMLA_AGPR_ZERO_ASM ::: SMLA_ALL_AGPRS);
+}
+// acc(R / 32, (R % 32) / 4) += A B
+template <int R>
+__device__ __forceinline__ void acc128_mfma(const bf16x8& a, const bf16x8& b, float d0, float d1) {
+  static_assert(R % 4 == 0 && R < 256, "one tuple of the AGPR file");
+  acc128_mfma_t<R / 4>(a, b, d0, d1);
+}
+template <int R>
+__device__ __forceinline__ f32x4 acc128_read() {
+  float x0, x1, x2, x3;
+  acc128_read_t<R / 4>(x0, x1, x2, x3);
+  return f32x4{x0, x1, x2, x3};
+}
+template <int R>
+__device__ __forceinline__ void acc128_scale(float f) {
+  acc128_scale_t<R / 4>(f);
+}
+
+constexpr int k128Ring = 4;  // ring of 32-row tiles
+constexpr int k128Ahead = k128Ring - 1;
+constexpr int k128Cap = 1024;  // top-k entries compacted per segment
+
+struct Smem128 {
+  uint8_t area[k128Ring * kBK * kRowStride];  // gather ring; 128 staged o rows at the end
+  uint8_t pbuf[2][8 * 64 * 16];               // P fragments of tile j, by tile parity: [head block][lane][16 B]
+  float fac[2][128];                          // rescale factors, [li * 8 + head block], written with a flag
+  uint8_t flag[2][4];                         // per wave (byte w): its factors of this tile were written
+  float osc[128];                             // output scale of each head, [li * 8 + head block]
+  int32_t list[k128Cap];
+  __device__ __forceinline__ uint32_t tile(int b) { return lds_addr(area + b * kBK * kRowStride); }
+  __device__ __forceinline__ int32_t& wcount(int c, int w) { return ((int32_t*)area)[c * 4 + w]; }
+};
+static_assert(sizeof(Smem128) <= 160 * 1024, "one workgroup per CU");
+static_assert(k128Ring * kBK == 128, "the ring doubles as the staging of 128 output rows");
+
+// An empty asm that "redefines" its operands: code using them cannot move above it.
+template <typename T>
+__device__ __forceinline__ void pin1(T& v) {
+  asm volatile("" : "+v"(v));
+}
+template <typename... T>
+__device__ __forceinline__ void pin(T&... v) {
+  (pin1(v), ...);
+}
+// Plain v_max_f32 (the fmaxf lowering first canonicalises both operands, two
+// more instructions; a NaN logit reaches the output through exp2 either way).
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ uint32_t bf16pair(float a, float b) {
+  const bf16x4 v = bf16x4{(__bf16)a, (__bf16)b, (__bf16)0.f, (__bf16)0.f};
+  return __builtin_bit_cast(u32x2, v)[0];
+}
+
+// S MFMA with operands it does not read (ordering only).
+__device__ __forceinline__ void mfma_s_dep(f32x4& c, const u32x4& a, const u32x4& b, float d0, float d1) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b), "v"(d0), "v"(d1));
+}
+__device__ __forceinline__ void mfma_s_first_dep(f32x4& c, const u32x4& a, const u32x4& b, float d0, float d1) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b), "v"(d0), "v"(d1));
+}
+
+// The gather of one tile for the 128-head workgroup: wave w moves rows
+// [8 w, 8 w + 8), lane L < 8 forming row 8 w + L's source address (a pool row,
+// or the zero row past the tile's count); one LDS-DMA load per row.
+struct Gather128 {
+  uint32_t dst0;      // LDS address of this wave's first row
+  uint32_t alo, ahi;  // lane L < 8: source address of row L
+  bool active;
+  template <int R>
+  __device__ __forceinline__ void row(int lane) const {
+    if (!active) return;
+    const uint32_t rlo = (uint32_t)__builtin_amdgcn_readlane(alo, R);
+    const uint32_t rhi = (uint32_t)__builtin_amdgcn_readlane(ahi, R);
+    const uint16_t* rs = (const uint16_t*)(uintptr_t)(((uint64_t)rhi << 32) | rlo);
+    __builtin_amdgcn_global_load_lds(rs + 8 * lane, (LDS_AS void*)(uintptr_t)(dst0 + R * kRowStride), 16, 0, 0);
+  }
+  __device__ __forceinline__ void all(int lane) const {
+    static_for<0, kBK / 4>([&](auto rc) { row<decltype(rc)::value>(lane); });
+  }
+};
+// The list entry of this lane's row (every lane reads an in-bounds entry, so no
+// branch merges the pending register); the raw read is completed by a later
+// wait that takes it as an operand.
+__device__ __forceinline__ int opaque_lane(int lane) {  // recomputed at each use, not held in a register
+  asm volatile("" : "+v"(lane));
+  return lane;
+}
+__device__ __forceinline__ uint32_t gather128_read(const int32_t* list, int i, int lane, int w) {
+  const int pos = min(i * kBK + w * (kBK / 4) + (opaque_lane(lane) & 7), k128Cap - 1);
+  uint32_t e;
+  asm volatile("ds_read_b32 %0, %1" : "=v"(e) : "v"(lds_addr(list + pos)));
+  return e;
+}
+__device__ __forceinline__ Gather128 gather128_make(uint32_t e, int i, int n, bool act, uint32_t buf,
+                                                   const uint16_t* kv, int lane, int w) {
+  Gather128 ga;
+  ga.active = act;
+  const int r0 = w * (kBK / 4);
+  const int cnt = act ? min(kBK, n - i * kBK) : 0;
+  ga.dst0 = buf + r0 * kRowStride;
+  const bool have = act && lane < kBK / 4 && r0 + lane < cnt;
+  const uint16_t* src = have ? uniform_ptr(kv) + (size_t)e * kD : kZeroRowBf16;
+  const uint64_t a = (uint64_t)(uintptr_t)src;
+  ga.alo = (uint32_t)a;
+  ga.ahi = (uint32_t)(a >> 32);
+  return ga;
+}
+__device__ __forceinline__ Gather128 gather128(const int32_t* list, int i, int n, bool act, uint32_t buf,
+                                               const uint16_t* kv, int lane, int w) {
+  uint32_t e = gather128_read(list, i, lane, w);
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(e));
+  return gather128_make(e, i, n, act, buf, kv, lane, w);
+}
+
+// Phase Y: S = K Q^T from the tile at krow, 16 k-steps of four MFMAs (four
+// independent chains), the K fragments of k-step u + KPF read between the
+// first MFMAs of step u, and the rows of the next gather between the later
+// ones. s[sh][hb] = S^T[slot 16 sh + 4g + i][head 32 w + 16 hb + li].
+constexpr int kYKPF = 2;
+struct NoTail {
+  __device__ __forceinline__ void operator()() {}
+};
+// tail() runs after the last MFMA is issued (the next phase's first reads).
+template <typename Tail = NoTail>
+__device__ __forceinline__ void phase_y128(uint32_t krow, const bf16x8 (&qf)[2][16], f32x4 (&s)[2][2],
+                                           const Gather128& ga, int lane, Tail&& tail = NoTail{}) {
+  constexpr int KST = kYKPF + 1;
+  u32x4 kf[KST][2];
+  auto kread = [&](auto kc, auto hc) {
+    constexpr int k = decltype(kc)::value, h = decltype(hc)::value;
+    kf[k % KST][h] = ds_read_b128<16 * kRowStride * h + 64 * k>(krow);
+  };
+  static_for<0, kYKPF>([&](auto kc) {
+    kread(kc, Int<0>{});
+    kread(kc, Int<1>{});
+  });
+  static_for<0, 16>([&](auto uc) {
+    constexpr int u = decltype(uc)::value;
+    // reads issued after K(u): K(u+1) .. K(u+KPF-1)
+    constexpr int wc = 2 * ((kYKPF - 1) < (15 - u) ? (kYKPF - 1) : (15 - u));
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(kf[u % KST][0]), "+v"(kf[u % KST][1]) : "n"(wc));
+    static_for<0, 4>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int sh = i >> 1, hb = i & 1;
+      const u32x4 qb = __builtin_bit_cast(u32x4, qf[hb][u]);
+      if constexpr (u == 0) mfma_s_first(s[sh][hb], kf[0][sh], qb);
+      else mfma_s(s[sh][hb], kf[u % KST][sh], qb);
+      if constexpr (i < 2 && u + kYKPF < 16) kread(Int<u + kYKPF>{}, Int<i>{});
+      if constexpr (i == 2 && u % 2 == 0) ga.template row<u / 2>(lane);
+      if constexpr (u == 15 && i == 3) tail();
+    });
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");  // MFMA write -> VALU read distance
+#pragma unroll
+  for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) asm volatile("" : "+v"(s[sh][hb]));
+}
+
+// Per-token softmax state of this lane's two heads (32 w + 16 hb + li).
+// The reference max m_ref (log2 units) is not kept: it is -nmu, or -inf while
+// thr is -inf (nothing seen yet).
+struct Soft128 {
+  float l_part[2];  // this lane's share of the row sum relative to m_ref
+  float nmu[2];     // -m_ref (0 while m_ref is -inf)
+  float thr[2];     // a raw S value above this moves the reference: (m_ref + tau) / c
+  __device__ __forceinline__ float m_ref(int hb) const { return thr[hb] == -INFINITY ? -INFINITY : -nmu[hb]; }
+};
+// Softmax temporaries of one tile.
+struct SoftT {
+  float t[2][4];
+  float mxr[2];
+  uint32_t flag;
+};
+struct Deps {
+  float d0, d1;
+};
+
+// The rare step: a lane's tile max passed its threshold somewhere in the wave.
+// Every head takes its row max across the four lanes; where that passes the
+// reference by more than kLazyTau the reference moves to it and what earlier
+// tiles accumulated is rescaled (factor published for every wave; 1 elsewhere).
+// Exact: the final normalisation uses the same reference.
+__device__ __forceinline__ void soft128_move(SoftT& tt, Soft128& ss, float c, float inv_c, uint32_t facw) {
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const float mx = row4_max(tt.mxr[hb]) * c;
+    const float mr = ss.m_ref(hb);
+    const float mn = mx > mr + kLazyTau ? mx : mr;
+    // a head whose reference is still -inf has nothing accumulated: its factor stays 1
+    const float alpha = (mn == mr || mr == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mr - mn);
+    ss.l_part[hb] *= alpha;
+    ss.nmu[hb] = mn == -INFINITY ? 0.f : -mn;
+    ss.thr[hb] = (mn + kLazyTau) * inv_c;
+    *(LDS_AS float*)(uintptr_t)(facw + 4 * hb) = alpha;  // the four lanes of a head write the same value
+  }
+  tt.flag = 1;
+}
+
+// Group G of the softmax of one tile, run between two MFMAs of phase X. The
+// logits are scale * log2(e) * S with the scale taken positive (q is negated
+// for a negative scale), so the max is taken on S itself and p = 2^(c S - m)
+// is one fma and one exp2. MASK: the tile is partial (slots >= cnt -> -inf).
+template <int G, bool MASK>
+__device__ __forceinline__ Deps soft128_group(f32x4 (&s)[2][2], SoftT& tt, Soft128& ss, float c, float inv_c, int cnt,
+                                              int g, uint32_t pbw, uint32_t facw, uint32_t flagw) {
+  constexpr int M = MASK ? 8 : 0;
+  if constexpr (MASK && G < 8) {  // two elements (hb = G & 1, e = 2 (G >> 1) ..) past the count -> -inf
+    constexpr int hb = G & 1, e0 = 2 * (G >> 1), sh = e0 >> 2, i0 = e0 & 3;
+    pin(s[sh][hb]);
+    const int lim = cnt - 4 * g;  // slot 16 sh + 4 g + i is valid iff 16 sh + i < lim
+#pragma unroll
+    for (int i = i0; i < i0 + 2; ++i) s[sh][hb][i] = (16 * sh + i) < lim ? s[sh][hb][i] : -INFINITY;
+    return {s[sh][hb][i0], s[sh][hb][i0 + 1]};
+  } else if constexpr (G < M + 4) {  // tile max, in-lane: two three-way maxima per group
+    constexpr int hb = (G - M) & 1, part = (G - M) >> 1;
+    pin(s[0][hb], s[1][hb]);
+    if constexpr (part == 0) {
+      tt.t[hb][0] = vmax3(s[0][hb][0], s[0][hb][1], s[0][hb][2]);
+      tt.t[hb][1] = vmax3(s[0][hb][3], s[1][hb][0], s[1][hb][1]);
+      return {tt.t[hb][0], tt.t[hb][1]};
+    } else {
+      pin(tt.t[hb][0], tt.t[hb][1]);
+      tt.t[hb][2] = vmax3(s[1][hb][2], s[1][hb][3], tt.t[hb][0]);
+      tt.mxr[hb] = vmax(tt.t[hb][2], tt.t[hb][1]);
+      return {tt.mxr[hb], tt.mxr[hb]};
+    }
+  } else if constexpr (G < M + 8) {  // (free slots)
+    return {c, c};
+  } else if constexpr (G == M + 8) {  // does the reference move (rare)?
+    pin(tt.mxr[0], tt.mxr[1], ss.thr[0], ss.thr[1]);
+    tt.flag = 0;
+    if (__ballot(tt.mxr[0] > ss.thr[0] || tt.mxr[1] > ss.thr[1]) != 0ull) soft128_move(tt, ss, c, inv_c, facw);
+    return {ss.nmu[0], ss.nmu[1]};
+  } else if constexpr (G < M + 25) {  // p = 2^(c S - m), in place
+    constexpr int k = G - M - 9, hb = k & 1, e = k >> 1, sh = e >> 2, i = e & 3;
+    pin(s[sh][hb], ss.nmu[hb]);
+    s[sh][hb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sh][hb][i], c, ss.nmu[hb]));
+    return {s[sh][hb][i], s[sh][hb][i]};
+  } else if constexpr (G < M + 29) {  // P in bf16 (the B-operand layout of the P.V MFMA), published
+    constexpr int hb = (G - M - 25) & 1, sh = (G - M - 25) >> 1;
+    pin(s[sh][hb]);
+    const u32x2 pk = u32x2{bf16pair(s[sh][hb][0], s[sh][hb][1]), bf16pair(s[sh][hb][2], s[sh][hb][3])};
+    *(LDS_AS u32x2*)(uintptr_t)(pbw + 1024 * hb + 8 * sh) = pk;
+    return {__uint_as_float(pk[0]), __uint_as_float(pk[1])};
+  } else if constexpr (G < M + 33) {  // row sums of the fp32 p, in place: pairs
+    constexpr int hb = (G - M - 29) & 1, sh = (G - M - 29) >> 1;
+    pin(s[sh][hb]);
+    s[sh][hb][0] = s[sh][hb][0] + s[sh][hb][1];
+    s[sh][hb][2] = s[sh][hb][2] + s[sh][hb][3];
+    return {s[sh][hb][0], s[sh][hb][2]};
+  } else if constexpr (G < M + 35) {
+    constexpr int hb = (G - M - 33) & 1;
+    pin(s[0][hb], s[1][hb]);
+    s[0][hb][0] = s[0][hb][0] + s[0][hb][2];
+    s[1][hb][0] = s[1][hb][0] + s[1][hb][2];
+    return {s[0][hb][0], s[1][hb][0]};
+  } else if constexpr (G < M + 37) {
+    constexpr int hb = (G - M - 35) & 1;
+    pin(s[0][hb], s[1][hb], ss.l_part[hb]);
+    ss.l_part[hb] += s[0][hb][0] + s[1][hb][0];
+    return {ss.l_part[hb], ss.l_part[hb]};
+  } else if constexpr (G == M + 37) {  // publish whether factors were written
+    pin(tt.flag);
+    *(LDS_AS uint8_t*)(uintptr_t)(flagw) = (uint8_t)tt.flag;
+    return {c, c};
+  } else {
+    return {c, c};
+  }
+}
+template <bool MASK>
+constexpr int kSoftGroups128 = MASK ? 46 : 38;
+
+// The whole softmax of one tile with no MFMAs to interleave (the first tile).
+template <bool MASK>
+__device__ __forceinline__ void soft128_plain(f32x4 (&s)[2][2], Soft128& ss, float c, float inv_c, int cnt, int g,
+                                              uint32_t pbw, uint32_t facw, uint32_t flagw) {
+  SoftT tt;
+  static_for<0, kSoftGroups128<MASK>>([&](auto gc) {
+    (void)soft128_group<decltype(gc)::value, MASK>(s, tt, ss, c, inv_c, cnt, g, pbw, facw, flagw);
+  });
+}
+
+// The first LDS reads of phase X, issued ahead (during the previous phase Y,
+// or right after the barrier): the list entry of the gather after next, the
+// four wave flags (one dword), the P fragments of head blocks 0..3 and the
+// first kXVPF V fragments. Completed by the waits of phase X, which take them
+// as operands.
+constexpr int kXVPF = 2;
+struct XPre {
+  uint32_t e;
+  uint32_t fl;  // byte w: wave w's flag
+  u32x4 pf[4];
+  u32x2 vf[kXVPF + 1][2];  // the V^T fragment ring of phase X; the first VPF prefetched
+};
+__device__ __forceinline__ void x_prefetch(XPre& xp, const int32_t* list, int gi, int lane, int w, uint32_t flag_rd,
+                                           uint32_t pbase, uint32_t vrow) {
+  xp.e = gather128_read(list, gi, lane, w);
+  asm volatile("ds_read_b32 %0, %1" : "=v"(xp.fl) : "v"(flag_rd));
+  static_for<0, 4>([&](auto oc) { xp.pf[decltype(oc)::value] = ds_read_b128<1024 * decltype(oc)::value>(pbase); });
+  static_for<0, kXVPF>([&](auto pc) {
+    constexpr int pp = decltype(pc)::value;
+    xp.vf[pp][0] = ds_read_tr16_b64<32 * pp>(vrow);
+    xp.vf[pp][1] = ds_read_tr16_b64<16 * kRowStride + 32 * pp>(vrow);
+  });
+}
+
+// Phase X LDS reads, in issue order: the prefetch above (1 + 1 + 4 + 2 VPF
+// reads); at step u, V(u + VPF) between its first two MFMAs; at step 7 the P
+// fragments of head blocks 4..7, each into the register of the one its MFMA
+// has just read. Step u multiplies d-tile u % 8 with head blocks 4 (u / 8) .. +4
+// (V(u): the V^T fragment of that d-tile; each is read twice). The factors,
+// when a flag is set, are read and waited for apart.
+struct PhaseX128 {
+  static constexpr int kPro = 2 + 4 + 2 * kXVPF;
+  static constexpr int before(int u) {  // reads issued before the wait of step u
+    int r = kPro;
+    for (int s = 0; s < u; ++s) r += (s + kXVPF < 16 ? 2 : 0) + (s == 7 ? 4 : 0);
+    return r;
+  }
+  static constexpr int pos_v(int p) {
+    if (p < kXVPF) return 6 + 2 * (p + 1);
+    const int s = p - kXVPF;  // issued in step s: V half 0, [P 4], V half 1 at step 7
+    return before(s) + (s == 7 ? 3 : 2);
+  }
+  static constexpr int wait_at(int u) {
+    int need = pos_v(u);
+    if (u == 0 && need < 6) need = 6;
+    if (u == 8 && need < before(8)) need = before(8);  // the P fragments of head blocks 4..7
+    return before(u) - need;
+  }
+};
+
+// Slot k (MFMA k of 64) of phase X runs softmax group (k NG) / 64 when that is
+// the first slot of its group: NG groups spread evenly over the 64 MFMAs.
+template <int NG>
+constexpr int soft_group_at(int k) {
+  return (k * NG) % 64 < NG ? (k * NG) / 64 : -1;
+}
+
+// Phase X of iteration j: apply the factors of tile j (if a wave moved its
+// references), then O^T += V^T P^T for the wave's 8 d-tiles x 8 head blocks,
+// with the softmax groups of tile j+1 between the MFMAs (SOFT; MASK: tile j+1
+// is partial). xp: the prefetched reads, completed here.
+template <bool SOFT, bool MASK>
+__device__ __forceinline__ void phase_x128(XPre& xp, uint32_t vrow, uint32_t pbase, uint32_t fac_rd, f32x4 (&s)[2][2],
+                                           Soft128& ss, float c, float inv_c, int cnt, int g, uint32_t pbw,
+                                           uint32_t facw, uint32_t flagw) {
+  using Px = PhaseX128;
+  constexpr int VST = kXVPF + 1;
+  u32x4 (&pf)[4] = xp.pf;
+  u32x2 (&vf)[VST][2] = xp.vf;
+  auto vread = [&](auto pc, auto hc) {
+    constexpr int pp = decltype(pc)::value, h = decltype(hc)::value;
+    vf[pp % VST][h] = ds_read_tr16_b64<16 * kRowStride * h + 32 * (pp % 8)>(vrow);
+  };
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(xp.fl), "+v"(xp.e) : "n"(Px::kPro - 2));
+  const uint32_t fl = xp.fl;
+  if (__ballot(fl != 0u) != 0ull) {
+    // some wave moved references: rescale what earlier tiles accumulated for
+    // its heads (head block o belongs to wave o / 2)
+    u32x4 f0 = ds_read_b128<0>(fac_rd);
+    u32x4 f1 = ds_read_b128<16>(fac_rd);
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f0), "+v"(f1));
+    asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");  // MFMA write -> accumulator read distance
+    static_for<0, 8>([&](auto oc) {
+      constexpr int o = decltype(oc)::value;
+      const float fo = __uint_as_float(o < 4 ? f0[o] : f1[o - 4]);
+      if (__ballot(((fl >> (8 * (o / 2))) & 0xffu) != 0u && fo != 1.f) != 0ull)
+        static_for<0, 8>([&](auto dc) { acc128_scale<32 * o + 4 * decltype(dc)::value>(fo); });
+    });
+    asm volatile("s_nop 4" ::: "memory");  // accumulators rescaled by VALU, read by the MFMAs below
+  }
+  SoftT tt;
+  Deps dep{c, c};
+  constexpr int NG = kSoftGroups128<MASK>;
+  static_for<0, 16>([&](auto uc) {
+    constexpr int u = decltype(uc)::value;
+    constexpr int dt = u % 8, o0 = 4 * (u / 8);
+    if constexpr (u == 0 || u == 8)
+      asm volatile("s_waitcnt lgkmcnt(%6)"
+                   : "+v"(vf[u % VST][0]), "+v"(vf[u % VST][1]), "+v"(pf[0]), "+v"(pf[1]), "+v"(pf[2]), "+v"(pf[3])
+                   : "n"(Px::wait_at(u)));
+    else
+      asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(vf[u % VST][0]), "+v"(vf[u % VST][1]) : "n"(Px::wait_at(u)));
+    const bf16x8 va =
+        __builtin_bit_cast(bf16x8, u32x4{vf[u % VST][0][0], vf[u % VST][0][1], vf[u % VST][1][0], vf[u % VST][1][1]});
+    static_for<0, 4>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      acc128_mfma<32 * (o0 + i) + 4 * dt>(va, __builtin_bit_cast(bf16x8, pf[i]), dep.d0, dep.d1);
+      if constexpr (u + kXVPF < 16 && i < 2) vread(Int<u + kXVPF>{}, Int<i>{});
+      // the second pass's P fragment replaces this one after its last reader
+      if constexpr (u == 7) pf[i] = ds_read_b128<1024 * (4 + i)>(pbase);
+      constexpr int G = soft_group_at<NG>(4 * u + i);
+      if constexpr (SOFT && G >= 0) dep = soft128_group<G, MASK>(s, tt, ss, c, inv_c, cnt, g, pbw, facw, flagw);
+    });
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
+template <bool NEG>
+__device__ __forceinline__ void smla_fwd128_body(const Params& p) {
+  __shared__ __attribute__((aligned(16))) Smem128 sm;
+
+  int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int g = lane >> 4;
+  int li = lane & 15;
+
+  const int vb = xcd_remap(blockIdx.x, gridDim.x);
+  const int t = p.T - 1 - vb / p.head_groups;  // latest (heaviest) tokens first
+  const int hbase = (vb % p.head_groups) * 128;
+  int hs = hbase + 32 * w + li;  // S heads of this lane: hs and hs + 16
+
+  // exchange addresses (tile parity par: + par * the buffer size): P of head
+  // block o at pbuf + 1024 o + 16 lane; the factor of head 16 o + li at
+  // fac + 4 (8 li + o); wave w's flag at byte flag + w
+  const uint32_t pb0 = lds_addr(sm.pbuf[0]) + 16 * lane;
+  const uint32_t fac0 = lds_addr(sm.fac[0]) + 32 * li;
+  const uint32_t flag0 = lds_addr(sm.flag[0]);
+  constexpr uint32_t kPbPar = sizeof(sm.pbuf[0]), kFacPar = sizeof(sm.fac[0]), kFlagPar = sizeof(sm.flag[0]);
+  const uint32_t pb_own = pb0 + 2048 * w;  // head blocks 2w, 2w + 1
+  const uint32_t fac_own = fac0 + 8 * w;   // entries 8 li + 2w, + 1
+  const uint32_t flag_own = flag0 + w;
+
+  // logits c * S with c > 0: a negative scale is carried by q (negation is exact)
+  const float c = NEG ? -p.scale_log2 : p.scale_log2;
+  const float inv_c = 1.f / c;
+  Soft128 ss;
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    ss.l_part[hb] = 0.f;
+    ss.nmu[hb] = 0.f;
+    ss.thr[hb] = -INFINITY;
+  }
+  const int32_t* trow = p.topk + (size_t)t * p.topk_n;
+  // the first segment's entries are loaded ahead of q, so that its compaction
+  // does not wait for q (loads land in issue order)
+  SegmentRaw<4, k128Cap> raw0;
+  const int len0 = min(k128Cap, p.topk_n);
+  compact_load(raw0, len0 > 0 ? trow : (const int32_t*)(const void*)p.q, len0, lane, w);  // q: any valid address
+  bf16x8 qf[2][16];
+  load_q_any(qf[0], p, t, hs, g);
+  load_q_any(qf[1], p, t, hs + 16, g);
+  acc128_claim_and_zero();  // while q is in flight
+
+  const uint16_t* kvp = p.kv;
+  Gather128 none;
+  none.active = false;
+  none.dst0 = none.alo = none.ahi = 0;
+  // first segment compacted outside the loop: a wait at the loop's join would
+  // otherwise cover q as well
+  int n = compact_finish<4>(raw0, len0, p.nkv, sm, lane, w);
+  for (int seg0 = 0; seg0 < p.topk_n; seg0 += k128Cap) {
+    if (seg0 > 0) {
+      lds_barrier();  // previous segment's list, tiles and exchange fully consumed
+      const int len = min(k128Cap, p.topk_n - seg0);
+      compact_load(raw0, trow + seg0, len, lane, w);
+      n = compact_finish<4>(raw0, len, p.nkv, sm, lane, w);
+    }
+    const int nt = (n + kBK - 1) / kBK;
+    if (nt == 0) continue;
+#pragma unroll
+    for (int i = 0; i < k128Ahead; ++i) gather128(sm.list, i, n, i < nt, sm.tile(i), kvp, lane, w).all(lane);
+    if constexpr (NEG) {  // after the gathers are issued: this waits for q
+      if (seg0 == 0) {
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int k = 0; k < 16; ++k)
+            qf[hb][k] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, qf[hb][k]) ^ 0x80008000u);
+      }
+    }
+    // tiles 0 and 1 landed (tile 2 may be in flight)
+    wait_vmcnt_le(2 < nt ? kBK / 4 : 0);
+    lds_barrier();
+    f32x4 s[2][2];
+    // S(0), its softmax (P(0) in parity 0), S(1)
+    phase_y128(k_frag_addr(sm.tile(0), g, li), qf, s, none, lane);
+    if (nt > 1) {
+      soft128_plain<false>(s, ss, c, inv_c, kBK, g, pb_own, fac_own, flag_own);
+      phase_y128(k_frag_addr(sm.tile(1), g, li), qf, s, none, lane);
+    } else {
+      soft128_plain<true>(s, ss, c, inv_c, tile_rows(0, n), g, pb_own, fac_own, flag_own);
+    }
+    lds_barrier();  // P(0) visible
+    // Iteration j: phase X accumulates P.V(j) with the softmax of tile j+1
+    // between its MFMAs; one barrier (P(j+1) and tile j+2 visible, tile j-1
+    // free); phase Y computes S(j+2) and gathers tile j+3 into tile j-1's slot,
+    // and issues the first reads of phase X(j+1) behind its last MFMA.
+    XPre xp;
+    x_prefetch(xp, sm.list, k128Ahead, lane, w, flag0, pb0, v_frag_addr(sm.tile(0), g, li) + 256 * w);
+    for (int j = 0; j < nt; ++j) {
+      const uint32_t par = j & 1, nxt = par ^ 1;
+      const uint32_t vrow = v_frag_addr(sm.tile(j % k128Ring), g, li) + 256 * w;
+      const uint32_t pbase = pb0 + kPbPar * par, fac_rd = fac0 + kFacPar * par;
+      const uint32_t pbw = pb_own + kPbPar * nxt, facw = fac_own + kFacPar * nxt, flagw = flag_own + kFlagPar * nxt;
+      if (j + 2 < nt)  // tile j + 1 is full: only the last tile of a segment is partial
+        phase_x128<true, false>(xp, vrow, pbase, fac_rd, s, ss, c, inv_c, kBK, g, pbw, facw, flagw);
+      else if (j + 1 < nt)
+        phase_x128<true, true>(xp, vrow, pbase, fac_rd, s, ss, c, inv_c, tile_rows(j + 1, n), g, pbw, facw, flagw);
+      else
+        phase_x128<false, false>(xp, vrow, pbase, fac_rd, s, ss, c, inv_c, kBK, g, pbw, facw, flagw);
+      const uint32_t e = xp.e;  // list entry of tile j + 3 (completed in phase X)
+      wait_vmcnt_le(0);         // tile j + 2 landed (issued in phase Y of iteration j - 1)
+      lds_barrier();
+      if (j + 1 >= nt) break;
+      // the reads phase X(j+1) starts with: tile j+1, P(j+1), the flags of tile j+1
+      const uint32_t vrow1 = v_frag_addr(sm.tile((j + 1) % k128Ring), g, li) + 256 * w;
+      auto pre = [&]() {
+        x_prefetch(xp, sm.list, j + 1 + k128Ahead, lane, w, flag0 + kFlagPar * nxt, pb0 + kPbPar * nxt, vrow1);
+      };
+      if (j + 2 < nt) {
+        const bool gnext = j + k128Ahead < nt;
+        const Gather128 ga =
+            gather128_make(e, j + k128Ahead, n, gnext, sm.tile((j + k128Ahead) % k128Ring), kvp, lane, w);
+        phase_y128(k_frag_addr(sm.tile((j + 2) % k128Ring), g, li), qf, s, ga, lane, pre);
+      } else {
+        pre();
+      }
+    }
+  }
+
+  // ---- finalise: fold the sink, normalise, stage the 128 rows, store ----
+  // lane-derived addresses are recomputed here rather than kept live across
+  // the loop (a value kept there could land in the accumulators' AGPRs)
+  {
+    int ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    lane = ln;
+  }
+  g = lane >> 4;
+  li = lane & 15;
+  hs = hbase + 32 * w + li;
+  float oscale[2];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const int head = hs + 16 * hb;
+    const float sk = (p.sink != nullptr && head < p.H) ? p.sink[head] : -INFINITY;
+    const bool has_sink = !(sk == -INFINITY);
+    const HeadEnd he = head_end(ss.l_part[hb], ss.m_ref(hb), sk, has_sink, sk * kLog2e);
+    if (g == 0 && head < p.H) p.lse[(size_t)t * p.H + head] = he.lse;
+    oscale[hb] = he.oscale;
+  }
+  const uint32_t osc_own = lds_addr(sm.osc) + 32 * li + 8 * w;
+  if (g == 0) {
+    *(LDS_AS float*)(uintptr_t)(osc_own) = oscale[0];
+    *(LDS_AS float*)(uintptr_t)(osc_own + 4) = oscale[1];
+  }
+  lds_barrier();  // every wave is done with the tiles; output scales visible
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");  // MFMA write -> accumulator read distance
+  u32x4 f0 = ds_read_b128<0>(lds_addr(sm.osc) + 32 * li);
+  u32x4 f1 = ds_read_b128<16>(lds_addr(sm.osc) + 32 * li);
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f0), "+v"(f1));
+  // row 16 o + li of the staging, bytes 2 (128 w + 16 dt + 4 g)
+  const uint32_t st = sm.tile(0) + 256 * w + 8 * g + li * kRowStride;
+  static_for<0, 8>([&](auto oc) {
+    constexpr int o = decltype(oc)::value;
+    const float fo = __uint_as_float(o < 4 ? f0[o] : f1[o - 4]);
+    static_for<0, 8>([&](auto dc) {
+      constexpr int dt = decltype(dc)::value;
+      const f32x4 v = acc128_read<32 * o + 4 * dt>() * fo;
+      const bf16x4 v4 = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+      *(LDS_AS bf16x4*)(uintptr_t)(st + 16 * o * kRowStride + 32 * dt) = v4;
+    });
+  });
+  lds_barrier();  // all 128 rows staged
+  // wave w stores rows 32 w .. 32 w + 31: lane L writes bytes [16 L, 16 L + 16) of each
+#pragma unroll 8
+  for (int r = 0; r < 32; ++r) {
+    const int row = 32 * w + r;
+    const int hr = hbase + row;
+    const u32x4 val = *(LDS_AS const u32x4*)(uintptr_t)(sm.tile(0) + row * kRowStride + 16 * lane);
+    if (hr < p.H) __builtin_nontemporal_store(val, (u32x4*)(p.out + ((size_t)t * p.H + hr) * kD + 8 * lane));
+  }
+}
+
+// NEG: the scale is negative (carried by q, negated at load)
+template <bool NEG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void smla_fwd128_kernel(const Params p) {
+  smla_fwd128_body<NEG>(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -1064,13 +1696,17 @@ struct Variant {
 // 1024-entry list fits four per CU and measured 1.3x slower).
 constexpr int kR16Nbuf = 1;
 constexpr int kR16Cap = 512;
+// The one-workgroup-per-token kernel for more than 64 heads (smla_fwd128_kernel)
+// is not yet faster than two 64-head workgroups per token of the D-split
+// kernel, so the latter is dispatched.
+constexpr bool kFwd128 = false;
 
 Variant pick_variant(int64_t H, int64_t topk, bool fp8) {
   (void)topk;
   if (H <= 16 && !fp8) return {1, "smla_fwd16_kernel<1, 512>"};
   if (H <= 16) return {1, "smla_fwd16_fp8_kernel<2, 512>"};
   if (H <= 32) return {2, fp8 ? "smla_fwd_fp8_kernel<2, 2>" : "smla_fwd_kernel<2, 2>"};
-  if (!fp8) return {4, "smla_fwd_kernel<4, 2>"};
+  if (!fp8) return {4, (H > 64 && kFwd128) ? "smla_fwd128_kernel" : "smla_fwd_kernel<4, 2>"};
   if (H <= 64) return {4, "smla_fwd_fp8_kernel<4, 4>"};
   return {8, "smla_fwd_fp8_kernel<8, 4>"};
 }
@@ -1206,6 +1842,14 @@ int run_prefill(const void* q, const void* kv, const int32_t* topk_indices, cons
       }
       (void)hipGetLastError();
     }
+  }
+  if (kFwd128 && H > 64 && !fp8) {
+    p.head_groups = (int)((H + 127) / 128);
+    if (p.scale_log2 < 0.f)
+      hipLaunchKernelGGL(smla_fwd128_kernel<true>, dim3((unsigned)(T * p.head_groups)), dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL(smla_fwd128_kernel<false>, dim3((unsigned)(T * p.head_groups)), dim3(256), 0, s, p);
+    return hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
   }
   if (H <= 16) {
     if (fp8) hipLaunchKernelGGL((smla_fwd16_fp8_kernel<2, 512>), dim3((unsigned)units), dim3(64), 0, s, p);
