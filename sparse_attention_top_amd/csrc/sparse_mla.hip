@@ -34,6 +34,8 @@
 // their logits forced to -inf, so stale LDS contents never reach the output.
 
 
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "smla_common.h"
@@ -726,17 +728,16 @@ constexpr int k128Ahead = k128Ring - 1;
 constexpr int k128Cap = 1024;  // top-k entries compacted per segment
 
 struct Smem128 {
-  uint8_t area[k128Ring * kBK * kRowStride];  // gather ring; 128 staged o rows at the end
+  uint8_t area[k128Ring * kBK * kRowStride];  // gather ring
   uint8_t pbuf[2][8 * 64 * 16];               // P fragments of tile j, by tile parity: [head block][lane][16 B]
   float fac[2][128];                          // rescale factors, [li * 8 + head block], written with a flag
   uint8_t flag[2][4];                         // per wave (byte w): its factors of this tile were written
   float osc[128];                             // output scale of each head, [li * 8 + head block]
-  int32_t list[k128Cap];
+  int32_t list[2][k128Cap];                   // compacted lists of this unit and the next (by unit parity)
+  int32_t wcnt[16];                           // per-wave counts of the compaction
   __device__ __forceinline__ uint32_t tile(int b) { return lds_addr(area + b * kBK * kRowStride); }
-  __device__ __forceinline__ int32_t& wcount(int c, int w) { return ((int32_t*)area)[c * 4 + w]; }
 };
 static_assert(sizeof(Smem128) <= 160 * 1024, "one workgroup per CU");
-static_assert(k128Ring * kBK == 128, "the ring doubles as the staging of 128 output rows");
 
 // An empty asm that "redefines" its operands: code using them cannot move above it.
 template <typename T>
@@ -774,14 +775,13 @@ __device__ __forceinline__ void mfma_s_first_dep(f32x4& c, const u32x4& a, const
 
 // The gather of one tile for the 128-head workgroup: wave w moves rows
 // [8 w, 8 w + 8), lane L < 8 forming row 8 w + L's source address (a pool row,
-// or the zero row past the tile's count); one LDS-DMA load per row.
+// or the zero row past the tile's count, or for a tile past the unit's last);
+// one LDS-DMA load per row, issued without a branch.
 struct Gather128 {
   uint32_t dst0;      // LDS address of this wave's first row
   uint32_t alo, ahi;  // lane L < 8: source address of row L
-  bool active;
   template <int R>
   __device__ __forceinline__ void row(int lane) const {
-    if (!active) return;
     const uint32_t rlo = (uint32_t)__builtin_amdgcn_readlane(alo, R);
     const uint32_t rhi = (uint32_t)__builtin_amdgcn_readlane(ahi, R);
     const uint16_t* rs = (const uint16_t*)(uintptr_t)(((uint64_t)rhi << 32) | rlo);
@@ -807,7 +807,6 @@ __device__ __forceinline__ uint32_t gather128_read(const int32_t* list, int i, i
 __device__ __forceinline__ Gather128 gather128_make(uint32_t e, int i, int n, bool act, uint32_t buf,
                                                    const uint16_t* kv, int lane, int w) {
   Gather128 ga;
-  ga.active = act;
   const int r0 = w * (kBK / 4);
   const int cnt = act ? min(kBK, n - i * kBK) : 0;
   ga.dst0 = buf + r0 * kRowStride;
@@ -833,10 +832,14 @@ constexpr int kYKPF = 2;
 struct NoTail {
   __device__ __forceinline__ void operator()() {}
 };
+struct NoGather {  // a phase Y with no gather
+  template <int R>
+  __device__ __forceinline__ void row(int) const {}
+};
 // tail() runs after the last MFMA is issued (the next phase's first reads).
-template <typename Tail = NoTail>
-__device__ __forceinline__ void phase_y128(uint32_t krow, const bf16x8 (&qf)[2][16], f32x4 (&s)[2][2],
-                                           const Gather128& ga, int lane, Tail&& tail = NoTail{}) {
+template <typename GA, typename Tail = NoTail>
+__device__ __forceinline__ void phase_y128(uint32_t krow, const bf16x8 (&qf)[2][16], f32x4 (&s)[2][2], const GA& ga,
+                                           int lane, Tail&& tail = NoTail{}) {
   constexpr int KST = kYKPF + 1;
   u32x4 kf[KST][2];
   auto kread = [&](auto kc, auto hc) {
@@ -1112,19 +1115,113 @@ __device__ __forceinline__ void phase_x128(XPre& xp, uint32_t vrow, uint32_t pba
   });
 }
 
+// The 128-head kernel is persistent: workgroup b of G owns the units
+// (token, head group of 128) r G + (b, or G - 1 - b for odd r), r = 0, 1, ...
+// Unit v is token T - 1 - v / head_groups, head group v % head_groups: each
+// workgroup gets one unit of every run of G, and the alternating order evens
+// out the drift of the weights within a run. A workgroup takes its K units
+// starting at its r = b % K and wrapping around, so that workgroups do not
+// all reach a unit's end (128 KiB of output stores each) at the same time.
+struct Sched128 {
+  int b, G, K, r0;
+  __device__ __forceinline__ Sched128(int b_, int G_, int units) : b(b_), G(G_) {
+    const int full = units / G, rem = units % G;
+    K = full + ((rem > 0 && ((full & 1) ? G - 1 - b : b) < rem) ? 1 : 0);
+    r0 = K > 0 ? b % K : 0;
+  }
+  // the unit taken i-th (i < K)
+  __device__ __forceinline__ int unit(int i) const {
+    int r = r0 + i;
+    r = r >= K ? r - K : r;
+    return r * G + ((r & 1) ? G - 1 - b : b);
+  }
+};
+
+// The top-k entries of a unit are moved into a list buffer by LDS-DMA (wave w
+// moves positions 256 c + 64 w + lane, and later reads them back), then
+// compacted in place. Positions past len read entry len - 1 (dropped by
+// compact128); trow holds at least one entry.
+__device__ __forceinline__ void raw128_dma(uint32_t list_lds, const int32_t* trow, int len, int lane, int w) {
+#pragma unroll
+  for (int c = 0; c < k128Cap / 256; ++c) {
+    const int pos = c * 256 + w * 64 + lane;
+    __builtin_amdgcn_global_load_lds(trow + max(min(pos, len - 1), 0),
+                                     (LDS_AS void*)(uintptr_t)(list_lds + 4 * (c * 256 + w * 64)), 4, 0, 0);
+  }
+}
+// Compacts the valid entries (position < len, slot < nkv) of a list buffer in
+// place, order kept; returns the count. Every read precedes the first barrier
+// and every write follows it. The DMA that filled the buffer has completed.
+__device__ __forceinline__ int compact128(uint32_t list_lds, int len, uint32_t nkv, uint32_t wcnt_lds, int lane, int w) {
+  constexpr int NC = k128Cap / 256;
+  int raw[NC];
+  uint64_t bal[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int pos = c * 256 + w * 64 + lane;
+    // (asm: the entries came by DMA, waited for by the caller)
+    asm volatile("ds_read_b32 %0, %1" : "=v"(raw[c]) : "v"(list_lds + 4 * pos));
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    asm volatile("" : "+v"(raw[c]));
+    const int pos = c * 256 + w * 64 + lane;
+    bal[c] = __ballot(pos < len && (uint32_t)raw[c] < nkv);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) *(LDS_AS int32_t*)(uintptr_t)(wcnt_lds + 4 * (c * 4 + w)) = __popcll(bal[c]);
+  }
+  lds_barrier();
+  int base = 0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ci = __builtin_amdgcn_readfirstlane(*(LDS_AS const int32_t*)(uintptr_t)(wcnt_lds + 4 * (c * 4 + i)));
+      off += (i < w) ? ci : 0;
+      tot += ci;
+    }
+    if ((bal[c] >> lane) & 1ull) *(LDS_AS int32_t*)(uintptr_t)(list_lds + 4 * (base + off + lane_rank(bal[c]))) = raw[c];
+    base += tot;
+  }
+  lds_barrier();
+  return __builtin_amdgcn_readfirstlane(base);
+}
+
+// The output rows of head block O (heads 16 O + li) from the accumulators:
+// tuple acc(O, dt) holds, in lane (li, g), d = 128 w + 16 dt + 4 g .. + 4. Two
+// tuples (dt, dt + 1) are scaled and rounded, then the odd 16-lane rows of the
+// first are exchanged with the even rows of the second, after which lane
+// (li, g) holds eight consecutive d, 16 (dt + (g & 1)) + 8 (g >> 1) .. + 8, of
+// one of them: one 16 B store, 64 contiguous bytes per head and tuple pair.
+template <int O>
+__device__ __forceinline__ void store128_block(uint16_t* orow, bool ok, float fo, int g) {
+  f32x4 a[8];  // all eight tuples first: the reads are ordered asm, the arithmetic then overlaps
+  static_for<0, 8>([&](auto dc) { a[decltype(dc)::value] = acc128_read<32 * O + 4 * decltype(dc)::value>(); });
+  static_for<0, 4>([&](auto pc) {
+    constexpr int dt = 2 * decltype(pc)::value;
+    const f32x4 x = a[dt] * fo;
+    const f32x4 y = a[dt + 1] * fo;
+    const auto s0 = __builtin_amdgcn_permlane16_swap(bf16pair(x[0], x[1]), bf16pair(y[0], y[1]), false, false);
+    const auto s1 = __builtin_amdgcn_permlane16_swap(bf16pair(x[2], x[3]), bf16pair(y[2], y[3]), false, false);
+    const u32x4 v = u32x4{s0[0], s1[0], s0[1], s1[1]};
+    if (ok) *(u32x4*)(orow + 16 * (dt + (g & 1)) + 8 * (g >> 1)) = v;
+  });
+}
+
 template <bool NEG>
 __device__ __forceinline__ void smla_fwd128_body(const Params& p) {
   __shared__ __attribute__((aligned(16))) Smem128 sm;
 
-  int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int g = lane >> 4;
-  int li = lane & 15;
-
-  const int vb = xcd_remap(blockIdx.x, gridDim.x);
-  const int t = p.T - 1 - vb / p.head_groups;  // latest (heaviest) tokens first
-  const int hbase = (vb % p.head_groups) * 128;
-  int hs = hbase + 32 * w + li;  // S heads of this lane: hs and hs + 16
+  const int g = lane >> 4;
+  const int li = lane & 15;
+  const int nwg = gridDim.x, b = blockIdx.x;
+  const int units = p.T * p.head_groups;
 
   // exchange addresses (tile parity par: + par * the buffer size): P of head
   // block o at pbuf + 1024 o + 16 lane; the factor of head 16 o + li at
@@ -1136,156 +1233,179 @@ __device__ __forceinline__ void smla_fwd128_body(const Params& p) {
   const uint32_t pb_own = pb0 + 2048 * w;  // head blocks 2w, 2w + 1
   const uint32_t fac_own = fac0 + 8 * w;   // entries 8 li + 2w, + 1
   const uint32_t flag_own = flag0 + w;
+  const uint32_t wcnt = lds_addr(sm.wcnt);
 
   // logits c * S with c > 0: a negative scale is carried by q (negation is exact)
   const float c = NEG ? -p.scale_log2 : p.scale_log2;
   const float inv_c = 1.f / c;
-  Soft128 ss;
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    ss.l_part[hb] = 0.f;
-    ss.nmu[hb] = 0.f;
-    ss.thr[hb] = -INFINITY;
-  }
-  const int32_t* trow = p.topk + (size_t)t * p.topk_n;
-  // the first segment's entries are loaded ahead of q, so that its compaction
-  // does not wait for q (loads land in issue order)
-  SegmentRaw<4, k128Cap> raw0;
-  const int len0 = min(k128Cap, p.topk_n);
-  compact_load(raw0, len0 > 0 ? trow : (const int32_t*)(const void*)p.q, len0, lane, w);  // q: any valid address
-  bf16x8 qf[2][16];
-  load_q_any(qf[0], p, t, hs, g);
-  load_q_any(qf[1], p, t, hs + 16, g);
-  acc128_claim_and_zero();  // while q is in flight
-
+  const int len = p.topk_n;  // <= k128Cap: one segment per unit
+  auto trow_of = [&](int t) {  // any valid address when there are no entries
+    return len > 0 ? p.topk + (size_t)t * len : (const int32_t*)(const void*)p.q;
+  };
+  auto token_of = [&](int v) { return p.T - 1 - v / p.head_groups; };
+  auto hbase_of = [&](int v) { return (v % p.head_groups) * 128; };
   const uint16_t* kvp = p.kv;
-  Gather128 none;
-  none.active = false;
-  none.dst0 = none.alo = none.ahi = 0;
-  // first segment compacted outside the loop: a wait at the loop's join would
-  // otherwise cover q as well
-  int n = compact_finish<4>(raw0, len0, p.nkv, sm, lane, w);
-  for (int seg0 = 0; seg0 < p.topk_n; seg0 += k128Cap) {
-    if (seg0 > 0) {
-      lds_barrier();  // previous segment's list, tiles and exchange fully consumed
-      const int len = min(k128Cap, p.topk_n - seg0);
-      compact_load(raw0, trow + seg0, len, lane, w);
-      n = compact_finish<4>(raw0, len, p.nkv, sm, lane, w);
-    }
+
+  // first unit: its entries, q, the next unit's entries; compaction waits for
+  // the first four loads only (loads land in issue order)
+  const Sched128 sched(b, nwg, units);  // K >= 1: the grid is no larger than the units
+  int v = sched.unit(0);
+  int t = token_of(v), hbase = hbase_of(v);
+  raw128_dma(lds_addr(sm.list[0]), trow_of(t), len, lane, w);
+  bf16x8 qf[2][16];
+  load_q_any(qf[0], p, t, hbase + 32 * w + li, g);
+  load_q_any(qf[1], p, t, hbase + 32 * w + 16 + li, g);
+  const bool two = sched.K > 1;
+  if (two) raw128_dma(lds_addr(sm.list[1]), trow_of(token_of(sched.unit(1))), len, lane, w);
+  acc128_claim_and_zero();
+  // issued: 4 list loads, 32 q loads (, 4 loads of the next list)
+  if (two) asm volatile("s_waitcnt vmcnt(36)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+  int n = compact128(lds_addr(sm.list[0]), len, p.nkv, wcnt, lane, w);
+#pragma unroll
+  for (int i = 0; i < k128Ahead; ++i)
+    gather128(sm.list[0], i, n, i < (n + kBK - 1) / kBK, sm.tile(i), kvp, lane, w).all(lane);
+
+  Soft128 ss;
+  for (int r = 0;; ++r) {
+    // unit v (token t, heads hbase ..): list r & 1 compacted (n entries), its
+    // tiles 0..2 and q issued
+    const int32_t* lst = sm.list[r & 1];
     const int nt = (n + kBK - 1) / kBK;
-    if (nt == 0) continue;
+    const bool more = r + 1 < sched.K;
+    const int vn = more ? sched.unit(r + 1) : 0;
+    const int tn = more ? token_of(vn) : 0, hbn = more ? hbase_of(vn) : 0;
 #pragma unroll
-    for (int i = 0; i < k128Ahead; ++i) gather128(sm.list, i, n, i < nt, sm.tile(i), kvp, lane, w).all(lane);
-    if constexpr (NEG) {  // after the gathers are issued: this waits for q
-      if (seg0 == 0) {
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-          for (int k = 0; k < 16; ++k)
-            qf[hb][k] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, qf[hb][k]) ^ 0x80008000u);
-      }
+    for (int hb = 0; hb < 2; ++hb) {
+      ss.l_part[hb] = 0.f;
+      ss.nmu[hb] = 0.f;
+      ss.thr[hb] = -INFINITY;
     }
-    // tiles 0 and 1 landed (tile 2 may be in flight)
-    wait_vmcnt_le(2 < nt ? kBK / 4 : 0);
+    // the sinks of this lane's two heads, loaded here so that the boundary
+    // does not wait for them behind the next q
+    float sk[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int head = hbase + 32 * w + 16 * hb + li;
+      sk[hb] = (p.sink != nullptr && head < p.H) ? p.sink[head] : -INFINITY;
+    }
+    wait_vmcnt_le(0);  // q and tiles 0..2 (and the previous unit's stores)
+    asm volatile("" : "+v"(sk[0]), "+v"(sk[1]));
     lds_barrier();
-    f32x4 s[2][2];
-    // S(0), its softmax (P(0) in parity 0), S(1)
-    phase_y128(k_frag_addr(sm.tile(0), g, li), qf, s, none, lane);
-    if (nt > 1) {
-      soft128_plain<false>(s, ss, c, inv_c, kBK, g, pb_own, fac_own, flag_own);
-      phase_y128(k_frag_addr(sm.tile(1), g, li), qf, s, none, lane);
-    } else {
-      soft128_plain<true>(s, ss, c, inv_c, tile_rows(0, n), g, pb_own, fac_own, flag_own);
+    if constexpr (NEG) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          qf[hb][k] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, qf[hb][k]) ^ 0x80008000u);
     }
-    lds_barrier();  // P(0) visible
-    // Iteration j: phase X accumulates P.V(j) with the softmax of tile j+1
-    // between its MFMAs; one barrier (P(j+1) and tile j+2 visible, tile j-1
-    // free); phase Y computes S(j+2) and gathers tile j+3 into tile j-1's slot,
-    // and issues the first reads of phase X(j+1) behind its last MFMA.
+    f32x4 s[2][2];
     XPre xp;
-    x_prefetch(xp, sm.list, k128Ahead, lane, w, flag0, pb0, v_frag_addr(sm.tile(0), g, li) + 256 * w);
-    for (int j = 0; j < nt; ++j) {
+    // phase X of tile j: accumulates P.V(j); SOFT: with the softmax of tile
+    // j + 1 between its MFMAs (MASK: tile j + 1 is the partial last one)
+    auto phase_x = [&](int j, auto soft, auto mask) {
       const uint32_t par = j & 1, nxt = par ^ 1;
       const uint32_t vrow = v_frag_addr(sm.tile(j % k128Ring), g, li) + 256 * w;
       const uint32_t pbase = pb0 + kPbPar * par, fac_rd = fac0 + kFacPar * par;
       const uint32_t pbw = pb_own + kPbPar * nxt, facw = fac_own + kFacPar * nxt, flagw = flag_own + kFlagPar * nxt;
-      if (j + 2 < nt)  // tile j + 1 is full: only the last tile of a segment is partial
-        phase_x128<true, false>(xp, vrow, pbase, fac_rd, s, ss, c, inv_c, kBK, g, pbw, facw, flagw);
-      else if (j + 1 < nt)
-        phase_x128<true, true>(xp, vrow, pbase, fac_rd, s, ss, c, inv_c, tile_rows(j + 1, n), g, pbw, facw, flagw);
-      else
-        phase_x128<false, false>(xp, vrow, pbase, fac_rd, s, ss, c, inv_c, kBK, g, pbw, facw, flagw);
-      const uint32_t e = xp.e;  // list entry of tile j + 3 (completed in phase X)
-      wait_vmcnt_le(0);         // tile j + 2 landed (issued in phase Y of iteration j - 1)
-      lds_barrier();
-      if (j + 1 >= nt) break;
-      // the reads phase X(j+1) starts with: tile j+1, P(j+1), the flags of tile j+1
-      const uint32_t vrow1 = v_frag_addr(sm.tile((j + 1) % k128Ring), g, li) + 256 * w;
-      auto pre = [&]() {
-        x_prefetch(xp, sm.list, j + 1 + k128Ahead, lane, w, flag0 + kFlagPar * nxt, pb0 + kPbPar * nxt, vrow1);
-      };
-      if (j + 2 < nt) {
-        const bool gnext = j + k128Ahead < nt;
-        const Gather128 ga =
-            gather128_make(e, j + k128Ahead, n, gnext, sm.tile((j + k128Ahead) % k128Ring), kvp, lane, w);
-        phase_y128(k_frag_addr(sm.tile((j + 2) % k128Ring), g, li), qf, s, ga, lane, pre);
+      phase_x128<decltype(soft)::value, decltype(mask)::value>(xp, vrow, pbase, fac_rd, s, ss, c, inv_c,
+                                                              decltype(mask)::value ? tile_rows(j + 1, n) : kBK, g,
+                                                              pbw, facw, flagw);
+    };
+    // the first reads of phase X(j): tile j, P(j), the flags of tile j, and
+    // the list entry of the gather of tile j + 3
+    auto prefetch_x = [&](int j) {
+      const uint32_t par = j & 1;
+      x_prefetch(xp, lst, j + k128Ahead, lane, w, flag0 + kFlagPar * par, pb0 + kPbPar * par,
+                 v_frag_addr(sm.tile(j % k128Ring), g, li) + 256 * w);
+    };
+    if (nt > 0) {
+      const NoGather none;
+      // S(0), its softmax (P(0) in parity 0), S(1)
+      phase_y128(k_frag_addr(sm.tile(0), g, li), qf, s, none, lane);
+      if (nt > 1) {
+        soft128_plain<false>(s, ss, c, inv_c, kBK, g, pb_own, fac_own, flag_own);
+        phase_y128(k_frag_addr(sm.tile(1), g, li), qf, s, none, lane);
       } else {
-        pre();
+        soft128_plain<true>(s, ss, c, inv_c, tile_rows(0, n), g, pb_own, fac_own, flag_own);
+      }
+      lds_barrier();  // P(0) visible
+      prefetch_x(0);
+      // Iteration j: phase X(j) with the softmax of tile j+1 (full) between
+      // its MFMAs; one barrier (P(j+1) and tile j+2 visible, tile j-1 free);
+      // phase Y computes S(j+2) and gathers tile j+3 into tile j-1's slot, and
+      // issues the first reads of phase X(j+1) behind its last MFMA.
+      for (int j = 0; j + 2 < nt; ++j) {
+        phase_x(j, std::true_type{}, std::false_type{});
+        const uint32_t e = xp.e;  // list entry of tile j + 3 (completed in phase X)
+        wait_vmcnt_le(0);         // tile j + 2 landed (issued in phase Y of iteration j - 1)
+        lds_barrier();
+        const Gather128 ga = gather128_make(e, j + k128Ahead, n, j + k128Ahead < nt,
+                                            sm.tile((j + k128Ahead) % k128Ring), kvp, lane, w);
+        phase_y128(k_frag_addr(sm.tile((j + 2) % k128Ring), g, li), qf, s, ga, lane, [&]() { prefetch_x(j + 1); });
       }
     }
-  }
+    // every S of this unit is done: q of the next unit (this unit's again for
+    // the last, unused) lands under the last two phases X and the boundary
+    load_q_any(qf[0], p, more ? tn : t, (more ? hbn : hbase) + 32 * w + li, g);
+    load_q_any(qf[1], p, more ? tn : t, (more ? hbn : hbase) + 32 * w + 16 + li, g);
+    if (nt > 1) {  // X(nt - 2) with the softmax of the last tile; nothing more to wait for
+      phase_x(nt - 2, std::true_type{}, std::true_type{});
+      lds_barrier();
+      prefetch_x(nt - 1);
+    }
+    if (nt > 0) {
+      phase_x(nt - 1, std::false_type{}, std::false_type{});
+      lds_barrier();
+    }
 
-  // ---- finalise: fold the sink, normalise, stage the 128 rows, store ----
-  // lane-derived addresses are recomputed here rather than kept live across
-  // the loop (a value kept there could land in the accumulators' AGPRs)
-  {
-    int ln;
-    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
-    lane = ln;
-  }
-  g = lane >> 4;
-  li = lane & 15;
-  hs = hbase + 32 * w + li;
-  float oscale[2];
+    // ---- unit boundary: lse and output scales of this unit; the next unit's
+    // list compacted and its first tiles issued; this unit's rows stored ----
+    {
+      const int hs = hbase + 32 * w + li;
+      float oscale[2];
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    const int head = hs + 16 * hb;
-    const float sk = (p.sink != nullptr && head < p.H) ? p.sink[head] : -INFINITY;
-    const bool has_sink = !(sk == -INFINITY);
-    const HeadEnd he = head_end(ss.l_part[hb], ss.m_ref(hb), sk, has_sink, sk * kLog2e);
-    if (g == 0 && head < p.H) p.lse[(size_t)t * p.H + head] = he.lse;
-    oscale[hb] = he.oscale;
-  }
-  const uint32_t osc_own = lds_addr(sm.osc) + 32 * li + 8 * w;
-  if (g == 0) {
-    *(LDS_AS float*)(uintptr_t)(osc_own) = oscale[0];
-    *(LDS_AS float*)(uintptr_t)(osc_own + 4) = oscale[1];
-  }
-  lds_barrier();  // every wave is done with the tiles; output scales visible
-  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");  // MFMA write -> accumulator read distance
-  u32x4 f0 = ds_read_b128<0>(lds_addr(sm.osc) + 32 * li);
-  u32x4 f1 = ds_read_b128<16>(lds_addr(sm.osc) + 32 * li);
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f0), "+v"(f1));
-  // row 16 o + li of the staging, bytes 2 (128 w + 16 dt + 4 g)
-  const uint32_t st = sm.tile(0) + 256 * w + 8 * g + li * kRowStride;
-  static_for<0, 8>([&](auto oc) {
-    constexpr int o = decltype(oc)::value;
-    const float fo = __uint_as_float(o < 4 ? f0[o] : f1[o - 4]);
-    static_for<0, 8>([&](auto dc) {
-      constexpr int dt = decltype(dc)::value;
-      const f32x4 v = acc128_read<32 * o + 4 * dt>() * fo;
-      const bf16x4 v4 = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-      *(LDS_AS bf16x4*)(uintptr_t)(st + 16 * o * kRowStride + 32 * dt) = v4;
-    });
-  });
-  lds_barrier();  // all 128 rows staged
-  // wave w stores rows 32 w .. 32 w + 31: lane L writes bytes [16 L, 16 L + 16) of each
-#pragma unroll 8
-  for (int r = 0; r < 32; ++r) {
-    const int row = 32 * w + r;
-    const int hr = hbase + row;
-    const u32x4 val = *(LDS_AS const u32x4*)(uintptr_t)(sm.tile(0) + row * kRowStride + 16 * lane);
-    if (hr < p.H) __builtin_nontemporal_store(val, (u32x4*)(p.out + ((size_t)t * p.H + hr) * kD + 8 * lane));
+      for (int hb = 0; hb < 2; ++hb) {
+        const int head = hs + 16 * hb;
+        const bool has_sink = !(sk[hb] == -INFINITY);
+        const HeadEnd he = head_end(ss.l_part[hb], ss.m_ref(hb), sk[hb], has_sink, sk[hb] * kLog2e);
+        if (g == 0 && head < p.H) p.lse[(size_t)t * p.H + head] = he.lse;
+        oscale[hb] = he.oscale;
+      }
+      const uint32_t osc_own = lds_addr(sm.osc) + 32 * li + 8 * w;
+      if (g == 0) {
+        *(LDS_AS float*)(uintptr_t)(osc_own) = oscale[0];
+        *(LDS_AS float*)(uintptr_t)(osc_own + 4) = oscale[1];
+      }
+    }
+    // output scales visible after the first barrier of the compaction
+    const int nn = more ? compact128(lds_addr(sm.list[(r + 1) & 1]), len, p.nkv, wcnt, lane, w) : 0;
+    if (!more) lds_barrier();
+    u32x4 f0 = ds_read_b128<0>(lds_addr(sm.osc) + 32 * li);
+    u32x4 f1 = ds_read_b128<16>(lds_addr(sm.osc) + 32 * li);
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f0), "+v"(f1));
+    asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");  // MFMA write -> accumulator read distance
+    {
+      uint16_t* orow = p.out + ((size_t)t * p.H + hbase + li) * kD + 128 * w;
+      static_for<0, 8>([&](auto oc) {
+        constexpr int o = decltype(oc)::value;
+        const float fo = __uint_as_float(o < 4 ? f0[o] : f1[o - 4]);
+        store128_block<o>(orow + (size_t)16 * o * kD, hbase + 16 * o + li < p.H, fo, g);
+      });
+    }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < k128Ahead; ++i)
+        gather128(sm.list[(r + 1) & 1], i, nn, i < (nn + kBK - 1) / kBK, sm.tile(i), kvp, lane, w).all(lane);
+      if (r + 2 < sched.K)  // into this unit's list buffer, read no more
+        raw128_dma(lds_addr(sm.list[r & 1]), trow_of(token_of(sched.unit(r + 2))), len, lane, w);
+    }
+    acc128_claim_and_zero();
+    if (!more) break;
+    v = vn;
+    t = tn;
+    hbase = hbn;
+    n = nn;
   }
 }
 
@@ -1699,14 +1819,13 @@ constexpr int kR16Cap = 512;
 // The one-workgroup-per-token kernel for more than 64 heads (smla_fwd128_kernel)
 // is not yet faster than two 64-head workgroups per token of the D-split
 // kernel, so the latter is dispatched.
-constexpr bool kFwd128 = false;
+constexpr bool kFwd128 = true;
 
 Variant pick_variant(int64_t H, int64_t topk, bool fp8) {
-  (void)topk;
   if (H <= 16 && !fp8) return {1, "smla_fwd16_kernel<1, 512>"};
   if (H <= 16) return {1, "smla_fwd16_fp8_kernel<2, 512>"};
   if (H <= 32) return {2, fp8 ? "smla_fwd_fp8_kernel<2, 2>" : "smla_fwd_kernel<2, 2>"};
-  if (!fp8) return {4, (H > 64 && kFwd128) ? "smla_fwd128_kernel" : "smla_fwd_kernel<4, 2>"};
+  if (!fp8) return {4, (H > 64 && kFwd128 && topk <= k128Cap) ? "smla_fwd128_kernel" : "smla_fwd_kernel<4, 2>"};
   if (H <= 64) return {4, "smla_fwd_fp8_kernel<4, 4>"};
   return {8, "smla_fwd_fp8_kernel<8, 4>"};
 }
@@ -1768,6 +1887,19 @@ int check_args(const void* q, const void* kv, const void* topk_indices, size_t i
   if (!aligned(lse, 4) || (topk_indices && !aligned(topk_indices, idx_align)) || (attn_sink && !aligned(attn_sink, 4)))
     return SMLA_ERR_MISALIGNED;
   return SMLA_OK;
+}
+
+// Compute units of device dev, looked up once: the grid of a persistent
+// kernel (any positive grid is correct; more than one workgroup per CU only
+// queues).
+int cu_count(int dev) {
+  static std::atomic<int> cache[64];
+  if (dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 // Enqueue the forward for int32 top-k rows (arguments already checked, T > 0).
@@ -1843,12 +1975,14 @@ int run_prefill(const void* q, const void* kv, const int32_t* topk_indices, cons
       (void)hipGetLastError();
     }
   }
-  if (kFwd128 && H > 64 && !fp8) {
+  if (kFwd128 && H > 64 && !fp8 && topk <= k128Cap) {
     p.head_groups = (int)((H + 127) / 128);
+    const int64_t units128 = T * p.head_groups;
+    const unsigned grid = (unsigned)std::min<int64_t>(units128, cu_count(dev));  // persistent
     if (p.scale_log2 < 0.f)
-      hipLaunchKernelGGL(smla_fwd128_kernel<true>, dim3((unsigned)(T * p.head_groups)), dim3(256), 0, s, p);
+      hipLaunchKernelGGL(smla_fwd128_kernel<true>, dim3(grid), dim3(256), 0, s, p);
     else
-      hipLaunchKernelGGL(smla_fwd128_kernel<false>, dim3((unsigned)(T * p.head_groups)), dim3(256), 0, s, p);
+      hipLaunchKernelGGL(smla_fwd128_kernel<false>, dim3(grid), dim3(256), 0, s, p);
     return hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
   }
   if (H <= 16) {
