@@ -166,6 +166,15 @@ __device__ __forceinline__ void wait_vmcnt_le(int n) {
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// The lane index, computed where it is used (an asm the compiler cannot fold
+// into an earlier value): for code after a long loop, so that lane-derived
+// values need not stay live across it.
+__device__ __forceinline__ int fresh_lane_id() {
+  int ln;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+  return ln;
+}
+
 __device__ __forceinline__ int lane_rank(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }

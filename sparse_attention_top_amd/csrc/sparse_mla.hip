@@ -153,7 +153,8 @@ struct TileIssue8 {
     const bool valid = act && (lane & 31) < cnt;
     uint32_t e = 0;
     if (valid) {
-      asm volatile("ds_read_b32 %0, %1" : "=v"(e) : "v"(lds_addr(list + i * kBK + (lane & 31))));
+      // (the lane index recomputed: an address kept live from the start was spilled)
+      asm volatile("ds_read_b32 %0, %1" : "=v"(e) : "v"(lds_addr(list + i * kBK + (fresh_lane_id() & 31))));
     }
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(e));
     const uint8_t* row = valid ? uniform_ptr(kv) + ((uint64_t)e << 9) : uniform_ptr(kZeroRow8);
@@ -602,22 +603,25 @@ __device__ __forceinline__ void smla_fwd_body(const Params& p, const SplitArgs& 
   // o goes through LDS (row pitch kRowStride) so that each global store
   // writes one whole 1 KiB row per instruction. The sink is read only here,
   // so that its load latency is not on the way to the first tile.
-  const float sk = (p.sink != nullptr && head < p.H) ? p.sink[head] : -INFINITY;
+  // lane-derived values are recomputed here rather than kept live across the
+  // tile loop (where they would take registers, or be spilled)
+  const int lane_f = fresh_lane_id(), g_f = lane_f >> 4, li_f = lane_f & 15, head_f = head_base + li_f;
+  const float sk = (p.sink != nullptr && head_f < p.H) ? p.sink[head_f] : -INFINITY;
   const bool has_sink = !(sk == -INFINITY);
   const float sink_l2 = sk * kLog2e;
+  HeadEnd he = head_end(l_part, m_ref, sk, has_sink, sink_l2);
+  if constexpr (FP8) he.oscale *= p.out_scale;  // V == code * dequant scale
+  if (g_f == 0 && head_f < p.H) p.lse[(size_t)t * p.H + head_f] = he.lse;
   if constexpr (NW > 1) lds_barrier();  // all waves are done with the tiles
   const uint32_t ob = sm.stage() + (uint32_t)w * 16 * kRowStride;
   mfma_agpr_drain(acc);
-  HeadEnd he = head_end(l_part, m_ref, sk, has_sink, sink_l2);
-  if constexpr (FP8) he.oscale *= p.out_scale;  // V == code * dequant scale
-  if (g == 0 && head < p.H) p.lse[(size_t)t * p.H + head] = he.lse;
   if constexpr (DS) {
     // every wave scales its columns of all 64 heads by the owners' output scales
-    if (g == 0) *(LDS_AS float*)(uintptr_t)(fac_own) = he.oscale;
+    if (g_f == 0) *(LDS_AS float*)(uintptr_t)(lds_addr(sm.fac) + 16 * li_f + 4 * w) = he.oscale;
     lds_barrier();
-    u32x4 f = ds_read_b128<0>(fac_rd);
+    u32x4 f = ds_read_b128<0>(lds_addr(sm.fac) + 16 * li_f);
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f));
-    const uint32_t st = sm.stage() + 256 * w + 8 * g;  // row 16 o + li, bytes 2 (128 w + 16 dt + 4 g)
+    const uint32_t st = sm.stage() + 256 * w + 8 * g_f;  // row 16 o + li, bytes 2 (128 w + 16 dt + 4 g)
 #pragma unroll
     for (int o = 0; o < 4; ++o) {
       const float fo = __uint_as_float(f[o]);
@@ -625,7 +629,7 @@ __device__ __forceinline__ void smla_fwd_body(const Params& p, const SplitArgs& 
       for (int dt = 0; dt < 8; ++dt) {
         const f32x4 v = acc[8 * o + dt] * fo;
         const bf16x4 v4 = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-        *(LDS_AS bf16x4*)(uintptr_t)(st + (16 * o + li) * kRowStride + 32 * dt) = v4;
+        *(LDS_AS bf16x4*)(uintptr_t)(st + (16 * o + li_f) * kRowStride + 32 * dt) = v4;
       }
     }
     lds_barrier();  // the rows of every head staged
@@ -636,7 +640,7 @@ __device__ __forceinline__ void smla_fwd_body(const Params& p, const SplitArgs& 
     for (int dt = 0; dt < 32; ++dt) {
       const f32x4 o = acc[dt] * he.oscale;
       const bf16x4 ob4 = bf16x4{(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
-      *(LDS_AS bf16x4*)(uintptr_t)(ob + li * kRowStride + 32 * dt + 8 * g) = ob4;
+      *(LDS_AS bf16x4*)(uintptr_t)(ob + li_f * kRowStride + 32 * dt + 8 * g_f) = ob4;
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
@@ -644,8 +648,8 @@ __device__ __forceinline__ void smla_fwd_body(const Params& p, const SplitArgs& 
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int hr = head_base + r;
-    const u32x4 val = *(LDS_AS const u32x4*)(uintptr_t)(ob + r * kRowStride + 16 * lane);
-    if (hr < p.H) __builtin_nontemporal_store(val, (u32x4*)(p.out + ((size_t)t * p.H + hr) * kD + 8 * lane));
+    const u32x4 val = *(LDS_AS const u32x4*)(uintptr_t)(ob + r * kRowStride + 16 * lane_f);
+    if (hr < p.H) __builtin_nontemporal_store(val, (u32x4*)(p.out + ((size_t)t * p.H + hr) * kD + 8 * lane_f));
   }
 }
 
@@ -1712,11 +1716,11 @@ __device__ __forceinline__ void smla_fwd16_body(const Params& p) {
   const float sk = (p.sink != nullptr && head < p.H) ? p.sink[head] : -INFINITY;
   const bool has_sink = !(sk == -INFINITY);
   const float sink_l2 = sk * kLog2e;
-  const uint32_t ob = sm.stage();
-  mfma_agpr_drain(acc);
   HeadEnd he = head_end(l_part, m_ref, sk, has_sink, sink_l2);
   if constexpr (FP8) he.oscale *= p.out_scale;  // V == code * dequant scale
   if (g == 0 && head < p.H) p.lse[(size_t)t * p.H + head] = he.lse;
+  const uint32_t ob = sm.stage();
+  mfma_agpr_drain(acc);
 #pragma unroll
   for (int dt = 0; dt < 32; ++dt) {
     const f32x4 o = acc[dt] * he.oscale;

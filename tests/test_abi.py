@@ -54,6 +54,9 @@ def test_kernel_names():
     assert lib.sparse_mla_kernel_name(8, 64, 0) == lib.sparse_mla_kernel_name(16, 64, 0)
     assert lib.sparse_mla_kernel_name(64, 512, 0).startswith(b"smla_fwd_kernel<")
     assert lib.sparse_mla_kernel_name(128, 2048, 0) == b"smla_fwd_kernel<4, 2>"  # two 64-head groups
+    assert lib.sparse_mla_kernel_name(128, 1024, 0) == b"smla_fwd128_kernel"  # persistent, 128 heads per unit
+    assert lib.sparse_mla_kernel_name(96, 512, 0) == b"smla_fwd128_kernel"
+    assert lib.sparse_mla_kernel_name(64, 512, 0) == b"smla_fwd_kernel<4, 2>"
     assert lib.sparse_mla_kernel_name(16, 640, 0).startswith(b"smla_fwd16_kernel<")  # 16-row tiles at H <= 16
     assert lib.sparse_mla_kernel_name(16, 2048, 1).startswith(b"smla_fwd16_fp8_kernel<")
     assert lib.sparse_mla_kernel_name(128, 512, 1).startswith(b"smla_fwd_fp8_kernel<8,")

@@ -1,10 +1,14 @@
-"""Occupancy the forward kernels are designed for (CPU only: a device-only compile).
+"""Occupancy and register use the kernels are designed for (CPU only: device-only compiles).
 
 The speed of each variant rests on how many of its workgroups share a compute
 unit, which its LDS size and register count decide: the 16-row H <= 16 kernels
 at 19 KiB run eight per CU (two waves per SIMD), the four-wave D-split kernel two
-per CU. A few stray bytes of LDS silently cost a whole workgroup per CU, so the
-compiler's resource report is checked here.
+per CU, the persistent 128-head kernel one per CU at one wave per SIMD. A few
+stray bytes of LDS silently cost a whole workgroup per CU, and a register spill
+puts scratch traffic (sharing the memory counter with the gathers) into the
+loop, so the compiler's resource report is checked here: no kernel of the
+library may use scratch. The 128-head kernel keeps its accumulators by hand in
+the AGPR file; the compiler must not place any value of its own there.
 """
 
 import os
@@ -26,6 +30,8 @@ EXPECTED = {
     "smla_fwd_kernel<4, 2>": (2, 2),
     "smla_fwd_kernel<2, 2>": (2, 1),
     "smla_fwd_fp8_kernel<8, 4>": (1, 2),
+    "smla_fwd128_kernel<false>": (1, 1),
+    "smla_fwd128_kernel<true>": (1, 1),
 }
 
 MANGLED = {
@@ -34,17 +40,24 @@ MANGLED = {
     "smla_fwd_kernel<4, 2>": "15smla_fwd_kernelILi4ELi2EE",
     "smla_fwd_kernel<2, 2>": "15smla_fwd_kernelILi2ELi2EE",
     "smla_fwd_fp8_kernel<8, 4>": "smla_fwd_fp8_kernelILi8ELi4EE",
+    "smla_fwd128_kernel<false>": "smla_fwd128_kernelILb0EE",
+    "smla_fwd128_kernel<true>": "smla_fwd128_kernelILb1EE",
 }
+BWD = os.path.join(ROOT, "sparse_attention_top_amd", "csrc", "sparse_mla_bwd.hip")
 
 
-@pytest.fixture(scope="module")
-def resources(tmp_path_factory):
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "--cuda-device-only"]
+
+
+def _need_hipcc():
     if not os.path.exists(HIPCC) or shutil.which("ld.lld", path="/opt/rocm/llvm/bin") is None:
         pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("occ") / "fwd.o"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "--cuda-device-only", "-c", "-o", str(out), SRC,
-           "-Rpass-analysis=kernel-resource-usage"]
+
+
+def _report(src, out):
+    cmd = [HIPCC] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-c", "-o", str(out), src,
+                             "-Rpass-analysis=kernel-resource-usage"]
     proc = subprocess.run(cmd, capture_output=True, text=True)
     assert proc.returncode == 0, proc.stderr[-2000:]
     res, cur = {}, None
@@ -54,10 +67,23 @@ def resources(tmp_path_factory):
             cur = m.group(1)
             res[cur] = {}
             continue
-        m = re.search(r"remark:\s+(LDS Size \[bytes/block\]|Occupancy \[waves/SIMD\]|VGPRs|AGPRs): (\d+)", line)
+        m = re.search(r"remark:\s+(LDS Size \[bytes/block\]|Occupancy \[waves/SIMD\]|VGPRs|AGPRs|"
+                      r"ScratchSize \[bytes/lane\]|VGPRs Spill): (\d+)", line)
         if m and cur:
             res[cur][m.group(1)] = int(m.group(2))
     return res
+
+
+@pytest.fixture(scope="module")
+def resources(tmp_path_factory):
+    _need_hipcc()
+    return _report(SRC, tmp_path_factory.mktemp("occ") / "fwd.o")
+
+
+@pytest.fixture(scope="module")
+def resources_bwd(tmp_path_factory):
+    _need_hipcc()
+    return _report(BWD, tmp_path_factory.mktemp("occ") / "bwd.o")
 
 
 @pytest.mark.parametrize("kernel", sorted(EXPECTED))
@@ -71,3 +97,45 @@ def test_forward_kernel_occupancy(resources, kernel):
         kernel, lds, LDS_PER_CU // lds, wgs)
     assert r["Occupancy [waves/SIMD]"] >= waves, "%s: %d waves per SIMD, designed for %d" % (
         kernel, r["Occupancy [waves/SIMD]"], waves)
+
+
+def _own(res):
+    """The library's own kernels (library templates it instantiates are not checked)."""
+    return {k: v for k, v in res.items() if "smla_" in k}
+
+
+@pytest.mark.parametrize("which", ["forward", "backward"])
+def test_no_scratch(resources, resources_bwd, which):
+    res = _own(resources if which == "forward" else resources_bwd)
+    assert res
+    bad = {k: (v.get("ScratchSize [bytes/lane]"), v.get("VGPRs Spill")) for k, v in res.items()
+           if v.get("ScratchSize [bytes/lane]", 0) or v.get("VGPRs Spill", 0)}
+    assert not bad, "kernels using scratch (bytes per lane, VGPRs spilled): %s" % bad
+
+
+def test_fwd128_agprs_left_to_the_accumulators(tmp_path):
+    """In the 128-head kernel every AGPR operand must come from the hand-written
+    accumulator asm: an AGPR the compiler allocates (for a spill or a copy)
+    would overwrite an accumulator."""
+    _need_hipcc()
+    out = tmp_path / "fwd.s"
+    cmd = [HIPCC] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-S", "-o", str(out), SRC]
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    assert proc.returncode == 0, proc.stderr[-2000:]
+    text = out.read_text()
+    found = 0
+    for m in re.finditer(r"^(_Z\S*smla_fwd128_kernel\S*):", text, re.M):
+        found += 1
+        body = text[m.end():text.index("s_endpgm", m.end())]
+        in_asm, bad = False, []
+        for line in body.split("\n"):
+            if ";;#ASMSTART" in line:
+                in_asm = True
+            elif ";;#ASMEND" in line:
+                in_asm = False
+            elif not in_asm:
+                code = line.split(";")[0].strip()
+                if code and re.search(r"\ba\[?\d", code):
+                    bad.append(code)
+        assert not bad, "%s: compiler-generated AGPR operands: %s" % (m.group(1), bad[:5])
+    assert found == 2
