@@ -5,7 +5,11 @@ One step = one call of the forward over one synthetic batch (the whole path:
 top-k compaction, KV gather, both contractions, softmax, store). Inputs are
 resident in HBM before the timed region. Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wide|large|tp4|small|tiny]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload large|wide|tp4|small|tiny|...]
+
+The headline is the largest 128-head workload (large: T=8192, topk 1024);
+every other workload is a secondary entry with its own seed, input digest,
+warm and cold timings, roofline and CPU-oracle baseline.
 """
 
 from __future__ import annotations
@@ -29,20 +33,55 @@ D = 512
 
 
 def algorithmic(inp: dict) -> dict:
-    """Work the operation must do (valid slots only)."""
+    """Work the operation must do (valid slots only).
+
+    gathered_bytes is logical: one pool row per valid slot, most of them served
+    by L2 / MALL (window rows are shared by consecutive tokens). compulsory_bytes
+    is what must cross HBM at least once: q, o, lse, the indices, and every
+    referenced pool row once."""
     T, H, k = inp["T"], inp["H"], inp["topk_n"]
-    nvalid = int(((inp["topk"] >= 0) & (inp["topk"] < inp["num_kv"])).sum())
+    valid = (inp["topk"] >= 0) & (inp["topk"] < inp["num_kv"])
+    nvalid = int(valid.sum())
     flops = 4.0 * H * D * nvalid  # S = QK^T and O = PV, 2 flop per MAC each
     row = 512.0 if inp.get("kv_scale") is not None else 1024.0  # fp8 or bf16 pool row
     gathered = row * nvalid  # one pool row per valid slot (K == V)
     io = T * H * 1024.0 * 2 + T * H * 4.0 + T * k * 4.0  # q + o + lse + indices
-    return {"valid_slots": nvalid, "flops": flops, "gathered_bytes": gathered, "bytes": gathered + io}
+    rows = np.unique(inp["topk"][valid]).size
+    return {"valid_slots": nvalid, "flops": flops, "gathered_bytes": gathered, "bytes": gathered + io,
+            "compulsory_bytes": io + row * rows, "referenced_rows": int(rows)}
+
+
+def gpu_clock_sampler():
+    """Returns a function that samples the GPU's graphics clock (MHz) through
+    amdsmi, or None where amdsmi is not available."""
+    try:
+        import amdsmi
+
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception:
+        return None
+
+    def sample():
+        try:
+            v = amdsmi.amdsmi_get_gpu_metrics_info(h).get("current_gfxclk")
+            if isinstance(v, (int, float)) and 0 < v < 10000:
+                return float(v)
+        except Exception:
+            pass
+        try:
+            c = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
+            return float(c.get("clk"))
+        except Exception:
+            return None
+
+    return sample
 
 
 def source_digest() -> str:
     h = hashlib.sha256()
-    for rel in ("sparse_attention_top_amd/csrc/smla_common.h", "sparse_attention_top_amd/csrc/sparse_mla.hip",
-                "include/sparse_mla.h"):
+    for rel in ("sparse_attention_top_amd/csrc/smla_common.h", "sparse_attention_top_amd/csrc/smla_acc128.h",
+                "sparse_attention_top_amd/csrc/sparse_mla.hip", "include/sparse_mla.h"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -62,9 +101,10 @@ def traffic_from_profiles(kernel: str, workload: str):
     return None
 
 
-def time_gpu(run, steps, warmup, stream, flush=None):
+def time_gpu(run, steps, warmup, stream, flush=None, clock=None):
     """Warm (back-to-back) timing, or cold when `flush` is given: it runs before every
-    launch, outside the bracketing events. Returns wall seconds and per-launch stats (ms)."""
+    launch, outside the bracketing events. Returns wall seconds and per-launch stats (ms);
+    with a clock sampler, also the graphics clock under the same workload."""
     import torch
 
     for _ in range(warmup):
@@ -82,8 +122,36 @@ def time_gpu(run, steps, warmup, stream, flush=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per_launch = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return wall, {"mean": float(np.mean(per_launch)), "median": float(np.median(per_launch)),
-                  "min": float(np.min(per_launch))}
+    st = {"mean": float(np.mean(per_launch)), "median": float(np.median(per_launch)),
+          "min": float(np.min(per_launch))}
+    if clock is not None:
+        st["gfx_clock_mhz"] = loaded_clock(run, clock)
+    return wall, st
+
+
+def loaded_clock(run, clock, seconds: float = 0.6, settle: float = 0.2):
+    """The graphics clock while the workload runs back to back (after the timed
+    region, so the sampling costs it nothing): amdsmi's current_gfxclk, which
+    the SMU refreshes every few tens of ms, sampled after `settle` seconds."""
+    import torch
+
+    mhz, t0 = [], time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        ev = torch.cuda.Event()
+        for _ in range(8):
+            run()
+        ev.record()
+        if time.perf_counter() - t0 >= settle and len(mhz) < 200:
+            v = clock()
+            if v is not None:
+                mhz.append(v)
+        while not ev.query():
+            time.sleep(0.001)
+    torch.cuda.synchronize()
+    if not mhz:
+        return None
+    return {"median": float(np.median(mhz)), "min": float(np.min(mhz)), "max": float(np.max(mhz)),
+            "samples": len(mhz), "source": "amdsmi current_gfxclk, workload running back to back"}
 
 
 def cpu_model():
@@ -96,32 +164,48 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(inp: dict, target_s: float = 15.0):
-    """The oracle, untuned, on the host cores over an evenly spaced token sample."""
+_ORACLE_THREADS = None
+
+
+def cpu_baseline(inp: dict, target_s: float = 15.0, threads: int = 0):
+    """The oracle, untuned, on the host cores (all of them, or `threads`) over an
+    evenly spaced token sample grown toward target_s of wall time; the whole call
+    when it fits. Reported in the workload's own unit (TFLOP/s for H > 16,
+    gathered GB/s for H <= 16) and as ms per call extrapolated to every token."""
     import oracle
 
+    global _ORACLE_THREADS
+    if _ORACLE_THREADS is None:
+        _ORACLE_THREADS = oracle.threads()  # before any single-thread run changes the default
+    nthr = threads if threads > 0 else _ORACLE_THREADS
     T = inp["T"]
-    n = max(1, min(T, 128))
+
+    def run(tokens):
+        t0 = time.perf_counter()
+        oracle.forward(inp["q"], inp["kv"], inp["topk"], inp["sink"], inp["scale"], tokens=tokens,
+                       want_exact=False, want_bf16=True, kv_scale=inp.get("kv_scale"), threads=nthr)
+        return time.perf_counter() - t0
+
+    n = max(1, min(T, 32 if nthr == 1 else 128))
     tokens = np.linspace(0, T - 1, n).round().astype(np.int64)
-    t0 = time.perf_counter()
-    oracle.forward(inp["q"], inp["kv"], inp["topk"], inp["sink"], inp["scale"], tokens=tokens,
-                   want_exact=False, want_bf16=True, kv_scale=inp.get("kv_scale"))
-    dt = time.perf_counter() - t0
+    dt = run(tokens)
     if dt < target_s / 4 and n < T:  # grow the sample toward the target wall time
         n = int(min(T, n * max(1.0, target_s / max(dt, 1e-3))))
         tokens = np.linspace(0, T - 1, n).round().astype(np.int64)
-        t0 = time.perf_counter()
-        oracle.forward(inp["q"], inp["kv"], inp["topk"], inp["sink"], inp["scale"], tokens=tokens,
-                       want_exact=False, want_bf16=True, kv_scale=inp.get("kv_scale"))
-        dt = time.perf_counter() - t0
-    nv = int(((inp["topk"][tokens] >= 0) & (inp["topk"][tokens] < inp["num_kv"])).sum())
-    flops = 4.0 * inp["H"] * D * nv
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
+        dt = run(tokens)
+    valid = (inp["topk"][tokens] >= 0) & (inp["topk"][tokens] < inp["num_kv"])
+    nv = int(valid.sum())
+    row = 512.0 if inp.get("kv_scale") is not None else 1024.0
+    if inp["H"] > 16:
+        value, unit = 4.0 * inp["H"] * D * nv / dt / 1e12, "TFLOP/s"
+    else:
+        value, unit = row * nv / dt / 1e9, "GB/s"
+    return {"value": value, "unit": unit, "cores": nthr, "kind": "oracle",
             "sample": "%d of %d tokens (evenly spaced), %d valid slots, %.2f s wall" % (len(tokens), T, nv, dt),
-            "ms_per_call_extrapolated": dt * 1e3 * inp["T"] / len(tokens), "cpu_model": cpu_model()}
+            "ms_per_call_extrapolated": dt * 1e3 * T / len(tokens), "cpu_model": cpu_model()}
 
 
-def measure(name: str, steps: int, warmup: int, cold_steps: int = 0, idx64: bool = False):
+def measure(name: str, steps: int, warmup: int, cold_steps: int = 0, idx64: bool = False, clock=None):
     import torch
 
     from sparse_attention_top_amd import kernel_name, sparse_mla_prefill, synth
@@ -143,15 +227,17 @@ def measure(name: str, steps: int, warmup: int, cold_steps: int = 0, idx64: bool
     def run():
         sparse_mla_prefill(q, kv, topk, sink, inp["scale"], out=out, lse=lse, kv_scale=kv_scale)
 
-    wall, st = time_gpu(run, steps, warmup, stream)
+    wall, st = time_gpu(run, steps, warmup, stream, clock=clock)
     alg = algorithmic(inp)
     t = {"wall_s": wall, "ms_per_call": wall * 1e3 / steps, "kernel_ms_mean": st["mean"],
          "kernel_ms_median": st["median"], "kernel_ms_min": st["min"],
          "kernel": kernel_name(inp["H"], inp["topk_n"], kv_scale is not None)}
+    if "gfx_clock_mhz" in st:
+        t["gfx_clock_mhz"] = st["gfx_clock_mhz"]
     # few (token, head group) units: the library splits each top-k row and merges (the split path's kernels)
     H, fp8 = inp["H"], kv_scale is not None
     nw = 1 if H <= 16 else 2 if H <= 32 else (8 if fp8 and H > 64 else 4)
-    units = inp["T"] * -(-H // (16 * nw))
+    units = inp["T"] * -(-H // (16 * nw))  # as the library counts them to choose the split path
     if units < torch.cuda.get_device_properties(dev).multi_processor_count and inp["topk_n"] >= 128:
         t["kernel"] = "smla_fwd%s_split_kernel<%d, %d> + smla_merge_kernel" % ("_fp8" if fp8 else "", nw,
                                                                               4 if fp8 and nw >= 4 else 2)
@@ -204,14 +290,56 @@ def measure_bwd(name: str, steps: int, warmup: int):
 
 
 def roofline(alg, t, kernel, workload, bound):
+    """The dominant kernel against its bound. MFMA-bound (H > 16): valid-slot flops
+    over the bf16 dense peak. Otherwise HBM: the compulsory bytes (q, o, lse,
+    indices, each referenced pool row once) over the HBM peak; the logical
+    gathered bytes, mostly L2/MALL hits, are reported apart as gathered_gbs."""
     if bound == "mfma":
         achieved = alg["flops"] / (t["kernel_ms_mean"] * 1e-3) / 1e12
-        peak, unit = PEAK_BF16_TFLOPS, "TFLOP/s"
+        peak, unit, what = PEAK_BF16_TFLOPS, "TFLOP/s", "4 H 512 flop per valid slot"
     else:
-        achieved = alg["bytes"] / (t["kernel_ms_mean"] * 1e-3) / 1e9
-        peak, unit = PEAK_HBM_GBS, "GB/s"
+        achieved = alg["compulsory_bytes"] / (t["kernel_ms_mean"] * 1e-3) / 1e9
+        peak, unit, what = PEAK_HBM_GBS, "GB/s", "compulsory HBM bytes: q + o + lse + indices + referenced rows once"
     return {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
-            "traffic": traffic_from_profiles(kernel, workload), "kernel": kernel}
+            "traffic": traffic_from_profiles(kernel, workload), "kernel": kernel, "work": what}
+
+
+def entry(name: str, steps: int, warmup: int, cold_steps: int, clock, cpu: bool, idx64: bool = False) -> dict:
+    """One workload: warm and cold timings, roofline, seed and input digest, CPU baseline."""
+    from sparse_attention_top_amd import synth
+
+    inp, alg, t = measure(name, steps, warmup, cold_steps=cold_steps, idx64=idx64, clock=clock)
+    cfg = inp["config"]
+    bound = "mfma" if inp["H"] > 16 else "hbm"
+    e = {"workload": name + (":int64" if idx64 else ""), "T": cfg.T, "H": cfg.H, "topk": cfg.topk,
+         "num_kv": cfg.num_kv, "seed": cfg.seed, "inputs_sha256": synth.fingerprint(inp)[:16],
+         "valid_slots": alg["valid_slots"], "steps": steps, "ms_per_call": t["ms_per_call"],
+         "kernel_ms_mean": t["kernel_ms_mean"], "kernel_ms_median": t["kernel_ms_median"],
+         "kernel_ms_min": t["kernel_ms_min"], "kernel": t["kernel"],
+         "tflops": alg["flops"] / (t["kernel_ms_mean"] * 1e-3) / 1e12,
+         "gathered_gbs": alg["gathered_bytes"] / (t["kernel_ms_mean"] * 1e-3) / 1e9,
+         "compulsory_gbs": alg["compulsory_bytes"] / (t["kernel_ms_mean"] * 1e-3) / 1e9,
+         "cold": t.get("cold"), "gfx_clock_mhz": t.get("gfx_clock_mhz"),
+         "roofline": roofline(alg, t, t["kernel"], name, bound)}
+    if inp.get("kv_scale") is not None:
+        e["pool"] = "fp8 e4m3 codes, per-tensor scale"
+    if idx64:
+        e["note"] = "int64 top-k rows: index conversion kernel + the int32 path"
+    if "split" in t["kernel"]:
+        e["note"] = ("few-token call: split-KV kernel + merge kernel; per-launch events include the "
+                     "host launch gap, rocprofv3 kernel time is the GPU figure")
+    if cpu and not idx64:
+        e["cpu_baseline"] = cpu_baseline(inp, target_s=2.0)
+        if name in ("tiny", "small"):
+            e["cpu_baseline_1thread"] = cpu_baseline(inp, target_s=2.0, threads=1)
+    return inp, alg, t, e
+
+
+# Secondary workloads: every other configuration of the benchmark, timed warm
+# (>= 50 launches, >= 200 for the sub-0.1 ms ones) and cold (each launch after
+# a 512 MiB overwrite), each with its own CPU-oracle baseline.
+SECONDARY = ("wide", "tp4", "small", "tiny", "glm", "decode", "tp4:int64", "tp4_fp8", "glm_fp8", "wide_fp8",
+             "wide_k1024")
 
 
 def main():
@@ -219,11 +347,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="wide", choices=["tiny", "small", "tp4", "wide", "large", "glm", "decode",
-                                                          "tp4_fp8", "wide_fp8", "glm_fp8", "wide_k1024", "long"])
+    ap.add_argument("--workload", default="large", choices=["tiny", "small", "tp4", "wide", "large", "glm", "decode",
+                                                           "tp4_fp8", "wide_fp8", "glm_fp8", "wide_k1024", "long"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timing of the main workload")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timings")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the clock sampling window (keeps the launch count fixed for profiling)")
     ap.add_argument("--bwd", action="store_true",
                     help="only time the backward on --workload and print its line (for profiling)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -251,27 +381,25 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": max(1, args.steps)}))
         return
 
-    from sparse_attention_top_amd import synth
-
     if args.bwd:
         print("bench: backward on %s, %d warmup + %d timed steps" % (args.workload, args.warmup, args.steps),
               file=sys.stderr, flush=True)
         print(json.dumps(measure_bwd(args.workload, args.steps, args.warmup)))
         return
 
+    clock = None if args.no_clock else gpu_clock_sampler()
     print("bench: workload %s, %d warmup + %d timed steps" % (args.workload, args.warmup, args.steps),
           file=sys.stderr, flush=True)
-    inp, alg, t = measure(args.workload, args.steps, args.warmup, cold_steps=0 if args.no_cold else min(args.steps, 20))
+    inp, alg, t = measure(args.workload, args.steps, args.warmup, cold_steps=0 if args.no_cold else min(args.steps, 20),
+                          clock=clock)
     bound = "mfma" if inp["H"] > 16 else "hbm"
     tflops = alg["flops"] / (t["ms_per_call"] * 1e-3) / 1e12
     gbs = alg["gathered_bytes"] / (t["ms_per_call"] * 1e-3) / 1e9
-    if bound == "mfma":
-        metric, value, unit = "sparse MLA prefill fwd TFLOPS (valid slots, H=%d)" % inp["H"], tflops, "TFLOP/s"
-    else:
-        metric, value, unit = "sparse MLA prefill fwd gathered-KV GB/s (H=%d)" % inp["H"], gbs, "GB/s"
+    metric = "sparse MLA prefill fwd TFLOPS (H=128) & gathered-KV GB/s (H=16), ms/call"
+    value, unit = (tflops, "TFLOP/s") if bound == "mfma" else (gbs, "GB/s")
     cfg = inp["config"]
-    if inp.get("kv_scale") is not None:
-        metric = metric + " [fp8 pool]"
+    from sparse_attention_top_amd import synth
+
     line = {
         "metric": metric,
         "value": value,
@@ -294,30 +422,26 @@ def main():
         "kernel_ms_median": t["kernel_ms_median"],
         "kernel_ms_min": t["kernel_ms_min"],
         "cold": t.get("cold"),
+        "gfx_clock_mhz": t.get("gfx_clock_mhz"),
         "roofline": roofline(alg, t, t["kernel"], cfg.name, bound),
     }
     print("bench: %s %.4f ms/call, %.1f TFLOP/s, %.1f GB/s gathered" % (cfg.name, t["ms_per_call"], tflops, gbs),
           file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle on a token sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(inp)
     if not args.no_secondary:
         sec = []
-        for other in ("tp4", "large", "small", "glm", "decode", "tp4:int64", "tp4_fp8", "glm_fp8", "wide_fp8"):
-            if other == args.workload:
-                continue
+        for other in SECONDARY:
             name2, _, kind = other.partition(":")
-            i2, a2, t2 = measure(name2, max(10, args.steps // 2), args.warmup, idx64=kind == "int64")
-            b2 = "mfma" if i2["H"] > 16 else "hbm"
-            sec.append({"workload": other, "ms_per_call": t2["ms_per_call"], "kernel_ms_mean": t2["kernel_ms_mean"],
-                        "kernel_ms_median": t2["kernel_ms_median"], "kernel_ms_min": t2["kernel_ms_min"],
-                        "tflops": a2["flops"] / (t2["ms_per_call"] * 1e-3) / 1e12,
-                        "gathered_gbs": a2["gathered_bytes"] / (t2["ms_per_call"] * 1e-3) / 1e9,
-                        "valid_slots": a2["valid_slots"],
-                        "roofline": roofline(a2, t2, t2["kernel"], other, b2)})
-            if kind == "int64":
-                sec[-1]["note"] = "int64 top-k rows: index conversion kernel + the int32 path"
-            if i2["T"] * -(-i2["H"] // 128) < 256:
-                sec[-1]["note"] = ("few-token call: split-KV kernel + merge kernel; per-launch events include the "
-                                   "host launch gap, rocprofv3 kernel time is the GPU figure")
-            print("bench: %s %.4f ms/call" % (other, t2["ms_per_call"]), file=sys.stderr, flush=True)
+            if name2 == args.workload and not kind:
+                continue
+            small = name2 in ("tiny", "small", "decode")
+            steps2 = max(200 if small else 50, args.steps)
+            _, _, _, e = entry(name2, steps2, args.warmup, 0 if args.no_cold else 10, clock,
+                               cpu=not args.no_cpu_baseline, idx64=kind == "int64")
+            sec.append(e)
+            print("bench: %s %.4f ms/call" % (other, e["kernel_ms_mean"]), file=sys.stderr, flush=True)
         for name in ("wide", "wide_k1024", "long", "tp4"):
             b = measure_bwd(name, max(10, args.steps // 2), args.warmup)
             sec.append(b)
@@ -325,9 +449,6 @@ def main():
                                                                              b["tflops_pages_formula"]),
                   file=sys.stderr, flush=True)
         line["secondary"] = sec
-    if not args.no_cpu_baseline:
-        print("bench: timing the CPU oracle on a token sample", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(line))
 
 

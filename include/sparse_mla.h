@@ -180,18 +180,37 @@ int sparse_mla_prefill_i64(const void* q, const void* kv, const int64_t* topk_in
  * H <= 128 (SMLA_ERR_BAD_SIZE above), num_kv < 2^31, T * round_up(topk, 32) < 2^31.
  *
  * Enqueued on `stream`. dkv is deterministic: each row sums its contributors
- * in (token, slot) order, with no atomics. The call takes stream-ordered
- * scratch from the library's per-device pool (the same pool as the forward's
- * split path) and returns it before the call's work ends: about
- * T * round_up(topk, 32) * (4 H + 1104) bytes plus the sort's workspace (wide
- * shape T=4096, H=128, topk=512: 3.4 GB); SMLA_ERR_NO_MEMORY if it cannot be
- * had, before any launch. The inverted index is a library radix sort that
- * clears its counters with hipMemsetAsync: do not capture this call into a
- * HIP graph.
+ * in (token, slot) order, with no atomics. The work runs in passes over
+ * consecutive tokens (the bound the page's R_CHUNK option serves, here over
+ * tokens: dq of a token is then complete within one pass); P, dS, the sort
+ * keys and the per-slot dkv terms exist for one pass at a time, about
+ * round_up(topk, 32) * (4 H + 1104) bytes per token of the pass. This entry
+ * point sizes the passes so that one pass's scratch stays under 4 GiB (one
+ * pass for T=4096, H=128, topk=512 at 3.4 GB; four for topk=1024 at T=8192);
+ * with more than one pass, dkv is summed in an fp32 accumulator of
+ * num_kv * 2 KiB and rounded to bf16 at the end (otherwise each row is rounded
+ * once from its fp32 sum directly). Scratch in all: the pass buffers, the sort's workspace, 4 T H +
+ * 4 (num_kv + 1) bytes and that accumulator, stream-ordered from the library's
+ * per-device pool (the forward's split path uses the same pool, which keeps at
+ * most 4.5 GiB between calls) and returned before the call's work ends;
+ * SMLA_ERR_NO_MEMORY if it cannot be had, before any launch. The inverted
+ * index is a library radix sort that clears its counters with hipMemsetAsync:
+ * do not capture this call into a HIP graph.
  */
 int sparse_mla_backward(const void* q, const void* kv, const void* dout, const void* o, const float* lse,
                         const int32_t* topk_indices, const float* attn_sink, float scale, void* dq, void* dkv,
                         float* d_sink, int64_t T, int64_t H, int64_t num_kv, int64_t topk, void* stream);
+
+/*
+ * sparse_mla_backward_chunked -- sparse_mla_backward with the pass size given:
+ * chunk_tokens > 0 tokens per pass (the last pass may be shorter), 0 as
+ * sparse_mla_backward chooses; SMLA_ERR_BAD_SIZE if negative. Same outputs up
+ * to the fp32 summation order of dkv across passes.
+ */
+int sparse_mla_backward_chunked(const void* q, const void* kv, const void* dout, const void* o, const float* lse,
+                                const int32_t* topk_indices, const float* attn_sink, float scale, void* dq, void* dkv,
+                                float* d_sink, int64_t T, int64_t H, int64_t num_kv, int64_t topk,
+                                int64_t chunk_tokens, void* stream);
 
 /* Human-readable text for a status code (static storage; never NULL). */
 const char* sparse_mla_status_string(int status);

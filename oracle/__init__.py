@@ -29,10 +29,11 @@ _lib = None
 
 
 def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (portable x86-64 code, OpenMP)."""
+    """Compile the oracle with gcc -O3 (portable x86-64 code: no -march, since the
+    library may run on another host; ISO C, so no floating-point contraction), OpenMP."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra",
+        cmd = ["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra",
                "-o", tmp, *_SRC, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)

@@ -94,14 +94,16 @@ def sparse_mla_prefill(q, kv, topk_indices, attn_sink=None, scale=None, out=None
     return out, lse
 
 
-def sparse_mla_backward(q, kv, dout, o, lse, topk_indices, attn_sink=None, scale=None):
+def sparse_mla_backward(q, kv, dout, o, lse, topk_indices, attn_sink=None, scale=None, chunk_tokens=None):
     """Gradients of ``sparse_mla_prefill``; returns ``(dq, dkv, d_sink)``.
 
     q, dout, o: bf16 [T, H, 512] (o and lse are the forward's outputs, lse
     sink-inclusive fp32 [T, H]); kv: bf16 [num_kv, 512]; topk_indices: int32
     [T, topk]; attn_sink: fp32 [H] or None (then d_sink is None); scale: float
     (default 1/sqrt(512)). H <= 128. dq and dkv come back bf16, d_sink fp32.
-    All tensors on the same GPU and contiguous; enqueued on the current stream.
+    chunk_tokens: tokens per pass (None: passes chosen so that one pass's
+    scratch stays under 4 GiB). All tensors on the same GPU and contiguous;
+    enqueued on the current stream.
     """
     import torch
 
@@ -128,18 +130,20 @@ def sparse_mla_backward(q, kv, dout, o, lse, topk_indices, attn_sink=None, scale
         _check(attn_sink.is_contiguous(), "attn_sink must be contiguous")
     if scale is None:
         scale = DEFAULT_SCALE
+    _check(chunk_tokens is None or int(chunk_tokens) >= 1, "chunk_tokens must be >= 1 (or None)")
     dq = torch.empty_like(q)
     dkv = torch.empty_like(kv)
     d_sink = torch.empty((H,), dtype=torch.float32, device=dev) if attn_sink is not None else None
     lib = _lib.load()
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        rc = lib.sparse_mla_backward(
+        rc = lib.sparse_mla_backward_chunked(
             q.data_ptr(), kv.data_ptr() if kv.numel() else None, dout.data_ptr(), o.data_ptr(), lse.data_ptr(),
             topk_indices.data_ptr() if topk_indices.numel() else None,
             attn_sink.data_ptr() if attn_sink is not None else None, float(scale),
             dq.data_ptr(), dkv.data_ptr() if dkv.numel() else None,
-            d_sink.data_ptr() if d_sink is not None else None, T, H, kv.shape[0], topk_indices.shape[1], stream)
+            d_sink.data_ptr() if d_sink is not None else None, T, H, kv.shape[0], topk_indices.shape[1],
+            int(chunk_tokens or 0), stream)
     if rc != 0:
         raise RuntimeError("sparse_mla_backward failed: %s (status %d)" % (_lib.status_string(rc), rc))
     return dq, dkv, d_sink

@@ -523,9 +523,12 @@ inline int cu_count(int dev) {
   return cache[dev];
 }
 
-// Stream-ordered scratch (the forward's split path, the backward) comes from a pool of our own per
-// device that keeps freed memory (its high-water mark) instead of handing it
-// back at every synchronisation.
+// Stream-ordered scratch (the forward's split path and int64 rows, the
+// backward) comes from a pool of our own per device that keeps up to
+// kPoolKeepBytes of freed memory between calls (so that repeated calls do not
+// map their scratch anew); memory above that returns to the device at the next
+// synchronisation.
+constexpr uint64_t kPoolKeepBytes = (uint64_t)9 << 29;  // 4.5 GiB
 inline hipMemPool_t scratch_pool(int dev) {
   static std::mutex mu;
   static hipMemPool_t pools[64];
@@ -542,7 +545,7 @@ inline hipMemPool_t scratch_pool(int dev) {
       (void)hipGetLastError();
       return nullptr;
     }
-    uint64_t keep = UINT64_MAX;
+    uint64_t keep = kPoolKeepBytes;
     (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
     pools[dev] = pool;
   }

@@ -20,7 +20,7 @@
 //   B2 smla_bwd_interm_kernel  one workgroup per token: the per-slot dkv
 //      contribution interm[t][j] = [scale dS ; P]^T [q ; dO], one MFMA
 //      contraction over heads (both terms side by side along K).
-//   B3 a stable radix sort of (row key, entry id) (hipcub) and the start of
+//   B3 a stable radix sort of (row key, entry id) (rocPRIM) and the start of
 //      each row's run: the scatter inverted, so each row gathers its own
 //      contributors in a fixed order (deterministic, no atomics).
 //   B4 smla_bwd_dkv_chunk_kernel / smla_bwd_dkv_fix_kernel: fixed 64-entry
@@ -29,7 +29,7 @@
 //      per-chunk partials in chunk order; rows nobody references get 0.
 //   B5 smla_bwd_dsink_kernel   fixed-order sum of the sink partials.
 
-#include <hipcub/hipcub.hpp>
+#include <rocprim/device/device_radix_sort.hpp>
 
 #include "smla_common.h"
 
@@ -453,14 +453,24 @@ __global__ __launch_bounds__(256) void smla_bwd_rowstart_kernel(const uint32_t* 
 // that spans chunks c0 .. c1 as tail[c0] + head[c0 + 1] + ... + head[c1], in
 // that order, and zero-fills rows no slot holds. The order of every sum is
 // fixed by the sort, so dkv is deterministic.
+// With token passes (acc != NULL), each pass adds its row sums to an fp32
+// accumulator instead (every row is touched by one wave per pass, passes run in
+// token order), and smla_bwd_dkv_out_kernel rounds it to bf16 at the end.
 constexpr int kChunk = 64;
 
 __device__ __forceinline__ void dkv_flush(const float (&a)[8], uint32_t r, uint32_t s0, uint32_t s1,
                                           const uint32_t* __restrict__ row_start, uint16_t* __restrict__ dkv,
-                                          float* __restrict__ head, float* __restrict__ tail, uint32_t c, int lane) {
+                                          float* __restrict__ acc, float* __restrict__ head, float* __restrict__ tail,
+                                          uint32_t c, int lane) {
   const bool before = row_start[r] < s0;
   const bool after = row_start[r + 1] > s1;
   if (!before && !after) {
+    if (acc != nullptr) {
+      f32x4* dst = (f32x4*)(acc + (size_t)r * kD + 8 * lane);
+      dst[0] += f32x4{a[0], a[1], a[2], a[3]};
+      dst[1] += f32x4{a[4], a[5], a[6], a[7]};
+      return;
+    }
     *(bf16x8*)(dkv + (size_t)r * kD + 8 * lane) = bf16x8{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3],
                                                          (__bf16)a[4], (__bf16)a[5], (__bf16)a[6], (__bf16)a[7]};
   } else {
@@ -474,8 +484,9 @@ __global__ __launch_bounds__(256) void smla_bwd_dkv_chunk_kernel(const uint32_t*
                                                                  const uint32_t* __restrict__ sval,
                                                                  const uint32_t* __restrict__ row_start,
                                                                  const uint16_t* __restrict__ interm,
-                                                                 uint16_t* __restrict__ dkv, float* __restrict__ head,
-                                                                 float* __restrict__ tail, uint32_t num_kv) {
+                                                                 uint16_t* __restrict__ dkv, float* __restrict__ acc,
+                                                                 float* __restrict__ head, float* __restrict__ tail,
+                                                                 uint32_t num_kv) {
   const int lane = threadIdx.x & 63;
   const uint32_t c = blockIdx.x * 4 + (threadIdx.x >> 6);
   const uint32_t nv = row_start[num_kv];  // entries with a valid key
@@ -497,7 +508,7 @@ __global__ __launch_bounds__(256) void smla_bwd_dkv_chunk_kernel(const uint32_t*
     for (int u = 0; u < 4; ++u) {
       if (e + u >= e1) break;
       if (rk[u] != cur) {
-        dkv_flush(a, cur, seg, e + u, row_start, dkv, head, tail, c, lane);
+        dkv_flush(a, cur, seg, e + u, row_start, dkv, acc, head, tail, c, lane);
         cur = rk[u];
         seg = e + u;
 #pragma unroll
@@ -508,20 +519,20 @@ __global__ __launch_bounds__(256) void smla_bwd_dkv_chunk_kernel(const uint32_t*
       for (int i = 0; i < 8; ++i) a[i] += (float)v[i];
     }
   }
-  dkv_flush(a, cur, seg, e1, row_start, dkv, head, tail, c, lane);
+  dkv_flush(a, cur, seg, e1, row_start, dkv, acc, head, tail, c, lane);
 }
 
 __global__ __launch_bounds__(256) void smla_bwd_dkv_fix_kernel(const uint32_t* __restrict__ row_start,
                                                                const float* __restrict__ head,
                                                                const float* __restrict__ tail, uint16_t* __restrict__ dkv,
-                                                               int64_t num_kv) {
+                                                               float* __restrict__ acc, int64_t num_kv) {
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= num_kv) return;
   const uint32_t s0 = row_start[r], s1 = row_start[r + 1];
   uint16_t* dst = dkv + r * kD + 8 * lane;
   if (s0 == s1) {
-    *(u32x4*)dst = u32x4{0u, 0u, 0u, 0u};
+    if (acc == nullptr) *(u32x4*)dst = u32x4{0u, 0u, 0u, 0u};
     return;
   }
   const uint32_t c0 = s0 / kChunk, c1 = (s1 - 1) / kChunk;
@@ -532,8 +543,26 @@ __global__ __launch_bounds__(256) void smla_bwd_dkv_fix_kernel(const uint32_t* _
     lo += *(const f32x4*)(head + (size_t)c * kD + 8 * lane);
     hi += *(const f32x4*)(head + (size_t)c * kD + 8 * lane + 4);
   }
+  if (acc != nullptr) {
+    f32x4* a = (f32x4*)(acc + r * kD + 8 * lane);
+    a[0] += lo;
+    a[1] += hi;
+    return;
+  }
   *(bf16x8*)dst = bf16x8{(__bf16)lo[0], (__bf16)lo[1], (__bf16)lo[2], (__bf16)lo[3],
                          (__bf16)hi[0], (__bf16)hi[1], (__bf16)hi[2], (__bf16)hi[3]};
+}
+
+// dkv = bf16(acc), after the last token pass
+__global__ __launch_bounds__(256) void smla_bwd_dkv_out_kernel(const float* __restrict__ acc,
+                                                              uint16_t* __restrict__ dkv, int64_t num_kv) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= num_kv) return;
+  const f32x4 lo = *(const f32x4*)(acc + r * kD + 8 * lane);
+  const f32x4 hi = *(const f32x4*)(acc + r * kD + 8 * lane + 4);
+  *(bf16x8*)(dkv + r * kD + 8 * lane) = bf16x8{(__bf16)lo[0], (__bf16)lo[1], (__bf16)lo[2], (__bf16)lo[3],
+                                              (__bf16)hi[0], (__bf16)hi[1], (__bf16)hi[2], (__bf16)hi[3]};
 }
 
 // ---- B5: d_sink[h] = -sum_t part[t][h], in a fixed order ----
@@ -562,13 +591,25 @@ int bwd_nw(int64_t H) { return H <= 16 ? 1 : (H <= 32 ? 2 : 4); }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-}  // namespace
+// The library's radix sort with its onesweep form for every size past one
+// block: by default it merge-sorts up to 2^20 pairs, which measured 2.7x
+// slower per pair than onesweep on the pass sizes used here (wide, two passes
+// of 2^20 pairs each: 287 vs 107 us per call).
+using SortConfig = rocprim::radix_sort_config<rocprim::default_config, rocprim::default_config,
+                                              rocprim::default_config, 4096>;
+hipError_t sort_pairs(void* tmp, size_t& bytes, const uint32_t* kin, uint32_t* kout, const uint32_t* vin,
+                      uint32_t* vout, int n, int end_bit, hipStream_t s) {
+  return rocprim::radix_sort_pairs<SortConfig>(tmp, bytes, kin, kout, vin, vout, n, 0u, (unsigned)end_bit, s);
+}
 
-extern "C" int sparse_mla_backward(const void* q, const void* kv, const void* dout, const void* o, const float* lse,
-                                   const int32_t* topk_indices, const float* attn_sink, float scale, void* dq,
-                                   void* dkv, float* d_sink, int64_t T, int64_t H, int64_t num_kv, int64_t topk,
-                                   void* stream) {
-  if (T < 0 || H < 1 || num_kv < 0 || topk < 0) return SMLA_ERR_BAD_SIZE;
+// Scratch of one token pass, at most (unless one token alone needs more): the
+// passes are chosen so that T_pass * per-token bytes stays below it.
+constexpr size_t kBwdPassBytes = (size_t)4 << 30;
+
+int run_backward(const void* q, const void* kv, const void* dout, const void* o, const float* lse,
+                 const int32_t* topk_indices, const float* attn_sink, float scale, void* dq, void* dkv, float* d_sink,
+                 int64_t T, int64_t H, int64_t num_kv, int64_t topk, int64_t chunk_tokens, void* stream) {
+  if (T < 0 || H < 1 || num_kv < 0 || topk < 0 || chunk_tokens < 0) return SMLA_ERR_BAD_SIZE;
   if (H > kBwdMaxH || T > INT32_MAX || topk > INT32_MAX || num_kv >= ((int64_t)1 << 31)) return SMLA_ERR_BAD_SIZE;
   if (!isfinite(scale)) return SMLA_ERR_BAD_SCALE;
   const int64_t TP = (topk + kBK - 1) / kBK * kBK;
@@ -599,37 +640,49 @@ extern "C" int sparse_mla_backward(const void* q, const void* kv, const void* do
   const int nw = bwd_nw(H);
   const int64_t heads_per_wg = 16 * nw;
   const int64_t head_groups = (H + heads_per_wg - 1) / heads_per_wg;
-  const int64_t N = T * TP;
   const int Hp = (int)((H + 15) / 16 * 16);
+
+  // Token passes: P, scale dS, the sort keys and the interm rows exist for one
+  // pass at a time (about TP (4 H + 1104) bytes per token). With more than one
+  // pass, each adds its dkv row sums to an fp32 accumulator.
+  const size_t per_token = (size_t)TP * (4 * (size_t)H + 4 * 4 + 2 * kD) + 4 + (size_t)TP / kChunk * 2 * kD * 4 + 2 * kD * 4;
+  int64_t C = chunk_tokens;
+  if (C == 0) {  // as few passes as the bound allows, of equal size
+    const int64_t cap = (int64_t)(kBwdPassBytes / per_token) > 0 ? (int64_t)(kBwdPassBytes / per_token) : 1;
+    const int64_t npass = (T + cap - 1) / cap;
+    C = (T + npass - 1) / npass;
+  }
+  C = C < 1 ? 1 : (C > T ? T : C);
+  const bool passes = C < T;
+  const int64_t Nc = C * TP;  // sorted entries of one pass
 
   const uint32_t nkv = kv ? (uint32_t)num_kv : 0u;
   int end_bit = 1;  // the sort looks at the bits the keys use (rows < nkv, the sentinel nkv)
   while (end_bit < 32 && ((uint64_t)1 << end_bit) <= (uint64_t)nkv) ++end_bit;
 
-  // scratch layout
+  // scratch layout: one pass's buffers, then what lives across passes
   size_t sort_bytes = 0;
   {
-    const hipError_t e = hipcub::DeviceRadixSort::SortPairs(nullptr, sort_bytes, (const uint32_t*)nullptr,
-                                                            (uint32_t*)nullptr, (const uint32_t*)nullptr,
-                                                            (uint32_t*)nullptr, (int)N, 0, end_bit, s);
+    const hipError_t e = sort_pairs(nullptr, sort_bytes, nullptr, nullptr, nullptr, nullptr, (int)Nc, end_bit, s);
     if (e != hipSuccess) return SMLA_ERR_LAUNCH;
   }
   const size_t A = 256;
   size_t off = 0;
-  const size_t o_p = off;      off = align_up(off + (size_t)T * H * TP * 2, A);
-  const size_t o_ds = off;     off = align_up(off + (size_t)T * H * TP * 2, A);
-  const size_t o_ck = off;     off = align_up(off + (size_t)N * 4, A);
-  const size_t o_cv = off;     off = align_up(off + (size_t)N * 4, A);
-  const size_t o_sk = off;     off = align_up(off + (size_t)N * 4, A);
-  const size_t o_sv = off;     off = align_up(off + (size_t)N * 4, A);
-  const size_t o_nc = off;     off = align_up(off + (size_t)T * 4, A);
-  const size_t o_dsp = off;    off = align_up(off + (size_t)T * H * 4, A);
-  const size_t o_rs = off;     off = align_up(off + (size_t)(num_kv + 1) * 4, A);
-  const size_t o_it = off;     off = align_up(off + (size_t)N * kD * 2, A);
-  const size_t nch = (size_t)(N + kChunk - 1) / kChunk;
+  const size_t o_p = off;      off = align_up(off + (size_t)C * H * TP * 2, A);
+  const size_t o_ds = off;     off = align_up(off + (size_t)C * H * TP * 2, A);
+  const size_t o_ck = off;     off = align_up(off + (size_t)Nc * 4, A);
+  const size_t o_cv = off;     off = align_up(off + (size_t)Nc * 4, A);
+  const size_t o_sk = off;     off = align_up(off + (size_t)Nc * 4, A);
+  const size_t o_sv = off;     off = align_up(off + (size_t)Nc * 4, A);
+  const size_t o_nc = off;     off = align_up(off + (size_t)C * 4, A);
+  const size_t o_it = off;     off = align_up(off + (size_t)Nc * kD * 2, A);
+  const size_t nch = (size_t)(Nc + kChunk - 1) / kChunk;
   const size_t o_hd = off;     off = align_up(off + nch * kD * 4, A);
   const size_t o_tl = off;     off = align_up(off + nch * kD * 4, A);
   const size_t o_tmp = off;    off = align_up(off + sort_bytes, A);
+  const size_t o_dsp = off;    off = align_up(off + (size_t)T * H * 4, A);
+  const size_t o_rs = off;     off = align_up(off + (size_t)(num_kv + 1) * 4, A);
+  const size_t o_acc = off;    off = align_up(off + (passes ? (size_t)num_kv * kD * 4 : 0), A);
   void* ws = nullptr;
   hipMemPool_t pool = scratch_pool(dev);
   if (pool == nullptr || hipMallocFromPoolAsync(&ws, off, pool, s) != hipSuccess || ws == nullptr) {
@@ -637,78 +690,95 @@ extern "C" int sparse_mla_backward(const void* q, const void* kv, const void* do
     return SMLA_ERR_NO_MEMORY;
   }
   char* b = (char*)ws;
-
-  BwdParams bp;
-  bp.q = (const uint16_t*)q;
-  bp.kv = (const uint16_t*)kv;
-  bp.dout = (const uint16_t*)dout;
-  bp.o = (const uint16_t*)o;
-  bp.lse = lse;
-  bp.topk = topk_indices;
-  bp.sink = attn_sink;
-  bp.dq = (uint16_t*)dq;
-  bp.pbuf = (uint16_t*)(b + o_p);
-  bp.dsbuf = (uint16_t*)(b + o_ds);
-  bp.ckey = (uint32_t*)(b + o_ck);
-  bp.cval = (uint32_t*)(b + o_cv);
-  bp.ncount = (int32_t*)(b + o_nc);
-  bp.dsink_part = (float*)(b + o_dsp);
-  bp.T = (int)T;
-  bp.H = (int)H;
-  bp.topk_n = (int)topk;
-  bp.TP = (int)TP;
-  bp.head_groups = (int)head_groups;
-  bp.nkv = nkv;
-  bp.sentinel = nkv;
-  bp.scale = scale;
-  bp.scale_log2 = scale * kLog2e;
-
-  const unsigned g1 = (unsigned)(T * head_groups);
-  if (nw == 1) hipLaunchKernelGGL((smla_bwd_dq_kernel<1, 2>), dim3(g1), dim3(64), 0, s, bp);
-  else if (nw == 2) hipLaunchKernelGGL((smla_bwd_dq_kernel<2, 2>), dim3(g1), dim3(128), 0, s, bp);
-  else hipLaunchKernelGGL((smla_bwd_dq_kernel<4, 2>), dim3(g1), dim3(256), 0, s, bp);
-  hipError_t err = hipGetLastError();
-
-  if (err == hipSuccess) {
-    InterParams ip;
-    ip.q = (const uint16_t*)q;
-    ip.dout = (const uint16_t*)dout;
-    ip.pbuf = bp.pbuf;
-    ip.dsbuf = bp.dsbuf;
-    ip.ncount = bp.ncount;
-    ip.interm = (uint16_t*)(b + o_it);
-    ip.T = (int)T;
-    ip.H = (int)H;
-    ip.Hp = Hp;
-    ip.TP = (int)TP;
-    const dim3 grid((unsigned)T);
-    switch (Hp / 16) {
-      case 1: hipLaunchKernelGGL(smla_bwd_interm_kernel<1>, grid, dim3(512), 0, s, ip); break;
-      case 2: hipLaunchKernelGGL(smla_bwd_interm_kernel<2>, grid, dim3(512), 0, s, ip); break;
-      case 3: hipLaunchKernelGGL(smla_bwd_interm_kernel<3>, grid, dim3(512), 0, s, ip); break;
-      case 4: hipLaunchKernelGGL(smla_bwd_interm_kernel<4>, grid, dim3(512), 0, s, ip); break;
-      case 5: hipLaunchKernelGGL(smla_bwd_interm_kernel<5>, grid, dim3(512), 0, s, ip); break;
-      case 6: hipLaunchKernelGGL(smla_bwd_interm_kernel<6>, grid, dim3(512), 0, s, ip); break;
-      case 7: hipLaunchKernelGGL(smla_bwd_interm_kernel<7>, grid, dim3(512), 0, s, ip); break;
-      default: hipLaunchKernelGGL(smla_bwd_interm_kernel<8>, grid, dim3(512), 0, s, ip); break;
-    }
+  float* acc = passes ? (float*)(b + o_acc) : nullptr;
+  hipError_t err = hipSuccess;
+  if (acc != nullptr && num_kv > 0) {
+    hipLaunchKernelGGL(smla_zero_kernel, dim3(1024), dim3(256), 0, s, (uint32_t*)acc, num_kv * kD);
     err = hipGetLastError();
   }
-  if (err == hipSuccess && num_kv > 0) {
-    size_t tb = sort_bytes;
-    err = hipcub::DeviceRadixSort::SortPairs((void*)(b + o_tmp), tb, bp.ckey, (uint32_t*)(b + o_sk), bp.cval,
-                                             (uint32_t*)(b + o_sv), (int)N, 0, end_bit, s);
+
+  for (int64_t t0 = 0; t0 < T && err == hipSuccess; t0 += C) {
+    const int64_t Tc = T - t0 < C ? T - t0 : C;  // tokens of this pass
+    const int64_t Nt = Tc * TP;
+    const size_t qoff = (size_t)t0 * H * kD;
+    BwdParams bp;
+    bp.q = (const uint16_t*)q + qoff;
+    bp.kv = (const uint16_t*)kv;
+    bp.dout = (const uint16_t*)dout + qoff;
+    bp.o = (const uint16_t*)o + qoff;
+    bp.lse = lse + (size_t)t0 * H;
+    bp.topk = topk_indices ? topk_indices + (size_t)t0 * topk : nullptr;
+    bp.sink = attn_sink;
+    bp.dq = (uint16_t*)dq + qoff;
+    bp.pbuf = (uint16_t*)(b + o_p);
+    bp.dsbuf = (uint16_t*)(b + o_ds);
+    bp.ckey = (uint32_t*)(b + o_ck);
+    bp.cval = (uint32_t*)(b + o_cv);
+    bp.ncount = (int32_t*)(b + o_nc);
+    bp.dsink_part = (float*)(b + o_dsp) + (size_t)t0 * H;
+    bp.T = (int)Tc;
+    bp.H = (int)H;
+    bp.topk_n = (int)topk;
+    bp.TP = (int)TP;
+    bp.head_groups = (int)head_groups;
+    bp.nkv = nkv;
+    bp.sentinel = nkv;
+    bp.scale = scale;
+    bp.scale_log2 = scale * kLog2e;
+
+    const unsigned g1 = (unsigned)(Tc * head_groups);
+    if (nw == 1) hipLaunchKernelGGL((smla_bwd_dq_kernel<1, 2>), dim3(g1), dim3(64), 0, s, bp);
+    else if (nw == 2) hipLaunchKernelGGL((smla_bwd_dq_kernel<2, 2>), dim3(g1), dim3(128), 0, s, bp);
+    else hipLaunchKernelGGL((smla_bwd_dq_kernel<4, 2>), dim3(g1), dim3(256), 0, s, bp);
+    err = hipGetLastError();
+
+    if (err == hipSuccess) {
+      InterParams ip;
+      ip.q = bp.q;
+      ip.dout = bp.dout;
+      ip.pbuf = bp.pbuf;
+      ip.dsbuf = bp.dsbuf;
+      ip.ncount = bp.ncount;
+      ip.interm = (uint16_t*)(b + o_it);
+      ip.T = (int)Tc;
+      ip.H = (int)H;
+      ip.Hp = Hp;
+      ip.TP = (int)TP;
+      const dim3 grid((unsigned)Tc);
+      switch (Hp / 16) {
+        case 1: hipLaunchKernelGGL(smla_bwd_interm_kernel<1>, grid, dim3(512), 0, s, ip); break;
+        case 2: hipLaunchKernelGGL(smla_bwd_interm_kernel<2>, grid, dim3(512), 0, s, ip); break;
+        case 3: hipLaunchKernelGGL(smla_bwd_interm_kernel<3>, grid, dim3(512), 0, s, ip); break;
+        case 4: hipLaunchKernelGGL(smla_bwd_interm_kernel<4>, grid, dim3(512), 0, s, ip); break;
+        case 5: hipLaunchKernelGGL(smla_bwd_interm_kernel<5>, grid, dim3(512), 0, s, ip); break;
+        case 6: hipLaunchKernelGGL(smla_bwd_interm_kernel<6>, grid, dim3(512), 0, s, ip); break;
+        case 7: hipLaunchKernelGGL(smla_bwd_interm_kernel<7>, grid, dim3(512), 0, s, ip); break;
+        default: hipLaunchKernelGGL(smla_bwd_interm_kernel<8>, grid, dim3(512), 0, s, ip); break;
+      }
+      err = hipGetLastError();
+    }
+    if (err == hipSuccess && num_kv > 0) {
+      size_t tb = sort_bytes;
+      err = sort_pairs((void*)(b + o_tmp), tb, bp.ckey, (uint32_t*)(b + o_sk), bp.cval, (uint32_t*)(b + o_sv),
+                       (int)Nt, end_bit, s);
+    }
+    if (err == hipSuccess && num_kv > 0) {
+      const size_t nch_t = (size_t)(Nt + kChunk - 1) / kChunk;
+      hipLaunchKernelGGL(smla_bwd_rowstart_kernel, dim3((unsigned)((num_kv + 1 + 255) / 256)), dim3(256), 0, s,
+                         (const uint32_t*)(b + o_sk), (uint32_t)Nt, (uint32_t)num_kv, (uint32_t*)(b + o_rs));
+      hipLaunchKernelGGL(smla_bwd_dkv_chunk_kernel, dim3((unsigned)((nch_t + 3) / 4)), dim3(256), 0, s,
+                         (const uint32_t*)(b + o_sk), (const uint32_t*)(b + o_sv), (const uint32_t*)(b + o_rs),
+                         (const uint16_t*)(b + o_it), (uint16_t*)dkv, acc, (float*)(b + o_hd), (float*)(b + o_tl),
+                         (uint32_t)num_kv);
+      hipLaunchKernelGGL(smla_bwd_dkv_fix_kernel, dim3((unsigned)((num_kv + 3) / 4)), dim3(256), 0, s,
+                         (const uint32_t*)(b + o_rs), (const float*)(b + o_hd), (const float*)(b + o_tl),
+                         (uint16_t*)dkv, acc, num_kv);
+      err = hipGetLastError();
+    }
   }
-  if (err == hipSuccess && num_kv > 0) {
-    hipLaunchKernelGGL(smla_bwd_rowstart_kernel, dim3((unsigned)((num_kv + 1 + 255) / 256)), dim3(256), 0, s,
-                       (const uint32_t*)(b + o_sk), (uint32_t)N, (uint32_t)num_kv, (uint32_t*)(b + o_rs));
-    hipLaunchKernelGGL(smla_bwd_dkv_chunk_kernel, dim3((unsigned)((nch + 3) / 4)), dim3(256), 0, s,
-                       (const uint32_t*)(b + o_sk), (const uint32_t*)(b + o_sv), (const uint32_t*)(b + o_rs),
-                       (const uint16_t*)(b + o_it), (uint16_t*)dkv, (float*)(b + o_hd), (float*)(b + o_tl),
-                       (uint32_t)num_kv);
-    hipLaunchKernelGGL(smla_bwd_dkv_fix_kernel, dim3((unsigned)((num_kv + 3) / 4)), dim3(256), 0, s,
-                       (const uint32_t*)(b + o_rs), (const float*)(b + o_hd), (const float*)(b + o_tl), (uint16_t*)dkv,
-                       num_kv);
+  if (err == hipSuccess && acc != nullptr && num_kv > 0) {
+    hipLaunchKernelGGL(smla_bwd_dkv_out_kernel, dim3((unsigned)((num_kv + 3) / 4)), dim3(256), 0, s, acc,
+                       (uint16_t*)dkv, num_kv);
     err = hipGetLastError();
   }
   if (err == hipSuccess && attn_sink) {
@@ -718,4 +788,22 @@ extern "C" int sparse_mla_backward(const void* q, const void* kv, const void* do
   }
   const hipError_t ferr = hipFreeAsync(ws, s);
   return (err == hipSuccess && ferr == hipSuccess) ? SMLA_OK : SMLA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int sparse_mla_backward(const void* q, const void* kv, const void* dout, const void* o, const float* lse,
+                                   const int32_t* topk_indices, const float* attn_sink, float scale, void* dq,
+                                   void* dkv, float* d_sink, int64_t T, int64_t H, int64_t num_kv, int64_t topk,
+                                   void* stream) {
+  return run_backward(q, kv, dout, o, lse, topk_indices, attn_sink, scale, dq, dkv, d_sink, T, H, num_kv, topk, 0,
+                      stream);
+}
+
+extern "C" int sparse_mla_backward_chunked(const void* q, const void* kv, const void* dout, const void* o,
+                                           const float* lse, const int32_t* topk_indices, const float* attn_sink,
+                                           float scale, void* dq, void* dkv, float* d_sink, int64_t T, int64_t H,
+                                           int64_t num_kv, int64_t topk, int64_t chunk_tokens, void* stream) {
+  return run_backward(q, kv, dout, o, lse, topk_indices, attn_sink, scale, dq, dkv, d_sink, T, H, num_kv, topk,
+                      chunk_tokens, stream);
 }

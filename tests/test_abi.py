@@ -169,6 +169,18 @@ def test_backward_argument_errors(kw, rc):
     assert callbwd(**kw) == rc
 
 
+def test_backward_chunked_argument_errors():
+    lib = _lib.load()
+    args = [0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, None, 0.0441, 0x7000, 0x8000, None, 4, 8, 16, 8]
+    assert lib.sparse_mla_backward_chunked(*args, -1, None) == _lib.SMLA_ERR_BAD_SIZE  # negative pass size
+    bad = list(args)
+    bad[12] = 129
+    assert lib.sparse_mla_backward_chunked(*bad, 2, None) == _lib.SMLA_ERR_BAD_SIZE
+    bad = list(args)
+    bad[8] = 0x7008
+    assert lib.sparse_mla_backward_chunked(*bad, 2, None) == _lib.SMLA_ERR_MISALIGNED
+
+
 def test_empty_sequence_is_ok_without_a_device():
     assert call(T=0, q=None, out=None, lse=None, topk=None, kv=None) == _lib.SMLA_OK
 

@@ -57,26 +57,26 @@ def check_grad(got, ref, mag, what):
         assert np.all(g == 0), "%s: reference is zero, got nonzero" % what
 
 
-def run_backward(q, kv, dout, o_bits, lse, topk, sink, scale):
+def run_backward(q, kv, dout, o_bits, lse, topk, sink, scale, chunk_tokens=None):
     qd, dd, od = to_dev_bf16(q), to_dev_bf16(dout), to_dev_bf16(o_bits)
     kvd = to_dev_bf16(kv) if kv.shape[0] else torch.empty((0, 512), dtype=torch.bfloat16, device=DEV)
     ld = torch.from_numpy(np.ascontiguousarray(lse, dtype=np.float32)).to(DEV)
     td = torch.from_numpy(np.ascontiguousarray(topk, dtype=np.int32)).to(DEV)
     sd = None if sink is None else torch.from_numpy(np.ascontiguousarray(sink, dtype=np.float32)).to(DEV)
-    dq, dkv, ds = sparse_mla_backward(qd, kvd, dd, od, ld, td, sd, scale)
+    dq, dkv, ds = sparse_mla_backward(qd, kvd, dd, od, ld, td, sd, scale, chunk_tokens=chunk_tokens)
     torch.cuda.synchronize()
     return (f64(bf16_bits(dq)), f64(bf16_bits(dkv)) if kv.shape[0] else np.zeros((0, 512)),
             None if ds is None else ds.cpu().numpy().astype(np.float64))
 
 
-def full_case(q, kv, topk, sink, scale, seed, what, tokens=None, rows=None):
+def full_case(q, kv, topk, sink, scale, seed, what, tokens=None, rows=None, chunk_tokens=None):
     """GPU forward, then GPU backward and oracle backward on the same inputs; compare."""
     print("backward case %s: T=%d H=%d topk=%d num_kv=%d sink=%s" % (
         what, q.shape[0], q.shape[1], topk.shape[1], kv.shape[0], sink is not None), flush=True)
     rng = np.random.default_rng(seed)
     dout = bf16(rng.standard_normal(q.shape))
     o_bits, lse = run_gpu(q, kv, topk, sink, scale)
-    dq, dkv, ds = run_backward(q, kv, dout, o_bits, lse, topk, sink, scale)
+    dq, dkv, ds = run_backward(q, kv, dout, o_bits, lse, topk, sink, scale, chunk_tokens)
     ref = oracle.backward(q, kv, dout, o_bits, lse, topk, sink, scale, tokens=tokens, rows=rows, want_mag=True)
     check_grad(dq if tokens is None else dq[tokens], ref["dq"], ref["dq_mag"], what + " dq")
     check_grad(dkv if rows is None else dkv[rows], ref["dkv"], ref["dkv_mag"], what + " dkv")
@@ -139,6 +139,24 @@ def test_backward_empty_topk_and_zero_tokens():
     assert dq.shape == (0, 16, 512) and np.all(dkv == 0) and np.all(ds == 0)
 
 
+@pytest.mark.parametrize("T,H,topk,chunk,dup", [(40, 128, 96, 7, False), (33, 16, 70, 1, True),
+                                                (64, 64, 128, 64, True), (50, 100, 40, 16, True)])
+def test_backward_token_passes(T, H, topk, chunk, dup):
+    """The backward in passes of `chunk` tokens (dkv summed across passes in
+    fp32) against the oracle, and against the single-pass call: dq and d_sink
+    are per token and come out bit-identical, dkv within the tolerance."""
+    q, kv, idx, s = random_case(T * 3 + chunk, T=T, H=H, topk=topk, num_kv=250, sink=True, dup=dup)
+    idx[:, :4] = 11  # a row shared by every pass
+    what = "passes of %d: T=%d H=%d topk=%d" % (chunk, T, H, topk)
+    dq, dkv, ds = full_case(q, kv, idx, s, synth.DEFAULT_SCALE, T + H, what, chunk_tokens=chunk)
+    rng = np.random.default_rng(T + H)
+    dout = bf16(rng.standard_normal(q.shape))
+    o_bits, lse = run_gpu(q, kv, idx, s, synth.DEFAULT_SCALE)
+    dq1, dkv1, ds1 = run_backward(q, kv, dout, o_bits, lse, idx, s, synth.DEFAULT_SCALE)
+    assert np.array_equal(dq, dq1), what + ": dq differs from the single pass"
+    assert np.array_equal(ds, ds1), what + ": d_sink differs from the single pass"
+
+
 def test_backward_is_deterministic():
     q, kv, idx, s = random_case(13, T=64, H=128, topk=128, num_kv=400, dup=True)
     rng = np.random.default_rng(14)
@@ -150,17 +168,19 @@ def test_backward_is_deterministic():
         assert np.array_equal(x, y)
 
 
-def test_backward_wide_full_size_sampled():
-    """The wide workload (T=4096, H=128, topk=512) at full size: dq of sampled
-    tokens, dkv of sampled rows (window rows and heavily shared pool rows), and
-    d_sink over all tokens, against the oracle."""
+@pytest.mark.parametrize("chunk", [None, 1000])
+def test_backward_wide_full_size_sampled(chunk):
+    """The wide workload (T=4096, H=128, topk=512) at full size, in one pass and
+    in five token passes: dq of sampled tokens, dkv of sampled rows (window rows
+    and heavily shared pool rows), and d_sink over all tokens, against the
+    oracle."""
     inp = synth.make_inputs("wide")
     T = inp["T"]
     tokens = np.linspace(0, T - 1, 24).astype(np.int64)
     num_kv = inp["kv"].shape[0]
     rows = np.array([0, 1, T // 2, T - 1, T, T + 1, T + 300, num_kv - 1], np.int64)
-    full_case(inp["q"], inp["kv"], inp["topk"], inp["sink"], inp["scale"], 15, "wide sampled", tokens=tokens,
-              rows=rows)
+    full_case(inp["q"], inp["kv"], inp["topk"], inp["sink"], inp["scale"], 15, "wide sampled (passes of %s)" % chunk,
+              tokens=tokens, rows=rows, chunk_tokens=chunk)
 
 
 @pytest.mark.parametrize("name", ["long", "tp4"])
