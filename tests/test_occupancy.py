@@ -32,6 +32,8 @@ EXPECTED = {
     "smla_fwd_fp8_kernel<8, 4>": (1, 2),
     "smla_fwd128_kernel<false>": (1, 1),
     "smla_fwd128_kernel<true>": (1, 1),
+    "smla_fwd128_mfma32_kernel<false>": (1, 1),
+    "smla_fwd128_mfma32_kernel<true>": (1, 1),
 }
 
 MANGLED = {
@@ -40,8 +42,10 @@ MANGLED = {
     "smla_fwd_kernel<4, 2>": "15smla_fwd_kernelILi4ELi2EE",
     "smla_fwd_kernel<2, 2>": "15smla_fwd_kernelILi2ELi2EE",
     "smla_fwd_fp8_kernel<8, 4>": "smla_fwd_fp8_kernelILi8ELi4EE",
-    "smla_fwd128_kernel<false>": "smla_fwd128_kernelILb0EE",
-    "smla_fwd128_kernel<true>": "smla_fwd128_kernelILb1EE",
+    "smla_fwd128_kernel<false>": "18smla_fwd128_kernelILb0EE",
+    "smla_fwd128_kernel<true>": "18smla_fwd128_kernelILb1EE",
+    "smla_fwd128_mfma32_kernel<false>": "smla_fwd128_mfma32_kernelILb0EE",
+    "smla_fwd128_mfma32_kernel<true>": "smla_fwd128_mfma32_kernelILb1EE",
 }
 BWD = os.path.join(ROOT, "sparse_attention_top_amd", "csrc", "sparse_mla_bwd.hip")
 
@@ -113,20 +117,28 @@ def test_no_scratch(resources, resources_bwd, which):
     assert not bad, "kernels using scratch (bytes per lane, VGPRs spilled): %s" % bad
 
 
-def test_fwd128_agprs_left_to_the_accumulators(tmp_path):
-    """In the 128-head kernel every AGPR operand must come from the hand-written
-    accumulator asm: an AGPR the compiler allocates (for a spill or a copy)
-    would overwrite an accumulator."""
+@pytest.fixture(scope="module")
+def forward_asm(tmp_path_factory):
     _need_hipcc()
-    out = tmp_path / "fwd.s"
+    out = tmp_path_factory.mktemp("asm") / "fwd.s"
     cmd = [HIPCC] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-S", "-o", str(out), SRC]
     proc = subprocess.run(cmd, capture_output=True, text=True)
     assert proc.returncode == 0, proc.stderr[-2000:]
-    text = out.read_text()
+    return out.read_text()
+
+
+def _bodies(text, pattern):
+    for m in re.finditer(r"^(_Z\S*(?:%s)\S*):" % pattern, text, re.M):
+        yield m.group(1), text[m.end():text.index("s_endpgm", m.end())]
+
+
+def test_fwd128_agprs_left_to_the_accumulators(forward_asm):
+    """In the 128-head kernels every AGPR operand must come from the hand-written
+    accumulator asm: an AGPR the compiler allocates (for a spill or a copy)
+    would overwrite an accumulator."""
     found = 0
-    for m in re.finditer(r"^(_Z\S*smla_fwd128_kernel\S*):", text, re.M):
+    for name, body in _bodies(forward_asm, "smla_fwd128_kernel|smla_fwd128_mfma32_kernel"):
         found += 1
-        body = text[m.end():text.index("s_endpgm", m.end())]
         in_asm, bad = False, []
         for line in body.split("\n"):
             if ";;#ASMSTART" in line:
@@ -137,5 +149,61 @@ def test_fwd128_agprs_left_to_the_accumulators(tmp_path):
                 code = line.split(";")[0].strip()
                 if code and re.search(r"\ba\[?\d", code):
                     bad.append(code)
-        assert not bad, "%s: compiler-generated AGPR operands: %s" % (m.group(1), bad[:5])
-    assert found == 2
+        assert not bad, "%s: compiler-generated AGPR operands: %s" % (name, bad[:5])
+    assert found == 4
+
+
+def _vgprs(operand):
+    m = re.match(r"v\[(\d+):(\d+)\]$", operand)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"v(\d+)$", operand)
+    return {int(m.group(1))} if m else set()
+
+
+# A VALU write of a VGPR read by an MFMA needs wait states in between. The
+# compiler inserts them only for the MFMAs it generates itself; the MFMAs of
+# the kernels are inline asm, and a constant the compiler materialised with a
+# v_mov just before one (a zero operand) was once read stale.
+MFMA_SRC_WAIT_STATES = 5
+
+
+@pytest.mark.parametrize("which", ["forward", "backward"])
+def test_no_valu_write_right_before_an_mfma_reads_it(forward_asm, tmp_path, which):
+    if which == "forward":
+        text = forward_asm
+    else:
+        out = tmp_path / "bwd.s"
+        cmd = [HIPCC] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-S", "-o", str(out), BWD]
+        proc = subprocess.run(cmd, capture_output=True, text=True)
+        assert proc.returncode == 0, proc.stderr[-2000:]
+        text = out.read_text()
+    checked, bad = 0, []
+    for name, body in _bodies(text, "smla_"):
+        ins = [l.split(";")[0].strip() for l in body.split("\n")]
+        ins = [l for l in ins if l and not l.startswith(".") and not l.endswith(":")]
+        for i, line in enumerate(ins):
+            if not line.startswith("v_mfma"):
+                continue
+            checked += 1
+            ops = [o.strip() for o in line.split(None, 1)[1].split(",")]
+            src = set().union(*(_vgprs(o) for o in ops[1:]))
+            ws, j = 0, i - 1
+            while j >= 0 and ws < MFMA_SRC_WAIT_STATES:
+                prev = ins[j]
+                if prev.startswith("s_nop"):
+                    ws += int(prev.split()[1], 0) + 1
+                elif prev.startswith("v_") and not prev.startswith(("v_mfma", "v_readlane", "v_readfirstlane", "v_cmp")):
+                    parts = prev.split(None, 1)
+                    dst = _vgprs(parts[1].split(",")[0].strip()) if len(parts) > 1 else set()
+                    if prev.startswith(("v_permlane", "v_swap")) and len(parts) > 1:
+                        dst |= _vgprs(parts[1].split(",")[1].strip())
+                    if dst & src:
+                        bad.append("%s: %s -> %s" % (name[-40:], prev, line))
+                        break
+                    ws += 1
+                else:
+                    ws += 1
+                j -= 1
+    assert checked > 0
+    assert not bad, "VALU writes read by an MFMA within %d wait states: %s" % (MFMA_SRC_WAIT_STATES, bad[:5])
