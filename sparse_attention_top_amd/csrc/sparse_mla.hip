@@ -735,16 +735,18 @@ constexpr int k128Ring = 4;  // ring of 32-row tiles
 constexpr int k128Ahead = k128Ring - 1;
 constexpr int k128Cap = 1024;  // top-k entries compacted per segment
 
-struct Smem128 {
-  uint8_t area[k128Ring * kBK * kRowStride];  // gather ring
+template <int PITCH>
+struct Smem128T {
+  uint8_t area[k128Ring * kBK * PITCH];  // gather ring, rows at pitch PITCH
   uint8_t pbuf[2][8 * 64 * 16];               // P fragments of tile j, by tile parity: [head block][lane][16 B]
   float fac[2][128];                          // rescale factors, [li * 8 + head block], written with a flag
   uint8_t flag[2][4];                         // per wave (byte w): its factors of this tile were written
   float osc[128];                             // output scale of each head, [li * 8 + head block]
   int32_t list[2][k128Cap];                   // compacted lists of this unit and the next (by unit parity)
   int32_t wcnt[16];                           // per-wave counts of the compaction
-  __device__ __forceinline__ uint32_t tile(int b) { return lds_addr(area + b * kBK * kRowStride); }
+  __device__ __forceinline__ uint32_t tile(int b) { return lds_addr(area + b * kBK * PITCH); }
 };
+using Smem128 = Smem128T<kRowStride>;
 static_assert(sizeof(Smem128) <= 160 * 1024, "one workgroup per CU");
 
 // An empty asm that "redefines" its operands: code using them cannot move above it.
@@ -785,7 +787,8 @@ __device__ __forceinline__ void mfma_s_first_dep(f32x4& c, const u32x4& a, const
 // [8 w, 8 w + 8), lane L < 8 forming row 8 w + L's source address (a pool row,
 // or the zero row past the tile's count, or for a tile past the unit's last);
 // one LDS-DMA load per row, issued without a branch.
-struct Gather128 {
+template <int PITCH>
+struct Gather128T {
   uint32_t dst0;      // LDS address of this wave's first row
   uint32_t alo, ahi;  // lane L < 8: source address of row L
   template <int R>
@@ -793,12 +796,13 @@ struct Gather128 {
     const uint32_t rlo = (uint32_t)__builtin_amdgcn_readlane(alo, R);
     const uint32_t rhi = (uint32_t)__builtin_amdgcn_readlane(ahi, R);
     const uint16_t* rs = (const uint16_t*)(uintptr_t)(((uint64_t)rhi << 32) | rlo);
-    __builtin_amdgcn_global_load_lds(rs + 8 * lane, (LDS_AS void*)(uintptr_t)(dst0 + R * kRowStride), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(rs + 8 * lane, (LDS_AS void*)(uintptr_t)(dst0 + R * PITCH), 16, 0, 0);
   }
   __device__ __forceinline__ void all(int lane) const {
     static_for<0, kBK / 4>([&](auto rc) { row<decltype(rc)::value>(lane); });
   }
 };
+using Gather128 = Gather128T<kRowStride>;
 // The list entry of this lane's row (every lane reads an in-bounds entry, so no
 // branch merges the pending register); the raw read is completed by a later
 // wait that takes it as an operand.
@@ -812,12 +816,13 @@ __device__ __forceinline__ uint32_t gather128_read(const int32_t* list, int i, i
   asm volatile("ds_read_b32 %0, %1" : "=v"(e) : "v"(lds_addr(list + pos)));
   return e;
 }
-__device__ __forceinline__ Gather128 gather128_make(uint32_t e, int i, int n, bool act, uint32_t buf,
-                                                   const uint16_t* kv, int lane, int w) {
-  Gather128 ga;
+template <int PITCH = kRowStride>
+__device__ __forceinline__ Gather128T<PITCH> gather128_make(uint32_t e, int i, int n, bool act, uint32_t buf,
+                                                           const uint16_t* kv, int lane, int w) {
+  Gather128T<PITCH> ga;
   const int r0 = w * (kBK / 4);
   const int cnt = act ? min(kBK, n - i * kBK) : 0;
-  ga.dst0 = buf + r0 * kRowStride;
+  ga.dst0 = buf + r0 * PITCH;
   const bool have = act && lane < kBK / 4 && r0 + lane < cnt;
   const uint16_t* src = have ? uniform_ptr(kv) + (size_t)e * kD : kZeroRowBf16;
   const uint64_t a = (uint64_t)(uintptr_t)src;
@@ -825,11 +830,12 @@ __device__ __forceinline__ Gather128 gather128_make(uint32_t e, int i, int n, bo
   ga.ahi = (uint32_t)(a >> 32);
   return ga;
 }
-__device__ __forceinline__ Gather128 gather128(const int32_t* list, int i, int n, bool act, uint32_t buf,
-                                               const uint16_t* kv, int lane, int w) {
+template <int PITCH = kRowStride>
+__device__ __forceinline__ Gather128T<PITCH> gather128(const int32_t* list, int i, int n, bool act, uint32_t buf,
+                                                      const uint16_t* kv, int lane, int w) {
   uint32_t e = gather128_read(list, i, lane, w);
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(e));
-  return gather128_make(e, i, n, act, buf, kv, lane, w);
+  return gather128_make<PITCH>(e, i, n, act, buf, kv, lane, w);
 }
 
 // Phase Y: S = K Q^T from the tile at krow, 16 k-steps of four MFMAs (four
@@ -1429,12 +1435,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // output tile per instruction (half the MFMA instructions, and half the V^T
 // reads per flop), so that each phase leaves more issue slots between its
 // MFMAs for the softmax, the transposing reads and the gather issue.
+//   MFMA row m of a tile (a token) is tile row m32_row(m): within each block of
+//     16 rows the two 2-bit halves of the index trade places. With the row
+//     pitch kM32Pitch (1040 B) the K reads (16 lanes on 16 rows) and the
+//     transposing V reads (32 lanes on 4 rows, 64 B each, the rows 4 apart)
+//     both spread over all LDS banks; in row order at a 1056 B pitch each of
+//     them ran at half the LDS rate (measured 125 B/clk per CU against 246
+//     and 200).
 //   S^T (32 tokens x 32 heads of this wave) = K Q^T: A = K [32 tokens x 16 d]
 //     (lane: token lane % 32, eight d of the k-step, one ds_read_b128), B =
 //     Q^T [16 d x 32 heads] held in VGPRs (32 k-steps). The sum runs over d in
 //     any order that K and Q share: k-step u, lane half h takes the 8-wide d
-//     chunk 4 (u / 2) + 2 h + u % 2, the order in which q arrives from the
-//     load below.
+//     chunk sigma(u, h) below, the order the q load leaves them in.
 //     s[r] = S^T[token 8 (r / 4) + 4 (lane / 32) + r % 4][head lane % 32]: one
 //     head per lane, sixteen of its tokens (the other sixteen in lane ^ 32).
 //   O^T (32 d x 32 heads) += V^T P^T per (d-tile, head block): A = V^T from
@@ -1445,6 +1457,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 //   acc tuple 4 b + dt (16 AGPRs): O^T[d 128 w + 32 dt + 8 (r / 4) + 4 h + r % 4]
 //     [head 32 b + lane % 32].
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kM32Pitch = kRowBytes + 16;
+__host__ __device__ constexpr int m32_row(int m) { return (m & ~15) | ((m & 3) << 2) | ((m >> 2) & 3); }
 
 template <int T>
 __device__ __forceinline__ void acc32_mfma(const bf16x8& a, const bf16x8& b, float d0) {
@@ -1458,70 +1473,120 @@ __device__ __forceinline__ void mfma32(f32x16& c, const u32x4& a, const u32x4& b
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
 }
 
-// Q^T fragments of the wave's 32 heads h0 .. h0 + 31, in two steps. The load:
-// lane (g = lane / 16, li = lane % 16) takes the d chunks 4 k + g of heads
-// h0 + li (into qf[2 k]) and h0 + 16 + li (into qf[2 k + 1]), so that one load
-// instruction reads 64 contiguous bytes of each of 16 rows (with one head per
-// lane and 32 bytes of 32 rows per instruction, the same 32 KiB took some
-// 14 000 cycles per unit to issue, against a few hundred). A head past H
-// loads head H - 1 (never stored), with no branch.
+// Q^T fragments of the wave's 32 heads h0 .. h0 + 31, in two steps. A 1 KiB
+// row of q is 64 chunks of 16 bytes (chunk c = d 8 c .. 8 c + 7); the address
+// unit serves a load at one 4-lane quad per cycle when each quad reads 64
+// contiguous bytes, and about four times slower when its lanes read different
+// rows (the natural MFMA operand layout, one head per lane).
+// The load: instruction i (0..31), lane L reads chunk 8 (i % 8) + 4 (L / 32) +
+// L % 4 of head 4 ((L / 4) % 8) + i / 8, so that each instruction reads 128
+// contiguous bytes of each of 8 rows. A head past H loads head H - 1 (never
+// stored), with no branch.
 __device__ __forceinline__ void load_q32(bf16x8 (&qf)[32], const Params& p, int t, int h0, int lane) {
-  const int li = lane & 15, g = lane >> 4;
-  const bf16x8* s0 = (const bf16x8*)(p.q + ((size_t)t * p.H + min(h0 + li, p.H - 1)) * kD + 8 * g);
-  const bf16x8* s1 = (const bf16x8*)(p.q + ((size_t)t * p.H + min(h0 + 16 + li, p.H - 1)) * kD + 8 * g);
+  const int nb = 4 * ((lane >> 2) & 7);
+  const int cofs = 8 * (4 * (lane >> 5) + (lane & 3));  // elements
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    qf[2 * k] = __builtin_nontemporal_load(s0 + 4 * k);
-    qf[2 * k + 1] = __builtin_nontemporal_load(s1 + 4 * k);
+  for (int hi = 0; hi < 4; ++hi) {
+    const bf16x8* src = (const bf16x8*)(p.q + ((size_t)t * p.H + min(h0 + nb + hi, p.H - 1)) * kD + cofs);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) qf[8 * hi + c] = __builtin_nontemporal_load(src + 8 * c);
   }
 }
-// Once the loads have landed: the odd 16-lane rows of qf[2 k] trade places with
-// the even rows of qf[2 k + 1] (v_permlane16_swap), after which lane (head
-// lane % 32, half h = lane / 32) holds chunk 4 k + 2 h in qf[2 k] and chunk
-// 4 k + 2 h + 1 in qf[2 k + 1] of its head: the B-operand layout of k-steps 2 k
-// and 2 k + 1. The VALU writes are followed by the wait states an MFMA reading
-// them needs.
-__device__ __forceinline__ void q32_to_operand(bf16x8 (&qf)[32]) {
+// One step of the transposition: lane bit B (1 or 2) trades places with bit
+// log2(B) + 3 of the register index. For each register pair (lo: index bit
+// clear, hi: set), a lane with bit B clear keeps lo and takes hi's value from
+// lane L ^ B in place of its own hi; a lane with bit B set does the converse.
+// One v_cndmask_b32 with a DPP quad permutation of its first source per value,
+// the lane masks in VCC (the compiler would emit a separate DPP move per value);
+// each block starts with the two wait states a DPP read of a VALU result needs.
+template <int B>
+__device__ __forceinline__ void q32_swap_step(bf16x8 (&qf)[32]) {
+  constexpr int R = B == 1 ? 8 : 16;  // register index bit
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    u32x4 a = __builtin_bit_cast(u32x4, qf[2 * k]), b = __builtin_bit_cast(u32x4, qf[2 * k + 1]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const auto sw = __builtin_amdgcn_permlane16_swap(a[i], b[i], false, false);
-      a[i] = sw[0];
-      b[i] = sw[1];
-    }
-    qf[2 * k] = __builtin_bit_cast(bf16x8, a);
-    qf[2 * k + 1] = __builtin_bit_cast(bf16x8, b);
+  for (int i = 0; i < 32; ++i) {
+    if (i & R) continue;
+    const u32x4 lo = __builtin_bit_cast(u32x4, qf[i]);
+    u32x4 hi = __builtin_bit_cast(u32x4, qf[i + R]);
+    u32x4 nl;  // the new lo; the new hi is written in place, after every read of the old hi
+#define SMLA_Q32_STEP(PERM, LOWER, UPPER)                                                                         \
+  asm volatile("s_nop 1\n\t"                                                                                      \
+               "s_mov_b32 vcc_lo, " LOWER "\n\ts_mov_b32 vcc_hi, " LOWER "\n\t"                                   \
+               "v_cndmask_b32_dpp %0, %4, %8, vcc " PERM " row_mask:0xf bank_mask:0xf\n\t"                         \
+               "v_cndmask_b32_dpp %1, %5, %9, vcc " PERM " row_mask:0xf bank_mask:0xf\n\t"                         \
+               "v_cndmask_b32_dpp %2, %6, %10, vcc " PERM " row_mask:0xf bank_mask:0xf\n\t"                        \
+               "v_cndmask_b32_dpp %3, %7, %11, vcc " PERM " row_mask:0xf bank_mask:0xf\n\t"                        \
+               "s_mov_b32 vcc_lo, " UPPER "\n\ts_mov_b32 vcc_hi, " UPPER "\n\t"                                   \
+               "v_cndmask_b32_dpp %4, %8, %4, vcc " PERM " row_mask:0xf bank_mask:0xf\n\t"                         \
+               "v_cndmask_b32_dpp %5, %9, %5, vcc " PERM " row_mask:0xf bank_mask:0xf\n\t"                         \
+               "v_cndmask_b32_dpp %6, %10, %6, vcc " PERM " row_mask:0xf bank_mask:0xf\n\t"                        \
+               "v_cndmask_b32_dpp %7, %11, %7, vcc " PERM " row_mask:0xf bank_mask:0xf"                              \
+               : "=&v"(nl[0]), "=&v"(nl[1]), "=&v"(nl[2]), "=&v"(nl[3]), "+v"(hi[0]), "+v"(hi[1]), "+v"(hi[2]),   \
+                 "+v"(hi[3])                                                                                     \
+               : "v"(lo[0]), "v"(lo[1]), "v"(lo[2]), "v"(lo[3])                                                  \
+               : "vcc")
+    if constexpr (B == 1)
+      SMLA_Q32_STEP("quad_perm:[1,0,3,2]", "0x55555555", "0xaaaaaaaa");
+    else
+      SMLA_Q32_STEP("quad_perm:[2,3,0,1]", "0x33333333", "0xcccccccc");
+#undef SMLA_Q32_STEP
+    qf[i] = __builtin_bit_cast(bf16x8, nl);
+    qf[i + R] = __builtin_bit_cast(bf16x8, hi);
   }
+}
+// Once the loads have landed: two steps move the chunk bits out of lane bits
+// 0 and 1 and the head bits in, after which lane (head lane % 32, h = lane /
+// 32) holds in qf[u] the chunk sigma(u, h) = 8 (u % 8) + 4 h + 2 ((u / 16) % 2)
+// + (u / 8) % 2 of its head: the B operand of k-step u. The VALU writes are
+// followed by the wait states an MFMA reading them needs.
+__device__ __forceinline__ void q32_to_operand(bf16x8 (&qf)[32]) {
+  q32_swap_step<1>(qf);
+  q32_swap_step<2>(qf);
 #pragma unroll
   for (int u = 0; u < 32; ++u) asm volatile("" : "+v"(qf[u]));
   asm volatile("s_nop 4" ::: "memory");
 }
+// Byte offset, within a row, of the chunk sigma(u, 0) read by k-step u (lane
+// half h adds 64).
+template <int U>
+constexpr int q32_chunk_ofs = 128 * (U % 8) + 32 * ((U / 16) % 2) + 16 * ((U / 8) % 2);
 
 // Phase Y: S^T of tile krow for the wave's 32 heads, 32 k-steps of one MFMA
-// (one accumulator chain), K fragments kY32PF steps ahead, the eight gather
-// rows of the next tile every fourth step, tail() after the last MFMA.
+// (one accumulator chain), K fragments kY32PF steps ahead (the first ones
+// issued by y32_kpre, possibly before other work), the eight gather rows of
+// the next tile every fourth step, and tail() -- the first reads of the next
+// phase X, kXPre reads -- after MFMA kYTail, so that they land under the last
+// MFMAs; every wait counts the reads issued after the one it needs.
 constexpr int kY32PF = 3;
-template <typename GA, typename Tail = NoTail>
-__device__ __forceinline__ void phase_y32(uint32_t krow, const bf16x8 (&qf)[32], f32x16& s, const GA& ga, int lane,
-                                          Tail&& tail = NoTail{}) {
-  constexpr int KST = kY32PF + 1;
-  u32x4 kf[KST];
+constexpr int kYTail = 27;
+struct K32Frags {
+  u32x4 kf[kY32PF + 1];
+};
+__device__ __forceinline__ void y32_kpre(K32Frags& k, uint32_t krow) {
   static_for<0, kY32PF>([&](auto kc) {
-    constexpr int k = decltype(kc)::value;
-    kf[k] = ds_read_b128<64 * (k / 2) + 16 * (k % 2)>(krow);
+    constexpr int i = decltype(kc)::value;
+    k.kf[i] = ds_read_b128<q32_chunk_ofs<i>>(krow);
   });
+}
+template <int XPRE>
+constexpr int y32_wait(int u) {  // LDS reads issued after K(u) by the wait of step u
+  int n = (kY32PF - 1) < (31 - u) ? (kY32PF - 1) : (31 - u);
+  if (XPRE > 0 && kYTail < u && u <= kYTail + kY32PF) n += XPRE;  // the prefetch, issued after K(kYTail + PF)
+  return n;
+}
+template <int XPRE, typename GA, typename Tail>
+__device__ __forceinline__ void phase_y32(K32Frags& k, uint32_t krow, const bf16x8 (&qf)[32], f32x16& s, const GA& ga,
+                                          int lane, Tail&& tail) {
+  constexpr int KST = kY32PF + 1;
+  u32x4 (&kf)[KST] = k.kf;
   static_for<0, 32>([&](auto uc) {
     constexpr int u = decltype(uc)::value;
-    constexpr int wc = (kY32PF - 1) < (31 - u) ? (kY32PF - 1) : (31 - u);  // reads issued after K(u)
-    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(kf[u % KST]) : "n"(wc));
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(kf[u % KST]) : "n"(y32_wait<XPRE>(u)));
     if constexpr (u == 0) mfma32_first(s, kf[0], __builtin_bit_cast(u32x4, qf[0]));
     else mfma32(s, kf[u % KST], __builtin_bit_cast(u32x4, qf[u]));
     if constexpr (u + kY32PF < 32)
-      kf[(u + kY32PF) % KST] = ds_read_b128<64 * ((u + kY32PF) / 2) + 16 * ((u + kY32PF) % 2)>(krow);
+      kf[(u + kY32PF) % KST] = ds_read_b128<q32_chunk_ofs<u + kY32PF>>(krow);
     if constexpr (u % 4 == 1) ga.template row<u / 4>(lane);
-    if constexpr (u == 31) tail();
+    if constexpr (u == kYTail) tail();
     __builtin_amdgcn_sched_barrier(0);
   });
   asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" ::: "memory");  // MFMA write -> VALU read distance
@@ -1563,11 +1628,11 @@ template <int G, bool MASK>
 __device__ __forceinline__ float soft32_group(f32x16& s, Soft32T& tt, Soft32& ss, float c, float inv_c, int cnt,
                                               int h, uint32_t pbw, uint32_t facw, uint32_t flagw) {
   constexpr int M = MASK ? 4 : 0;
-  if constexpr (MASK && G < 4) {  // registers 4 G .. 4 G + 3: tokens 8 G + 4 h + i
+  if constexpr (MASK && G < 4) {  // registers 4 G .. 4 G + 3: MFMA rows 8 G + 4 h + i, tile rows b + 4 i
     pin1(s);
-    const int lim = cnt - 8 * G - 4 * h;
+    const int lim = cnt - (16 * (G / 2) + 2 * (G % 2) + h);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[4 * G + i] = i < lim ? s[4 * G + i] : -INFINITY;
+    for (int i = 0; i < 4; ++i) s[4 * G + i] = 4 * i < lim ? s[4 * G + i] : -INFINITY;
     return s[4 * G];
   } else if constexpr (G == M + 0) {  // tile max, in-lane
     pin1(s);
@@ -1646,12 +1711,13 @@ struct XPre32 {
   u32x4 pf[4];
   u32x2 vf[kX32PF + 1][2];
 };
-// V^T fragment (step q = 4 ks + dt): rows 16 ks + 4 h + (0..3) and + 8, 32 columns at 32 dt
+// V^T fragment (step q = 4 ks + dt): MFMA rows 16 ks + 4 h + (0..3) and + 8,
+// i.e. tile rows 16 ks + h + 4 (0..3) and + 2, 32 columns at 32 dt
 template <int Q>
 __device__ __forceinline__ void x32_vread(u32x2 (&v)[2], uint32_t vrow) {
   constexpr int ks = Q / 4, dt = Q % 4;
-  v[0] = ds_read_tr16_b64<16 * ks * kRowStride + 64 * dt>(vrow);
-  v[1] = ds_read_tr16_b64<(16 * ks + 8) * kRowStride + 64 * dt>(vrow);
+  v[0] = ds_read_tr16_b64<16 * ks * kM32Pitch + 64 * dt>(vrow);
+  v[1] = ds_read_tr16_b64<(16 * ks + 2) * kM32Pitch + 64 * dt>(vrow);
 }
 __device__ __forceinline__ void x32_prefetch(XPre32& xp, const int32_t* list, int gi, int lane, int w,
                                              uint32_t flag_rd, uint32_t pbase, uint32_t vrow) {
@@ -1684,18 +1750,27 @@ struct PhaseX32 {
   }
 };
 
+// The last kXTail steps of phase X run after mid(): the tile barrier and the
+// first K reads of the next phase Y, whose latency those MFMAs cover. The
+// softmax groups (and so every LDS write of the phase) come before.
+constexpr int kXTail = 2;
+constexpr int kXSlots = 4 * (8 - kXTail);
 template <int NG>
-constexpr int soft32_group_at(int k) {  // slot k (of 32 MFMAs) runs group (k NG) / 32 at its first slot
-  return (k * NG) % 32 < NG ? (k * NG) / 32 : -1;
+constexpr int soft32_group_at(int k) {  // slot k (of kXSlots) runs group (k NG) / kXSlots at its first slot
+  return k < kXSlots && (k * NG) % kXSlots < NG ? (k * NG) / kXSlots : -1;
 }
 
 // Phase X of tile j: the factors of tile j (if a wave moved its references),
 // then O^T += V^T P^T for the wave's 4 d-tiles x 4 head blocks x 2 k-steps,
-// with the softmax groups of tile j+1 between the MFMAs (SOFT; MASK: partial).
-template <bool SOFT, bool MASK>
+// with the softmax groups of tile j+1 between the MFMAs (SOFT; MASK: partial)
+// and mid() before the last kXTail steps. mid() ends every LDS read of the
+// phase (its barrier waits for them), so those steps wait for nothing.
+template <bool SOFT, bool MASK, typename Mid>
 __device__ __forceinline__ void phase_x32(XPre32& xp, uint32_t vrow, uint32_t pbase, uint32_t fac_rd, f32x16& s,
                                           Soft32& ss, float c, float inv_c, int cnt, int h, uint32_t pbw,
-                                          uint32_t facw, uint32_t flagw) {
+                                          uint32_t facw, uint32_t flagw, Mid&& mid) {
+  static_assert(kXSlots >= kSoftGroups32<true>, "softmax groups before mid()");
+  static_assert(kXTail <= kX32PF && kXTail <= 4, "every LDS read of the phase issued before mid()");
   using Px = PhaseX32;
   constexpr int VST = kX32PF + 1;
   u32x4 (&pf)[4] = xp.pf;
@@ -1724,7 +1799,10 @@ __device__ __forceinline__ void phase_x32(XPre32& xp, uint32_t vrow, uint32_t pb
     constexpr int q = decltype(qc)::value;
     constexpr int dt = q % 4;
     u32x2 (&vq)[2] = xp.vf[q % VST];
-    if constexpr (q == 0 || q == 4)
+    if constexpr (q == 8 - kXTail) mid();
+    if constexpr (q >= 8 - kXTail)
+      asm volatile("" : "+v"(vq[0]), "+v"(vq[1]));
+    else if constexpr (q == 0 || q == 4)
       asm volatile("s_waitcnt lgkmcnt(%6)"
                    : "+v"(vq[0]), "+v"(vq[1]), "+v"(pf[0]), "+v"(pf[1]), "+v"(pf[2]), "+v"(pf[3])
                    : "n"(Px::wait_at(q)));
@@ -1772,7 +1850,7 @@ __device__ __forceinline__ void store32_block(uint16_t* orow, bool ok, float fo,
 
 template <bool NEG>
 __device__ __forceinline__ void smla_fwd128_mfma32_body(const Params& p) {
-  __shared__ __attribute__((aligned(16))) Smem128 sm;
+  __shared__ __attribute__((aligned(16))) Smem128T<kM32Pitch> sm;
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1794,10 +1872,11 @@ __device__ __forceinline__ void smla_fwd128_mfma32_body(const Params& p) {
   const uint32_t fac_own = fac0 + 128 * w;
   const uint32_t flag_own = flag0 + w;
   const uint32_t wcnt = lds_addr(sm.wcnt);
-  // fragment addresses within a tile: K (token hl, d 8 h of each k-step) and
-  // V^T (rows 4 h + li / 4 (+ 8, + 16 ks), columns 16 ((lane >> 4) & 1) + 4 (li & 3) of each d-tile)
-  const uint32_t kofs = hl * kRowStride + 32 * h;
-  const uint32_t vofs = (4 * h + (li >> 2)) * kRowStride + 32 * (g & 1) + 8 * (li & 3) + 256 * w;
+  // fragment addresses within a tile: K (MFMA row hl, chunk sigma(u, h) of
+  // k-step u) and V^T (MFMA rows 4 h + li / 4 (+ 8, + 16 ks), that is tile rows
+  // 4 (li / 4) + h (+ 2, + 16 ks); columns 16 ((lane >> 4) & 1) + 4 (li & 3) of each d-tile)
+  const uint32_t kofs = m32_row(hl) * kM32Pitch + 64 * h;
+  const uint32_t vofs = (4 * (li >> 2) + h) * kM32Pitch + 32 * (g & 1) + 8 * (li & 3) + 256 * w;
 
   const float c = NEG ? -p.scale_log2 : p.scale_log2;
   const float inv_c = 1.f / c;
@@ -1824,7 +1903,7 @@ __device__ __forceinline__ void smla_fwd128_mfma32_body(const Params& p) {
   int n = compact128(lds_addr(sm.list[0]), len, p.nkv, wcnt, lane, w);
 #pragma unroll
   for (int i = 0; i < k128Ahead; ++i)
-    gather128(sm.list[0], i, n, i < (n + kBK - 1) / kBK, sm.tile(i), kvp, lane, w).all(lane);
+    gather128<kM32Pitch>(sm.list[0], i, n, i < (n + kBK - 1) / kBK, sm.tile(i), kvp, lane, w).all(lane);
 
   Soft32 ss;
   const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
@@ -1853,15 +1932,16 @@ __device__ __forceinline__ void smla_fwd128_mfma32_body(const Params& p) {
     q32_to_operand(qf);
     f32x16 s;
     XPre32 xp;
-    auto phase_x = [&](int j, auto soft, auto mask) {
+    auto phase_x = [&](int j, auto soft, auto mask, auto&& mid) {
       const uint32_t par = j & 1, nxt = par ^ 1;
       const uint32_t vrow = sm.tile(j % k128Ring) + vofs;
       const uint32_t pbase = pb0 + kPbPar * par, fac_rd = fac0 + kFacPar * par;
       const uint32_t pbw = pb_own + kPbPar * nxt, facw = fac_own + kFacPar * nxt, flagw = flag_own + kFlagPar * nxt;
       phase_x32<decltype(soft)::value, decltype(mask)::value>(xp, vrow, pbase, fac_rd, s, ss, c, inv_c,
                                                              decltype(mask)::value ? tile_rows(j + 1, n) : kBK, h,
-                                                             pbw, facw, flagw);
+                                                             pbw, facw, flagw, mid);
     };
+    auto lds_done = [&]() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
     auto prefetch_x = [&](int j) {
       const uint32_t par = j & 1;
       x32_prefetch(xp, lst, j + k128Ahead, lane, w, flag0 + kFlagPar * par, pb0 + kPbPar * par,
@@ -1869,33 +1949,44 @@ __device__ __forceinline__ void smla_fwd128_mfma32_body(const Params& p) {
     };
     if (nt > 0) {
       const NoGather none;
-      phase_y32(sm.tile(0) + kofs, qf, s, none, lane);
+      K32Frags kq;
+      y32_kpre(kq, sm.tile(0) + kofs);
+      phase_y32<0>(kq, sm.tile(0) + kofs, qf, s, none, lane, NoTail{});
       if (nt > 1) {
         soft32_plain<false>(s, ss, c, inv_c, kBK, h, pb_own, fac_own, flag_own);
-        phase_y32(sm.tile(1) + kofs, qf, s, none, lane);
+        y32_kpre(kq, sm.tile(1) + kofs);
+        phase_y32<0>(kq, sm.tile(1) + kofs, qf, s, none, lane, NoTail{});
       } else {
         soft32_plain<true>(s, ss, c, inv_c, tile_rows(0, n), h, pb_own, fac_own, flag_own);
       }
       lds_barrier();  // P(0) visible
       prefetch_x(0);
+      // Iteration j: phase X(j) with the softmax of tile j + 1; before its last
+      // steps one barrier (P(j + 1) and tile j + 2 visible, tile j - 1 free)
+      // and the first K reads of S(j + 2); phase Y computes S(j + 2), gathers
+      // tile j + 3 into tile j - 1's slot and issues the first reads of X(j + 1).
       for (int j = 0; j + 2 < nt; ++j) {
-        phase_x(j, std::true_type{}, std::false_type{});
-        const uint32_t e = xp.e;
-        wait_vmcnt_le(0);  // tile j + 2 landed (issued in phase Y of iteration j - 1)
-        lds_barrier();
-        const Gather128 ga = gather128_make(e, j + k128Ahead, n, j + k128Ahead < nt,
-                                            sm.tile((j + k128Ahead) % k128Ring), kvp, lane, w);
-        phase_y32(sm.tile((j + 2) % k128Ring) + kofs, qf, s, ga, lane, [&]() { prefetch_x(j + 1); });
+        Gather128T<kM32Pitch> ga;
+        const uint32_t krow = sm.tile((j + 2) % k128Ring) + kofs;
+        phase_x(j, std::true_type{}, std::false_type{}, [&]() {
+          const uint32_t e = xp.e;
+          wait_vmcnt_le(0);  // tile j + 2 landed (issued in phase Y of iteration j - 1)
+          lds_barrier();
+          ga = gather128_make<kM32Pitch>(e, j + k128Ahead, n, j + k128Ahead < nt,
+                                         sm.tile((j + k128Ahead) % k128Ring), kvp, lane, w);
+          y32_kpre(kq, krow);
+        });
+        phase_y32<PhaseX32::kPro>(kq, krow, qf, s, ga, lane, [&]() { prefetch_x(j + 1); });
       }
     }
     load_q32(qf, p, more ? tn : t, (more ? hbn : hbase) + 32 * w, lane);
     if (nt > 1) {
-      phase_x(nt - 2, std::true_type{}, std::true_type{});
+      phase_x(nt - 2, std::true_type{}, std::true_type{}, lds_done);
       lds_barrier();
       prefetch_x(nt - 1);
     }
     if (nt > 0) {
-      phase_x(nt - 1, std::false_type{}, std::false_type{});
+      phase_x(nt - 1, std::false_type{}, std::false_type{}, lds_done);
       lds_barrier();
     }
 
@@ -1933,7 +2024,7 @@ __device__ __forceinline__ void smla_fwd128_mfma32_body(const Params& p) {
     if (more) {
 #pragma unroll
       for (int i = 0; i < k128Ahead; ++i)
-        gather128(sm.list[(r + 1) & 1], i, nn, i < (nn + kBK - 1) / kBK, sm.tile(i), kvp, lane, w).all(lane);
+        gather128<kM32Pitch>(sm.list[(r + 1) & 1], i, nn, i < (nn + kBK - 1) / kBK, sm.tile(i), kvp, lane, w).all(lane);
       if (r + 2 < sched.K)  // into this unit's list buffer, read no more
         raw128_dma(lds_addr(sm.list[r & 1]), trow_of(token_of(sched.unit(r + 2))), len, lane, w);
     }
