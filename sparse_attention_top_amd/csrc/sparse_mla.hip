@@ -747,6 +747,16 @@ struct Smem128T {
   __device__ __forceinline__ uint32_t tile(int b) { return lds_addr(area + b * kBK * PITCH); }
 };
 using Smem128 = Smem128T<kRowStride>;
+// Tile rows of the persistent 128-head kernels: pitch 1040 B, and MFMA row m of
+// a tile (a token) held in tile row p128_row(m). Within each block of 16 rows
+// the first eight MFMA rows take the even tile rows and the last eight the odd
+// ones, so that the K fragment reads (16 lanes on 16 rows) and the transposing
+// V^T reads (32 lanes on 8 rows, 32 B each) both spread over all 64 LDS banks;
+// in row order at the 1056 B pitch the K reads met two-way conflicts.
+constexpr int k128Pitch = kRowBytes + 16;
+__host__ __device__ constexpr int p128_row(int m) {
+  return (m & 16) | ((m & 15) < 8 ? 2 * (m & 15) : 2 * ((m & 15) - 8) + 1);
+}
 static_assert(sizeof(Smem128) <= 160 * 1024, "one workgroup per CU");
 
 // An empty asm that "redefines" its operands: code using them cannot move above it.
@@ -858,7 +868,7 @@ __device__ __forceinline__ void phase_y128(uint32_t krow, const bf16x8 (&qf)[2][
   u32x4 kf[KST][2];
   auto kread = [&](auto kc, auto hc) {
     constexpr int k = decltype(kc)::value, h = decltype(hc)::value;
-    kf[k % KST][h] = ds_read_b128<16 * kRowStride * h + 64 * k>(krow);
+    kf[k % KST][h] = ds_read_b128<16 * k128Pitch * h + 64 * k>(krow);
   };
   static_for<0, kYKPF>([&](auto kc) {
     kread(kc, Int<0>{});
@@ -939,9 +949,10 @@ __device__ __forceinline__ Deps soft128_group(f32x4 (&s)[2][2], SoftT& tt, Soft1
   if constexpr (MASK && G < 8) {  // two elements (hb = G & 1, e = 2 (G >> 1) ..) past the count -> -inf
     constexpr int hb = G & 1, e0 = 2 * (G >> 1), sh = e0 >> 2, i0 = e0 & 3;
     pin(s[sh][hb]);
-    const int lim = cnt - 4 * g;  // slot 16 sh + 4 g + i is valid iff 16 sh + i < lim
+    // MFMA row 16 sh + 4 g + i is tile row 16 sh + 2 i + (g < 2 ? 8 g : 8 (g - 2) + 1)
+    const int lim = cnt - (g < 2 ? 8 * g : 8 * (g - 2) + 1);
 #pragma unroll
-    for (int i = i0; i < i0 + 2; ++i) s[sh][hb][i] = (16 * sh + i) < lim ? s[sh][hb][i] : -INFINITY;
+    for (int i = i0; i < i0 + 2; ++i) s[sh][hb][i] = (16 * sh + 2 * i) < lim ? s[sh][hb][i] : -INFINITY;
     return {s[sh][hb][i0], s[sh][hb][i0 + 1]};
   } else if constexpr (G < M + 4) {  // tile max, in-lane: two three-way maxima per group
     constexpr int hb = (G - M) & 1, part = (G - M) >> 1;
@@ -1032,7 +1043,7 @@ __device__ __forceinline__ void x_prefetch(XPre& xp, const int32_t* list, int gi
   static_for<0, kXVPF>([&](auto pc) {
     constexpr int pp = decltype(pc)::value;
     xp.vf[pp][0] = ds_read_tr16_b64<32 * pp>(vrow);
-    xp.vf[pp][1] = ds_read_tr16_b64<16 * kRowStride + 32 * pp>(vrow);
+    xp.vf[pp][1] = ds_read_tr16_b64<16 * k128Pitch + 32 * pp>(vrow);
   });
 }
 
@@ -1083,7 +1094,7 @@ __device__ __forceinline__ void phase_x128(XPre& xp, uint32_t vrow, uint32_t pba
   u32x2 (&vf)[VST][2] = xp.vf;
   auto vread = [&](auto pc, auto hc) {
     constexpr int pp = decltype(pc)::value, h = decltype(hc)::value;
-    vf[pp % VST][h] = ds_read_tr16_b64<16 * kRowStride * h + 32 * (pp % 8)>(vrow);
+    vf[pp % VST][h] = ds_read_tr16_b64<16 * k128Pitch * h + 32 * (pp % 8)>(vrow);
   };
   asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(xp.fl), "+v"(xp.e) : "n"(Px::kPro - 2));
   const uint32_t fl = xp.fl;
@@ -1228,7 +1239,7 @@ __device__ __forceinline__ void store128_block(uint16_t* orow, bool ok, float fo
 
 template <bool NEG>
 __device__ __forceinline__ void smla_fwd128_body(const Params& p) {
-  __shared__ __attribute__((aligned(16))) Smem128 sm;
+  __shared__ __attribute__((aligned(16))) Smem128T<k128Pitch> sm;
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1248,6 +1259,11 @@ __device__ __forceinline__ void smla_fwd128_body(const Params& p) {
   const uint32_t fac_own = fac0 + 8 * w;   // entries 8 li + 2w, + 1
   const uint32_t flag_own = flag0 + w;
   const uint32_t wcnt = lds_addr(sm.wcnt);
+  // fragment offsets within a tile: K (lane: MFMA rows li and 16 + li, chunk
+  // 4 k + g of k-step k); V^T (MFMA rows 4 g + li / 4 and + 16, 4 columns at
+  // 4 (li & 3) of each d-tile, this wave's 128 columns)
+  const uint32_t kofs = p128_row(li) * k128Pitch + 16 * g;
+  const uint32_t vofs = p128_row(4 * g + (li >> 2)) * k128Pitch + 8 * (li & 3) + 256 * w;
 
   // logits c * S with c > 0: a negative scale is carried by q (negation is exact)
   const float c = NEG ? -p.scale_log2 : p.scale_log2;
@@ -1278,7 +1294,7 @@ __device__ __forceinline__ void smla_fwd128_body(const Params& p) {
   int n = compact128(lds_addr(sm.list[0]), len, p.nkv, wcnt, lane, w);
 #pragma unroll
   for (int i = 0; i < k128Ahead; ++i)
-    gather128(sm.list[0], i, n, i < (n + kBK - 1) / kBK, sm.tile(i), kvp, lane, w).all(lane);
+    gather128<k128Pitch>(sm.list[0], i, n, i < (n + kBK - 1) / kBK, sm.tile(i), kvp, lane, w).all(lane);
 
   Soft128 ss;
   for (int r = 0;; ++r) {
@@ -1319,7 +1335,7 @@ __device__ __forceinline__ void smla_fwd128_body(const Params& p) {
     // j + 1 between its MFMAs (MASK: tile j + 1 is the partial last one)
     auto phase_x = [&](int j, auto soft, auto mask) {
       const uint32_t par = j & 1, nxt = par ^ 1;
-      const uint32_t vrow = v_frag_addr(sm.tile(j % k128Ring), g, li) + 256 * w;
+      const uint32_t vrow = opaque(sm.tile(j % k128Ring) + vofs);
       const uint32_t pbase = pb0 + kPbPar * par, fac_rd = fac0 + kFacPar * par;
       const uint32_t pbw = pb_own + kPbPar * nxt, facw = fac_own + kFacPar * nxt, flagw = flag_own + kFlagPar * nxt;
       phase_x128<decltype(soft)::value, decltype(mask)::value>(xp, vrow, pbase, fac_rd, s, ss, c, inv_c,
@@ -1331,15 +1347,15 @@ __device__ __forceinline__ void smla_fwd128_body(const Params& p) {
     auto prefetch_x = [&](int j) {
       const uint32_t par = j & 1;
       x_prefetch(xp, lst, j + k128Ahead, lane, w, flag0 + kFlagPar * par, pb0 + kPbPar * par,
-                 v_frag_addr(sm.tile(j % k128Ring), g, li) + 256 * w);
+                 opaque(sm.tile(j % k128Ring) + vofs));
     };
     if (nt > 0) {
       const NoGather none;
       // S(0), its softmax (P(0) in parity 0), S(1)
-      phase_y128(k_frag_addr(sm.tile(0), g, li), qf, s, none, lane);
+      phase_y128(opaque(sm.tile(0) + kofs), qf, s, none, lane);
       if (nt > 1) {
         soft128_plain<false>(s, ss, c, inv_c, kBK, g, pb_own, fac_own, flag_own);
-        phase_y128(k_frag_addr(sm.tile(1), g, li), qf, s, none, lane);
+        phase_y128(opaque(sm.tile(1) + kofs), qf, s, none, lane);
       } else {
         soft128_plain<true>(s, ss, c, inv_c, tile_rows(0, n), g, pb_own, fac_own, flag_own);
       }
@@ -1354,9 +1370,9 @@ __device__ __forceinline__ void smla_fwd128_body(const Params& p) {
         const uint32_t e = xp.e;  // list entry of tile j + 3 (completed in phase X)
         wait_vmcnt_le(0);         // tile j + 2 landed (issued in phase Y of iteration j - 1)
         lds_barrier();
-        const Gather128 ga = gather128_make(e, j + k128Ahead, n, j + k128Ahead < nt,
+        const auto ga = gather128_make<k128Pitch>(e, j + k128Ahead, n, j + k128Ahead < nt,
                                             sm.tile((j + k128Ahead) % k128Ring), kvp, lane, w);
-        phase_y128(k_frag_addr(sm.tile((j + 2) % k128Ring), g, li), qf, s, ga, lane, [&]() { prefetch_x(j + 1); });
+        phase_y128(opaque(sm.tile((j + 2) % k128Ring) + kofs), qf, s, ga, lane, [&]() { prefetch_x(j + 1); });
       }
     }
     // every S of this unit is done: q of the next unit (this unit's again for
@@ -1410,7 +1426,7 @@ __device__ __forceinline__ void smla_fwd128_body(const Params& p) {
     if (more) {
 #pragma unroll
       for (int i = 0; i < k128Ahead; ++i)
-        gather128(sm.list[(r + 1) & 1], i, nn, i < (nn + kBK - 1) / kBK, sm.tile(i), kvp, lane, w).all(lane);
+        gather128<k128Pitch>(sm.list[(r + 1) & 1], i, nn, i < (nn + kBK - 1) / kBK, sm.tile(i), kvp, lane, w).all(lane);
       if (r + 2 < sched.K)  // into this unit's list buffer, read no more
         raw128_dma(lds_addr(sm.list[r & 1]), trow_of(token_of(sched.unit(r + 2))), len, lane, w);
     }
@@ -1427,618 +1443,6 @@ __device__ __forceinline__ void smla_fwd128_body(const Params& p) {
 template <bool NEG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void smla_fwd128_kernel(const Params p) {
   smla_fwd128_body<NEG>(p);
-}
-
-// ---------------------------------------------------------------------------
-// The 128-head kernel on the 32x32x16 MFMA. The same workgroup, schedule, LDS
-// and unit boundary as smla_fwd128_kernel; the two contractions take a 32x32
-// output tile per instruction (half the MFMA instructions, and half the V^T
-// reads per flop), so that each phase leaves more issue slots between its
-// MFMAs for the softmax, the transposing reads and the gather issue.
-//   MFMA row m of a tile (a token) is tile row m32_row(m): within each block of
-//     16 rows the two 2-bit halves of the index trade places. With the row
-//     pitch kM32Pitch (1040 B) the K reads (16 lanes on 16 rows) and the
-//     transposing V reads (32 lanes on 4 rows, 64 B each, the rows 4 apart)
-//     both spread over all LDS banks; in row order at a 1056 B pitch each of
-//     them ran at half the LDS rate (measured 125 B/clk per CU against 246
-//     and 200).
-//   S^T (32 tokens x 32 heads of this wave) = K Q^T: A = K [32 tokens x 16 d]
-//     (lane: token lane % 32, eight d of the k-step, one ds_read_b128), B =
-//     Q^T [16 d x 32 heads] held in VGPRs (32 k-steps). The sum runs over d in
-//     any order that K and Q share: k-step u, lane half h takes the 8-wide d
-//     chunk sigma(u, h) below, the order the q load leaves them in.
-//     s[r] = S^T[token 8 (r / 4) + 4 (lane / 32) + r % 4][head lane % 32]: one
-//     head per lane, sixteen of its tokens (the other sixteen in lane ^ 32).
-//   O^T (32 d x 32 heads) += V^T P^T per (d-tile, head block): A = V^T from
-//     two transposing reads, B = P^T [16 k x 32 heads]. The k order of a
-//     k-step s is tokens 16 s + 4 h + (0..3) then 16 s + 8 + 4 h + (0..3) for
-//     lane half h, which is exactly S^T registers 8 s .. 8 s + 7: P leaves the
-//     softmax already in B-operand layout.
-//   acc tuple 4 b + dt (16 AGPRs): O^T[d 128 w + 32 dt + 8 (r / 4) + 4 h + r % 4]
-//     [head 32 b + lane % 32].
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-constexpr int kM32Pitch = kRowBytes + 16;
-__host__ __device__ constexpr int m32_row(int m) { return (m & ~15) | ((m & 3) << 2) | ((m >> 2) & 3); }
-
-template <int T>
-__device__ __forceinline__ void acc32_mfma(const bf16x8& a, const bf16x8& b, float d0) {
-  static_assert(T >= 0 && T < 16, "one 16-register tuple");
-  acc32_mfma_t<T>(a, b, d0);
-}
-__device__ __forceinline__ void mfma32_first(f32x16& c, const u32x4& a, const u32x4& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma32(f32x16& c, const u32x4& a, const u32x4& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
-}
-
-// Q^T fragments of the wave's 32 heads h0 .. h0 + 31, in two steps. A 1 KiB
-// row of q is 64 chunks of 16 bytes (chunk c = d 8 c .. 8 c + 7); the address
-// unit serves a load at one 4-lane quad per cycle when each quad reads 64
-// contiguous bytes, and about four times slower when its lanes read different
-// rows (the natural MFMA operand layout, one head per lane).
-// The load: instruction i (0..31), lane L reads chunk 8 (i % 8) + 4 (L / 32) +
-// L % 4 of head 4 ((L / 4) % 8) + i / 8, so that each instruction reads 128
-// contiguous bytes of each of 8 rows. A head past H loads head H - 1 (never
-// stored), with no branch.
-__device__ __forceinline__ void load_q32(bf16x8 (&qf)[32], const Params& p, int t, int h0, int lane) {
-  const int nb = 4 * ((lane >> 2) & 7);
-  const int cofs = 8 * (4 * (lane >> 5) + (lane & 3));  // elements
-#pragma unroll
-  for (int hi = 0; hi < 4; ++hi) {
-    const bf16x8* src = (const bf16x8*)(p.q + ((size_t)t * p.H + min(h0 + nb + hi, p.H - 1)) * kD + cofs);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) qf[8 * hi + c] = __builtin_nontemporal_load(src + 8 * c);
-  }
-}
-// One step of the transposition: lane bit B (1 or 2) trades places with bit
-// log2(B) + 3 of the register index. For each register pair (lo: index bit
-// clear, hi: set), a lane with bit B clear keeps lo and takes hi's value from
-// lane L ^ B in place of its own hi; a lane with bit B set does the converse.
-// One v_cndmask_b32 with a DPP quad permutation of its first source per value,
-// the lane masks in VCC (the compiler would emit a separate DPP move per value);
-// each block starts with the two wait states a DPP read of a VALU result needs.
-template <int B>
-__device__ __forceinline__ void q32_swap_step(bf16x8 (&qf)[32]) {
-  constexpr int R = B == 1 ? 8 : 16;  // register index bit
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    if (i & R) continue;
-    const u32x4 lo = __builtin_bit_cast(u32x4, qf[i]);
-    u32x4 hi = __builtin_bit_cast(u32x4, qf[i + R]);
-    u32x4 nl;  // the new lo; the new hi is written in place, after every read of the old hi
-#define SMLA_Q32_STEP(PERM, LOWER, UPPER)                                                                         \
-  asm volatile("s_nop 1\n\t"                                                                                      \
-               "s_mov_b32 vcc_lo, " LOWER "\n\ts_mov_b32 vcc_hi, " LOWER "\n\t"                                   \
-               "v_cndmask_b32_dpp %0, %4, %8, vcc " PERM " row_mask:0xf bank_mask:0xf\n\t"                         \
-               "v_cndmask_b32_dpp %1, %5, %9, vcc " PERM " row_mask:0xf bank_mask:0xf\n\t"                         \
-               "v_cndmask_b32_dpp %2, %6, %10, vcc " PERM " row_mask:0xf bank_mask:0xf\n\t"                        \
-               "v_cndmask_b32_dpp %3, %7, %11, vcc " PERM " row_mask:0xf bank_mask:0xf\n\t"                        \
-               "s_mov_b32 vcc_lo, " UPPER "\n\ts_mov_b32 vcc_hi, " UPPER "\n\t"                                   \
-               "v_cndmask_b32_dpp %4, %8, %4, vcc " PERM " row_mask:0xf bank_mask:0xf\n\t"                         \
-               "v_cndmask_b32_dpp %5, %9, %5, vcc " PERM " row_mask:0xf bank_mask:0xf\n\t"                         \
-               "v_cndmask_b32_dpp %6, %10, %6, vcc " PERM " row_mask:0xf bank_mask:0xf\n\t"                        \
-               "v_cndmask_b32_dpp %7, %11, %7, vcc " PERM " row_mask:0xf bank_mask:0xf"                              \
-               : "=&v"(nl[0]), "=&v"(nl[1]), "=&v"(nl[2]), "=&v"(nl[3]), "+v"(hi[0]), "+v"(hi[1]), "+v"(hi[2]),   \
-                 "+v"(hi[3])                                                                                     \
-               : "v"(lo[0]), "v"(lo[1]), "v"(lo[2]), "v"(lo[3])                                                  \
-               : "vcc")
-    if constexpr (B == 1)
-      SMLA_Q32_STEP("quad_perm:[1,0,3,2]", "0x55555555", "0xaaaaaaaa");
-    else
-      SMLA_Q32_STEP("quad_perm:[2,3,0,1]", "0x33333333", "0xcccccccc");
-#undef SMLA_Q32_STEP
-    qf[i] = __builtin_bit_cast(bf16x8, nl);
-    qf[i + R] = __builtin_bit_cast(bf16x8, hi);
-  }
-}
-// Once the loads have landed: two steps move the chunk bits out of lane bits
-// 0 and 1 and the head bits in, after which lane (head lane % 32, h = lane /
-// 32) holds in qf[u] the chunk sigma(u, h) = 8 (u % 8) + 4 h + 2 ((u / 16) % 2)
-// + (u / 8) % 2 of its head: the B operand of k-step u. The VALU writes are
-// followed by the wait states an MFMA reading them needs.
-__device__ __forceinline__ void q32_to_operand(bf16x8 (&qf)[32]) {
-  q32_swap_step<1>(qf);
-  q32_swap_step<2>(qf);
-#pragma unroll
-  for (int u = 0; u < 32; ++u) asm volatile("" : "+v"(qf[u]));
-  asm volatile("s_nop 4" ::: "memory");
-}
-// Byte offset, within a row, of the chunk sigma(u, 0) read by k-step u (lane
-// half h adds 64).
-template <int U>
-constexpr int q32_chunk_ofs = 128 * (U % 8) + 32 * ((U / 16) % 2) + 16 * ((U / 8) % 2);
-
-// Phase Y: S^T of tile krow for the wave's 32 heads, 32 k-steps of one MFMA
-// (one accumulator chain), K fragments kY32PF steps ahead (the first ones
-// issued by y32_kpre, possibly before other work), the eight gather rows of
-// the next tile every fourth step, and tail() -- the first reads of the next
-// phase X, kXPre reads -- after MFMA kYTail, so that they land under the last
-// MFMAs; every wait counts the reads issued after the one it needs.
-constexpr int kY32PF = 3;
-constexpr int kYTail = 27;
-struct K32Frags {
-  u32x4 kf[kY32PF + 1];
-};
-__device__ __forceinline__ void y32_kpre(K32Frags& k, uint32_t krow) {
-  static_for<0, kY32PF>([&](auto kc) {
-    constexpr int i = decltype(kc)::value;
-    k.kf[i] = ds_read_b128<q32_chunk_ofs<i>>(krow);
-  });
-}
-template <int XPRE>
-constexpr int y32_wait(int u) {  // LDS reads issued after K(u) by the wait of step u
-  int n = (kY32PF - 1) < (31 - u) ? (kY32PF - 1) : (31 - u);
-  if (XPRE > 0 && kYTail < u && u <= kYTail + kY32PF) n += XPRE;  // the prefetch, issued after K(kYTail + PF)
-  return n;
-}
-template <int XPRE, typename GA, typename Tail>
-__device__ __forceinline__ void phase_y32(K32Frags& k, uint32_t krow, const bf16x8 (&qf)[32], f32x16& s, const GA& ga,
-                                          int lane, Tail&& tail) {
-  constexpr int KST = kY32PF + 1;
-  u32x4 (&kf)[KST] = k.kf;
-  static_for<0, 32>([&](auto uc) {
-    constexpr int u = decltype(uc)::value;
-    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(kf[u % KST]) : "n"(y32_wait<XPRE>(u)));
-    if constexpr (u == 0) mfma32_first(s, kf[0], __builtin_bit_cast(u32x4, qf[0]));
-    else mfma32(s, kf[u % KST], __builtin_bit_cast(u32x4, qf[u]));
-    if constexpr (u + kY32PF < 32)
-      kf[(u + kY32PF) % KST] = ds_read_b128<q32_chunk_ofs<u + kY32PF>>(krow);
-    if constexpr (u % 4 == 1) ga.template row<u / 4>(lane);
-    if constexpr (u == kYTail) tail();
-    __builtin_amdgcn_sched_barrier(0);
-  });
-  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" ::: "memory");  // MFMA write -> VALU read distance
-  asm volatile("" : "+v"(s));
-}
-
-// Per-token softmax state of this lane's head (lane % 32; lane ^ 32 holds the same).
-struct Soft32 {
-  float l_part;  // this lane's share of the row sum (its sixteen tokens) relative to m_ref
-  float nmu;     // -m_ref (0 while m_ref is -inf)
-  float thr;     // a raw S value above this moves the reference: (m_ref + tau) / c
-  __device__ __forceinline__ float m_ref() const { return thr == -INFINITY ? -INFINITY : -nmu; }
-};
-struct Soft32T {
-  float t[3];
-  float mxr;
-  uint32_t flag;
-};
-
-// The rare step: some lane's tile max passed its threshold. Each head takes its
-// max over its two lanes; where that passes the reference by more than
-// kLazyTau the reference moves (factor published for the P.V waves; 1 elsewhere).
-__device__ __forceinline__ void soft32_move(Soft32T& tt, Soft32& ss, float c, float inv_c, uint32_t facw) {
-  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tt.mxr), __float_as_uint(tt.mxr), false, false);
-  const float mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
-  const float mr = ss.m_ref();
-  const float mn = mx > mr + kLazyTau ? mx : mr;
-  const float alpha = (mn == mr || mr == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mr - mn);
-  ss.l_part *= alpha;
-  ss.nmu = mn == -INFINITY ? 0.f : -mn;
-  ss.thr = (mn + kLazyTau) * inv_c;
-  *(LDS_AS float*)(uintptr_t)(facw) = alpha;  // both lanes of a head write the same value
-  tt.flag = 1;
-}
-
-// Group G of the softmax of one tile, between two MFMAs of phase X. MASK: the
-// tile is partial (tokens >= cnt -> -inf). Logits are c S with c > 0.
-template <int G, bool MASK>
-__device__ __forceinline__ float soft32_group(f32x16& s, Soft32T& tt, Soft32& ss, float c, float inv_c, int cnt,
-                                              int h, uint32_t pbw, uint32_t facw, uint32_t flagw) {
-  constexpr int M = MASK ? 4 : 0;
-  if constexpr (MASK && G < 4) {  // registers 4 G .. 4 G + 3: MFMA rows 8 G + 4 h + i, tile rows b + 4 i
-    pin1(s);
-    const int lim = cnt - (16 * (G / 2) + 2 * (G % 2) + h);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s[4 * G + i] = 4 * i < lim ? s[4 * G + i] : -INFINITY;
-    return s[4 * G];
-  } else if constexpr (G == M + 0) {  // tile max, in-lane
-    pin1(s);
-    tt.t[0] = vmax3(s[0], s[1], s[2]);
-    tt.t[1] = vmax3(s[3], s[4], s[5]);
-    tt.t[2] = vmax3(s[6], s[7], s[8]);
-    return tt.t[2];
-  } else if constexpr (G == M + 1) {
-    pin1(s);
-    pin(tt.t[0], tt.t[1], tt.t[2]);
-    tt.t[0] = vmax3(tt.t[0], s[9], s[10]);
-    tt.t[1] = vmax3(tt.t[1], s[11], s[12]);
-    tt.t[2] = vmax3(tt.t[2], s[13], s[14]);
-    return tt.t[2];
-  } else if constexpr (G == M + 2) {
-    pin1(s);
-    pin(tt.t[0], tt.t[1], tt.t[2]);
-    tt.mxr = vmax3(tt.t[0], tt.t[1], vmax(tt.t[2], s[15]));
-    return tt.mxr;
-  } else if constexpr (G == M + 3) {  // does the reference move (rare)?
-    pin(tt.mxr, ss.thr);
-    tt.flag = 0;
-    if (__ballot(tt.mxr > ss.thr) != 0ull) soft32_move(tt, ss, c, inv_c, facw);
-    return ss.nmu;
-  } else if constexpr (G < M + 12) {  // p = 2^(c S - m), in place, two per group
-    constexpr int e = 2 * (G - M - 4);
-    pin1(s);
-    pin1(ss.nmu);
-    s[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, ss.nmu));
-    s[e + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e + 1], c, ss.nmu));
-    return s[e + 1];
-  } else if constexpr (G < M + 14) {  // P of k-step ks in bf16 (B-operand layout), published
-    constexpr int ks = G - M - 12;
-    pin1(s);
-    const u32x4 pk = u32x4{bf16pair(s[8 * ks], s[8 * ks + 1]), bf16pair(s[8 * ks + 2], s[8 * ks + 3]),
-                           bf16pair(s[8 * ks + 4], s[8 * ks + 5]), bf16pair(s[8 * ks + 6], s[8 * ks + 7])};
-    *(LDS_AS u32x4*)(uintptr_t)(pbw + 4096 * ks) = pk;
-    return __uint_as_float(pk[3]);
-  } else if constexpr (G < M + 18) {  // row sums of the fp32 p, in place
-    constexpr int q = G - M - 14;  // registers 4 q .. 4 q + 3
-    pin1(s);
-    s[4 * q] = (s[4 * q] + s[4 * q + 1]) + (s[4 * q + 2] + s[4 * q + 3]);
-    return s[4 * q];
-  } else if constexpr (G == M + 18) {
-    pin1(s);
-    pin1(ss.l_part);
-    ss.l_part += (s[0] + s[4]) + (s[8] + s[12]);
-    return ss.l_part;
-  } else if constexpr (G == M + 19) {  // publish whether a factor was written
-    pin1(tt.flag);
-    *(LDS_AS uint8_t*)(uintptr_t)(flagw) = (uint8_t)tt.flag;
-    return c;
-  } else {
-    return c;
-  }
-}
-template <bool MASK>
-constexpr int kSoftGroups32 = MASK ? 24 : 20;
-
-template <bool MASK>
-__device__ __forceinline__ void soft32_plain(f32x16& s, Soft32& ss, float c, float inv_c, int cnt, int h, uint32_t pbw,
-                                             uint32_t facw, uint32_t flagw) {
-  Soft32T tt;
-  static_for<0, kSoftGroups32<MASK>>([&](auto gc) {
-    (void)soft32_group<decltype(gc)::value, MASK>(s, tt, ss, c, inv_c, cnt, h, pbw, facw, flagw);
-  });
-}
-
-// The first LDS reads of phase X, issued ahead: the list entry of the gather
-// after next, the four wave flags, the P fragments of k-step 0 for the four
-// head blocks, and the first kX32PF V^T fragments.
-constexpr int kX32PF = 2;
-struct XPre32 {
-  uint32_t e;
-  uint32_t fl;
-  u32x4 pf[4];
-  u32x2 vf[kX32PF + 1][2];
-};
-// V^T fragment (step q = 4 ks + dt): MFMA rows 16 ks + 4 h + (0..3) and + 8,
-// i.e. tile rows 16 ks + h + 4 (0..3) and + 2, 32 columns at 32 dt
-template <int Q>
-__device__ __forceinline__ void x32_vread(u32x2 (&v)[2], uint32_t vrow) {
-  constexpr int ks = Q / 4, dt = Q % 4;
-  v[0] = ds_read_tr16_b64<16 * ks * kM32Pitch + 64 * dt>(vrow);
-  v[1] = ds_read_tr16_b64<(16 * ks + 2) * kM32Pitch + 64 * dt>(vrow);
-}
-__device__ __forceinline__ void x32_prefetch(XPre32& xp, const int32_t* list, int gi, int lane, int w,
-                                             uint32_t flag_rd, uint32_t pbase, uint32_t vrow) {
-  xp.e = gather128_read(list, gi, lane, w);
-  asm volatile("ds_read_b32 %0, %1" : "=v"(xp.fl) : "v"(flag_rd));
-  static_for<0, 4>([&](auto bc) { xp.pf[decltype(bc)::value] = ds_read_b128<1024 * decltype(bc)::value>(pbase); });
-  static_for<0, kX32PF>([&](auto qc) { x32_vread<decltype(qc)::value>(xp.vf[decltype(qc)::value], vrow); });
-}
-
-// LDS reads of phase X in issue order: the prefetch (1 + 1 + 4 + 2 PF); at step
-// q (k-step q / 4, d-tile q % 4), V(q + PF) after its first MFMA; at step 3,
-// the k-step 1 P fragment of head block b after MFMA b (into its register).
-struct PhaseX32 {
-  static constexpr int kPro = 2 + 4 + 2 * kX32PF;
-  static constexpr int before(int q) {  // reads issued before the wait of step q
-    int r = kPro;
-    for (int s = 0; s < q; ++s) r += (s + kX32PF < 8 ? 2 : 0) + (s == 3 ? 4 : 0);
-    return r;
-  }
-  static constexpr int pos_v(int q) {  // position (1-based count) of the second read of V(q)
-    if (q < kX32PF) return 6 + 2 * (q + 1);
-    const int s = q - kX32PF;  // issued in step s, right after its first MFMA
-    return before(s) + 2;
-  }
-  static constexpr int wait_at(int q) {
-    int need = pos_v(q);
-    if (q == 0 && need < 6) need = 6;
-    if (q == 4 && need < before(4)) need = before(4);  // the k-step 1 P fragments
-    return before(q) - need;
-  }
-};
-
-// The last kXTail steps of phase X run after mid(): the tile barrier and the
-// first K reads of the next phase Y, whose latency those MFMAs cover. The
-// softmax groups (and so every LDS write of the phase) come before.
-constexpr int kXTail = 2;
-constexpr int kXSlots = 4 * (8 - kXTail);
-template <int NG>
-constexpr int soft32_group_at(int k) {  // slot k (of kXSlots) runs group (k NG) / kXSlots at its first slot
-  return k < kXSlots && (k * NG) % kXSlots < NG ? (k * NG) / kXSlots : -1;
-}
-
-// Phase X of tile j: the factors of tile j (if a wave moved its references),
-// then O^T += V^T P^T for the wave's 4 d-tiles x 4 head blocks x 2 k-steps,
-// with the softmax groups of tile j+1 between the MFMAs (SOFT; MASK: partial)
-// and mid() before the last kXTail steps. mid() ends every LDS read of the
-// phase (its barrier waits for them), so those steps wait for nothing.
-template <bool SOFT, bool MASK, typename Mid>
-__device__ __forceinline__ void phase_x32(XPre32& xp, uint32_t vrow, uint32_t pbase, uint32_t fac_rd, f32x16& s,
-                                          Soft32& ss, float c, float inv_c, int cnt, int h, uint32_t pbw,
-                                          uint32_t facw, uint32_t flagw, Mid&& mid) {
-  static_assert(kXSlots >= kSoftGroups32<true>, "softmax groups before mid()");
-  static_assert(kXTail <= kX32PF && kXTail <= 4, "every LDS read of the phase issued before mid()");
-  using Px = PhaseX32;
-  constexpr int VST = kX32PF + 1;
-  u32x4 (&pf)[4] = xp.pf;
-  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(xp.fl), "+v"(xp.e) : "n"(Px::kPro - 2));
-  const uint32_t fl = xp.fl;
-  if (__ballot(fl != 0u) != 0ull) {
-    // some wave moved references: rescale the head blocks of the waves that did
-    float f[4];
-    asm volatile("ds_read_b32 %0, %1 offset:0" : "=v"(f[0]) : "v"(fac_rd));
-    asm volatile("ds_read_b32 %0, %1 offset:128" : "=v"(f[1]) : "v"(fac_rd));
-    asm volatile("ds_read_b32 %0, %1 offset:256" : "=v"(f[2]) : "v"(fac_rd));
-    asm volatile("ds_read_b32 %0, %1 offset:384" : "=v"(f[3]) : "v"(fac_rd));
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]));
-    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" ::: "memory");  // MFMA write -> accumulator read distance
-    static_for<0, 4>([&](auto bc) {
-      constexpr int b = decltype(bc)::value;
-      if (__ballot(((fl >> (8 * b)) & 0xffu) != 0u && f[b] != 1.f) != 0ull)
-        static_for<0, 4>([&](auto dc) { acc32_scale_t<4 * b + decltype(dc)::value>(f[b]); });
-    });
-    asm volatile("s_nop 4" ::: "memory");  // accumulators rescaled by VALU, read by the MFMAs below
-  }
-  Soft32T tt;
-  float dep = c;
-  constexpr int NG = kSoftGroups32<MASK>;
-  static_for<0, 8>([&](auto qc) {
-    constexpr int q = decltype(qc)::value;
-    constexpr int dt = q % 4;
-    u32x2 (&vq)[2] = xp.vf[q % VST];
-    if constexpr (q == 8 - kXTail) mid();
-    if constexpr (q >= 8 - kXTail)
-      asm volatile("" : "+v"(vq[0]), "+v"(vq[1]));
-    else if constexpr (q == 0 || q == 4)
-      asm volatile("s_waitcnt lgkmcnt(%6)"
-                   : "+v"(vq[0]), "+v"(vq[1]), "+v"(pf[0]), "+v"(pf[1]), "+v"(pf[2]), "+v"(pf[3])
-                   : "n"(Px::wait_at(q)));
-    else
-      asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(vq[0]), "+v"(vq[1]) : "n"(Px::wait_at(q)));
-    const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{vq[0][0], vq[0][1], vq[1][0], vq[1][1]});
-    static_for<0, 4>([&](auto bc) {
-      constexpr int b = decltype(bc)::value;
-      acc32_mfma<4 * b + dt>(va, __builtin_bit_cast(bf16x8, pf[b]), dep);
-      if constexpr (b == 0 && q + kX32PF < 8) x32_vread<q + kX32PF>(xp.vf[(q + kX32PF) % VST], vrow);
-      // the k-step 1 P fragment replaces this one after its last reader
-      if constexpr (q == 3) pf[b] = ds_read_b128<4096 + 1024 * b>(pbase);
-      constexpr int G = soft32_group_at<NG>(4 * q + b);
-      if constexpr (SOFT && G >= 0) dep = soft32_group<G, MASK>(s, tt, ss, c, inv_c, cnt, h, pbw, facw, flagw);
-    });
-    __builtin_amdgcn_sched_barrier(0);
-  });
-}
-
-// Output of head block b: per d-tile, scale and round the tuple, then exchange
-// the upper half-wave of each register of pair (j, j + 1) with the lower half
-// of the other (v_permlane32_swap), after which lane (head, half) holds eight
-// consecutive d: 32 dt + 16 pair + 8 half .. + 8. 16-byte stores.
-template <int B>
-__device__ __forceinline__ void store32_block(uint16_t* orow, bool ok, float fo, int half) {
-  static_for<0, 4>([&](auto dc) {
-    constexpr int dt = decltype(dc)::value;
-    float a[16];
-    acc32_read_t<4 * B + dt>(a);
-    uint32_t x[4][2];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[j][0] = bf16pair(a[4 * j] * fo, a[4 * j + 1] * fo);
-      x[j][1] = bf16pair(a[4 * j + 2] * fo, a[4 * j + 3] * fo);
-    }
-#pragma unroll
-    for (int pr = 0; pr < 2; ++pr) {
-      const auto s0 = __builtin_amdgcn_permlane32_swap(x[2 * pr][0], x[2 * pr + 1][0], false, false);
-      const auto s1 = __builtin_amdgcn_permlane32_swap(x[2 * pr][1], x[2 * pr + 1][1], false, false);
-      const u32x4 v = u32x4{s0[0], s1[0], s0[1], s1[1]};
-      if (ok) *(u32x4*)(orow + 32 * dt + 16 * pr + 8 * half) = v;
-    }
-  });
-}
-
-template <bool NEG>
-__device__ __forceinline__ void smla_fwd128_mfma32_body(const Params& p) {
-  __shared__ __attribute__((aligned(16))) Smem128T<kM32Pitch> sm;
-
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 4;
-  const int li = lane & 15;
-  const int h = lane >> 5;    // half of the wave: which sixteen tokens of a tile, which 8 d of a K fragment
-  const int hl = lane & 31;   // head within the wave's 32 (S) or a head block (P.V)
-  const int nwg = gridDim.x, b = blockIdx.x;
-  const int units = p.T * p.head_groups;
-
-  // exchange addresses (tile parity par: + par * the buffer size): P of head
-  // block o, k-step ks at pbuf + 4096 ks + 1024 o + 16 lane; the factor of
-  // head 32 o + hl at fac + 128 o + 4 hl; wave w's flag at byte flag + w
-  const uint32_t pb0 = lds_addr(sm.pbuf[0]) + 16 * lane;
-  const uint32_t fac0 = lds_addr(sm.fac[0]) + 4 * hl;
-  const uint32_t flag0 = lds_addr(sm.flag[0]);
-  constexpr uint32_t kPbPar = sizeof(sm.pbuf[0]), kFacPar = sizeof(sm.fac[0]), kFlagPar = sizeof(sm.flag[0]);
-  const uint32_t pb_own = pb0 + 1024 * w;
-  const uint32_t fac_own = fac0 + 128 * w;
-  const uint32_t flag_own = flag0 + w;
-  const uint32_t wcnt = lds_addr(sm.wcnt);
-  // fragment addresses within a tile: K (MFMA row hl, chunk sigma(u, h) of
-  // k-step u) and V^T (MFMA rows 4 h + li / 4 (+ 8, + 16 ks), that is tile rows
-  // 4 (li / 4) + h (+ 2, + 16 ks); columns 16 ((lane >> 4) & 1) + 4 (li & 3) of each d-tile)
-  const uint32_t kofs = m32_row(hl) * kM32Pitch + 64 * h;
-  const uint32_t vofs = (4 * (li >> 2) + h) * kM32Pitch + 32 * (g & 1) + 8 * (li & 3) + 256 * w;
-
-  const float c = NEG ? -p.scale_log2 : p.scale_log2;
-  const float inv_c = 1.f / c;
-  const int len = p.topk_n;  // <= k128Cap: one segment per unit
-  auto trow_of = [&](int t) {
-    return len > 0 ? p.topk + (size_t)t * len : (const int32_t*)(const void*)p.q;
-  };
-  auto token_of = [&](int v) { return p.T - 1 - v / p.head_groups; };
-  auto hbase_of = [&](int v) { return (v % p.head_groups) * 128; };
-  const uint16_t* kvp = p.kv;
-
-  const Sched128 sched(b, nwg, units);
-  int v = sched.unit(0);
-  int t = token_of(v), hbase = hbase_of(v);
-  raw128_dma(lds_addr(sm.list[0]), trow_of(t), len, lane, w);
-  bf16x8 qf[32];
-  load_q32(qf, p, t, hbase + 32 * w, lane);
-  const bool two = sched.K > 1;
-  if (two) raw128_dma(lds_addr(sm.list[1]), trow_of(token_of(sched.unit(1))), len, lane, w);
-  acc128_claim_and_zero();
-  // issued: 4 list loads, 32 q loads (, 4 loads of the next list)
-  if (two) asm volatile("s_waitcnt vmcnt(36)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
-  int n = compact128(lds_addr(sm.list[0]), len, p.nkv, wcnt, lane, w);
-#pragma unroll
-  for (int i = 0; i < k128Ahead; ++i)
-    gather128<kM32Pitch>(sm.list[0], i, n, i < (n + kBK - 1) / kBK, sm.tile(i), kvp, lane, w).all(lane);
-
-  Soft32 ss;
-  const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
-  for (int r = 0;; ++r) {
-    const int32_t* lst = sm.list[r & 1];
-    const int nt = (n + kBK - 1) / kBK;
-    const bool more = r + 1 < sched.K;
-    const int vn = more ? sched.unit(r + 1) : 0;
-    const int tn = more ? token_of(vn) : 0, hbn = more ? hbase_of(vn) : 0;
-    ss.l_part = 0.f;
-    ss.nmu = 0.f;
-    ss.thr = -INFINITY;
-    float sk;
-    {
-      const int head = hbase + 32 * w + hl;
-      sk = (p.sink != nullptr && head < p.H) ? p.sink[head] : -INFINITY;
-    }
-    wait_vmcnt_le(0);  // q and tiles 0..2 (and the previous unit's stores)
-    asm volatile("" : "+v"(sk));
-    lds_barrier();
-    if constexpr (NEG) {
-#pragma unroll
-      for (int k = 0; k < 32; ++k)
-        qf[k] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, qf[k]) ^ 0x80008000u);
-    }
-    q32_to_operand(qf);
-    f32x16 s;
-    XPre32 xp;
-    auto phase_x = [&](int j, auto soft, auto mask, auto&& mid) {
-      const uint32_t par = j & 1, nxt = par ^ 1;
-      const uint32_t vrow = sm.tile(j % k128Ring) + vofs;
-      const uint32_t pbase = pb0 + kPbPar * par, fac_rd = fac0 + kFacPar * par;
-      const uint32_t pbw = pb_own + kPbPar * nxt, facw = fac_own + kFacPar * nxt, flagw = flag_own + kFlagPar * nxt;
-      phase_x32<decltype(soft)::value, decltype(mask)::value>(xp, vrow, pbase, fac_rd, s, ss, c, inv_c,
-                                                             decltype(mask)::value ? tile_rows(j + 1, n) : kBK, h,
-                                                             pbw, facw, flagw, mid);
-    };
-    auto lds_done = [&]() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
-    auto prefetch_x = [&](int j) {
-      const uint32_t par = j & 1;
-      x32_prefetch(xp, lst, j + k128Ahead, lane, w, flag0 + kFlagPar * par, pb0 + kPbPar * par,
-                   sm.tile(j % k128Ring) + vofs);
-    };
-    if (nt > 0) {
-      const NoGather none;
-      K32Frags kq;
-      y32_kpre(kq, sm.tile(0) + kofs);
-      phase_y32<0>(kq, sm.tile(0) + kofs, qf, s, none, lane, NoTail{});
-      if (nt > 1) {
-        soft32_plain<false>(s, ss, c, inv_c, kBK, h, pb_own, fac_own, flag_own);
-        y32_kpre(kq, sm.tile(1) + kofs);
-        phase_y32<0>(kq, sm.tile(1) + kofs, qf, s, none, lane, NoTail{});
-      } else {
-        soft32_plain<true>(s, ss, c, inv_c, tile_rows(0, n), h, pb_own, fac_own, flag_own);
-      }
-      lds_barrier();  // P(0) visible
-      prefetch_x(0);
-      // Iteration j: phase X(j) with the softmax of tile j + 1; before its last
-      // steps one barrier (P(j + 1) and tile j + 2 visible, tile j - 1 free)
-      // and the first K reads of S(j + 2); phase Y computes S(j + 2), gathers
-      // tile j + 3 into tile j - 1's slot and issues the first reads of X(j + 1).
-      for (int j = 0; j + 2 < nt; ++j) {
-        Gather128T<kM32Pitch> ga;
-        const uint32_t krow = sm.tile((j + 2) % k128Ring) + kofs;
-        phase_x(j, std::true_type{}, std::false_type{}, [&]() {
-          const uint32_t e = xp.e;
-          wait_vmcnt_le(0);  // tile j + 2 landed (issued in phase Y of iteration j - 1)
-          lds_barrier();
-          ga = gather128_make<kM32Pitch>(e, j + k128Ahead, n, j + k128Ahead < nt,
-                                         sm.tile((j + k128Ahead) % k128Ring), kvp, lane, w);
-          y32_kpre(kq, krow);
-        });
-        phase_y32<PhaseX32::kPro>(kq, krow, qf, s, ga, lane, [&]() { prefetch_x(j + 1); });
-      }
-    }
-    load_q32(qf, p, more ? tn : t, (more ? hbn : hbase) + 32 * w, lane);
-    if (nt > 1) {
-      phase_x(nt - 2, std::true_type{}, std::true_type{}, lds_done);
-      lds_barrier();
-      prefetch_x(nt - 1);
-    }
-    if (nt > 0) {
-      phase_x(nt - 1, std::false_type{}, std::false_type{}, lds_done);
-      lds_barrier();
-    }
-
-    // ---- unit boundary ----
-    {
-      const int head = hbase + 32 * w + hl;
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss.l_part), __float_as_uint(ss.l_part),
-                                                       false, false);
-      const float lsum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-      const bool has_sink = !(sk == -INFINITY);
-      const HeadEnd he = head_end_sum(lsum, ss.m_ref(), sk, has_sink, sk * kLog2e);
-      if (h == 0 && head < p.H) p.lse[(size_t)t * p.H + head] = he.lse;
-      if (h == 0) *(LDS_AS float*)(uintptr_t)(lds_addr(sm.osc) + 128 * w + 4 * hl) = he.oscale;
-    }
-    const int nn = more ? compact128(lds_addr(sm.list[(r + 1) & 1]), len, p.nkv, wcnt, lane, w) : 0;
-    if (!more) lds_barrier();
-    float fo[4];
-    {
-      const uint32_t osc_rd = lds_addr(sm.osc) + 4 * hl;  // output scale of head 32 o + hl at + 128 o
-      asm volatile("ds_read_b32 %0, %1 offset:0" : "=v"(fo[0]) : "v"(osc_rd));
-      asm volatile("ds_read_b32 %0, %1 offset:128" : "=v"(fo[1]) : "v"(osc_rd));
-      asm volatile("ds_read_b32 %0, %1 offset:256" : "=v"(fo[2]) : "v"(osc_rd));
-      asm volatile("ds_read_b32 %0, %1 offset:384" : "=v"(fo[3]) : "v"(osc_rd));
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fo[0]), "+v"(fo[1]), "+v"(fo[2]), "+v"(fo[3]));
-    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" ::: "memory");  // MFMA write -> accumulator read distance
-    {
-      uint16_t* orow = p.out + ((size_t)t * p.H + hbase + hl) * kD + 128 * w;
-      static_for<0, 4>([&](auto oc) {
-        constexpr int o = decltype(oc)::value;
-        store32_block<o>(orow + (size_t)32 * o * kD, hbase + 32 * o + hl < p.H, fo[o], h);
-        static_for<0, 4>([&](auto dc) { acc32_zero_t<4 * o + decltype(dc)::value>(zero4); });
-      });
-    }
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < k128Ahead; ++i)
-        gather128<kM32Pitch>(sm.list[(r + 1) & 1], i, nn, i < (nn + kBK - 1) / kBK, sm.tile(i), kvp, lane, w).all(lane);
-      if (r + 2 < sched.K)  // into this unit's list buffer, read no more
-        raw128_dma(lds_addr(sm.list[r & 1]), trow_of(token_of(sched.unit(r + 2))), len, lane, w);
-    }
-    if (!more) break;
-    v = vn;
-    t = tn;
-    hbase = hbn;
-    n = nn;
-  }
-}
-
-template <bool NEG>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void smla_fwd128_mfma32_kernel(const Params p) {
-  smla_fwd128_mfma32_body<NEG>(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -2446,7 +1850,6 @@ constexpr int kR16Cap = 512;
 // is not yet faster than two 64-head workgroups per token of the D-split
 // kernel, so the latter is dispatched.
 constexpr bool kFwd128 = true;
-constexpr bool kFwd128Mfma32 = true;  // its 32x32x16 form
 
 Variant pick_variant(int64_t H, int64_t topk, bool fp8) {
   if (H <= 16 && !fp8) return {1, "smla_fwd16_kernel<1, 512>"};
@@ -2606,13 +2009,10 @@ int run_prefill(const void* q, const void* kv, const int32_t* topk_indices, cons
     p.head_groups = (int)((H + 127) / 128);
     const int64_t units128 = T * p.head_groups;
     const unsigned grid = (unsigned)std::min<int64_t>(units128, cu_count(dev));  // persistent
-    if (kFwd128Mfma32) {
-      if (p.scale_log2 < 0.f) hipLaunchKernelGGL(smla_fwd128_mfma32_kernel<true>, dim3(grid), dim3(256), 0, s, p);
-      else hipLaunchKernelGGL(smla_fwd128_mfma32_kernel<false>, dim3(grid), dim3(256), 0, s, p);
-    } else {
-      if (p.scale_log2 < 0.f) hipLaunchKernelGGL(smla_fwd128_kernel<true>, dim3(grid), dim3(256), 0, s, p);
-      else hipLaunchKernelGGL(smla_fwd128_kernel<false>, dim3(grid), dim3(256), 0, s, p);
-    }
+    if (p.scale_log2 < 0.f)
+      hipLaunchKernelGGL(smla_fwd128_kernel<true>, dim3(grid), dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL(smla_fwd128_kernel<false>, dim3(grid), dim3(256), 0, s, p);
     return hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
   }
   if (H <= 16) {

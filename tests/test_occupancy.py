@@ -32,8 +32,6 @@ EXPECTED = {
     "smla_fwd_fp8_kernel<8, 4>": (1, 2),
     "smla_fwd128_kernel<false>": (1, 1),
     "smla_fwd128_kernel<true>": (1, 1),
-    "smla_fwd128_mfma32_kernel<false>": (1, 1),
-    "smla_fwd128_mfma32_kernel<true>": (1, 1),
 }
 
 MANGLED = {
@@ -44,8 +42,6 @@ MANGLED = {
     "smla_fwd_fp8_kernel<8, 4>": "smla_fwd_fp8_kernelILi8ELi4EE",
     "smla_fwd128_kernel<false>": "18smla_fwd128_kernelILb0EE",
     "smla_fwd128_kernel<true>": "18smla_fwd128_kernelILb1EE",
-    "smla_fwd128_mfma32_kernel<false>": "smla_fwd128_mfma32_kernelILb0EE",
-    "smla_fwd128_mfma32_kernel<true>": "smla_fwd128_mfma32_kernelILb1EE",
 }
 BWD = os.path.join(ROOT, "sparse_attention_top_amd", "csrc", "sparse_mla_bwd.hip")
 
@@ -133,11 +129,11 @@ def _bodies(text, pattern):
 
 
 def test_fwd128_agprs_left_to_the_accumulators(forward_asm):
-    """In the 128-head kernels every AGPR operand must come from the hand-written
+    """In the 128-head kernel every AGPR operand must come from the hand-written
     accumulator asm: an AGPR the compiler allocates (for a spill or a copy)
     would overwrite an accumulator."""
     found = 0
-    for name, body in _bodies(forward_asm, "smla_fwd128_kernel|smla_fwd128_mfma32_kernel"):
+    for name, body in _bodies(forward_asm, "smla_fwd128_kernel"):
         found += 1
         in_asm, bad = False, []
         for line in body.split("\n"):
@@ -150,7 +146,7 @@ def test_fwd128_agprs_left_to_the_accumulators(forward_asm):
                 if code and re.search(r"\ba\[?\d", code):
                     bad.append(code)
         assert not bad, "%s: compiler-generated AGPR operands: %s" % (name, bad[:5])
-    assert found == 4
+    assert found == 2
 
 
 def _vgprs(operand):
