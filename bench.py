@@ -52,8 +52,9 @@ def algorithmic(inp: dict) -> dict:
 
 
 def gpu_clock_sampler():
-    """Returns a function that samples the GPU's graphics clock (MHz) through
-    amdsmi, or None where amdsmi is not available."""
+    """Returns a function that samples the GPU's graphics clock (MHz) and socket
+    power (W) through amdsmi as a pair (either may be None), or None where amdsmi
+    is not available. sample.power_cap_w holds the board's power limit."""
     try:
         import amdsmi
 
@@ -62,19 +63,27 @@ def gpu_clock_sampler():
     except Exception:
         return None
 
+    def num(v, hi):
+        return float(v) if isinstance(v, (int, float)) and 0 < v < hi else None
+
     def sample():
+        mhz = watts = None
         try:
-            v = amdsmi.amdsmi_get_gpu_metrics_info(h).get("current_gfxclk")
-            if isinstance(v, (int, float)) and 0 < v < 10000:
-                return float(v)
+            m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+            mhz, watts = num(m.get("current_gfxclk"), 10000), num(m.get("current_socket_power"), 5000)
         except Exception:
             pass
-        try:
-            c = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
-            return float(c.get("clk"))
-        except Exception:
-            return None
+        if mhz is None:
+            try:
+                mhz = num(amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX).get("clk"), 10000)
+            except Exception:
+                pass
+        return mhz, watts
 
+    try:
+        sample.power_cap_w = amdsmi.amdsmi_get_power_cap_info(h).get("power_cap") / 1e6
+    except Exception:
+        sample.power_cap_w = None
     return sample
 
 
@@ -129,29 +138,73 @@ def time_gpu(run, steps, warmup, stream, flush=None, clock=None):
     return wall, st
 
 
-def loaded_clock(run, clock, seconds: float = 0.6, settle: float = 0.2):
-    """The graphics clock while the workload runs back to back (after the timed
-    region, so the sampling costs it nothing): amdsmi's current_gfxclk, which
-    the SMU refreshes every few tens of ms, sampled after `settle` seconds."""
+def loaded_clock(run, clock, seconds: float = 1.5, settle: float = 0.8):
+    """The graphics clock and socket power while the workload runs back to back
+    (after the timed region, so the sampling costs it nothing): amdsmi's
+    current_gfxclk and current_socket_power, which the SMU refreshes every few
+    tens of ms, sampled after `settle` seconds (the power manager needs most of
+    a second to settle at the board limit)."""
     import torch
 
-    mhz, t0 = [], time.perf_counter()
+    mhz, watts, t0 = [], [], time.perf_counter()
     while time.perf_counter() - t0 < seconds:
         ev = torch.cuda.Event()
         for _ in range(8):
             run()
         ev.record()
-        if time.perf_counter() - t0 >= settle and len(mhz) < 200:
-            v = clock()
-            if v is not None:
-                mhz.append(v)
+        if time.perf_counter() - t0 >= settle and len(mhz) < 400:
+            c, w = clock()
+            if c is not None:
+                mhz.append(c)
+            if w is not None:
+                watts.append(w)
         while not ev.query():
             time.sleep(0.001)
     torch.cuda.synchronize()
     if not mhz:
         return None
-    return {"median": float(np.median(mhz)), "min": float(np.min(mhz)), "max": float(np.max(mhz)),
-            "samples": len(mhz), "source": "amdsmi current_gfxclk, workload running back to back"}
+    out = {"median": float(np.median(mhz)), "min": float(np.min(mhz)), "max": float(np.max(mhz)),
+           "samples": len(mhz), "source": "amdsmi current_gfxclk, workload running back to back"}
+    if watts:
+        out["socket_power_w"] = float(np.median(watts))
+        out["board_power_cap_w"] = getattr(clock, "power_cap_w", None)
+    return out
+
+
+def gemm_at_power_limit(clock, n: int = 8192, seconds: float = 2.5):
+    """A library bf16 GEMM (torch.matmul, n x n x n) run back to back for a few
+    seconds: the dense MFMA rate a tuned vendor kernel sustains at this board's
+    power limit, the practical ceiling next to the nominal peak."""
+    import torch
+
+    a = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16).contiguous()
+    c = torch.empty(n, n, device="cuda:0", dtype=torch.bfloat16)
+    torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    rates, mhz, watts, t0 = [], [], [], time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            torch.matmul(a, b, out=c)
+        e1.record()
+        e1.synchronize()
+        if time.perf_counter() - t0 > seconds / 2:
+            rates.append(10 * 2.0 * n ** 3 / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+            if clock is not None:
+                cv, wv = clock()
+                if cv is not None:
+                    mhz.append(cv)
+                if wv is not None:
+                    watts.append(wv)
+    out = {"tflops": float(np.median(rates)), "shape": "bf16 %d x %d x %d, torch.matmul" % (n, n, n),
+           "seconds": seconds}
+    if mhz:
+        out["gfx_clock_mhz"] = float(np.median(mhz))
+    if watts:
+        out["socket_power_w"] = float(np.median(watts))
+    return out
 
 
 def cpu_model():
@@ -427,6 +480,11 @@ def main():
     }
     print("bench: %s %.4f ms/call, %.1f TFLOP/s, %.1f GB/s gathered" % (cfg.name, t["ms_per_call"], tflops, gbs),
           file=sys.stderr, flush=True)
+    if clock is not None and bound == "mfma":
+        g = gemm_at_power_limit(clock)
+        line["gemm_at_power_limit"] = g
+        line["roofline"]["frac_of_power_limited_gemm"] = line["roofline"]["achieved"] / g["tflops"]
+        print("bench: library bf16 GEMM at the power limit %.0f TFLOP/s" % g["tflops"], file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a token sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(inp)
