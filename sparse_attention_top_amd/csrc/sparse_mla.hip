@@ -304,17 +304,13 @@ struct SlabCodes {
 struct HeadEnd {
   float oscale, lse;
 };
-// lsum: the head's whole row sum relative to m_ref
-__device__ __forceinline__ HeadEnd head_end_sum(float lsum, float m_ref, float sink, bool has_sink, float sink_l2) {
+__device__ __forceinline__ HeadEnd head_end(float l_part, float m_ref, float sink, bool has_sink, float sink_l2) {
+  const float lsum = row4_sum(l_part);
   if (lsum == 0.f) return {0.f, has_sink ? sink : -INFINITY};
   const float mf = has_sink ? __builtin_fmaxf(m_ref, sink_l2) : m_ref;
   const float a = __builtin_amdgcn_exp2f(m_ref - mf);
   const float lf = lsum * a + (has_sink ? __builtin_amdgcn_exp2f(sink_l2 - mf) : 0.f);
   return {a / lf, (mf + __builtin_amdgcn_logf(lf)) * kLn2};
-}
-// l_part: this lane's share, summed over the four 16-lane rows that hold the head
-__device__ __forceinline__ HeadEnd head_end(float l_part, float m_ref, float sink, bool has_sink, float sink_l2) {
-  return head_end_sum(row4_sum(l_part), m_ref, sink, has_sink, sink_l2);
 }
 
 __device__ __forceinline__ void load_q(bf16x8 (&qf)[16], const Params& p, int t, int head, int g) {
@@ -735,28 +731,16 @@ constexpr int k128Ring = 4;  // ring of 32-row tiles
 constexpr int k128Ahead = k128Ring - 1;
 constexpr int k128Cap = 1024;  // top-k entries compacted per segment
 
-template <int PITCH>
-struct Smem128T {
-  uint8_t area[k128Ring * kBK * PITCH];  // gather ring, rows at pitch PITCH
+struct Smem128 {
+  uint8_t area[k128Ring * kBK * kRowStride];  // gather ring
   uint8_t pbuf[2][8 * 64 * 16];               // P fragments of tile j, by tile parity: [head block][lane][16 B]
   float fac[2][128];                          // rescale factors, [li * 8 + head block], written with a flag
   uint8_t flag[2][4];                         // per wave (byte w): its factors of this tile were written
   float osc[128];                             // output scale of each head, [li * 8 + head block]
   int32_t list[2][k128Cap];                   // compacted lists of this unit and the next (by unit parity)
   int32_t wcnt[16];                           // per-wave counts of the compaction
-  __device__ __forceinline__ uint32_t tile(int b) { return lds_addr(area + b * kBK * PITCH); }
+  __device__ __forceinline__ uint32_t tile(int b) { return lds_addr(area + b * kBK * kRowStride); }
 };
-using Smem128 = Smem128T<kRowStride>;
-// Tile rows of the persistent 128-head kernels: pitch 1040 B, and MFMA row m of
-// a tile (a token) held in tile row p128_row(m). Within each block of 16 rows
-// the first eight MFMA rows take the even tile rows and the last eight the odd
-// ones, so that the K fragment reads (16 lanes on 16 rows) and the transposing
-// V^T reads (32 lanes on 8 rows, 32 B each) both spread over all 64 LDS banks;
-// in row order at the 1056 B pitch the K reads met two-way conflicts.
-constexpr int k128Pitch = kRowBytes + 16;
-__host__ __device__ constexpr int p128_row(int m) {
-  return (m & 16) | ((m & 15) < 8 ? 2 * (m & 15) : 2 * ((m & 15) - 8) + 1);
-}
 static_assert(sizeof(Smem128) <= 160 * 1024, "one workgroup per CU");
 
 // An empty asm that "redefines" its operands: code using them cannot move above it.
@@ -797,8 +781,7 @@ __device__ __forceinline__ void mfma_s_first_dep(f32x4& c, const u32x4& a, const
 // [8 w, 8 w + 8), lane L < 8 forming row 8 w + L's source address (a pool row,
 // or the zero row past the tile's count, or for a tile past the unit's last);
 // one LDS-DMA load per row, issued without a branch.
-template <int PITCH>
-struct Gather128T {
+struct Gather128 {
   uint32_t dst0;      // LDS address of this wave's first row
   uint32_t alo, ahi;  // lane L < 8: source address of row L
   template <int R>
@@ -806,13 +789,12 @@ struct Gather128T {
     const uint32_t rlo = (uint32_t)__builtin_amdgcn_readlane(alo, R);
     const uint32_t rhi = (uint32_t)__builtin_amdgcn_readlane(ahi, R);
     const uint16_t* rs = (const uint16_t*)(uintptr_t)(((uint64_t)rhi << 32) | rlo);
-    __builtin_amdgcn_global_load_lds(rs + 8 * lane, (LDS_AS void*)(uintptr_t)(dst0 + R * PITCH), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(rs + 8 * lane, (LDS_AS void*)(uintptr_t)(dst0 + R * kRowStride), 16, 0, 0);
   }
   __device__ __forceinline__ void all(int lane) const {
     static_for<0, kBK / 4>([&](auto rc) { row<decltype(rc)::value>(lane); });
   }
 };
-using Gather128 = Gather128T<kRowStride>;
 // The list entry of this lane's row (every lane reads an in-bounds entry, so no
 // branch merges the pending register); the raw read is completed by a later
 // wait that takes it as an operand.
@@ -826,13 +808,12 @@ __device__ __forceinline__ uint32_t gather128_read(const int32_t* list, int i, i
   asm volatile("ds_read_b32 %0, %1" : "=v"(e) : "v"(lds_addr(list + pos)));
   return e;
 }
-template <int PITCH = kRowStride>
-__device__ __forceinline__ Gather128T<PITCH> gather128_make(uint32_t e, int i, int n, bool act, uint32_t buf,
-                                                           const uint16_t* kv, int lane, int w) {
-  Gather128T<PITCH> ga;
+__device__ __forceinline__ Gather128 gather128_make(uint32_t e, int i, int n, bool act, uint32_t buf,
+                                                   const uint16_t* kv, int lane, int w) {
+  Gather128 ga;
   const int r0 = w * (kBK / 4);
   const int cnt = act ? min(kBK, n - i * kBK) : 0;
-  ga.dst0 = buf + r0 * PITCH;
+  ga.dst0 = buf + r0 * kRowStride;
   const bool have = act && lane < kBK / 4 && r0 + lane < cnt;
   const uint16_t* src = have ? uniform_ptr(kv) + (size_t)e * kD : kZeroRowBf16;
   const uint64_t a = (uint64_t)(uintptr_t)src;
@@ -840,12 +821,11 @@ __device__ __forceinline__ Gather128T<PITCH> gather128_make(uint32_t e, int i, i
   ga.ahi = (uint32_t)(a >> 32);
   return ga;
 }
-template <int PITCH = kRowStride>
-__device__ __forceinline__ Gather128T<PITCH> gather128(const int32_t* list, int i, int n, bool act, uint32_t buf,
-                                                      const uint16_t* kv, int lane, int w) {
+__device__ __forceinline__ Gather128 gather128(const int32_t* list, int i, int n, bool act, uint32_t buf,
+                                               const uint16_t* kv, int lane, int w) {
   uint32_t e = gather128_read(list, i, lane, w);
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(e));
-  return gather128_make<PITCH>(e, i, n, act, buf, kv, lane, w);
+  return gather128_make(e, i, n, act, buf, kv, lane, w);
 }
 
 // Phase Y: S = K Q^T from the tile at krow, 16 k-steps of four MFMAs (four
@@ -868,7 +848,7 @@ __device__ __forceinline__ void phase_y128(uint32_t krow, const bf16x8 (&qf)[2][
   u32x4 kf[KST][2];
   auto kread = [&](auto kc, auto hc) {
     constexpr int k = decltype(kc)::value, h = decltype(hc)::value;
-    kf[k % KST][h] = ds_read_b128<16 * k128Pitch * h + 64 * k>(krow);
+    kf[k % KST][h] = ds_read_b128<16 * kRowStride * h + 64 * k>(krow);
   };
   static_for<0, kYKPF>([&](auto kc) {
     kread(kc, Int<0>{});
@@ -949,10 +929,9 @@ __device__ __forceinline__ Deps soft128_group(f32x4 (&s)[2][2], SoftT& tt, Soft1
   if constexpr (MASK && G < 8) {  // two elements (hb = G & 1, e = 2 (G >> 1) ..) past the count -> -inf
     constexpr int hb = G & 1, e0 = 2 * (G >> 1), sh = e0 >> 2, i0 = e0 & 3;
     pin(s[sh][hb]);
-    // MFMA row 16 sh + 4 g + i is tile row 16 sh + 2 i + (g < 2 ? 8 g : 8 (g - 2) + 1)
-    const int lim = cnt - (g < 2 ? 8 * g : 8 * (g - 2) + 1);
+    const int lim = cnt - 4 * g;  // slot 16 sh + 4 g + i is valid iff 16 sh + i < lim
 #pragma unroll
-    for (int i = i0; i < i0 + 2; ++i) s[sh][hb][i] = (16 * sh + 2 * i) < lim ? s[sh][hb][i] : -INFINITY;
+    for (int i = i0; i < i0 + 2; ++i) s[sh][hb][i] = (16 * sh + i) < lim ? s[sh][hb][i] : -INFINITY;
     return {s[sh][hb][i0], s[sh][hb][i0 + 1]};
   } else if constexpr (G < M + 4) {  // tile max, in-lane: two three-way maxima per group
     constexpr int hb = (G - M) & 1, part = (G - M) >> 1;
@@ -1043,7 +1022,7 @@ __device__ __forceinline__ void x_prefetch(XPre& xp, const int32_t* list, int gi
   static_for<0, kXVPF>([&](auto pc) {
     constexpr int pp = decltype(pc)::value;
     xp.vf[pp][0] = ds_read_tr16_b64<32 * pp>(vrow);
-    xp.vf[pp][1] = ds_read_tr16_b64<16 * k128Pitch + 32 * pp>(vrow);
+    xp.vf[pp][1] = ds_read_tr16_b64<16 * kRowStride + 32 * pp>(vrow);
   });
 }
 
@@ -1094,7 +1073,7 @@ __device__ __forceinline__ void phase_x128(XPre& xp, uint32_t vrow, uint32_t pba
   u32x2 (&vf)[VST][2] = xp.vf;
   auto vread = [&](auto pc, auto hc) {
     constexpr int pp = decltype(pc)::value, h = decltype(hc)::value;
-    vf[pp % VST][h] = ds_read_tr16_b64<16 * k128Pitch * h + 32 * (pp % 8)>(vrow);
+    vf[pp % VST][h] = ds_read_tr16_b64<16 * kRowStride * h + 32 * (pp % 8)>(vrow);
   };
   asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(xp.fl), "+v"(xp.e) : "n"(Px::kPro - 2));
   const uint32_t fl = xp.fl;
@@ -1239,7 +1218,7 @@ __device__ __forceinline__ void store128_block(uint16_t* orow, bool ok, float fo
 
 template <bool NEG>
 __device__ __forceinline__ void smla_fwd128_body(const Params& p) {
-  __shared__ __attribute__((aligned(16))) Smem128T<k128Pitch> sm;
+  __shared__ __attribute__((aligned(16))) Smem128 sm;
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1259,11 +1238,6 @@ __device__ __forceinline__ void smla_fwd128_body(const Params& p) {
   const uint32_t fac_own = fac0 + 8 * w;   // entries 8 li + 2w, + 1
   const uint32_t flag_own = flag0 + w;
   const uint32_t wcnt = lds_addr(sm.wcnt);
-  // fragment offsets within a tile: K (lane: MFMA rows li and 16 + li, chunk
-  // 4 k + g of k-step k); V^T (MFMA rows 4 g + li / 4 and + 16, 4 columns at
-  // 4 (li & 3) of each d-tile, this wave's 128 columns)
-  const uint32_t kofs = p128_row(li) * k128Pitch + 16 * g;
-  const uint32_t vofs = p128_row(4 * g + (li >> 2)) * k128Pitch + 8 * (li & 3) + 256 * w;
 
   // logits c * S with c > 0: a negative scale is carried by q (negation is exact)
   const float c = NEG ? -p.scale_log2 : p.scale_log2;
@@ -1294,7 +1268,7 @@ __device__ __forceinline__ void smla_fwd128_body(const Params& p) {
   int n = compact128(lds_addr(sm.list[0]), len, p.nkv, wcnt, lane, w);
 #pragma unroll
   for (int i = 0; i < k128Ahead; ++i)
-    gather128<k128Pitch>(sm.list[0], i, n, i < (n + kBK - 1) / kBK, sm.tile(i), kvp, lane, w).all(lane);
+    gather128(sm.list[0], i, n, i < (n + kBK - 1) / kBK, sm.tile(i), kvp, lane, w).all(lane);
 
   Soft128 ss;
   for (int r = 0;; ++r) {
@@ -1335,7 +1309,7 @@ __device__ __forceinline__ void smla_fwd128_body(const Params& p) {
     // j + 1 between its MFMAs (MASK: tile j + 1 is the partial last one)
     auto phase_x = [&](int j, auto soft, auto mask) {
       const uint32_t par = j & 1, nxt = par ^ 1;
-      const uint32_t vrow = opaque(sm.tile(j % k128Ring) + vofs);
+      const uint32_t vrow = v_frag_addr(sm.tile(j % k128Ring), g, li) + 256 * w;
       const uint32_t pbase = pb0 + kPbPar * par, fac_rd = fac0 + kFacPar * par;
       const uint32_t pbw = pb_own + kPbPar * nxt, facw = fac_own + kFacPar * nxt, flagw = flag_own + kFlagPar * nxt;
       phase_x128<decltype(soft)::value, decltype(mask)::value>(xp, vrow, pbase, fac_rd, s, ss, c, inv_c,
@@ -1347,15 +1321,15 @@ __device__ __forceinline__ void smla_fwd128_body(const Params& p) {
     auto prefetch_x = [&](int j) {
       const uint32_t par = j & 1;
       x_prefetch(xp, lst, j + k128Ahead, lane, w, flag0 + kFlagPar * par, pb0 + kPbPar * par,
-                 opaque(sm.tile(j % k128Ring) + vofs));
+                 v_frag_addr(sm.tile(j % k128Ring), g, li) + 256 * w);
     };
     if (nt > 0) {
       const NoGather none;
       // S(0), its softmax (P(0) in parity 0), S(1)
-      phase_y128(opaque(sm.tile(0) + kofs), qf, s, none, lane);
+      phase_y128(k_frag_addr(sm.tile(0), g, li), qf, s, none, lane);
       if (nt > 1) {
         soft128_plain<false>(s, ss, c, inv_c, kBK, g, pb_own, fac_own, flag_own);
-        phase_y128(opaque(sm.tile(1) + kofs), qf, s, none, lane);
+        phase_y128(k_frag_addr(sm.tile(1), g, li), qf, s, none, lane);
       } else {
         soft128_plain<true>(s, ss, c, inv_c, tile_rows(0, n), g, pb_own, fac_own, flag_own);
       }
@@ -1370,9 +1344,9 @@ __device__ __forceinline__ void smla_fwd128_body(const Params& p) {
         const uint32_t e = xp.e;  // list entry of tile j + 3 (completed in phase X)
         wait_vmcnt_le(0);         // tile j + 2 landed (issued in phase Y of iteration j - 1)
         lds_barrier();
-        const auto ga = gather128_make<k128Pitch>(e, j + k128Ahead, n, j + k128Ahead < nt,
+        const Gather128 ga = gather128_make(e, j + k128Ahead, n, j + k128Ahead < nt,
                                             sm.tile((j + k128Ahead) % k128Ring), kvp, lane, w);
-        phase_y128(opaque(sm.tile((j + 2) % k128Ring) + kofs), qf, s, ga, lane, [&]() { prefetch_x(j + 1); });
+        phase_y128(k_frag_addr(sm.tile((j + 2) % k128Ring), g, li), qf, s, ga, lane, [&]() { prefetch_x(j + 1); });
       }
     }
     // every S of this unit is done: q of the next unit (this unit's again for
@@ -1426,7 +1400,7 @@ __device__ __forceinline__ void smla_fwd128_body(const Params& p) {
     if (more) {
 #pragma unroll
       for (int i = 0; i < k128Ahead; ++i)
-        gather128<k128Pitch>(sm.list[(r + 1) & 1], i, nn, i < (nn + kBK - 1) / kBK, sm.tile(i), kvp, lane, w).all(lane);
+        gather128(sm.list[(r + 1) & 1], i, nn, i < (nn + kBK - 1) / kBK, sm.tile(i), kvp, lane, w).all(lane);
       if (r + 2 < sched.K)  // into this unit's list buffer, read no more
         raw128_dma(lds_addr(sm.list[r & 1]), trow_of(token_of(sched.unit(r + 2))), len, lane, w);
     }
