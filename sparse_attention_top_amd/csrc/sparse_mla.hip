@@ -328,11 +328,15 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[16], const Params& p, int t,
 }
 
 // As load_q with no branch: a head past H loads head H - 1 (its results are
-// never stored), so no wait for q is forced where control flow joins.
+// never stored), so no wait for q is forced where control flow joins. Cached
+// loads: each instruction reads one half of sixteen 128-byte lines and the
+// next k-step the other half, which a non-temporal load may already have
+// evicted (the 128-head kernel fetched 0.06 GB more per launch at T = 8192
+// with non-temporal loads, and took 1% longer).
 __device__ __forceinline__ void load_q_any(bf16x8 (&qf)[16], const Params& p, int t, int head, int g) {
   const bf16x8* src = (const bf16x8*)(p.q + ((size_t)t * p.H + min(head, p.H - 1)) * kD + 8 * g);
 #pragma unroll
-  for (int k = 0; k < 16; ++k) qf[k] = __builtin_nontemporal_load(src + 4 * k);
+  for (int k = 0; k < 16; ++k) qf[k] = src[4 * k];
 }
 
 // ---- D-split P.V (four waves, 64 heads, bf16 pool) ----
@@ -1119,25 +1123,37 @@ __device__ __forceinline__ void phase_x128(XPre& xp, uint32_t vrow, uint32_t pba
   });
 }
 
-// The 128-head kernel is persistent: workgroup b of G owns the units
-// (token, head group of 128) r G + (b, or G - 1 - b for odd r), r = 0, 1, ...
-// Unit v is token T - 1 - v / head_groups, head group v % head_groups: each
-// workgroup gets one unit of every run of G, and the alternating order evens
-// out the drift of the weights within a run. A workgroup takes its K units
-// starting at its r = b % K and wrapping around, so that workgroups do not
-// all reach a unit's end (128 KiB of output stores each) at the same time.
+// The 128-head kernel is persistent: workgroup b of G owns one unit (token,
+// head group of 128) of every run of G, unit r G + slot_r(b) in run r. Unit v
+// is token T - 1 - v / head_groups, head group v % head_groups. Workgroups are
+// dispatched to the kNumXcd XCDs in turn, so workgroup b = x + kNumXcd c runs
+// on XCD x; when G is a multiple of kNumXcd, the slots of run r that XCD x
+// holds are the consecutive x G / kNumXcd .. + G / kNumXcd - 1 (c, or its
+// mirror for odd r), so that its CUs work on neighbouring tokens at once and
+// share their sliding-window rows in that XCD's L2. The alternating order
+// evens out the drift of the weights within a run. The workgroups of XCD x
+// take their K runs starting at run x K / kNumXcd and wrapping around, so
+// that the XCDs do not all reach a unit's end (128 KiB of output stores per
+// workgroup) at the same time.
 struct Sched128 {
-  int b, G, K, r0;
+  int b, G, K, r0, x, c, per;
+  __device__ __forceinline__ int slot(int r) const {
+    if (per == 0) return (r & 1) ? G - 1 - b : b;
+    return x * per + ((r & 1) ? per - 1 - c : c);
+  }
   __device__ __forceinline__ Sched128(int b_, int G_, int units) : b(b_), G(G_) {
+    per = (G % kNumXcd == 0) ? G / kNumXcd : 0;
+    x = b % kNumXcd;
+    c = b / kNumXcd;
     const int full = units / G, rem = units % G;
-    K = full + ((rem > 0 && ((full & 1) ? G - 1 - b : b) < rem) ? 1 : 0);
-    r0 = K > 0 ? b % K : 0;
+    K = full + ((rem > 0 && slot(full) < rem) ? 1 : 0);
+    r0 = K > 0 ? (per == 0 ? b % K : (x * K / kNumXcd) % K) : 0;
   }
   // the unit taken i-th (i < K)
   __device__ __forceinline__ int unit(int i) const {
     int r = r0 + i;
     r = r >= K ? r - K : r;
-    return r * G + ((r & 1) ? G - 1 - b : b);
+    return r * G + slot(r);
   }
 };
 
