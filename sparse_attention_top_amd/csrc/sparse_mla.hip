@@ -1832,17 +1832,19 @@ struct Variant {
 // 4 tiles, dequantised once into two shared bf16 tiles, so that the conversion
 // is not repeated per head group.
 // 16-row variant for H <= 16 and a bf16 pool (single pass): one tile and a
-// 512-entry list, eight workgroups per CU (a ring of two tiles with a
-// 1024-entry list fits four per CU and measured 1.3x slower).
+// 640-entry list, eight workgroups per CU (a ring of two tiles with a
+// 1024-entry list fits four per CU and measured 1.3x slower). 640 entries
+// take a 640-slot row in one segment (the second segment's index loads
+// stalled the wave: 512 entries were 0.8% slower there).
 constexpr int kR16Nbuf = 1;
-constexpr int kR16Cap = 512;
+constexpr int kR16Cap = 640;
 // The one-workgroup-per-token kernel for more than 64 heads (smla_fwd128_kernel)
 // is not yet faster than two 64-head workgroups per token of the D-split
 // kernel, so the latter is dispatched.
 constexpr bool kFwd128 = true;
 
 Variant pick_variant(int64_t H, int64_t topk, bool fp8) {
-  if (H <= 16 && !fp8) return {1, "smla_fwd16_kernel<1, 512>"};
+  if (H <= 16 && !fp8) return {1, "smla_fwd16_kernel<1, 640>"};
   if (H <= 16) return {1, "smla_fwd16_fp8_kernel<2, 512>"};
   if (H <= 32) return {2, fp8 ? "smla_fwd_fp8_kernel<2, 2>" : "smla_fwd_kernel<2, 2>"};
   if (!fp8) return {4, (H > 64 && kFwd128 && topk <= k128Cap) ? "smla_fwd128_kernel" : "smla_fwd_kernel<4, 2>"};

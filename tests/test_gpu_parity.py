@@ -114,15 +114,15 @@ def test_head_counts(H):
     compare(o, lse, oracle_ref(inp), what="H=%d" % H)
 
 
-H16_EDGES = [(15, 40, 0.0), (16, 40, 0.0), (17, 40, 0.0), (512, 900, 0.0), (513, 900, 0.0), (1039, 2000, 0.0),
-             (1100, 2000, 0.5)]
+H16_EDGES = [(15, 40, 0.0), (16, 40, 0.0), (17, 40, 0.0), (512, 900, 0.0), (513, 900, 0.0), (640, 900, 0.0),
+             (641, 900, 0.0), (1039, 2000, 0.0), (1100, 2000, 0.5), (1281, 2000, 0.0)]
 
 
 @pytest.mark.parametrize("topk,num_kv,p_invalid", H16_EDGES)
 def test_h16_tile_and_segment_edges(topk, num_kv, p_invalid):
-    """H <= 16 runs 16-row tiles from 512-entry compaction segments: counts one short of, at and one past a tile and
-    a segment, a row of two segments plus a partial tile, and one where half the slots are invalid (segments whose
-    valid counts are not multiples of 16). 300 tokens: more (token, head group) units than the MI355X's 256 CUs, so
+    """H <= 16 runs 16-row tiles from 640-entry compaction segments: counts one short of, at and one past a tile and
+    a segment, rows of two and three segments with a partial tile, and one where half the slots are invalid
+    (segments whose valid counts are not multiples of 16); 512 and 513 are the edges of an earlier segment size. 300 tokens: more (token, head group) units than the MI355X's 256 CUs, so
     every row takes the single-pass 16-row kernel, not the split path."""
     inp = make_random(2500 + topk, T=300, H=16, num_kv=num_kv, topk=topk, p_invalid=p_invalid)
     o, lse = run_case(inp)
