@@ -114,6 +114,18 @@ def test_head_counts(H):
     compare(o, lse, oracle_ref(inp), what="H=%d" % H)
 
 
+@pytest.mark.parametrize("T,H", [(100, 128), (1000, 128), (260, 200)])
+def test_h128_persistent_schedule(T, H):
+    """The persistent 128-head kernel deals units (token, group of 128 heads) to its workgroups by XCD when the grid
+    is a multiple of the eight XCDs, and one unit per run of the grid otherwise. Top-k rows of 96 entries keep every
+    shape on that kernel (the split path needs 128): a grid of 100 (not a multiple of 8), 1000 units on 256
+    workgroups (a partial fourth run of 232), and 260 tokens of two head groups (520 units: a last run of 8). Every
+    unit must be computed exactly once: all tokens are compared."""
+    inp = make_random(2700 + T + H, T=T, H=H, num_kv=1500, topk=96, p_invalid=0.2)
+    o, lse = run_case(inp)
+    compare(o, lse, oracle_ref(inp), what="H=%d T=%d" % (H, T))
+
+
 H16_EDGES = [(15, 40, 0.0), (16, 40, 0.0), (17, 40, 0.0), (512, 900, 0.0), (513, 900, 0.0), (640, 900, 0.0),
              (641, 900, 0.0), (1039, 2000, 0.0), (1100, 2000, 0.5), (1281, 2000, 0.0)]
 
@@ -122,8 +134,9 @@ H16_EDGES = [(15, 40, 0.0), (16, 40, 0.0), (17, 40, 0.0), (512, 900, 0.0), (513,
 def test_h16_tile_and_segment_edges(topk, num_kv, p_invalid):
     """H <= 16 runs 16-row tiles from 640-entry compaction segments: counts one short of, at and one past a tile and
     a segment, rows of two and three segments with a partial tile, and one where half the slots are invalid
-    (segments whose valid counts are not multiples of 16); 512 and 513 are the edges of an earlier segment size. 300 tokens: more (token, head group) units than the MI355X's 256 CUs, so
-    every row takes the single-pass 16-row kernel, not the split path."""
+    (segments whose valid counts are not multiples of 16); 512 and 513 are the edges of an earlier segment size.
+    300 tokens: more (token, head group) units than the MI355X's 256 CUs, so every row takes the single-pass 16-row
+    kernel, not the split path."""
     inp = make_random(2500 + topk, T=300, H=16, num_kv=num_kv, topk=topk, p_invalid=p_invalid)
     o, lse = run_case(inp)
     compare(o, lse, oracle_ref(inp), what="H=16 topk=%d" % topk)
