@@ -319,25 +319,48 @@ struct TileIssue {
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(e));
     my = e;
   }
+  // As init, with this lane's list entry list[i BK + r0 + lane] already read
+  // (any value where that position is at or past the tile's count).
+  __device__ __forceinline__ void init_with(int e_read, int i, int n, bool act, uint32_t buf, const uint16_t* kv_,
+                                            int lane, int w) {
+    kv = uniform_ptr(kv_);
+    active = act;
+    const int r0 = w * RPW;
+    const int cnt = act ? min(BK, n - i * BK) : 0;
+    dst0 = buf + r0 * kRowStride;
+    my = (act && lane < RPW && r0 + lane < cnt) ? e_read : -1;
+  }
   // Lane L < RPW forms the 64-bit source address of row r0 + L once (vector
   // ops); each row then costs two lane reads, the LDS base and the load.
-  __device__ __forceinline__ void all(int lane) const {
-    if (!active) return;
+  // The row source addresses in scalar registers (formed ahead of the loads
+  // when the caller holds them across other work).
+  struct Rows {
+    uint64_t a[RPW];
+  };
+  __device__ __forceinline__ void rows(Rows& r) const {
     const uint16_t* src = my >= 0 ? kv + (size_t)(uint32_t)my * kD : kZeroRowBf16;
     const uint64_t a = (uint64_t)(uintptr_t)src;
     const uint32_t alo = (uint32_t)a, ahi = (uint32_t)(a >> 32);
-    uint64_t ra[RPW];  // all lane reads first: no read-to-load wait per row
     static_for<0, RPW>([&](auto rc) {
       constexpr int RR = decltype(rc)::value;
       const uint32_t rlo = (uint32_t)__builtin_amdgcn_readlane(alo, RR);
       const uint32_t rhi = (uint32_t)__builtin_amdgcn_readlane(ahi, RR);
-      ra[RR] = ((uint64_t)rhi << 32) | rlo;
+      r.a[RR] = ((uint64_t)rhi << 32) | rlo;
     });
+  }
+  __device__ __forceinline__ void issue(const Rows& r, int lane) const {
+    if (!active) return;
     static_for<0, RPW>([&](auto rc) {
       constexpr int RR = decltype(rc)::value;
-      const uint16_t* rs = (const uint16_t*)(uintptr_t)ra[RR];
+      const uint16_t* rs = (const uint16_t*)(uintptr_t)r.a[RR];
       __builtin_amdgcn_global_load_lds(rs + 8 * lane, (LDS_AS void*)(uintptr_t)(dst0 + RR * kRowStride), 16, 0, 0);
     });
+  }
+  __device__ __forceinline__ void all(int lane) const {
+    if (!active) return;
+    Rows r;  // all lane reads first: no read-to-load wait per row
+    rows(r);
+    issue(r, lane);
   }
   // LDS-DMA instructions all() issues
   __device__ __forceinline__ int count() const { return active ? RPW : 0; }

@@ -1680,6 +1680,7 @@ __device__ __forceinline__ void tile_pv8r16(uint32_t vaddr, const bf16x4& pk, f3
 template <int NBUF, int CAP, bool FP8>
 __device__ __forceinline__ void smla_fwd16_body(const Params& p) {
   static_assert(NBUF == 1 || NBUF == 2, "ring of one or two 16-row tiles");
+  static_assert(FP8 || NBUF == 1, "a bf16 pool runs one tile at a time (the next tile's list entries are read ahead)");
   constexpr int AHEAD = NBUF - 1;
   using SM = Smem16<NBUF, CAP, FP8>;
   __shared__ __attribute__((aligned(16))) SM sm;
@@ -1712,17 +1713,35 @@ __device__ __forceinline__ void smla_fwd16_body(const Params& p) {
       is.init(sm.list, i, n, i < ntiles, sm.tile(i), kvp, lane, 0);
       is.all(lane);
     }
+    // bf16 (one tile in flight): the list entries and row addresses of tile
+    // j + 1 are formed during tile j, so that its gather issues at once
+    typename TileIssue<1, kBK16>::Rows rw{};
+    TileIssue<1, kBK16> nx{};
+    if constexpr (!FP8) {
+      nx.init(sm.list, 0, n, true, sm.tile(0), p.kv, lane, 0);
+      nx.rows(rw);
+    }
     for (int j = 0; j < ntiles; ++j) {
-      Issue is;
       const bool ahead = j + AHEAD < ntiles;
-      is.init(sm.list, j + AHEAD, n, ahead, sm.tile((j + AHEAD) % NBUF), kvp, lane, 0);
-      is.all(lane);
+      if constexpr (FP8) {
+        Issue is;
+        is.init(sm.list, j + AHEAD, n, ahead, sm.tile((j + AHEAD) % NBUF), kvp, lane, 0);
+        is.all(lane);
+      } else {
+        nx.issue(rw, lane);
+      }
+      int e_next = 0;
+      if constexpr (!FP8) e_next = sm.list[min((j + 1) * kBK16 + li, CAP - 1)];
       wait_vmcnt_le(AHEAD > 0 && ahead ? kDma : 0);  // tile j landed (tile j + AHEAD may be in flight)
       const uint32_t tb = sm.tile(j % NBUF);
       f32x4 sv;
       if constexpr (FP8) tile_s8r16<3>(opaque(tb + 16 * (li + 16 * (g >> 1)) + 8 * (g & 1)), qf, sv);
       else tile_s16<3>(k_frag_addr(tb, g, li), qf, sv);
       tile_softmax16(sv, min(kBK16, n - j * kBK16), p.scale_log2, g, m_ref, l_part, acc, pk);
+      if constexpr (!FP8) {
+        nx.init_with(e_next, j + 1, n, j + 1 < ntiles, sm.tile(0), p.kv, lane, 0);
+        nx.rows(rw);
+      }
       if constexpr (FP8) tile_pv8r16(v8r16_frag_addr(tb, g, li), pk, acc);
       else tile_pv16(v_frag_addr(tb, g, li), pk, acc);
     }
