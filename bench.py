@@ -261,7 +261,7 @@ def cpu_baseline(inp: dict, target_s: float = 15.0, threads: int = 0):
 def measure(name: str, steps: int, warmup: int, cold_steps: int = 0, idx64: bool = False, clock=None):
     import torch
 
-    from sparse_attention_top_amd import kernel_name, sparse_mla_prefill, synth
+    from sparse_attention_top_amd import fp8_pool_decoded, kernel_name, sparse_mla_prefill, synth
 
     inp = synth.make_inputs(name)
     dev = torch.device("cuda:0")
@@ -282,13 +282,16 @@ def measure(name: str, steps: int, warmup: int, cold_steps: int = 0, idx64: bool
 
     wall, st = time_gpu(run, steps, warmup, stream, clock=clock)
     alg = algorithmic(inp)
+    # an fp8 pool is either read by the fp8 kernels or decoded once per call into a bf16 copy for the bf16 ones
+    decoded = kv_scale is not None and fp8_pool_decoded(inp["T"], inp["topk_n"], inp["num_kv"])
+    H, fp8 = inp["H"], kv_scale is not None and not decoded
     t = {"wall_s": wall, "ms_per_call": wall * 1e3 / steps, "kernel_ms_mean": st["mean"],
-         "kernel_ms_median": st["median"], "kernel_ms_min": st["min"],
-         "kernel": kernel_name(inp["H"], inp["topk_n"], kv_scale is not None)}
+         "kernel_ms_median": st["median"], "kernel_ms_min": st["min"], "kernel": kernel_name(H, inp["topk_n"], fp8)}
+    if decoded:
+        t["pool_decode"] = "smla_fp8_pool_decode_kernel (the pool to bf16 code values, each call, inside the events)"
     if "gfx_clock_mhz" in st:
         t["gfx_clock_mhz"] = st["gfx_clock_mhz"]
     # few (token, head group) units: the library splits each top-k row and merges (the split path's kernels)
-    H, fp8 = inp["H"], kv_scale is not None
     nw = 1 if H <= 16 else 2 if H <= 32 else (8 if fp8 and H > 64 else 4)
     units = inp["T"] * -(-H // (16 * nw))  # as the library counts them to choose the split path
     if units < torch.cuda.get_device_properties(dev).multi_processor_count and inp["topk_n"] >= 128:
@@ -376,6 +379,8 @@ def entry(name: str, steps: int, warmup: int, cold_steps: int, clock, cpu: bool,
          "roofline": roofline(alg, t, t["kernel"], name, bound)}
     if inp.get("kv_scale") is not None:
         e["pool"] = "fp8 e4m3 codes, per-tensor scale"
+        if t.get("pool_decode"):
+            e["pool_decode"] = t["pool_decode"]
     if idx64:
         e["note"] = "int64 top-k rows: index conversion kernel + the int32 path"
     if "split" in t["kernel"]:
@@ -478,6 +483,8 @@ def main():
         "gfx_clock_mhz": t.get("gfx_clock_mhz"),
         "roofline": roofline(alg, t, t["kernel"], cfg.name, bound),
     }
+    if t.get("pool_decode"):
+        line["pool_decode"] = t["pool_decode"]
     print("bench: %s %.4f ms/call, %.1f TFLOP/s, %.1f GB/s gathered" % (cfg.name, t["ms_per_call"], tflops, gbs),
           file=sys.stderr, flush=True)
     if clock is not None and bound == "mfma":

@@ -90,7 +90,8 @@ typedef enum {
  * high-water mark: 2 KiB per (unit, split, head), under 140 MB in all; a few
  * MiB for decode-sized calls). If that scratch cannot
  * be had, the call runs the single-pass path instead; the result differs only
- * by floating-point rounding order. No other call allocates.
+ * by floating-point rounding order. Apart from that, only the int64-row, fp8
+ * (when it decodes its pool) and backward entry points take scratch.
  */
 int sparse_mla_prefill(const void* q, const void* kv, const int32_t* topk_indices, const float* attn_sink,
                        float scale, void* out, float* lse, int64_t T, int64_t H, int64_t num_kv,
@@ -130,13 +131,43 @@ int sparse_mla_prefill_noalloc(const void* q, const void* kv, const int32_t* top
  * for sparse_mla_prefill (int32 rows). The forward pages only mention fp8
  * caches, as a type their Triton path could not take ("[Triton/Gluon] [CI]
  * [gfx942] Tuned sparse MLA prefill for DSv4.1-Flash TP4; fix attn_sink in
- * Triton fallback" (aiter PR #6002), description and review); the gather
- * moves half the bytes of a bf16 pool. SMLA_ERR_BAD_SCALE if kv_scale or
- * scale * kv_scale is not finite.
+ * Triton fallback" (aiter PR #6002), description and review). SMLA_ERR_BAD_SCALE
+ * if kv_scale or scale * kv_scale is not finite.
+ *
+ * Two ways to run it, chosen per call (see sparse_mla_set_fp8_pool_decode):
+ * the fp8 kernels gather the codes (half the bytes of a bf16 row) and convert
+ * them in registers; or the whole pool is first decoded into bf16 copies of
+ * its code values (exact) in stream-ordered scratch of num_kv KiB, taken from
+ * the same pool as the split path's and freed stream-ordered after the call,
+ * and the bf16 kernels run on that copy with the dequant scale folded in. The
+ * second is faster when the call gathers many times the pool's rows; by
+ * default it is taken when num_kv <= 262144 (256 MiB of copy) and
+ * T * topk >= 8 num_kv, and when its scratch cannot be had the fp8 kernels
+ * run. Results of the two agree to floating-point rounding order.
  */
 int sparse_mla_prefill_fp8(const void* q, const void* kv, float kv_scale, const int32_t* topk_indices,
                            const float* attn_sink, float scale, void* out, float* lse, int64_t T, int64_t H,
                            int64_t num_kv, int64_t topk, void* stream);
+
+/* How sparse_mla_prefill_fp8 treats the pool (process-wide; the default is AUTO). */
+#define SMLA_FP8_POOL_DECODE_NEVER 0  /* always the fp8 kernels                                   */
+#define SMLA_FP8_POOL_DECODE_AUTO 1   /* decode to a bf16 copy when it pays (sizes as above)       */
+#define SMLA_FP8_POOL_DECODE_ALWAYS 2 /* decode whenever the scratch can be had                    */
+
+/*
+ * sparse_mla_set_fp8_pool_decode -- set the mode above for every later
+ * sparse_mla_prefill_fp8 call of the process (all devices, all threads; calls
+ * already enqueued are not affected). Returns the previous mode, or -1 (and
+ * changes nothing) for a value that is not one of the three.
+ */
+int sparse_mla_set_fp8_pool_decode(int mode);
+
+/*
+ * sparse_mla_fp8_pool_decoded -- 1 if a sparse_mla_prefill_fp8 call of these
+ * sizes would decode the pool under the current mode (given its scratch can be
+ * had), else 0. No device is needed.
+ */
+int sparse_mla_fp8_pool_decoded(int64_t T, int64_t topk, int64_t num_kv);
 
 /*
  * sparse_mla_prefill_i64 -- the same operation with int64 top-k rows

@@ -15,7 +15,8 @@ from . import _lib
 HEAD_DIM = 512
 DEFAULT_SCALE = 1.0 / math.sqrt(HEAD_DIM)
 
-__all__ = ["sparse_mla_prefill", "sparse_mla_backward", "kernel_name", "HEAD_DIM", "DEFAULT_SCALE"]
+__all__ = ["sparse_mla_prefill", "sparse_mla_backward", "kernel_name", "set_fp8_pool_decode", "fp8_pool_decoded",
+           "HEAD_DIM", "DEFAULT_SCALE"]
 
 
 def _check(cond: bool, msg: str):
@@ -156,3 +157,22 @@ def kernel_name(H: int, topk: int, kv_fp8: bool = False) -> str:
     if name is None:
         raise ValueError("need H >= 1 and topk >= 0")
     return name.decode()
+
+
+_FP8_MODES = {"never": _lib.FP8_POOL_DECODE_NEVER, "auto": _lib.FP8_POOL_DECODE_AUTO,
+              "always": _lib.FP8_POOL_DECODE_ALWAYS}
+
+
+def set_fp8_pool_decode(mode: str) -> str:
+    """How an fp8 pool is read, process-wide: "never" (the fp8 kernels gather
+    codes), "auto" (the default: decode the pool once per call into a bf16
+    copy and run the bf16 kernels when the call gathers many times the pool's
+    rows) or "always". Returns the previous mode."""
+    _check(mode in _FP8_MODES, "mode must be one of %s" % sorted(_FP8_MODES))
+    prev = _lib.load().sparse_mla_set_fp8_pool_decode(_FP8_MODES[mode])
+    return {v: k for k, v in _FP8_MODES.items()}[prev]
+
+
+def fp8_pool_decoded(T: int, topk: int, num_kv: int) -> bool:
+    """Whether an fp8 call of these sizes decodes its pool under the current mode."""
+    return bool(_lib.load().sparse_mla_fp8_pool_decoded(int(T), int(topk), int(num_kv)))

@@ -52,6 +52,8 @@ SIGNATURES = {
         ctypes.c_int64,  # chunk_tokens
         ctypes.c_void_p,  # stream
     ]),
+    "sparse_mla_set_fp8_pool_decode": (ctypes.c_int, [ctypes.c_int]),
+    "sparse_mla_fp8_pool_decoded": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]),
     "sparse_mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "sparse_mla_kernel_name": (ctypes.c_char_p, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int]),
     "sparse_mla_version": (ctypes.c_int, []),
@@ -66,6 +68,10 @@ SMLA_ERR_NO_DEVICE = -5
 SMLA_ERR_LAUNCH = -6
 SMLA_ERR_NO_MEMORY = -7
 SMLA_ERR_SCRATCH_LIMIT = -8
+
+FP8_POOL_DECODE_NEVER = 0
+FP8_POOL_DECODE_AUTO = 1
+FP8_POOL_DECODE_ALWAYS = 2
 
 _lib = None
 

@@ -57,7 +57,7 @@ struct Params {
   int topk_n;
   int head_groups;
   float scale_log2;  // scale * log2(e) (times the pool's dequant scale for fp8 pools)
-  float out_scale;   // fp8 pools: the dequant scale, applied to o at the end
+  float out_scale;   // the pool's dequant scale (1 for bf16), applied to o at the end
 };
 
 // Split over the top-k row (few tokens): split `sp` of a row covers raw
@@ -614,7 +614,7 @@ __device__ __forceinline__ void smla_fwd_body(const Params& p, const SplitArgs& 
   const bool has_sink = !(sk == -INFINITY);
   const float sink_l2 = sk * kLog2e;
   HeadEnd he = head_end(l_part, m_ref, sk, has_sink, sink_l2);
-  if constexpr (FP8) he.oscale *= p.out_scale;  // V == code * dequant scale
+  he.oscale *= p.out_scale;  // 1, or the dequant scale of an fp8 pool (V == code * scale)
   if (g_f == 0 && head_f < p.H) p.lse[(size_t)t * p.H + head_f] = he.lse;
   if constexpr (NW > 1) lds_barrier();  // all waves are done with the tiles
   const uint32_t ob = sm.stage() + (uint32_t)w * 16 * kRowStride;
@@ -1390,7 +1390,7 @@ __device__ __forceinline__ void smla_fwd128_body(const Params& p) {
         const bool has_sink = !(sk[hb] == -INFINITY);
         const HeadEnd he = head_end(ss.l_part[hb], ss.m_ref(hb), sk[hb], has_sink, sk[hb] * kLog2e);
         if (g == 0 && head < p.H) p.lse[(size_t)t * p.H + head] = he.lse;
-        oscale[hb] = he.oscale;
+        oscale[hb] = he.oscale * p.out_scale;  // 1, or an fp8 pool's dequant scale
       }
       const uint32_t osc_own = lds_addr(sm.osc) + 32 * li + 8 * w;
       if (g == 0) {
@@ -1752,7 +1752,7 @@ __device__ __forceinline__ void smla_fwd16_body(const Params& p) {
   const bool has_sink = !(sk == -INFINITY);
   const float sink_l2 = sk * kLog2e;
   HeadEnd he = head_end(l_part, m_ref, sk, has_sink, sink_l2);
-  if constexpr (FP8) he.oscale *= p.out_scale;  // V == code * dequant scale
+  he.oscale *= p.out_scale;  // 1, or the dequant scale of an fp8 pool (V == code * scale)
   if (g == 0 && head < p.H) p.lse[(size_t)t * p.H + head] = he.lse;
   const uint32_t ob = sm.stage();
   mfma_agpr_drain(acc);
@@ -1966,8 +1966,10 @@ int run_prefill(const void* q, const void* kv, const int32_t* topk_indices, cons
   if (topk == 0 || !kv) p.nkv = 0;
   p.topk_n = (int)topk;
   p.head_groups = (int)head_groups;
-  p.scale_log2 = scale * (fp8 ? kv_scale : 1.f) * kLog2e;
-  p.out_scale = fp8 ? kv_scale : 1.f;
+  // a pool of fp8 codes (read by the fp8 kernels, or decoded to bf16 code
+  // values beforehand) carries its dequant scale here; 1 for a bf16 pool
+  p.scale_log2 = scale * kv_scale * kLog2e;
+  p.out_scale = kv_scale;
   SplitArgs sa;
   sa.nsplit = 1;
   sa.split_len = (int)topk;
@@ -2036,6 +2038,23 @@ int run_prefill(const void* q, const void* kv, const int32_t* topk_indices, cons
   return err == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
 }
 
+// An OCP FP8 E4M3 pool -> bf16 copies of its code values, 16 codes per thread
+// per step (exact: every code value is a bf16 value; the two NaN codes stay
+// NaN). The dequant scale is not applied here: the kernels fold it into the
+// logit scale and the output scale, as the fp8 kernels do.
+__global__ __launch_bounds__(256) void smla_fp8_pool_decode_kernel(const uint8_t* __restrict__ codes,
+                                                                   uint16_t* __restrict__ out, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256) {
+    const u32x4 c = __builtin_nontemporal_load((const u32x4*)codes + i);
+    u32x4 lo = fp8x8_to_bf16(u32x2{c[0], c[1]});
+    u32x4 hi = fp8x8_to_bf16(u32x2{c[2], c[3]});
+    valu_to_mfma(lo, hi);  // the asm conversions' results are read by the stores below
+    u32x4* d = (u32x4*)out + 2 * i;
+    d[0] = lo;
+    d[1] = hi;
+  }
+}
+
 // int64 top-k rows -> int32: a valid index (0 <= v < num_kv) becomes its row
 // number, anything else -1, so an index at or past 2^31 can never alias a row.
 __global__ __launch_bounds__(256) void smla_idx64_kernel(const int64_t* __restrict__ in, int32_t* __restrict__ out,
@@ -2098,6 +2117,33 @@ extern "C" int sparse_mla_prefill_noalloc(const void* q, const void* kv, const i
                      false, 1.f, ws, kNoAllocScratchBytes);
 }
 
+// An fp8 call may first decode the whole pool into bf16 scratch and run the
+// bf16 kernels on it: a 16-row fp8 tile costs each wave 128 two-code
+// conversions per use, more than its halved gather saves, while one decode
+// pass moves num_kv * 1.5 KiB. Worth it when the call gathers many times the
+// pool's rows (T * topk >= 8 num_kv) and the copy is modest (<= 256 MiB);
+// decode-sized calls and very large pools keep the fp8 kernels.
+static constexpr int64_t kFp8DecodeMaxRows = ((int64_t)256 << 20) / kRowBytes;
+static constexpr int64_t kFp8DecodeMinReuse = 8;
+static std::atomic<int> g_fp8_pool_decode{SMLA_FP8_POOL_DECODE_AUTO};
+
+static bool fp8_pool_decoded(int64_t T, int64_t topk, int64_t num_kv) {
+  const int mode = g_fp8_pool_decode.load(std::memory_order_relaxed);
+  if (mode == SMLA_FP8_POOL_DECODE_NEVER || T <= 0 || topk <= 0 || num_kv <= 0) return false;
+  if (mode == SMLA_FP8_POOL_DECODE_ALWAYS) return true;
+  return num_kv <= kFp8DecodeMaxRows && kFp8DecodeMinReuse * num_kv <= T * topk;
+}
+
+extern "C" int sparse_mla_set_fp8_pool_decode(int mode) {
+  if (mode != SMLA_FP8_POOL_DECODE_NEVER && mode != SMLA_FP8_POOL_DECODE_AUTO && mode != SMLA_FP8_POOL_DECODE_ALWAYS)
+    return -1;
+  return g_fp8_pool_decode.exchange(mode);
+}
+
+extern "C" int sparse_mla_fp8_pool_decoded(int64_t T, int64_t topk, int64_t num_kv) {
+  return fp8_pool_decoded(T, topk, num_kv) ? 1 : 0;
+}
+
 extern "C" int sparse_mla_prefill_fp8(const void* q, const void* kv, float kv_scale, const int32_t* topk_indices,
                                       const float* attn_sink, float scale, void* out, float* lse, int64_t T,
                                       int64_t H, int64_t num_kv, int64_t topk, void* stream) {
@@ -2107,8 +2153,27 @@ extern "C" int sparse_mla_prefill_fp8(const void* q, const void* kv, float kv_sc
   if (T == 0) return SMLA_OK;
   int dev = -1;
   if ((rc = current_device(&dev)) != SMLA_OK) return rc;
-  return run_prefill(q, kv, topk_indices, attn_sink, scale, out, lse, T, H, num_kv, topk, dev, (hipStream_t)stream,
-                     true, kv_scale);
+  hipStream_t s = (hipStream_t)stream;
+  if (fp8_pool_decoded(T, topk, num_kv)) {
+    void* ws = nullptr;
+    hipMemPool_t pool = scratch_pool(dev);
+    if (pool != nullptr && hipMallocFromPoolAsync(&ws, (size_t)num_kv * kRowBytes, pool, s) == hipSuccess &&
+        ws != nullptr) {
+      const int64_t n16 = num_kv * (kD / 16);
+      const int64_t want = (n16 + 255) / 256;
+      const unsigned blocks = (unsigned)(want < 8192 ? want : 8192);
+      hipLaunchKernelGGL(smla_fp8_pool_decode_kernel, dim3(blocks), dim3(256), 0, s, (const uint8_t*)kv,
+                         (uint16_t*)ws, n16);
+      rc = hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
+      if (rc == SMLA_OK)
+        rc = run_prefill(q, ws, topk_indices, attn_sink, scale, out, lse, T, H, num_kv, topk, dev, s, false,
+                         kv_scale);
+      if (hipFreeAsync(ws, s) != hipSuccess && rc == SMLA_OK) rc = SMLA_ERR_LAUNCH;
+      return rc;
+    }
+    (void)hipGetLastError();  // no scratch: the fp8 kernels read the codes directly
+  }
+  return run_prefill(q, kv, topk_indices, attn_sink, scale, out, lse, T, H, num_kv, topk, dev, s, true, kv_scale);
 }
 
 extern "C" int sparse_mla_prefill_i64(const void* q, const void* kv, const int64_t* topk_indices,

@@ -181,6 +181,29 @@ def test_backward_chunked_argument_errors():
     assert lib.sparse_mla_backward_chunked(*bad, 2, None) == _lib.SMLA_ERR_MISALIGNED
 
 
+def test_fp8_pool_decode_policy():
+    """An fp8 call decodes its pool to a bf16 copy (by default) when it gathers at least 8x the pool's rows and
+    the copy is at most 256 MiB; the mode switch returns the previous mode and refuses unknown values."""
+    from sparse_attention_top_amd import fp8_pool_decoded, set_fp8_pool_decode
+
+    lib = _lib.load()
+    assert set_fp8_pool_decode("auto") == "auto"
+    assert fp8_pool_decoded(16384, 640, 20480)          # tp4: 10.5 M slots over a 20 MiB pool
+    assert fp8_pool_decoded(4096, 512, 5120)            # wide
+    assert not fp8_pool_decoded(16, 640, 20480)         # decode-sized call: fewer slots than 8x the pool
+    assert not fp8_pool_decoded(16384, 2048, 2200000)   # a 2.1 GiB paged pool: its copy is too large
+    assert fp8_pool_decoded(1 << 20, 64, 262144) and not fp8_pool_decoded(1 << 20, 64, 262145)
+    assert not fp8_pool_decoded(0, 640, 100) and not fp8_pool_decoded(10, 0, 100) and not fp8_pool_decoded(10, 10, 0)
+    assert set_fp8_pool_decode("always") == "auto"
+    assert fp8_pool_decoded(16, 640, 20480) and fp8_pool_decoded(16384, 2048, 2200000)
+    assert set_fp8_pool_decode("never") == "always"
+    assert not fp8_pool_decoded(16384, 640, 20480)
+    assert lib.sparse_mla_set_fp8_pool_decode(7) == -1 and lib.sparse_mla_set_fp8_pool_decode(-1) == -1
+    assert set_fp8_pool_decode("auto") == "never"
+    with pytest.raises(RuntimeError):
+        set_fp8_pool_decode("sometimes")
+
+
 def test_empty_sequence_is_ok_without_a_device():
     assert call(T=0, q=None, out=None, lse=None, topk=None, kv=None) == _lib.SMLA_OK
 

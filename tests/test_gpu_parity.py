@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 import torch
 
-from sparse_attention_top_amd import synth
+from sparse_attention_top_amd import fp8_pool_decoded, set_fp8_pool_decode, synth
 
 from gpu_util import DEV, compare, oracle_ref, run_case, run_gpu
 
@@ -438,18 +438,29 @@ def test_int64_indices_never_wrap(T, H, topk, num_kv):
 
 
 # ---- fp8 (OCP E4M3) pools ----
+# Each case runs both ways an fp8 pool is read: by the fp8 kernels ("direct")
+# and decoded once per call into a bf16 copy for the bf16 kernels ("decoded").
+
+@pytest.fixture(params=["direct", "decoded"])
+def fp8_path(request):
+    prev = set_fp8_pool_decode("never" if request.param == "direct" else "always")
+    yield request.param
+    set_fp8_pool_decode(prev)
+
 
 @pytest.mark.parametrize("name,T", [("tiny_fp8", None), ("tp4_fp8", 768), ("wide_fp8", 384), ("glm_fp8", 512)])
-def test_fp8_pool_truncated_all_tokens(name, T):
+def test_fp8_pool_truncated_all_tokens(name, T, fp8_path):
     inp = synth.make_inputs(name, T=T)
     o, lse = run_case(inp)
     stats = compare(o, lse, oracle_ref(inp), what="%s T=%s" % (name, inp["T"]))
     print(name, inp["T"], stats)
 
 
-@pytest.mark.parametrize("name,k", [("tp4_fp8", 32), ("glm_fp8", 16)])
-def test_fp8_pool_full_size_sampled(name, k):
+@pytest.mark.parametrize("name,k,decoded", [("tp4_fp8", 32, True), ("glm_fp8", 16, False)])
+def test_fp8_pool_full_size_sampled(name, k, decoded):
+    """At full size under the default mode: tp4's 20 MiB pool is decoded, glm's 2.1 GiB paged pool is not."""
     inp, o, lse = full_case(name)
+    assert fp8_pool_decoded(inp["T"], inp["topk_n"], inp["num_kv"]) == decoded
     tok = sample_tokens(inp["topk"], inp["num_kv"], k, seed=9)
     compare(o, lse, oracle_ref(inp, tokens=tok), tokens=tok, what="%s full" % name)
 
@@ -464,7 +475,7 @@ def make_random_fp8(seed, T, H, num_kv, topk, p_invalid=0.15, sink=True, kv_scal
 
 @pytest.mark.parametrize("T,H,topk,num_kv", [(20, 16, 300, 900), (16, 128, 200, 600), (3, 16, 1024, 3000),
                                              (2, 128, 777, 2000), (9, 40, 96, 300)])
-def test_fp8_pool_random(T, H, topk, num_kv):
+def test_fp8_pool_random(T, H, topk, num_kv, fp8_path):
     """Random rows and every code value (subnormals, both signs, the largest); few-token shapes
     take the split path."""
     inp = make_random_fp8(6000 + T + H, T, H, num_kv, topk)
@@ -473,7 +484,7 @@ def test_fp8_pool_random(T, H, topk, num_kv):
 
 
 @pytest.mark.parametrize("topk,num_kv,p_invalid", H16_EDGES)
-def test_fp8_h16_tile_and_segment_edges(topk, num_kv, p_invalid):
+def test_fp8_h16_tile_and_segment_edges(topk, num_kv, p_invalid, fp8_path):
     """The fp8 16-row kernel (8 KiB slab tiles, 512-entry segments) at the same tile and segment edges, single pass
     (300 tokens)."""
     inp = make_random_fp8(7500 + topk, 300, 16, num_kv, topk, p_invalid=p_invalid)
@@ -481,7 +492,7 @@ def test_fp8_h16_tile_and_segment_edges(topk, num_kv, p_invalid):
     compare(o, lse, oracle_ref(inp), what="fp8 H=16 topk=%d" % topk)
 
 
-def test_fp8_nan_code_stays_local_and_invalid_rows():
+def test_fp8_nan_code_stays_local_and_invalid_rows(fp8_path):
     inp = make_random_fp8(6100, T=12, H=16, num_kv=400, topk=64, p_invalid=0.1)
     idx = inp["topk"]
     idx[0, :] = -1                                   # no valid slot
