@@ -297,6 +297,9 @@ def measure(name: str, steps: int, warmup: int, cold_steps: int = 0, idx64: bool
     if units < torch.cuda.get_device_properties(dev).multi_processor_count and inp["topk_n"] >= 128:
         t["kernel"] = "smla_fwd%s_split_kernel<%d, %d> + smla_merge_kernel" % ("_fp8" if fp8 else "", nw,
                                                                               4 if fp8 and nw >= 4 else 2)
+    elif idx64 and H <= 16 and not fp8:  # the 16-row kernel reads int64 rows itself
+        t["kernel"] = t["kernel"].replace("smla_fwd16_kernel<1, ", "smla_fwd16_i64_kernel<")
+        t["idx64_native"] = True
     if cold_steps:
         # cold caches: overwrite 512 MiB (more than the 256 MB MALL plus 8 x 4 MB of L2) before each launch
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -382,7 +385,8 @@ def entry(name: str, steps: int, warmup: int, cold_steps: int, clock, cpu: bool,
         if t.get("pool_decode"):
             e["pool_decode"] = t["pool_decode"]
     if idx64:
-        e["note"] = "int64 top-k rows: index conversion kernel + the int32 path"
+        e["note"] = ("int64 top-k rows, read by the 16-row kernel itself" if t.get("idx64_native") else
+                     "int64 top-k rows: index conversion kernel + the int32 path")
     if "split" in t["kernel"]:
         e["note"] = ("few-token call: split-KV kernel + merge kernel; per-launch events include the "
                      "host launch gap, rocprofv3 kernel time is the GPU figure")

@@ -179,11 +179,13 @@ int sparse_mla_fp8_pool_decoded(int64_t T, int64_t topk, int64_t num_kv);
  * slot indices are kept as int64, because a cast to int32 wrapped slots at or
  * past 2^31 onto valid rows. Here every index is compared as a 64-bit value:
  * valid iff 0 <= idx < num_kv, anything else (2^32 + r included) is an
- * invalid slot. A first kernel maps the rows to int32 row numbers (-1 for
+ * invalid slot. At H <= 16 in a single pass (T at least the device's compute
+ * units, or rows under 128 entries) the forward kernel reads the int64 rows
+ * itself. Otherwise a first kernel maps the rows to int32 row numbers (-1 for
  * invalid) in stream-ordered scratch of 4 * T * topk bytes from the library's
- * per-device pool (SMLA_ERR_NO_MEMORY if that cannot be had); the forward then
- * runs as for int32 rows, so results are bitwise those of sparse_mla_prefill
- * on the equivalent int32 rows.
+ * per-device pool (SMLA_ERR_NO_MEMORY if that cannot be had) and the forward
+ * runs as for int32 rows. Either way results are bitwise those of
+ * sparse_mla_prefill on the equivalent int32 rows.
  */
 int sparse_mla_prefill_i64(const void* q, const void* kv, const int64_t* topk_indices, const float* attn_sink,
                            float scale, void* out, float* lse, int64_t T, int64_t H, int64_t num_kv,

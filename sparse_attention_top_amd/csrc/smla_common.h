@@ -213,6 +213,19 @@ __device__ __forceinline__ void compact_load(SegmentRaw<NW, CAP>& r, const int32
     r.raw[c] = trow[max(min(pos, len - 1), 0)];
   }
 }
+// int64 rows: an entry is valid iff 0 <= v < nkv in 64-bit arithmetic (nkv <=
+// 2^31); a valid entry is narrowed to int32, anything else becomes -1, so a
+// value such as 2^32 + r never wraps onto row r. The rest is the int32 form's.
+template <int NW, int CAP>
+__device__ __forceinline__ void compact_load(SegmentRaw<NW, CAP>& r, const int64_t* __restrict__ trow, int len, int lane,
+                                             int w, uint32_t nkv) {
+#pragma unroll
+  for (int c = 0; c < SegmentRaw<NW, CAP>::MAXC; ++c) {
+    const int pos = c * SegmentRaw<NW, CAP>::CH + w * 64 + lane;
+    const int64_t v = trow[max(min(pos, len - 1), 0)];
+    r.raw[c] = (uint64_t)v < (uint64_t)nkv ? (int32_t)v : -1;
+  }
+}
 template <int NW, typename SM, int CAP>
 __device__ __forceinline__ int compact_finish(const SegmentRaw<NW, CAP>& rr, int len, uint32_t nkv, SM& sm, int lane,
                                               int w) {
@@ -264,6 +277,13 @@ __device__ __forceinline__ int compact_segment(const int32_t* __restrict__ trow,
                                                int w) {
   SegmentRaw<NW, CAP> r;
   compact_load(r, trow, len, lane, w);
+  return compact_finish<NW>(r, len, nkv, sm, lane, w);
+}
+template <int NW, typename SM, int CAP = kListCap>
+__device__ __forceinline__ int compact_segment(const int64_t* __restrict__ trow, int len, uint32_t nkv, SM& sm, int lane,
+                                               int w) {
+  SegmentRaw<NW, CAP> r;
+  compact_load(r, trow, len, lane, w, nkv);
   return compact_finish<NW>(r, len, nkv, sm, lane, w);
 }
 

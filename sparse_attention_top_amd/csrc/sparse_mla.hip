@@ -48,6 +48,7 @@ struct Params {
   const uint16_t* q;
   const uint16_t* kv;
   const int32_t* topk;
+  const int64_t* topk64;  // int64 rows, read by the 16-row kernel itself (topk unused then), else null
   const float* sink;
   uint16_t* out;
   float* lse;
@@ -1677,9 +1678,10 @@ __device__ __forceinline__ void tile_pv8r16(uint32_t vaddr, const bf16x4& pk, f3
 // One workgroup (one wave) per token. Tile j+NBUF-1 is gathered at the top of
 // iteration j (its ring slot was last read in iteration j-1, whose reads have
 // completed), then the wave waits for tile j and computes it.
-template <int NBUF, int CAP, bool FP8>
+template <int NBUF, int CAP, bool FP8, bool I64 = false>
 __device__ __forceinline__ void smla_fwd16_body(const Params& p) {
   static_assert(NBUF == 1 || NBUF == 2, "ring of one or two 16-row tiles");
+  static_assert(!(I64 && FP8), "int64 rows are read directly by the bf16 kernel only");
   static_assert(FP8 || NBUF == 1, "a bf16 pool runs one tile at a time (the next tile's list entries are read ahead)");
   constexpr int AHEAD = NBUF - 1;
   using SM = Smem16<NBUF, CAP, FP8>;
@@ -1699,7 +1701,10 @@ __device__ __forceinline__ void smla_fwd16_body(const Params& p) {
   load_q(qf, p, t, head, g);
   bf16x4 pk;
 
-  const int32_t* trow = p.topk + (size_t)t * p.topk_n;
+  using Idx = typename std::conditional<I64, int64_t, int32_t>::type;
+  const Idx* trow;
+  if constexpr (I64) trow = p.topk64 + (size_t)t * p.topk_n;
+  else trow = p.topk + (size_t)t * p.topk_n;
   using Issue = typename std::conditional<FP8, TileIssue8r16, TileIssue<1, kBK16>>::type;
   using Elem = typename std::conditional<FP8, uint8_t, uint16_t>::type;
   const Elem* kvp = (const Elem*)p.kv;
@@ -1781,6 +1786,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NBUF == 1 ? 
 template <int NBUF, int CAP>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void smla_fwd16_fp8_kernel(const Params p) {
   smla_fwd16_body<NBUF, CAP, true>(p);
+}
+
+// The bf16 16-row kernel on int64 top-k rows: the compaction tests each entry
+// in 64 bits and narrows the valid ones, so no conversion pass precedes it.
+template <int CAP>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void smla_fwd16_i64_kernel(const Params p) {
+  smla_fwd16_body<1, CAP, false, true>(p);
 }
 
 // Merge of the splits of one (token, head), one wave each: lane s < nsplit
@@ -1949,7 +1961,7 @@ int cu_count(int dev) {
 int run_prefill(const void* q, const void* kv, const int32_t* topk_indices, const float* attn_sink, float scale,
                 void* out, float* lse, int64_t T, int64_t H, int64_t num_kv, int64_t topk, int dev,
                 hipStream_t s, bool fp8 = false, float kv_scale = 1.f, void* fixed_ws = nullptr,
-                size_t fixed_cap = 0) {
+                size_t fixed_cap = 0, const int64_t* topk64 = nullptr) {
   const Variant var = pick_variant(H, topk, fp8);
   const int64_t heads_per_wg = (int64_t)16 * var.nw;
   const int64_t head_groups = (H + heads_per_wg - 1) / heads_per_wg;
@@ -1957,6 +1969,7 @@ int run_prefill(const void* q, const void* kv, const int32_t* topk_indices, cons
   p.q = (const uint16_t*)q;
   p.kv = (const uint16_t*)kv;
   p.topk = topk_indices;
+  p.topk64 = topk64;
   p.sink = attn_sink;
   p.out = (uint16_t*)out;
   p.lse = lse;
@@ -1964,6 +1977,8 @@ int run_prefill(const void* q, const void* kv, const int32_t* topk_indices, cons
   p.H = (int)H;
   p.nkv = (uint32_t)(num_kv < ((int64_t)1 << 31) ? num_kv : ((int64_t)1 << 31));
   if (topk == 0 || !kv) p.nkv = 0;
+  // int64 rows are taken only by the single-pass 16-row kernel (the caller checks)
+  if (topk64 != nullptr && (H > 16 || fp8)) return SMLA_ERR_BAD_SIZE;
   p.topk_n = (int)topk;
   p.head_groups = (int)head_groups;
   // a pool of fp8 codes (read by the fp8 kernels, or decoded to bf16 code
@@ -1981,7 +1996,7 @@ int run_prefill(const void* q, const void* kv, const int32_t* topk_indices, cons
   // over several workgroups, then merge (stream-ordered scratch; if it cannot
   // be had, the single-pass path below still gives the result).
   const int64_t cus = cu_count(dev);
-  if (cus > 0 && units < cus && topk >= 2 * kMinSplitLen) {
+  if (topk64 == nullptr && cus > 0 && units < cus && topk >= 2 * kMinSplitLen) {
     const int64_t slots = (var.nw == 8 ? 1 : 2) * cus;  // resident workgroups
     int64_t ns = (slots + units - 1) / units;
     ns = ns < topk / kMinSplitLen ? ns : topk / kMinSplitLen;
@@ -2030,6 +2045,7 @@ int run_prefill(const void* q, const void* kv, const int32_t* topk_indices, cons
   }
   if (H <= 16) {
     if (fp8) hipLaunchKernelGGL((smla_fwd16_fp8_kernel<2, 512>), dim3((unsigned)units), dim3(64), 0, s, p);
+    else if (topk64 != nullptr) hipLaunchKernelGGL((smla_fwd16_i64_kernel<kR16Cap>), dim3((unsigned)units), dim3(64), 0, s, p);
     else hipLaunchKernelGGL((smla_fwd16_kernel<kR16Nbuf, kR16Cap>), dim3((unsigned)units), dim3(64), 0, s, p);
     return hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
   }
@@ -2053,6 +2069,14 @@ __global__ __launch_bounds__(256) void smla_fp8_pool_decode_kernel(const uint8_t
     d[0] = lo;
     d[1] = hi;
   }
+}
+
+// Whether a bf16 call runs the single-pass 16-row kernel: H <= 16 and either
+// as many tokens as compute units or rows too short to split (the split
+// condition of run_prefill, whose units are the tokens at H <= 16).
+bool single_pass16(int64_t T, int64_t H, int64_t topk, int dev) {
+  const int64_t cus = cu_count(dev);
+  return H <= 16 && !(cus > 0 && T < cus && topk >= 2 * kMinSplitLen);
 }
 
 // int64 top-k rows -> int32: a valid index (0 <= v < num_kv) becomes its row
@@ -2185,6 +2209,10 @@ extern "C" int sparse_mla_prefill_i64(const void* q, const void* kv, const int64
   if ((rc = current_device(&dev)) != SMLA_OK) return rc;
   hipStream_t s = (hipStream_t)stream;
   if (topk == 0) return run_prefill(q, kv, nullptr, attn_sink, scale, out, lse, T, H, num_kv, topk, dev, s);
+  // H <= 16 in a single pass: the 16-row kernel reads the int64 rows itself
+  if (single_pass16(T, H, topk, dev))
+    return run_prefill(q, kv, nullptr, attn_sink, scale, out, lse, T, H, num_kv, topk, dev, s, false, 1.f, nullptr, 0,
+                       topk_indices);
   const int64_t n = T * topk;
   void* ws = nullptr;
   hipMemPool_t pool = scratch_pool(dev);

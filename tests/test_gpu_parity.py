@@ -417,11 +417,14 @@ def test_decode_workload_full():
 
 # ---- int64 top-k rows ----
 
-@pytest.mark.parametrize("T,H,topk,num_kv", [(40, 16, 300, 1000), (24, 128, 512, 2000), (3, 16, 1024, 4000)])
+@pytest.mark.parametrize("T,H,topk,num_kv", [(40, 16, 300, 1000), (24, 128, 512, 2000), (3, 16, 1024, 4000),
+                                             (300, 16, 640, 2000), (300, 8, 1281, 3000), (40, 16, 100, 500)])
 def test_int64_indices_never_wrap(T, H, topk, num_kv):
     """int64 rows: values 2^32 + r (which an int32 cast would turn into row r), 2^31 and large
     negatives are invalid; the result equals the oracle and, bitwise, the int32 path on the
-    equivalent rows (invalid -> -1)."""
+    equivalent rows (invalid -> -1). At H <= 16 in a single pass (300 tokens, or rows under 128
+    entries) the 16-row kernel reads the int64 rows itself, over one, two or three list segments;
+    the other shapes convert the rows first."""
     inp = make_random(5000 + T + H, T=T, H=H, num_kv=num_kv, topk=topk, p_invalid=0.1)
     rng = np.random.default_rng(T * H)
     idx = inp["topk"].astype(np.int64)
@@ -434,6 +437,16 @@ def test_int64_indices_never_wrap(T, H, topk, num_kv):
     compare(o64, l64, ref, what="int64 T=%d H=%d" % (T, H))
     idx32 = np.where((idx >= 0) & (idx < num_kv), idx, -1).astype(np.int32)
     o32, l32 = run_gpu(inp["q"], inp["kv"], idx32, inp["sink"], inp["scale"])
+    assert np.array_equal(o64, o32) and np.array_equal(l64.view(np.uint32), l32.view(np.uint32))
+
+
+def test_int64_rows_full_size_tp4_bitwise():
+    """tp4 at full size with its rows as int64 and every invalid entry written as 2^32 + 5 (row 5 after an int32
+    cast): the 16-row kernel reads them itself, and the result equals the int32 call bit for bit."""
+    inp, o32, l32 = full_case("tp4")
+    idx = inp["topk"].astype(np.int64)
+    idx[idx < 0] = 2**32 + 5
+    o64, l64 = run_gpu(inp["q"], inp["kv"], idx, inp["sink"], inp["scale"])
     assert np.array_equal(o64, o32) and np.array_equal(l64.view(np.uint32), l32.view(np.uint32))
 
 

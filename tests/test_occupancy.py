@@ -26,6 +26,7 @@ LDS_PER_CU = 160 * 1024
 # kernel (demangled template form) -> (workgroups per CU its LDS must allow, waves per SIMD)
 EXPECTED = {
     "smla_fwd16_kernel<1, 640>": (8, 2),
+    "smla_fwd16_i64_kernel<640>": (8, 2),
     "smla_fwd16_fp8_kernel<2, 512>": (8, 2),
     "smla_fwd_kernel<4, 2>": (2, 2),
     "smla_fwd_kernel<2, 2>": (2, 1),
@@ -36,6 +37,7 @@ EXPECTED = {
 
 MANGLED = {
     "smla_fwd16_kernel<1, 640>": "smla_fwd16_kernelILi1ELi640EE",
+    "smla_fwd16_i64_kernel<640>": "smla_fwd16_i64_kernelILi640EE",
     "smla_fwd16_fp8_kernel<2, 512>": "smla_fwd16_fp8_kernelILi2ELi512EE",
     "smla_fwd_kernel<4, 2>": "15smla_fwd_kernelILi4ELi2EE",
     "smla_fwd_kernel<2, 2>": "15smla_fwd_kernelILi2ELi2EE",
