@@ -245,6 +245,21 @@ int sparse_mla_backward_chunked(const void* q, const void* kv, const void* dout,
                                 float* d_sink, int64_t T, int64_t H, int64_t num_kv, int64_t topk,
                                 int64_t chunk_tokens, void* stream);
 
+/*
+ * sparse_mla_backward_i64 -- sparse_mla_backward_chunked with int64 top-k rows
+ * (int64 [T, topk], contiguous, 8-byte aligned; validity as for
+ * sparse_mla_prefill_i64: 0 <= idx < num_kv compared in 64 bits). The rows are
+ * first mapped to int32 row numbers (-1 for invalid) in stream-ordered scratch
+ * of 4 * T * topk bytes from the library's per-device pool; the gradients are
+ * then bitwise those of the int32 backward on the equivalent rows. Argument
+ * errors return before anything is enqueued; SMLA_ERR_NO_MEMORY may also come
+ * after the mapping (the backward's own scratch), with no output written.
+ */
+int sparse_mla_backward_i64(const void* q, const void* kv, const void* dout, const void* o, const float* lse,
+                            const int64_t* topk_indices, const float* attn_sink, float scale, void* dq, void* dkv,
+                            float* d_sink, int64_t T, int64_t H, int64_t num_kv, int64_t topk, int64_t chunk_tokens,
+                            void* stream);
+
 /* Human-readable text for a status code (static storage; never NULL). */
 const char* sparse_mla_status_string(int status);
 

@@ -100,7 +100,7 @@ def sparse_mla_backward(q, kv, dout, o, lse, topk_indices, attn_sink=None, scale
 
     q, dout, o: bf16 [T, H, 512] (o and lse are the forward's outputs, lse
     sink-inclusive fp32 [T, H]); kv: bf16 [num_kv, 512]; topk_indices: int32
-    [T, topk]; attn_sink: fp32 [H] or None (then d_sink is None); scale: float
+    or int64 [T, topk]; attn_sink: fp32 [H] or None (then d_sink is None); scale: float
     (default 1/sqrt(512)). H <= 128. dq and dkv come back bf16, d_sink fp32.
     chunk_tokens: tokens per pass (None: passes chosen so that one pass's
     scratch stays under 4 GiB). All tensors on the same GPU and contiguous;
@@ -120,7 +120,8 @@ def sparse_mla_backward(q, kv, dout, o, lse, topk_indices, attn_sink=None, scale
     _check(kv.dim() == 2 and kv.shape[1] == HEAD_DIM, "kv must be [num_kv, 512], got %s" % (tuple(kv.shape),))
     _check(lse.device == dev and lse.dtype == torch.float32 and tuple(lse.shape) == (T, H),
            "lse must be float32 [T, H] on q's device")
-    _check(topk_indices.device == dev and topk_indices.dtype == torch.int32, "topk_indices must be int32 on %s" % dev)
+    _check(topk_indices.device == dev and topk_indices.dtype in (torch.int32, torch.int64),
+           "topk_indices must be int32 or int64 on %s" % dev)
     _check(topk_indices.dim() == 2 and topk_indices.shape[0] == T, "topk_indices must be [T, topk]")
     if attn_sink is not None:
         _check(attn_sink.device == dev and attn_sink.dtype == torch.float32 and tuple(attn_sink.shape) == (H,),
@@ -138,7 +139,8 @@ def sparse_mla_backward(q, kv, dout, o, lse, topk_indices, attn_sink=None, scale
     lib = _lib.load()
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        rc = lib.sparse_mla_backward_chunked(
+        entry = lib.sparse_mla_backward_i64 if topk_indices.dtype == torch.int64 else lib.sparse_mla_backward_chunked
+        rc = entry(
             q.data_ptr(), kv.data_ptr() if kv.numel() else None, dout.data_ptr(), o.data_ptr(), lse.data_ptr(),
             topk_indices.data_ptr() if topk_indices.numel() else None,
             attn_sink.data_ptr() if attn_sink is not None else None, float(scale),

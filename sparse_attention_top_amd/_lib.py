@@ -52,6 +52,14 @@ SIGNATURES = {
         ctypes.c_int64,  # chunk_tokens
         ctypes.c_void_p,  # stream
     ]),
+    "sparse_mla_backward_i64": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,  # q, kv, dout, o, lse
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,  # topk (int64), sink, scale
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,  # dq, dkv, d_sink
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,  # T, H, num_kv, topk
+        ctypes.c_int64,  # chunk_tokens
+        ctypes.c_void_p,  # stream
+    ]),
     "sparse_mla_set_fp8_pool_decode": (ctypes.c_int, [ctypes.c_int]),
     "sparse_mla_fp8_pool_decoded": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]),
     "sparse_mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),

@@ -535,6 +535,17 @@ __device__ __forceinline__ void tile_pv(uint32_t vrow, const bf16x8& pk, f32x4 (
   });
 }
 
+// int64 top-k rows -> int32: a valid index (0 <= v < num_kv) becomes its row
+// number, anything else -1, so an index at or past 2^31 can never alias a row.
+__global__ __launch_bounds__(256) void smla_idx64_kernel(const int64_t* __restrict__ in, int32_t* __restrict__ out,
+                                                         int64_t n, int64_t num_kv) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+    const int64_t v = in[i];
+    out[i] = (v >= 0 && v < num_kv) ? (int32_t)v : -1;
+  }
+}
+
 // Max and sum over the 64 lanes of a wave.
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll

@@ -2079,16 +2079,6 @@ bool single_pass16(int64_t T, int64_t H, int64_t topk, int dev) {
   return H <= 16 && !(cus > 0 && T < cus && topk >= 2 * kMinSplitLen);
 }
 
-// int64 top-k rows -> int32: a valid index (0 <= v < num_kv) becomes its row
-// number, anything else -1, so an index at or past 2^31 can never alias a row.
-__global__ __launch_bounds__(256) void smla_idx64_kernel(const int64_t* __restrict__ in, int32_t* __restrict__ out,
-                                                         int64_t n, int64_t num_kv) {
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
-    const int64_t v = in[i];
-    out[i] = (v >= 0 && v < num_kv) ? (int32_t)v : -1;
-  }
-}
 
 }  // namespace
 

@@ -606,9 +606,11 @@ hipError_t sort_pairs(void* tmp, size_t& bytes, const uint32_t* kin, uint32_t* k
 // passes are chosen so that T_pass * per-token bytes stays below it.
 constexpr size_t kBwdPassBytes = (size_t)4 << 30;
 
-int run_backward(const void* q, const void* kv, const void* dout, const void* o, const float* lse,
-                 const int32_t* topk_indices, const float* attn_sink, float scale, void* dq, void* dkv, float* d_sink,
-                 int64_t T, int64_t H, int64_t num_kv, int64_t topk, int64_t chunk_tokens, void* stream) {
+// Argument checks of the backward (no device access); idx_align: 4 for int32
+// rows, 8 for int64.
+int bwd_check(const void* q, const void* kv, const void* dout, const void* o, const float* lse,
+              const void* topk_indices, size_t idx_align, const float* attn_sink, float scale, void* dq, void* dkv,
+              float* d_sink, int64_t T, int64_t H, int64_t num_kv, int64_t topk, int64_t chunk_tokens) {
   if (T < 0 || H < 1 || num_kv < 0 || topk < 0 || chunk_tokens < 0) return SMLA_ERR_BAD_SIZE;
   if (H > kBwdMaxH || T > INT32_MAX || topk > INT32_MAX || num_kv >= ((int64_t)1 << 31)) return SMLA_ERR_BAD_SIZE;
   if (!isfinite(scale)) return SMLA_ERR_BAD_SCALE;
@@ -621,9 +623,19 @@ int run_backward(const void* q, const void* kv, const void* dout, const void* o,
   if (!aligned(q, 16) || !aligned(dout, 16) || !aligned(o, 16) || !aligned(dq, 16) || (kv && !aligned(kv, 16)) ||
       (dkv && !aligned(dkv, 16)))
     return SMLA_ERR_MISALIGNED;
-  if (!aligned(lse, 4) || (topk_indices && !aligned(topk_indices, 4)) || (attn_sink && !aligned(attn_sink, 4)) ||
+  if (!aligned(lse, 4) || (topk_indices && !aligned(topk_indices, idx_align)) || (attn_sink && !aligned(attn_sink, 4)) ||
       (d_sink && !aligned(d_sink, 4)))
     return SMLA_ERR_MISALIGNED;
+  return SMLA_OK;
+}
+
+int run_backward(const void* q, const void* kv, const void* dout, const void* o, const float* lse,
+                 const int32_t* topk_indices, const float* attn_sink, float scale, void* dq, void* dkv, float* d_sink,
+                 int64_t T, int64_t H, int64_t num_kv, int64_t topk, int64_t chunk_tokens, void* stream) {
+  const int rc0 = bwd_check(q, kv, dout, o, lse, topk_indices, 4, attn_sink, scale, dq, dkv, d_sink, T, H, num_kv,
+                            topk, chunk_tokens);
+  if (rc0 != SMLA_OK) return rc0;
+  const int64_t TP = (topk + kBK - 1) / kBK * kBK;
   int dev = 0;
   if (current_device(&dev) != SMLA_OK) return SMLA_ERR_NO_DEVICE;
   hipStream_t s = (hipStream_t)stream;
@@ -806,4 +818,37 @@ extern "C" int sparse_mla_backward_chunked(const void* q, const void* kv, const 
                                            int64_t num_kv, int64_t topk, int64_t chunk_tokens, void* stream) {
   return run_backward(q, kv, dout, o, lse, topk_indices, attn_sink, scale, dq, dkv, d_sink, T, H, num_kv, topk,
                       chunk_tokens, stream);
+}
+
+extern "C" int sparse_mla_backward_i64(const void* q, const void* kv, const void* dout, const void* o,
+                                       const float* lse, const int64_t* topk_indices, const float* attn_sink,
+                                       float scale, void* dq, void* dkv, float* d_sink, int64_t T, int64_t H,
+                                       int64_t num_kv, int64_t topk, int64_t chunk_tokens, void* stream) {
+  int rc = bwd_check(q, kv, dout, o, lse, topk_indices, 8, attn_sink, scale, dq, dkv, d_sink, T, H, num_kv, topk,
+                     chunk_tokens);
+  if (rc != SMLA_OK) return rc;
+  if (T == 0 || topk == 0)
+    return run_backward(q, kv, dout, o, lse, nullptr, attn_sink, scale, dq, dkv, d_sink, T, H, num_kv, topk,
+                        chunk_tokens, stream);
+  int dev = 0;
+  if (current_device(&dev) != SMLA_OK) return SMLA_ERR_NO_DEVICE;
+  hipStream_t s = (hipStream_t)stream;
+  // the rows as int32 row numbers (-1 where 0 <= v < num_kv fails in 64 bits), then the int32 backward
+  const int64_t n = T * topk;
+  void* ws = nullptr;
+  hipMemPool_t pool = scratch_pool(dev);
+  if (pool == nullptr || hipMallocFromPoolAsync(&ws, (size_t)n * sizeof(int32_t), pool, s) != hipSuccess ||
+      ws == nullptr) {
+    (void)hipGetLastError();
+    return SMLA_ERR_NO_MEMORY;
+  }
+  const int64_t want = (n + 255) / 256;
+  const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(smla_idx64_kernel, dim3(blocks), dim3(256), 0, s, topk_indices, (int32_t*)ws, n, num_kv);
+  rc = hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
+  if (rc == SMLA_OK)
+    rc = run_backward(q, kv, dout, o, lse, (const int32_t*)ws, attn_sink, scale, dq, dkv, d_sink, T, H, num_kv, topk,
+                      chunk_tokens, stream);
+  if (hipFreeAsync(ws, s) != hipSuccess && rc == SMLA_OK) rc = SMLA_ERR_LAUNCH;
+  return rc;
 }

@@ -181,6 +181,24 @@ def test_backward_chunked_argument_errors():
     assert lib.sparse_mla_backward_chunked(*bad, 2, None) == _lib.SMLA_ERR_MISALIGNED
 
 
+def test_backward_int64_argument_errors():
+    """The int64-row backward checks its arguments (int64 rows 8-byte aligned) before any device work."""
+    lib = _lib.load()
+    args = [0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, None, 0.0441, 0x7000, 0x8000, None, 4, 8, 16, 8, 0, None]
+    bad = list(args)
+    bad[5] = 0x6004  # 4-byte aligned only
+    assert lib.sparse_mla_backward_i64(*bad) == _lib.SMLA_ERR_MISALIGNED
+    bad = list(args)
+    bad[5] = None
+    assert lib.sparse_mla_backward_i64(*bad) == _lib.SMLA_ERR_NULL_POINTER
+    bad = list(args)
+    bad[12] = 129
+    assert lib.sparse_mla_backward_i64(*bad) == _lib.SMLA_ERR_BAD_SIZE
+    bad = list(args)
+    bad[15] = -1
+    assert lib.sparse_mla_backward_i64(*bad) == _lib.SMLA_ERR_BAD_SIZE
+
+
 def test_fp8_pool_decode_policy():
     """An fp8 call decodes its pool to a bf16 copy (by default) when it gathers at least 8x the pool's rows and
     the copy is at most 256 MiB; the mode switch returns the previous mode and refuses unknown values."""

@@ -57,11 +57,11 @@ def check_grad(got, ref, mag, what):
         assert np.all(g == 0), "%s: reference is zero, got nonzero" % what
 
 
-def run_backward(q, kv, dout, o_bits, lse, topk, sink, scale, chunk_tokens=None):
+def run_backward(q, kv, dout, o_bits, lse, topk, sink, scale, chunk_tokens=None, idx_dtype=np.int32):
     qd, dd, od = to_dev_bf16(q), to_dev_bf16(dout), to_dev_bf16(o_bits)
     kvd = to_dev_bf16(kv) if kv.shape[0] else torch.empty((0, 512), dtype=torch.bfloat16, device=DEV)
     ld = torch.from_numpy(np.ascontiguousarray(lse, dtype=np.float32)).to(DEV)
-    td = torch.from_numpy(np.ascontiguousarray(topk, dtype=np.int32)).to(DEV)
+    td = torch.from_numpy(np.ascontiguousarray(topk, dtype=idx_dtype)).to(DEV)
     sd = None if sink is None else torch.from_numpy(np.ascontiguousarray(sink, dtype=np.float32)).to(DEV)
     dq, dkv, ds = sparse_mla_backward(qd, kvd, dd, od, ld, td, sd, scale, chunk_tokens=chunk_tokens)
     torch.cuda.synchronize()
@@ -155,6 +155,26 @@ def test_backward_token_passes(T, H, topk, chunk, dup):
     dq1, dkv1, ds1 = run_backward(q, kv, dout, o_bits, lse, idx, s, synth.DEFAULT_SCALE)
     assert np.array_equal(dq, dq1), what + ": dq differs from the single pass"
     assert np.array_equal(ds, ds1), what + ": d_sink differs from the single pass"
+
+
+@pytest.mark.parametrize("H,chunk", [(16, None), (128, None), (16, 24)])
+def test_backward_int64_rows_bitwise(H, chunk):
+    """int64 rows, some of them 2^32 + r (which an int32 cast would turn into row r), 2^31 or large negatives: the
+    gradients equal the int32 backward's on the equivalent rows (invalid -> -1) bit for bit, in one pass or several."""
+    q, kv, idx, s = random_case(21 + H, T=64, H=H, topk=96, num_kv=300)
+    rng = np.random.default_rng(22 + H)
+    i64 = np.asarray(idx).astype(np.int64)
+    wrap = (rng.random(i64.shape) < 0.2) & (i64 >= 0)
+    i64[wrap] += 2**32
+    i64[:, 0] = 2**31
+    i64[:, 1] = -(2**40)
+    i32 = np.where((i64 >= 0) & (i64 < 300), i64, -1).astype(np.int32)
+    dout = bf16(rng.standard_normal(q.shape))
+    o_bits, lse = run_gpu(q, kv, i32, s, synth.DEFAULT_SCALE)
+    a = run_backward(q, kv, dout, o_bits, lse, i32, s, synth.DEFAULT_SCALE, chunk)
+    b = run_backward(q, kv, dout, o_bits, lse, i64, s, synth.DEFAULT_SCALE, chunk, idx_dtype=np.int64)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
 
 
 def test_backward_is_deterministic():
