@@ -69,7 +69,8 @@ def _load():
         ]
         lib.smla_oracle_backward.restype = ctypes.c_int
         lib.smla_oracle_backward.argtypes = [
-            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
@@ -134,10 +135,11 @@ def _bf16_to_f64(bits):
 
 
 def backward(q, kv, dout, o, lse, topk, sink, scale, tokens=None, rows=None, *, want_dq=True, want_dkv=True,
-             want_mag=False, threads=0):
+             want_mag=False, threads=0, kv_scale=None):
     """Gradients of the forward, written out from its definition.
 
-    q, dout: uint16 bf16 bits [T, H, 512]; kv: uint16 bf16 bits [num_kv, 512];
+    q, dout: uint16 bf16 bits [T, H, 512]; kv: uint16 bf16 bits [num_kv, 512], or
+    uint8 OCP FP8 E4M3 codes [num_kv, 512] with ``kv_scale`` (kv == code * kv_scale);
     o: the forward's output, uint16 bf16 bits or float64 [T, H, 512]; lse: float32
     or float64 [T, H] (sink-inclusive, natural log); topk: int32 [T, topk];
     sink: float32 [H] or None; scale: float. ``tokens`` selects the tokens whose
@@ -149,7 +151,8 @@ def backward(q, kv, dout, o, lse, topk, sink, scale, tokens=None, rows=None, *, 
     """
     q = np.ascontiguousarray(q, dtype=np.uint16)
     dout = np.ascontiguousarray(dout, dtype=np.uint16)
-    kv = np.ascontiguousarray(kv, dtype=np.uint16)
+    kv_fp8 = kv_scale is not None
+    kv = np.ascontiguousarray(kv, dtype=np.uint8 if kv_fp8 else np.uint16)
     o = np.asarray(o)
     o = _bf16_to_f64(o) if o.dtype == np.uint16 else np.ascontiguousarray(o, dtype=np.float64)
     lse = np.ascontiguousarray(lse, dtype=np.float64)
@@ -172,7 +175,8 @@ def backward(q, kv, dout, o, lse, topk, sink, scale, tokens=None, rows=None, *, 
     dkvm = np.empty_like(dkv) if (want_mag and dkv is not None) else None
     dsm = np.empty((H,), np.float64) if want_mag else None
     rc = _load().smla_oracle_backward(
-        _ptr(q), _ptr(kv) if num_kv > 0 else None, _ptr(dout), _ptr(o), _ptr(lse), _ptr(topk), _ptr(sink),
+        _ptr(q), _ptr(kv) if num_kv > 0 else None, int(kv_fp8), float(kv_scale) if kv_fp8 else 1.0, _ptr(dout),
+        _ptr(o), _ptr(lse), _ptr(topk), _ptr(sink),
         float(scale), T, H, num_kv, topk.shape[1], _ptr(tok), n_tok, _ptr(dq), _ptr(rws), rws.size, _ptr(dkv),
         _ptr(ds), _ptr(dqm), _ptr(dkvm), _ptr(dsm), int(threads))
     if rc != 0:

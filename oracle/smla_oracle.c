@@ -92,6 +92,12 @@ static double kv_at(const void* kv, int kv_fp8, double kv_scale, int64_t r, int 
   return bf16_to_double(((const uint16_t*)kv)[r * SMLA_ORACLE_D + d]);
 }
 
+/* The same element for the backward oracle beside this file (one decoding of
+ * the pool for both directions). */
+double smla_oracle_kv_value(const void* kv, int kv_fp8, double kv_scale, int64_t r, int d) {
+  return kv_at(kv, kv_fp8, kv_scale, r, d);
+}
+
 /* Index s of a top-k row of 4- or 8-byte signed integers. */
 static int64_t idx_at(const void* row, int idx64, int64_t s) {
   return idx64 ? ((const int64_t*)row)[s] : (int64_t)((const int32_t*)row)[s];

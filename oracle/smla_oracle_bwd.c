@@ -34,6 +34,11 @@
  * Precision: bf16 inputs widened exactly; o and lse taken as double; every
  * sum in double, in index order.
  *
+ * The pool may also hold OCP FP8 E4M3 codes with one dequant scale: every
+ * kv element above is then code value * kv_scale, decoded as the forward
+ * oracle decodes it (smla_oracle_kv_value), and dkv is the gradient with
+ * respect to those values.
+ *
  * dq is evaluated per (t, h) for a list of tokens; dkv for a list of rows,
  * each row scanning every (t, s) for the slots that hold it (plain, and
  * independent of how any index is built); d_sink over all tokens.
@@ -62,12 +67,23 @@ static double bw_bf16(uint16_t b) {
 
 static int bw_valid(int32_t r, int64_t num_kv) { return r >= 0 && (int64_t)r < num_kv; }
 
+/* element d of pool row r (bf16 bits, or an fp8 code times kv_scale): smla_oracle.c */
+double smla_oracle_kv_value(const void* kv, int kv_fp8, double kv_scale, int64_t r, int d);
+
+typedef struct {
+  const void* kv;
+  int fp8;
+  double scale;
+} BwPool;
+
+static double bw_kv(const BwPool* pool, int64_t r, int d) { return smla_oracle_kv_value(pool->kv, pool->fp8, pool->scale, r, d); }
+
 /* scale * q[t,h] . kv[r] and dO[t,h] . kv[r] */
-static void bw_dots(const uint16_t* qrow, const uint16_t* dorow, const uint16_t* kvrow, double scale, double* x,
-                    double* dp) {
+static void bw_dots(const uint16_t* qrow, const uint16_t* dorow, const BwPool* pool, int64_t r, double scale,
+                    double* x, double* dp) {
   double a = 0.0, b = 0.0;
   for (int d = 0; d < BWD_D; ++d) {
-    const double k = bw_bf16(kvrow[d]);
+    const double k = bw_kv(pool, r, d);
     a += bw_bf16(qrow[d]) * k;
     b += bw_bf16(dorow[d]) * k;
   }
@@ -76,19 +92,22 @@ static void bw_dots(const uint16_t* qrow, const uint16_t* dorow, const uint16_t*
 }
 
 /*
- * q, dout bf16 bits [T, H, 512]; kv bf16 bits [num_kv, 512]; o, lse double
+ * q, dout bf16 bits [T, H, 512]; kv bf16 bits [num_kv, 512] (kv_fp8 == 0) or
+ * OCP FP8 E4M3 codes [num_kv, 512] with kv_scale (kv_fp8 != 0); o, lse double
  * [T, H, 512] / [T, H]; topk int32 [T, topk_n]; sink fp32 [H] or NULL.
  * tokens int64 [n_tokens] (NULL: all T, then n_tokens must be T) -> dq double
  * [n_tokens, H, 512] (NULL: skipped). rows int64 [n_rows] -> dkv double
  * [n_rows, 512] (NULL: skipped). d_sink double [H] (NULL: skipped; zeros
  * without a sink). Returns 0, -1 on a bad argument, -2 out of memory.
  */
-int smla_oracle_backward(const uint16_t* q, const uint16_t* kv, const uint16_t* dout, const double* o,
+int smla_oracle_backward(const uint16_t* q, const void* kv, int kv_fp8, double kv_scale, const uint16_t* dout,
+                         const double* o,
                          const double* lse, const int32_t* topk, const float* sink, double scale, int64_t T, int64_t H,
                          int64_t num_kv, int64_t topk_n, const int64_t* tokens, int64_t n_tokens, double* dq,
                          const int64_t* rows, int64_t n_rows, double* dkv, double* d_sink, double* dq_mag,
                          double* dkv_mag, double* dsink_mag, int nthreads) {
   const int D = BWD_D;
+  const BwPool pool = {kv, kv_fp8, kv_scale};
   if (T < 0 || H < 1 || num_kv < 0 || topk_n < 0 || n_tokens < 0 || n_rows < 0) return -1;
   if (T > 0 && (!q || !dout || !o || !lse || (topk_n > 0 && !topk))) return -1;
   if (!tokens && dq && n_tokens != T) return -1;
@@ -129,14 +148,13 @@ int smla_oracle_backward(const uint16_t* q, const uint16_t* kv, const uint16_t* 
         for (int64_t s = 0; s < topk_n; ++s) {
           const int32_t r = topk[t * topk_n + s];
           if (!bw_valid(r, num_kv)) continue;
-          const uint16_t* kvrow = kv + (int64_t)r * D;
           double x, dp;
-          bw_dots(qrow, dorow, kvrow, scale, &x, &dp);
+          bw_dots(qrow, dorow, &pool, r, scale, &x, &dp);
           const double p = exp(x - lse[t * H + h]);
           const double ds = p * (dp - delta[t * H + h]);
-          for (int d = 0; d < D; ++d) g[d] += scale * ds * bw_bf16(kvrow[d]);
+          for (int d = 0; d < D; ++d) g[d] += scale * ds * bw_kv(&pool, r, d);
           if (gm)
-            for (int d = 0; d < D; ++d) gm[d] += fabs(scale * ds * bw_bf16(kvrow[d]));
+            for (int d = 0; d < D; ++d) gm[d] += fabs(scale * ds * bw_kv(&pool, r, d));
         }
       }
     }
@@ -152,7 +170,6 @@ int smla_oracle_backward(const uint16_t* q, const uint16_t* kv, const uint16_t* 
       for (int d = 0; d < D; ++d) g[d] = 0.0;
       if (gm)
         for (int d = 0; d < D; ++d) gm[d] = 0.0;
-      const uint16_t* kvrow = kv + r * D;
       for (int64_t t = 0; t < T; ++t) {
         for (int64_t s = 0; s < topk_n; ++s) {
           if ((int64_t)topk[t * topk_n + s] != r) continue;
@@ -160,7 +177,7 @@ int smla_oracle_backward(const uint16_t* q, const uint16_t* kv, const uint16_t* 
             const uint16_t* qrow = q + (t * H + h) * D;
             const uint16_t* dorow = dout + (t * H + h) * D;
             double x, dp;
-            bw_dots(qrow, dorow, kvrow, scale, &x, &dp);
+            bw_dots(qrow, dorow, &pool, r, scale, &x, &dp);
             const double p = exp(x - lse[t * H + h]);
             const double ds = p * (dp - delta[t * H + h]);
             for (int d = 0; d < D; ++d) g[d] += scale * ds * bw_bf16(qrow[d]) + p * bw_bf16(dorow[d]);

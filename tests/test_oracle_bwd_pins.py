@@ -183,3 +183,23 @@ def test_selected_tokens_and_rows_match_full_evaluation():
     part = oracle.backward(q, kv, dout, f["o"], f["lse"], idx, s, 0.2, tokens=[5, 1], rows=[29, 3, 0])
     assert np.array_equal(part["dq"], full["dq"][[5, 1]])
     assert np.array_equal(part["dkv"], full["dkv"][[29, 3, 0]])
+
+
+@pytest.mark.parametrize("seed", [41, 42])
+def test_fp8_pool_equals_bf16_pool_of_the_same_values(seed):
+    """An fp8 pool with a power-of-two dequant scale holds values that bf16 represents exactly (an E4M3 code value
+    has at most four significant bits): the fp8 form must give, bit for bit, the bf16 form's gradients on the pool of
+    those values (decoded here by torch's float8_e4m3fn, to which the forward oracle's decoding is pinned)."""
+    rng = np.random.default_rng(seed)
+    q, _, dout, idx, s = case(seed, T=4, H=3, num_kv=20, topk=9)
+    codes = rng.integers(0, 256, (20, D)).astype(np.uint8)
+    codes = np.where((codes & 0x7F) == 0x7F, 0x3C, codes)  # no NaN codes
+    kv_scale = 2.0 ** -4
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32).numpy() * np.float32(kv_scale)
+    kv_bf16 = bf16(vals)
+    assert np.array_equal(f64(kv_bf16), vals.astype(np.float64))  # exact in bf16
+    fwd = oracle.forward(q, kv_bf16, idx, s, synth.DEFAULT_SCALE, want_bf16=False)
+    a = oracle.backward(q, kv_bf16, dout, fwd["o"], fwd["lse"], idx, s, synth.DEFAULT_SCALE)
+    b = oracle.backward(q, codes, dout, fwd["o"], fwd["lse"], idx, s, synth.DEFAULT_SCALE, kv_scale=kv_scale)
+    for k in ("dq", "dkv", "d_sink"):
+        assert np.array_equal(a[k], b[k]), k
