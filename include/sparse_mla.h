@@ -260,6 +260,23 @@ int sparse_mla_backward_i64(const void* q, const void* kv, const void* dout, con
                             float* d_sink, int64_t T, int64_t H, int64_t num_kv, int64_t topk, int64_t chunk_tokens,
                             void* stream);
 
+/*
+ * sparse_mla_backward_fp8 -- sparse_mla_backward_chunked on a pool of OCP FP8
+ * E4M3 codes (kv: uint8 [num_kv, 512], 16-byte aligned) with one fp32 dequant
+ * scale: K == V == code value * kv_scale, as in sparse_mla_prefill_fp8, and
+ * dkv (bf16 [num_kv, 512]) is the gradient with respect to those values. The
+ * pool is first decoded into bf16 copies of its code values (exact) in
+ * stream-ordered scratch of num_kv KiB from the library's per-device pool;
+ * the backward then folds kv_scale into the logits, dP = dout . kv and dq.
+ * SMLA_ERR_BAD_SCALE if kv_scale or scale * kv_scale is not finite. Argument
+ * errors return before anything is enqueued; SMLA_ERR_NO_MEMORY may also come
+ * after the decoding (the backward's own scratch), with no output written.
+ */
+int sparse_mla_backward_fp8(const void* q, const void* kv, float kv_scale, const void* dout, const void* o,
+                            const float* lse, const int32_t* topk_indices, const float* attn_sink, float scale,
+                            void* dq, void* dkv, float* d_sink, int64_t T, int64_t H, int64_t num_kv, int64_t topk,
+                            int64_t chunk_tokens, void* stream);
+
 /* Human-readable text for a status code (static storage; never NULL). */
 const char* sparse_mla_status_string(int status);
 

@@ -95,11 +95,13 @@ def sparse_mla_prefill(q, kv, topk_indices, attn_sink=None, scale=None, out=None
     return out, lse
 
 
-def sparse_mla_backward(q, kv, dout, o, lse, topk_indices, attn_sink=None, scale=None, chunk_tokens=None):
+def sparse_mla_backward(q, kv, dout, o, lse, topk_indices, attn_sink=None, scale=None, chunk_tokens=None,
+                        kv_scale=None):
     """Gradients of ``sparse_mla_prefill``; returns ``(dq, dkv, d_sink)``.
 
     q, dout, o: bf16 [T, H, 512] (o and lse are the forward's outputs, lse
-    sink-inclusive fp32 [T, H]); kv: bf16 [num_kv, 512]; topk_indices: int32
+    sink-inclusive fp32 [T, H]); kv: bf16 [num_kv, 512], or float8_e4m3fn codes
+    with ``kv_scale`` (K == V == code * kv_scale; int32 rows); topk_indices: int32
     or int64 [T, topk]; attn_sink: fp32 [H] or None (then d_sink is None); scale: float
     (default 1/sqrt(512)). H <= 128. dq and dkv come back bf16, d_sink fp32.
     chunk_tokens: tokens per pass (None: passes chosen so that one pass's
@@ -116,7 +118,9 @@ def sparse_mla_backward(q, kv, dout, o, lse, topk_indices, attn_sink=None, scale
     for name, x in (("dout", dout), ("o", o)):
         _check(x.device == dev and x.dtype == torch.bfloat16 and x.shape == q.shape,
                "%s must be bfloat16 %s on %s" % (name, tuple(q.shape), dev))
-    _check(kv.device == dev and kv.dtype == torch.bfloat16, "kv must be bfloat16 on %s" % dev)
+    fp8 = kv.dtype == torch.float8_e4m3fn
+    _check(kv.device == dev and (kv.dtype == torch.bfloat16 or fp8), "kv must be bfloat16 or float8_e4m3fn on %s" % dev)
+    _check(fp8 == (kv_scale is not None), "kv_scale goes with a float8_e4m3fn pool (and only with one)")
     _check(kv.dim() == 2 and kv.shape[1] == HEAD_DIM, "kv must be [num_kv, 512], got %s" % (tuple(kv.shape),))
     _check(lse.device == dev and lse.dtype == torch.float32 and tuple(lse.shape) == (T, H),
            "lse must be float32 [T, H] on q's device")
@@ -134,19 +138,24 @@ def sparse_mla_backward(q, kv, dout, o, lse, topk_indices, attn_sink=None, scale
         scale = DEFAULT_SCALE
     _check(chunk_tokens is None or int(chunk_tokens) >= 1, "chunk_tokens must be >= 1 (or None)")
     dq = torch.empty_like(q)
-    dkv = torch.empty_like(kv)
+    dkv = torch.empty(kv.shape, dtype=torch.bfloat16, device=dev)
     d_sink = torch.empty((H,), dtype=torch.float32, device=dev) if attn_sink is not None else None
     lib = _lib.load()
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        entry = lib.sparse_mla_backward_i64 if topk_indices.dtype == torch.int64 else lib.sparse_mla_backward_chunked
-        rc = entry(
-            q.data_ptr(), kv.data_ptr() if kv.numel() else None, dout.data_ptr(), o.data_ptr(), lse.data_ptr(),
-            topk_indices.data_ptr() if topk_indices.numel() else None,
-            attn_sink.data_ptr() if attn_sink is not None else None, float(scale),
-            dq.data_ptr(), dkv.data_ptr() if dkv.numel() else None,
-            d_sink.data_ptr() if d_sink is not None else None, T, H, kv.shape[0], topk_indices.shape[1],
-            int(chunk_tokens or 0), stream)
+        kvp = kv.data_ptr() if kv.numel() else None
+        rest = (dout.data_ptr(), o.data_ptr(), lse.data_ptr(), topk_indices.data_ptr() if topk_indices.numel() else None,
+                attn_sink.data_ptr() if attn_sink is not None else None, float(scale),
+                dq.data_ptr(), dkv.data_ptr() if dkv.numel() else None,
+                d_sink.data_ptr() if d_sink is not None else None, T, H, kv.shape[0], topk_indices.shape[1],
+                int(chunk_tokens or 0), stream)
+        if fp8:
+            _check(topk_indices.dtype == torch.int32, "an fp8 pool takes int32 top-k rows in the backward")
+            rc = lib.sparse_mla_backward_fp8(q.data_ptr(), kvp, float(kv_scale), *rest)
+        elif topk_indices.dtype == torch.int64:
+            rc = lib.sparse_mla_backward_i64(q.data_ptr(), kvp, *rest)
+        else:
+            rc = lib.sparse_mla_backward_chunked(q.data_ptr(), kvp, *rest)
     if rc != 0:
         raise RuntimeError("sparse_mla_backward failed: %s (status %d)" % (_lib.status_string(rc), rc))
     return dq, dkv, d_sink

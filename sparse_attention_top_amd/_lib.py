@@ -60,6 +60,15 @@ SIGNATURES = {
         ctypes.c_int64,  # chunk_tokens
         ctypes.c_void_p,  # stream
     ]),
+    "sparse_mla_backward_fp8": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,  # q, kv (fp8 codes), kv_scale
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,  # dout, o, lse
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,  # topk, sink, scale
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,  # dq, dkv, d_sink
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,  # T, H, num_kv, topk
+        ctypes.c_int64,  # chunk_tokens
+        ctypes.c_void_p,  # stream
+    ]),
     "sparse_mla_set_fp8_pool_decode": (ctypes.c_int, [ctypes.c_int]),
     "sparse_mla_fp8_pool_decoded": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]),
     "sparse_mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),

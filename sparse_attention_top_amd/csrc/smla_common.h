@@ -535,6 +535,50 @@ __device__ __forceinline__ void tile_pv(uint32_t vrow, const bf16x8& pk, f32x4 (
   });
 }
 
+// Two OCP FP8 E4M3 codes (bytes 2 HI .. 2 HI + 1 of x) -> two bf16 (exact:
+// every code is a bf16 value; the two NaN codes stay NaN). gfx950's packed
+// scaled conversion with scale 1, issued as asm: the compiler's lowering of its
+// builtin keeps only the first element of the pair.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16(uint32_t x) {
+  uint32_t r;
+  if constexpr (HI) asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0 op_sel:[1,0,0]" : "=v"(r) : "v"(x));
+  else asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0" : "=v"(r) : "v"(x));
+  return r;
+}
+// Eight codes (little-endian bytes of v) -> eight bf16 in the same order.
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(const u32x2& v) {
+  return u32x4{fp8x2_to_bf16<false>(v[0]), fp8x2_to_bf16<true>(v[0]), fp8x2_to_bf16<false>(v[1]),
+               fp8x2_to_bf16<true>(v[1])};
+}
+
+// The conversions and MFMAs here are inline asm, so the compiler inserts none
+// of the wait states between an asm VALU write of a VGPR and its reader (an
+// MFMA source needs two on CDNA3/4; four are given). Taking the converted
+// values as in/out operands pins the conversion above the nops and the reader
+// below them.
+__device__ __forceinline__ void valu_to_mfma(u32x4& a, u32x4& b) {
+  asm volatile("s_nop 3" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void valu_to_mfma(u32x4& a) { asm volatile("s_nop 3" : "+v"(a)); }
+
+// An OCP FP8 E4M3 pool -> bf16 copies of its code values, 16 codes per thread
+// per step (exact: every code value is a bf16 value; the two NaN codes stay
+// NaN). The dequant scale is not applied here: the kernels fold it into the
+// logit scale and the output scale, as the fp8 kernels do.
+__global__ __launch_bounds__(256) void smla_fp8_pool_decode_kernel(const uint8_t* __restrict__ codes,
+                                                                   uint16_t* __restrict__ out, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256) {
+    const u32x4 c = __builtin_nontemporal_load((const u32x4*)codes + i);
+    u32x4 lo = fp8x8_to_bf16(u32x2{c[0], c[1]});
+    u32x4 hi = fp8x8_to_bf16(u32x2{c[2], c[3]});
+    valu_to_mfma(lo, hi);  // the asm conversions' results are read by the stores below
+    u32x4* d = (u32x4*)out + 2 * i;
+    d[0] = lo;
+    d[1] = hi;
+  }
+}
+
 // int64 top-k rows -> int32: a valid index (0 <= v < num_kv) becomes its row
 // number, anything else -1, so an index at or past 2^31 can never alias a row.
 __global__ __launch_bounds__(256) void smla_idx64_kernel(const int64_t* __restrict__ in, int32_t* __restrict__ out,

@@ -172,32 +172,6 @@ struct TileIssue8 {
   }
 };
 
-// Two OCP FP8 E4M3 codes (bytes 2 HI .. 2 HI + 1 of x) -> two bf16 (exact:
-// every code is a bf16 value; the two NaN codes stay NaN). gfx950's packed
-// scaled conversion with scale 1, issued as asm: the compiler's lowering of its
-// builtin keeps only the first element of the pair.
-template <bool HI>
-__device__ __forceinline__ uint32_t fp8x2_to_bf16(uint32_t x) {
-  uint32_t r;
-  if constexpr (HI) asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0 op_sel:[1,0,0]" : "=v"(r) : "v"(x));
-  else asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0" : "=v"(r) : "v"(x));
-  return r;
-}
-// Eight codes (little-endian bytes of v) -> eight bf16 in the same order.
-__device__ __forceinline__ u32x4 fp8x8_to_bf16(const u32x2& v) {
-  return u32x4{fp8x2_to_bf16<false>(v[0]), fp8x2_to_bf16<true>(v[0]), fp8x2_to_bf16<false>(v[1]),
-               fp8x2_to_bf16<true>(v[1])};
-}
-
-// The conversions and MFMAs here are inline asm, so the compiler inserts none
-// of the wait states between an asm VALU write of a VGPR and its reader (an
-// MFMA source needs two on CDNA3/4; four are given). Taking the converted
-// values as in/out operands pins the conversion above the nops and the reader
-// below them.
-__device__ __forceinline__ void valu_to_mfma(u32x4& a, u32x4& b) {
-  asm volatile("s_nop 3" : "+v"(a), "+v"(b));
-}
-__device__ __forceinline__ void valu_to_mfma(u32x4& a) { asm volatile("s_nop 3" : "+v"(a)); }
 
 // S^T = K Q^T from an fp8 tile: the K fragment of half sh and k-step k
 // (lane: row 16 sh + li, d = 32k + 8g .. +8) is 8 bytes at kaddr + 1024 k + 256 sh,
@@ -2054,22 +2028,6 @@ int run_prefill(const void* q, const void* kv, const int32_t* topk_indices, cons
   return err == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
 }
 
-// An OCP FP8 E4M3 pool -> bf16 copies of its code values, 16 codes per thread
-// per step (exact: every code value is a bf16 value; the two NaN codes stay
-// NaN). The dequant scale is not applied here: the kernels fold it into the
-// logit scale and the output scale, as the fp8 kernels do.
-__global__ __launch_bounds__(256) void smla_fp8_pool_decode_kernel(const uint8_t* __restrict__ codes,
-                                                                   uint16_t* __restrict__ out, int64_t n16) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256) {
-    const u32x4 c = __builtin_nontemporal_load((const u32x4*)codes + i);
-    u32x4 lo = fp8x8_to_bf16(u32x2{c[0], c[1]});
-    u32x4 hi = fp8x8_to_bf16(u32x2{c[2], c[3]});
-    valu_to_mfma(lo, hi);  // the asm conversions' results are read by the stores below
-    u32x4* d = (u32x4*)out + 2 * i;
-    d[0] = lo;
-    d[1] = hi;
-  }
-}
 
 // Whether a bf16 call runs the single-pass 16-row kernel: H <= 16 and either
 // as many tokens as compute units or rows too short to split (the split

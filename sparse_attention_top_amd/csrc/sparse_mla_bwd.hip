@@ -61,8 +61,10 @@ struct BwdParams {
   int head_groups;
   uint32_t nkv;      // slot valid iff (uint32)idx < nkv
   uint32_t sentinel;  // row key of unused positions (== nkv)
-  float scale;
-  float scale_log2;
+  float scale;       // for scale dS (the dkv term scale dS q)
+  float scale_log2;  // logits: scale * kv_scale * log2(e)
+  float kv_scale;    // 1, or the dequant scale of a pool of fp8 code values (dP = kv_scale dO . code)
+  float dq_scale;    // scale * kv_scale
 };
 
 template <int NW, int NBUF>
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
         for (int i = 0; i < 4; ++i) {
           const int slot = sh * 16 + 4 * g + i;
           const float pr = slot < cnt ? __builtin_amdgcn_exp2f(s[sh][i] * p.scale_log2 - lse_l2) : 0.f;
-          const float ds = pr * (dp[sh][i] - delta);
+          const float ds = pr * (dp[sh][i] * p.kv_scale - delta);
           pk[sh * 4 + i] = (__bf16)ds;
           pst[sh][i] = (__bf16)pr;
           dst[sh][i] = (__bf16)(ds * p.scale);
@@ -248,7 +250,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
   mfma_agpr_drain(acc);
 #pragma unroll
   for (int dt = 0; dt < 32; ++dt) {
-    const f32x4 v = acc[dt] * p.scale;
+    const f32x4 v = acc[dt] * p.dq_scale;
     const bf16x4 v4 = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
     *(LDS_AS bf16x4*)(uintptr_t)(ob + li * kRowStride + 32 * dt + 8 * g) = v4;
   }
@@ -631,7 +633,8 @@ int bwd_check(const void* q, const void* kv, const void* dout, const void* o, co
 
 int run_backward(const void* q, const void* kv, const void* dout, const void* o, const float* lse,
                  const int32_t* topk_indices, const float* attn_sink, float scale, void* dq, void* dkv, float* d_sink,
-                 int64_t T, int64_t H, int64_t num_kv, int64_t topk, int64_t chunk_tokens, void* stream) {
+                 int64_t T, int64_t H, int64_t num_kv, int64_t topk, int64_t chunk_tokens, void* stream,
+                 float kv_scale = 1.f) {
   const int rc0 = bwd_check(q, kv, dout, o, lse, topk_indices, 4, attn_sink, scale, dq, dkv, d_sink, T, H, num_kv,
                             topk, chunk_tokens);
   if (rc0 != SMLA_OK) return rc0;
@@ -736,7 +739,9 @@ int run_backward(const void* q, const void* kv, const void* dout, const void* o,
     bp.nkv = nkv;
     bp.sentinel = nkv;
     bp.scale = scale;
-    bp.scale_log2 = scale * kLog2e;
+    bp.scale_log2 = scale * kv_scale * kLog2e;
+    bp.kv_scale = kv_scale;
+    bp.dq_scale = scale * kv_scale;
 
     const unsigned g1 = (unsigned)(Tc * head_groups);
     if (nw == 1) hipLaunchKernelGGL((smla_bwd_dq_kernel<1, 2>), dim3(g1), dim3(64), 0, s, bp);
@@ -849,6 +854,42 @@ extern "C" int sparse_mla_backward_i64(const void* q, const void* kv, const void
   if (rc == SMLA_OK)
     rc = run_backward(q, kv, dout, o, lse, (const int32_t*)ws, attn_sink, scale, dq, dkv, d_sink, T, H, num_kv, topk,
                       chunk_tokens, stream);
+  if (hipFreeAsync(ws, s) != hipSuccess && rc == SMLA_OK) rc = SMLA_ERR_LAUNCH;
+  return rc;
+}
+
+extern "C" int sparse_mla_backward_fp8(const void* q, const void* kv, float kv_scale, const void* dout, const void* o,
+                                       const float* lse, const int32_t* topk_indices, const float* attn_sink,
+                                       float scale, void* dq, void* dkv, float* d_sink, int64_t T, int64_t H,
+                                       int64_t num_kv, int64_t topk, int64_t chunk_tokens, void* stream) {
+  int rc = bwd_check(q, kv, dout, o, lse, topk_indices, 4, attn_sink, scale, dq, dkv, d_sink, T, H, num_kv, topk,
+                     chunk_tokens);
+  if (rc != SMLA_OK) return rc;
+  if (!isfinite(kv_scale) || !isfinite(scale * kv_scale)) return SMLA_ERR_BAD_SCALE;
+  if (T == 0 || topk == 0 || num_kv == 0)  // no pool row is read
+    return run_backward(q, kv, dout, o, lse, topk_indices, attn_sink, scale, dq, dkv, d_sink, T, H, num_kv, topk,
+                        chunk_tokens, stream, kv_scale);
+  int dev = 0;
+  if (current_device(&dev) != SMLA_OK) return SMLA_ERR_NO_DEVICE;
+  hipStream_t s = (hipStream_t)stream;
+  // the pool as bf16 copies of its code values (exact), then the bf16 backward
+  // with the dequant scale in the logits, dP and dq
+  void* ws = nullptr;
+  hipMemPool_t pool = scratch_pool(dev);
+  if (pool == nullptr || hipMallocFromPoolAsync(&ws, (size_t)num_kv * kRowBytes, pool, s) != hipSuccess ||
+      ws == nullptr) {
+    (void)hipGetLastError();
+    return SMLA_ERR_NO_MEMORY;
+  }
+  const int64_t n16 = num_kv * (kD / 16);
+  const int64_t want = (n16 + 255) / 256;
+  const unsigned blocks = (unsigned)(want < 8192 ? want : 8192);
+  hipLaunchKernelGGL(smla_fp8_pool_decode_kernel, dim3(blocks), dim3(256), 0, s, (const uint8_t*)kv, (uint16_t*)ws,
+                     n16);
+  rc = hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
+  if (rc == SMLA_OK)
+    rc = run_backward(q, ws, dout, o, lse, topk_indices, attn_sink, scale, dq, dkv, d_sink, T, H, num_kv, topk,
+                      chunk_tokens, stream, kv_scale);
   if (hipFreeAsync(ws, s) != hipSuccess && rc == SMLA_OK) rc = SMLA_ERR_LAUNCH;
   return rc;
 }

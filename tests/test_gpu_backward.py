@@ -57,27 +57,31 @@ def check_grad(got, ref, mag, what):
         assert np.all(g == 0), "%s: reference is zero, got nonzero" % what
 
 
-def run_backward(q, kv, dout, o_bits, lse, topk, sink, scale, chunk_tokens=None, idx_dtype=np.int32):
+def run_backward(q, kv, dout, o_bits, lse, topk, sink, scale, chunk_tokens=None, idx_dtype=np.int32, kv_scale=None):
     qd, dd, od = to_dev_bf16(q), to_dev_bf16(dout), to_dev_bf16(o_bits)
-    kvd = to_dev_bf16(kv) if kv.shape[0] else torch.empty((0, 512), dtype=torch.bfloat16, device=DEV)
+    if kv_scale is not None:  # OCP FP8 E4M3 codes
+        kvd = torch.from_numpy(np.ascontiguousarray(kv, dtype=np.uint8)).to(DEV).view(torch.float8_e4m3fn)
+    else:
+        kvd = to_dev_bf16(kv) if kv.shape[0] else torch.empty((0, 512), dtype=torch.bfloat16, device=DEV)
     ld = torch.from_numpy(np.ascontiguousarray(lse, dtype=np.float32)).to(DEV)
     td = torch.from_numpy(np.ascontiguousarray(topk, dtype=idx_dtype)).to(DEV)
     sd = None if sink is None else torch.from_numpy(np.ascontiguousarray(sink, dtype=np.float32)).to(DEV)
-    dq, dkv, ds = sparse_mla_backward(qd, kvd, dd, od, ld, td, sd, scale, chunk_tokens=chunk_tokens)
+    dq, dkv, ds = sparse_mla_backward(qd, kvd, dd, od, ld, td, sd, scale, chunk_tokens=chunk_tokens, kv_scale=kv_scale)
     torch.cuda.synchronize()
     return (f64(bf16_bits(dq)), f64(bf16_bits(dkv)) if kv.shape[0] else np.zeros((0, 512)),
             None if ds is None else ds.cpu().numpy().astype(np.float64))
 
 
-def full_case(q, kv, topk, sink, scale, seed, what, tokens=None, rows=None, chunk_tokens=None):
+def full_case(q, kv, topk, sink, scale, seed, what, tokens=None, rows=None, chunk_tokens=None, kv_scale=None):
     """GPU forward, then GPU backward and oracle backward on the same inputs; compare."""
     print("backward case %s: T=%d H=%d topk=%d num_kv=%d sink=%s" % (
         what, q.shape[0], q.shape[1], topk.shape[1], kv.shape[0], sink is not None), flush=True)
     rng = np.random.default_rng(seed)
     dout = bf16(rng.standard_normal(q.shape))
-    o_bits, lse = run_gpu(q, kv, topk, sink, scale)
-    dq, dkv, ds = run_backward(q, kv, dout, o_bits, lse, topk, sink, scale, chunk_tokens)
-    ref = oracle.backward(q, kv, dout, o_bits, lse, topk, sink, scale, tokens=tokens, rows=rows, want_mag=True)
+    o_bits, lse = run_gpu(q, kv, topk, sink, scale, kv_scale=kv_scale)
+    dq, dkv, ds = run_backward(q, kv, dout, o_bits, lse, topk, sink, scale, chunk_tokens, kv_scale=kv_scale)
+    ref = oracle.backward(q, kv, dout, o_bits, lse, topk, sink, scale, tokens=tokens, rows=rows, want_mag=True,
+                          kv_scale=kv_scale)
     check_grad(dq if tokens is None else dq[tokens], ref["dq"], ref["dq_mag"], what + " dq")
     check_grad(dkv if rows is None else dkv[rows], ref["dkv"], ref["dkv_mag"], what + " dkv")
     if sink is not None:
@@ -111,6 +115,18 @@ def test_backward_tiny_config():
 def test_backward_random(H, topk, sink, dup):
     q, kv, idx, s = random_case(H * 7 + topk, T=40, H=H, topk=topk, num_kv=300, sink=sink, dup=dup)
     full_case(q, kv, idx, s, synth.DEFAULT_SCALE, H + topk, "random H=%d topk=%d" % (H, topk))
+
+
+@pytest.mark.parametrize("H,chunk", [(16, None), (128, None), (64, 24)])
+def test_backward_fp8_pool(H, chunk):
+    """A pool of fp8 codes (every code value but NaN: both signs, subnormals, the largest) with a dequant scale:
+    the GPU decodes it to bf16 code values and folds the scale into the logits, dP and dq; checked against the
+    oracle on the decoded values, in one pass and in several."""
+    q, _, idx, s = random_case(31 + H, T=48, H=H, topk=96, num_kv=300)
+    rng = np.random.default_rng(32 + H)
+    codes = rng.integers(0, 256, (300, 512)).astype(np.uint8)
+    codes = np.where((codes & 0x7F) == 0x7F, 0x30, codes)
+    full_case(q, codes, idx, s, synth.DEFAULT_SCALE, 33 + H, "fp8 H=%d" % H, chunk_tokens=chunk, kv_scale=0.03)
 
 
 def test_backward_multi_segment_row():
