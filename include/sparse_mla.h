@@ -222,13 +222,14 @@ int sparse_mla_prefill_i64(const void* q, const void* kv, const int64_t* topk_in
  * pass for T=4096, H=128, topk=512 at 3.4 GB; four for topk=1024 at T=8192);
  * with more than one pass, dkv is summed in an fp32 accumulator of
  * num_kv * 2 KiB and rounded to bf16 at the end (otherwise each row is rounded
- * once from its fp32 sum directly). Scratch in all: the pass buffers, the sort's workspace, 4 T H +
+ * once from its fp32 sum directly). Scratch in all: the pass buffers, the sort's counts, 4 T H +
  * 4 (num_kv + 1) bytes and that accumulator, stream-ordered from the library's
  * per-device pool (the forward's split path uses the same pool, which keeps at
  * most 4.5 GiB between calls) and returned before the call's work ends;
  * SMLA_ERR_NO_MEMORY if it cannot be had, before any launch. The inverted
- * index is a library radix sort that clears its counters with hipMemsetAsync:
- * do not capture this call into a HIP graph.
+ * index is a stable radix sort of the library's own that sets no memory, so
+ * the call can be captured into a HIP graph (its scratch then becomes the
+ * graph's allocation nodes).
  */
 int sparse_mla_backward(const void* q, const void* kv, const void* dout, const void* o, const float* lse,
                         const int32_t* topk_indices, const float* attn_sink, float scale, void* dq, void* dkv,

@@ -20,7 +20,7 @@
 //   B2 smla_bwd_interm_kernel  one workgroup per token: the per-slot dkv
 //      contribution interm[t][j] = [scale dS ; P]^T [q ; dO], one MFMA
 //      contraction over heads (both terms side by side along K).
-//   B3 a stable radix sort of (row key, entry id) (rocPRIM) and the start of
+//   B3 a stable radix sort of (row key, entry id) and the start of
 //      each row's run: the scatter inverted, so each row gathers its own
 //      contributors in a fixed order (deterministic, no atomics).
 //   B4 smla_bwd_dkv_chunk_kernel / smla_bwd_dkv_fix_kernel: fixed 64-entry
@@ -29,7 +29,6 @@
 //      per-chunk partials in chunk order; rows nobody references get 0.
 //   B5 smla_bwd_dsink_kernel   fixed-order sum of the sink partials.
 
-#include <rocprim/device/device_radix_sort.hpp>
 
 #include "smla_common.h"
 
@@ -432,6 +431,134 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   }
 }
 
+// ---- B3: stable LSD radix sort of (row key, entry id), 8-bit digits ----
+// Each pass is a stable counting sort on one digit of the key: blocks of
+// kSortBlock pairs count their digits (count), one workgroup per digit turns
+// that digit's block counts into exclusive offsets and a total (scan), and each block
+// places its pairs in order (scatter): within a chunk of 256 pairs, the lanes
+// of a wave holding the same digit are found with one ballot per digit bit,
+// ranked by lane, and offset by the same digit's count in the lower waves of
+// the chunk and in the block's earlier chunks. Every rank is a count, never
+// the order of an atomic, so the result is the same on every call. No memory
+// is set beforehand: each pass writes every count it reads.
+constexpr int kSortItems = 16;                 // chunks of 256 pairs per block
+constexpr int kSortBlock = 256 * kSortItems;   // pairs per block
+
+__global__ __launch_bounds__(256) void smla_sort_count_kernel(const uint32_t* __restrict__ keys, uint32_t n,
+                                                              int shift, uint32_t* __restrict__ counts) {
+  __shared__ uint32_t hist[256];
+  hist[threadIdx.x] = 0;
+  __syncthreads();
+  const uint32_t base = blockIdx.x * (uint32_t)kSortBlock;
+#pragma unroll 4
+  for (int i = 0; i < kSortItems; ++i) {
+    const uint32_t e = base + i * 256 + threadIdx.x;
+    if (e < n) atomicAdd(&hist[(keys[e] >> shift) & 255u], 1u);
+  }
+  __syncthreads();
+  counts[threadIdx.x * gridDim.x + blockIdx.x] = hist[threadIdx.x];
+}
+
+// Exclusive prefix sum over the blocks of one digit's counts (counts[d nb ..
+// d nb + nb), one workgroup per digit d), in tiles of 1024 (four per thread,
+// contiguous); the digit's total goes to totals[d].
+__global__ __launch_bounds__(256) void smla_sort_scan_kernel(uint32_t* __restrict__ counts, uint32_t nb,
+                                                             uint32_t* __restrict__ totals) {
+  __shared__ uint32_t part[256];
+  uint32_t* c = counts + (size_t)blockIdx.x * nb;
+  uint32_t carry = 0;
+  for (uint32_t t0 = 0; t0 < nb; t0 += 1024) {
+    uint32_t v[4], sum = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t i = t0 + 4 * threadIdx.x + k;
+      v[k] = i < nb ? c[i] : 0u;
+      sum += v[k];
+    }
+    part[threadIdx.x] = sum;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const uint32_t x = threadIdx.x >= (uint32_t)off ? part[threadIdx.x - off] : 0u;
+      __syncthreads();
+      part[threadIdx.x] += x;
+      __syncthreads();
+    }
+    uint32_t run = carry + (threadIdx.x ? part[threadIdx.x - 1] : 0u);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t i = t0 + 4 * threadIdx.x + k;
+      if (i < nb) c[i] = run;
+      run += v[k];
+    }
+    carry += part[255];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) totals[blockIdx.x] = carry;
+}
+
+__global__ __launch_bounds__(256) void smla_sort_scatter_kernel(const uint32_t* __restrict__ kin,
+                                                                const uint32_t* __restrict__ vin,
+                                                                uint32_t* __restrict__ kout, uint32_t* __restrict__ vout,
+                                                                uint32_t n, int shift,
+                                                                const uint32_t* __restrict__ offs,
+                                                                const uint32_t* __restrict__ totals) {
+  __shared__ uint32_t run[256];      // per digit: where this block's next pair of that digit goes
+  __shared__ uint32_t wcnt[4][256];  // per wave and digit: pairs of that digit in the current chunk
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // the digit's start: the totals of the lower digits (an exclusive scan of 256 in LDS)
+  run[threadIdx.x] = totals[threadIdx.x];
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const uint32_t x = threadIdx.x >= (uint32_t)off ? run[threadIdx.x - off] : 0u;
+    __syncthreads();
+    run[threadIdx.x] += x;
+    __syncthreads();
+  }
+  const uint32_t start = run[threadIdx.x] - totals[threadIdx.x];
+  __syncthreads();
+  run[threadIdx.x] = start + offs[threadIdx.x * gridDim.x + blockIdx.x];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) wcnt[k][threadIdx.x] = 0u;
+  __syncthreads();
+  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;  // lanes lower than this one
+  const uint32_t base = blockIdx.x * (uint32_t)kSortBlock;
+  uint32_t keys[kSortItems], vals[kSortItems];  // all of this thread's pairs first: one load latency per block
+#pragma unroll
+  for (int i = 0; i < kSortItems; ++i) {
+    const uint32_t e = base + i * 256 + threadIdx.x;
+    keys[i] = e < n ? kin[e] : 0u;
+    vals[i] = e < n ? vin[e] : 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < kSortItems; ++i) {
+    const uint32_t e = base + i * 256 + threadIdx.x;
+    const bool act = e < n;
+    const uint32_t key = keys[i];
+    const uint32_t val = vals[i];
+    const uint32_t d = (key >> shift) & 255u;
+    uint64_t peers = __ballot(act);  // active lanes of this wave with the same digit
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const uint64_t ones = __ballot((d >> bit) & 1u);
+      peers &= ((d >> bit) & 1u) ? ones : ~ones;
+    }
+    const uint32_t rank = (uint32_t)__popcll(peers & below);
+    if (act && rank == 0) wcnt[w][d] = (uint32_t)__popcll(peers);
+    __syncthreads();
+    if (act) {
+      uint32_t pos = run[d] + rank;
+      for (int k = 0; k < w; ++k) pos += wcnt[k][d];
+      kout[pos] = key;
+      vout[pos] = val;
+    }
+    __syncthreads();
+    run[threadIdx.x] += wcnt[0][threadIdx.x] + wcnt[1][threadIdx.x] + wcnt[2][threadIdx.x] + wcnt[3][threadIdx.x];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) wcnt[k][threadIdx.x] = 0u;
+    __syncthreads();
+  }
+}
+
 // ---- B3: start of each row's run in the sorted keys (lower bound) ----
 __global__ __launch_bounds__(256) void smla_bwd_rowstart_kernel(const uint32_t* __restrict__ skey, uint32_t n,
                                                                 uint32_t nrows, uint32_t* __restrict__ row_start) {
@@ -593,15 +720,30 @@ int bwd_nw(int64_t H) { return H <= 16 ? 1 : (H <= 32 ? 2 : 4); }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// The library's radix sort with its onesweep form for every size past one
-// block: by default it merge-sorts up to 2^20 pairs, which measured 2.7x
-// slower per pair than onesweep on the pass sizes used here (wide, two passes
-// of 2^20 pairs each: 287 vs 107 us per call).
-using SortConfig = rocprim::radix_sort_config<rocprim::default_config, rocprim::default_config,
-                                              rocprim::default_config, 4096>;
-hipError_t sort_pairs(void* tmp, size_t& bytes, const uint32_t* kin, uint32_t* kout, const uint32_t* vin,
-                      uint32_t* vout, int n, int end_bit, hipStream_t s) {
-  return rocprim::radix_sort_pairs<SortConfig>(tmp, bytes, kin, kout, vin, vout, n, 0u, (unsigned)end_bit, s);
+// Count buffer of the radix sort for n pairs: 256 digits per block, then the 256 digit totals.
+size_t sort_count_bytes(int64_t n) { return (size_t)256 * (size_t)((n + kSortBlock - 1) / kSortBlock + 1) * 4; }
+
+// Sort n (key, value) pairs by the low end_bit bits of the key, stably: the
+// pairs move between (k0, v0) and (k1, v1) once per 8-bit digit; the sorted
+// pairs end in (k0, v0) after an even number of passes, else in (k1, v1)
+// (*in_first says which).
+hipError_t sort_pairs(uint32_t* k0, uint32_t* v0, uint32_t* k1, uint32_t* v1, uint32_t* counts, int64_t n,
+                      int end_bit, hipStream_t s, bool* in_first) {
+  const unsigned nb = (unsigned)((n + kSortBlock - 1) / kSortBlock);
+  bool first = true;
+  for (int shift = 0; shift < end_bit && n > 0; shift += 8) {
+    const uint32_t* kin = first ? k0 : k1;
+    const uint32_t* vin = first ? v0 : v1;
+    uint32_t* kout = first ? k1 : k0;
+    uint32_t* vout = first ? v1 : v0;
+    hipLaunchKernelGGL(smla_sort_count_kernel, dim3(nb), dim3(256), 0, s, kin, (uint32_t)n, shift, counts);
+    hipLaunchKernelGGL(smla_sort_scan_kernel, dim3(256), dim3(256), 0, s, counts, nb, counts + (size_t)256 * nb);
+    hipLaunchKernelGGL(smla_sort_scatter_kernel, dim3(nb), dim3(256), 0, s, kin, vin, kout, vout, (uint32_t)n, shift,
+                       (const uint32_t*)counts, (const uint32_t*)(counts + (size_t)256 * nb));
+    first = !first;
+  }
+  *in_first = first;
+  return hipGetLastError();
 }
 
 // Scratch of one token pass, at most (unless one token alone needs more): the
@@ -676,11 +818,7 @@ int run_backward(const void* q, const void* kv, const void* dout, const void* o,
   while (end_bit < 32 && ((uint64_t)1 << end_bit) <= (uint64_t)nkv) ++end_bit;
 
   // scratch layout: one pass's buffers, then what lives across passes
-  size_t sort_bytes = 0;
-  {
-    const hipError_t e = sort_pairs(nullptr, sort_bytes, nullptr, nullptr, nullptr, nullptr, (int)Nc, end_bit, s);
-    if (e != hipSuccess) return SMLA_ERR_LAUNCH;
-  }
+  const size_t sort_bytes = sort_count_bytes(Nc);
   const size_t A = 256;
   size_t off = 0;
   const size_t o_p = off;      off = align_up(off + (size_t)C * H * TP * 2, A);
@@ -774,17 +912,21 @@ int run_backward(const void* q, const void* kv, const void* dout, const void* o,
       }
       err = hipGetLastError();
     }
+    uint32_t* skey = bp.ckey;  // where the sorted pairs end
+    uint32_t* sval = bp.cval;
     if (err == hipSuccess && num_kv > 0) {
-      size_t tb = sort_bytes;
-      err = sort_pairs((void*)(b + o_tmp), tb, bp.ckey, (uint32_t*)(b + o_sk), bp.cval, (uint32_t*)(b + o_sv),
-                       (int)Nt, end_bit, s);
+      bool in_first = true;
+      err = sort_pairs(bp.ckey, bp.cval, (uint32_t*)(b + o_sk), (uint32_t*)(b + o_sv), (uint32_t*)(b + o_tmp), Nt,
+                       end_bit, s, &in_first);
+      skey = in_first ? bp.ckey : (uint32_t*)(b + o_sk);
+      sval = in_first ? bp.cval : (uint32_t*)(b + o_sv);
     }
     if (err == hipSuccess && num_kv > 0) {
       const size_t nch_t = (size_t)(Nt + kChunk - 1) / kChunk;
       hipLaunchKernelGGL(smla_bwd_rowstart_kernel, dim3((unsigned)((num_kv + 1 + 255) / 256)), dim3(256), 0, s,
-                         (const uint32_t*)(b + o_sk), (uint32_t)Nt, (uint32_t)num_kv, (uint32_t*)(b + o_rs));
+                         (const uint32_t*)skey, (uint32_t)Nt, (uint32_t)num_kv, (uint32_t*)(b + o_rs));
       hipLaunchKernelGGL(smla_bwd_dkv_chunk_kernel, dim3((unsigned)((nch_t + 3) / 4)), dim3(256), 0, s,
-                         (const uint32_t*)(b + o_sk), (const uint32_t*)(b + o_sv), (const uint32_t*)(b + o_rs),
+                         (const uint32_t*)skey, (const uint32_t*)sval, (const uint32_t*)(b + o_rs),
                          (const uint16_t*)(b + o_it), (uint16_t*)dkv, acc, (float*)(b + o_hd), (float*)(b + o_tl),
                          (uint32_t)num_kv);
       hipLaunchKernelGGL(smla_bwd_dkv_fix_kernel, dim3((unsigned)((num_kv + 3) / 4)), dim3(256), 0, s,

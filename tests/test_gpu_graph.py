@@ -1,13 +1,14 @@
-"""HIP-graph capture of the forward, through the C ABI.
+"""HIP-graph capture of the forward and the backward.
 
-A serving loop captures the forward once and replays it. Every path a
+A serving or training loop captures the call once and replays it. Every forward path a
 capture can take is a plain kernel launch on the given stream: the single
 pass (16-row H <= 16 kernel, persistent 128-head kernel) and, for
 decode-sized calls, the split path of the entry point that allocates nothing
 (its partials in the library's static array, no memory set: every partial a
-call reads is written by the same call). Each graph is replayed several times
-with the program's own eager work and synchronisations in between (outputs
-poisoned, eager calls of the same entry point on other buffers), and every
+call reads is written by the same call). The backward takes stream-ordered
+scratch (allocation nodes in the graph) and sets no memory. Each graph is
+replayed several times with the program's own eager work and synchronisations
+in between (outputs poisoned, eager calls of the same entry point), and every
 replay must give the eager result bit for bit."""
 
 import numpy as np
@@ -95,3 +96,46 @@ def test_graph_replays_match_eager(case):
         assert np.array_equal(lse.cpu().numpy().view(np.uint32), l_ref.view(np.uint32)), \
             "%s: replay %d lse differs from the eager call" % (case, r)
         assert np.array_equal(bf16_bits(out_x), o_ref), "%s: eager call between replays differs" % case
+
+
+@pytest.mark.parametrize("case,chunk", [("wide", None), ("tp4", 100)])
+def test_backward_graph_replays_match_eager(case, chunk):
+    """The backward captured into a HIP graph: its scratch is stream-ordered (allocation nodes in the graph) and
+    its sort sets no memory, so each replay, with poisoned outputs and an eager backward in between, gives the
+    eager gradients bit for bit; tp4 in passes of 100 tokens (the fp32 dkv accumulator path)."""
+    from sparse_attention_top_amd import sparse_mla_backward, sparse_mla_prefill
+
+    inp = synth.make_inputs(case, T=256 if case == "wide" else 300)
+    q = to_dev_bf16(inp["q"])
+    kv = to_dev_bf16(inp["kv"])
+    tk = torch.from_numpy(np.ascontiguousarray(inp["topk"], dtype=np.int32)).to(DEV)
+    sk = torch.from_numpy(np.ascontiguousarray(inp["sink"])).to(DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5)
+    dout = torch.randn(q.shape, generator=g, device=DEV, dtype=torch.float32).to(torch.bfloat16)
+    o, lse = sparse_mla_prefill(q, kv, tk, sk, inp["scale"])
+    ref = [x.clone() for x in sparse_mla_backward(q, kv, dout, o, lse, tk, sk, inp["scale"], chunk_tokens=chunk)]
+    torch.cuda.synchronize()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sparse_mla_backward(q, kv, dout, o, lse, tk, sk, inp["scale"], chunk_tokens=chunk)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = sparse_mla_backward(q, kv, dout, o, lse, tk, sk, inp["scale"], chunk_tokens=chunk)
+    torch.cuda.synchronize()
+    for r in range(3):
+        for x in outs:
+            x.fill_(float("nan"))
+        eager = sparse_mla_backward(q, kv, dout, o, lse, tk, sk, inp["scale"], chunk_tokens=chunk)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, a, b, e in zip(("dq", "dkv", "d_sink"), outs, ref, eager):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)), \
+                "%s replay %d: %s differs from the eager call" % (case, r, name)
+            assert torch.equal(e, b), "%s: eager call between replays differs (%s)" % (case, name)
