@@ -418,6 +418,9 @@ def main():
                     help="skip the clock sampling window (keeps the launch count fixed for profiling)")
     ap.add_argument("--bwd", action="store_true",
                     help="only time the backward on --workload and print its line (for profiling)")
+    ap.add_argument("--fp8-pool-decode", default="auto", choices=["never", "auto", "always"],
+                    help="how fp8 pools are read: by the fp8 kernels (never), decoded once per call into a bf16 "
+                         "copy for the bf16 kernels (always), or as the library chooses (auto, the default)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -427,6 +430,11 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.fp8_pool_decode != "auto":
+        from sparse_attention_top_amd import set_fp8_pool_decode
+
+        set_fp8_pool_decode(args.fp8_pool_decode)
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
