@@ -282,11 +282,13 @@ int sparse_mla_backward_fp8(const void* q, const void* kv, float kv_scale, const
 const char* sparse_mla_status_string(int status);
 
 /*
- * Name of the kernel that sparse_mla_prefill (kv_fp8 == 0) or
- * sparse_mla_prefill_fp8 (kv_fp8 != 0) launches for H heads and top-k rows of
- * `topk` entries when the call is not split over the top-k row (static
- * storage, as it appears in profiler traces), or NULL when H < 1 or topk < 0.
- * Pure host function: no device access.
+ * Name of the kernel that sparse_mla_prefill (kv_fp8 == 0) launches for H
+ * heads and top-k rows of `topk` entries when the call is not split over the
+ * top-k row, or (kv_fp8 != 0) the kernel that reads an fp8 pool's codes
+ * directly; an fp8 call that decodes its pool (sparse_mla_fp8_pool_decoded)
+ * launches the kv_fp8 == 0 kernel after the decoding. Static storage, as the
+ * name appears in profiler traces; NULL when H < 1 or topk < 0. Pure host
+ * function: no device access.
  */
 const char* sparse_mla_kernel_name(int64_t H, int64_t topk, int kv_fp8);
 
