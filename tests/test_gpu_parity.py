@@ -151,6 +151,21 @@ def test_h128_rows_over_several_segments():
     compare(o, lse, oracle_ref(inp, tokens=tok), tokens=tok, what="H=128 topk=1500")
 
 
+@pytest.mark.parametrize("topk,p_invalid", [(1023, 0.0), (1024, 0.0), (1025, 0.0), (1025, 0.3)])
+def test_h128_kernel_switch_at_list_capacity(topk, p_invalid):
+    """The persistent 128-head kernel compacts a whole top-k row into one 1024-entry list; a longer row goes to the
+    D-split kernel (two 64-head groups, 1024-entry segments). Rows one short of, at and one past that capacity with
+    every slot valid, and one past it with 30% of the slots invalid (fewer valid slots than the capacity: the kernel
+    is chosen by the row length, so still the D-split one). 300 tokens keep the single pass; sampled tokens."""
+    from sparse_attention_top_amd import kernel_name
+
+    assert kernel_name(128, topk) == ("smla_fwd128_kernel" if topk <= 1024 else "smla_fwd_kernel<4, 2>")
+    inp = make_random(2800 + topk + int(10 * p_invalid), T=300, H=128, num_kv=3000, topk=topk, p_invalid=p_invalid)
+    o, lse = run_case(inp)
+    tok = np.arange(0, 300, 13)
+    compare(o, lse, oracle_ref(inp, tokens=tok), tokens=tok, what="H=128 topk=%d p_invalid=%.1f" % (topk, p_invalid))
+
+
 @pytest.mark.parametrize("topk,num_kv", [(1, 50), (31, 40), (33, 100), (2048, 3000), (2500, 4000), (4500, 6000)])
 def test_topk_extremes(topk, num_kv):
     """Single slots, tile-boundary counts and rows longer than one compaction segment."""
