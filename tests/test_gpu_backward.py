@@ -117,6 +117,15 @@ def test_backward_random(H, topk, sink, dup):
     full_case(q, kv, idx, s, synth.DEFAULT_SCALE, H + topk, "random H=%d topk=%d" % (H, topk))
 
 
+@pytest.mark.parametrize("H,topk", [(17, 50), (32, 64), (33, 48), (65, 40), (127, 36)])
+def test_backward_head_count_edges(H, topk):
+    """The dq phase runs 1, 2 or 4 waves of 16 heads (H <= 16, <= 32, above) and more than 64 heads as two
+    groups; the interm contraction pads H to a multiple of 16. One head past each step (17, 33, 65: a wave or a
+    group holding a single real head), 32 exactly, and 127 (the last group one head short)."""
+    q, kv, idx, s = random_case(H * 11 + topk, T=40, H=H, topk=topk, num_kv=300, sink=True, dup=False)
+    full_case(q, kv, idx, s, synth.DEFAULT_SCALE, 3 * H + topk, "edge H=%d topk=%d" % (H, topk))
+
+
 @pytest.mark.parametrize("H,chunk", [(16, None), (128, None), (64, 24)])
 def test_backward_fp8_pool(H, chunk):
     """A pool of fp8 codes (every code value but NaN: both signs, subnormals, the largest) with a dequant scale:
