@@ -7,7 +7,9 @@
 // o and a sink-inclusive natural-log lse. The C ABI is in
 // include/sparse_mla.h.
 //
-// Kernel structure (one workgroup per token and group of heads):
+// Kernel structure (a workgroup works on one token and group of heads at a
+// time: one such unit per workgroup, or, in the persistent 128-head kernel,
+// units dealt to each workgroup in an XCD-aware order):
 //   1. the token's top-k row is read and its valid slots (0 <= idx < num_kv,
 //      one unsigned compare) are compacted into an LDS list -- invalid slots
 //      are never dereferenced, so NaN/Inf in unused pool rows cannot reach
@@ -25,7 +27,8 @@
 //      normalisation uses the same reference;
 //   5. O^T += V^T P^T on bf16 MFMA, V read from the same LDS tile with the
 //      gfx950 transposing LDS load, P rounded to bf16 (at four waves each wave
-//      accumulates its 128 columns of d for all 64 heads from the P tiles the
+//      accumulates its 128 columns of d for all of the workgroup's heads, 64
+//      in the D-split kernel and 128 in the 128-head one, from the P tiles the
 //      waves publish in LDS);
 //   6. the sink is folded into the max and the denominator at the end, o is
 //      rounded to bf16 and lse converted back to natural log.
@@ -657,8 +660,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 }
 
 // ---------------------------------------------------------------------------
-// H > 64, bf16 pool, single pass: one four-wave workgroup per (token, group of
-// 128 heads), one workgroup per CU (one wave per SIMD, up to 512 registers).
+// H > 64, bf16 pool, single pass: four-wave workgroups, one per CU (one wave
+// per SIMD, up to 512 registers), each working on one (token, group of 128
+// heads) unit at a time and walking its share of the units (Sched128).
 //
 // Each wave owns 32 heads for S (Q^T of 32 heads in 128 VGPRs), so one K
 // fragment read from LDS feeds two MFMAs; P of every head goes through LDS and
@@ -1415,7 +1419,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // 32-row ring of two tiles takes 74 KiB, so only two one-wave workgroups fit
 // a CU and two of its four SIMDs hold a wave; with 16-row tiles the ring of
 // NBUF tiles and a list of CAP entries take 38 KiB (NBUF 2, CAP 1024: four
-// per CU, one wave per SIMD) or 19 KiB (NBUF 1, CAP 512: eight per CU, two
+// per CU, one wave per SIMD) or 19 KiB (NBUF 1, CAP 640: eight per CU, two
 // waves per SIMD). S^T is one 16-row half of the 32-row form; P.V uses the
 // 16x16x16 MFMA, whose A operand is one transposing read and whose B operand
 // is the four P values the S^T accumulator layout leaves in each lane.
@@ -1843,9 +1847,9 @@ struct Variant {
 // stalled the wave: 512 entries were 0.8% slower there).
 constexpr int kR16Nbuf = 1;
 constexpr int kR16Cap = 640;
-// The one-workgroup-per-token kernel for more than 64 heads (smla_fwd128_kernel)
-// is not yet faster than two 64-head workgroups per token of the D-split
-// kernel, so the latter is dispatched.
+// More than 64 heads over a bf16 pool run on the persistent 128-head kernel
+// (smla_fwd128_kernel) whenever the top-k row fits its 1024-entry list; longer
+// rows take two 64-head workgroups per token of the D-split kernel.
 constexpr bool kFwd128 = true;
 
 Variant pick_variant(int64_t H, int64_t topk, bool fp8) {

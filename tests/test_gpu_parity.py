@@ -502,7 +502,8 @@ def make_random_fp8(seed, T, H, num_kv, topk, p_invalid=0.15, sink=True, kv_scal
 
 
 @pytest.mark.parametrize("T,H,topk,num_kv", [(20, 16, 300, 900), (16, 128, 200, 600), (3, 16, 1024, 3000),
-                                             (2, 128, 777, 2000), (9, 40, 96, 300)])
+                                             (2, 128, 777, 2000), (9, 40, 96, 300), (12, 24, 150, 500),
+                                             (7, 65, 96, 400)])
 def test_fp8_pool_random(T, H, topk, num_kv, fp8_path):
     """Random rows and every code value (subnormals, both signs, the largest); few-token shapes
     take the split path."""
