@@ -401,6 +401,36 @@ __device__ __forceinline__ float row4_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// ---- 16-row tiles (one wave of up to 16 heads) ----
+constexpr int kBK16 = 16;  // rows per 16-row tile
+
+__device__ __forceinline__ void mfma16_acc(f32x4& c, const u32x2& a, const u32x2& b) {
+  asm volatile("v_mfma_f32_16x16x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
+// O^T += V^T P^T for a 16-row tile: per d-tile one transposing read gives
+// lane (g, li) V[4g .. 4g+3][16 dt + li], the A operand of the 16x16x16 MFMA.
+__device__ __forceinline__ void tile_pv16(uint32_t vrow, const bf16x4& pk, f32x4 (&acc)[32]) {
+  asm volatile("s_nop 4" ::: "memory");  // P written by VALU, read by MFMA below
+  constexpr int VPF = 6;
+  constexpr int VST = VPF + 1;
+  const u32x2 pb = __builtin_bit_cast(u32x2, pk);
+  u32x2 vf[VST];
+  auto vread = [&](auto dc) {
+    constexpr int dt = decltype(dc)::value;
+    vf[dt % VST] = ds_read_tr16_b64<32 * dt>(vrow);
+  };
+  static_for<0, VPF>([&](auto dc) { vread(dc); });
+  static_for<0, 32>([&](auto dc) {
+    constexpr int dt = decltype(dc)::value;
+    if constexpr (dt + VPF < 32) vread(Int<dt + VPF>{});
+    constexpr int younger = 31 - dt < VPF ? 31 - dt : VPF;
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(vf[dt % VST]) : "n"(younger));
+    mfma16_acc(acc[dt], vf[dt % VST], pb);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
 // ---- per-tile compute of one wave (16 heads x 32 slots) ----
 // Lane (g, li) owns head li of the wave's 16; LDS addresses are those of the
 // tile's buffer.

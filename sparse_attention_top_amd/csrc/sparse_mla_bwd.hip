@@ -130,6 +130,32 @@ __device__ __forceinline__ void tile_sdp(uint32_t krow, const bf16x8 (&qf)[16], 
   }
 }
 
+// Per token, lane (g, li) of a wave: the q and dO fragments of its head,
+// delta = rowsum(o . dO) of that head, its lse in log2 units, and the sink
+// partial exp(sink - lse) delta (zero fragments and no partial past H).
+__device__ __forceinline__ void dq_setup(const BwdParams& p, int t, int head, int g, bf16x8 (&qf)[16],
+                                         bf16x8 (&df)[16], float& delta, float& lse_l2) {
+  const bool hv = head < p.H;
+  load_frag(qf, p.q, t, p.H, head, g);
+  load_frag(df, p.dout, t, p.H, head, g);
+  {
+    bf16x8 of[16];
+    load_frag(of, p.o, t, p.H, head, g);
+    float part = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part += (float)of[k][e] * (float)df[k][e];
+    delta = row4_sum(part);  // the four 16-lane groups hold the four quarters of d
+  }
+  const float lse_v = hv ? p.lse[(size_t)t * p.H + head] : 0.f;
+  lse_l2 = lse_v * kLog2e;
+  if (p.sink != nullptr && hv && g == 0) {
+    const float sk = p.sink[head];
+    p.dsink_part[(size_t)t * p.H + head] = (sk == -INFINITY) ? 0.f : __expf(sk - lse_v) * delta;
+  }
+}
+
 // ---- B1: dq, P, scale dS, compacted row keys, sink partials ----
 template <int NW, int NBUF>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) void smla_bwd_dq_kernel(
@@ -149,25 +175,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
   const bool hv = head < p.H;
 
   bf16x8 qf[16], df[16];
-  load_frag(qf, p.q, t, p.H, head, g);
-  load_frag(df, p.dout, t, p.H, head, g);
-  float delta;
-  {
-    bf16x8 of[16];
-    load_frag(of, p.o, t, p.H, head, g);
-    float part = 0.f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) part += (float)of[k][e] * (float)df[k][e];
-    delta = row4_sum(part);  // the four 16-lane groups hold the four quarters of d
-  }
-  const float lse_v = hv ? p.lse[(size_t)t * p.H + head] : 0.f;
-  const float lse_l2 = lse_v * kLog2e;
-  if (p.sink != nullptr && hv && g == 0) {
-    const float sk = p.sink[head];
-    p.dsink_part[(size_t)t * p.H + head] = (sk == -INFINITY) ? 0.f : __expf(sk - lse_v) * delta;
-  }
+  float delta, lse_l2;
+  dq_setup(p, t, head, g, qf, df, delta, lse_l2);
 
   f32x4 acc[32];
 #pragma unroll
@@ -259,6 +268,156 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
     const int hr = head_base + r;
     const u32x4 val = *(LDS_AS const u32x4*)(uintptr_t)(ob + r * kRowStride + 16 * lane);
     if (hr < p.H) *(u32x4*)(p.dq + ((size_t)t * p.H + hr) * kD + 8 * lane) = val;
+  }
+}
+
+// ---- B1 at H <= 16: 16-row tiles ----
+// The same phase for one wave of up to 16 heads on 16-row tiles. A ring of two
+// and 640-entry compaction segments take 36 KiB of LDS, so four workgroups
+// share a CU, one wave on each SIMD, where the 32-row ring's 76 KiB leaves two
+// of the four SIMDs idle (the registers allow one wave per SIMD either way).
+// The next tile is gathered at the top of each iteration, under this tile's S,
+// dP, stores and P.V. 640 is a multiple of 32, so segments still start on
+// multiples of 32 positions and P, scale dS, the row keys and the position
+// counts keep the layout the later phases read; a segment's positions are
+// padded to its multiple of 32 with an all-invalid tile where needed.
+constexpr int kBwd16Cap = 640;
+static_assert(kBwd16Cap % kBK == 0, "segments start on multiples of 32 positions");
+
+template <int CAP>
+struct BwdSmem16 {
+  static constexpr int kTileBytes = kBK16 * kRowStride;
+  uint8_t area[2 * kTileBytes];  // ring of two tiles; the first 16 rows stage dq at the end
+  int32_t list[CAP];
+  __device__ __forceinline__ uint32_t tile(int b) { return lds_addr(area + b * kTileBytes); }
+  __device__ __forceinline__ uint32_t stage() { return lds_addr(area); }
+};
+
+// S^T = K Q^T and dP^T = K dO^T for a 16-row tile from one read of each K
+// fragment: s and dp hold S^T and dP^T[slot 4g + i][head li]; four MFMA chains
+// (each product split by k parity).
+template <int KPF>
+__device__ __forceinline__ void tile_sdp16(uint32_t krow, const bf16x8 (&qf)[16], const bf16x8 (&df)[16], f32x4& s,
+                                           f32x4& dp) {
+  constexpr int KST = KPF + 1;
+  f32x4 a[2][2];  // [S or dP][k parity]
+  u32x4 kf[KST];
+  auto kread = [&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    kf[k % KST] = ds_read_b128<64 * k>(krow);
+  };
+  static_for<0, KPF>([&](auto kc) { kread(kc); });
+  static_for<0, 16>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    if constexpr (k + KPF < 16) kread(Int<k + KPF>{});
+    constexpr int younger = 15 - k < KPF ? 15 - k : KPF;
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(kf[k % KST]) : "n"(younger));
+    if constexpr (k < 2) {
+      mfma_s_first(a[0][k], kf[k % KST], __builtin_bit_cast(u32x4, qf[k]));
+      mfma_s_first(a[1][k], kf[k % KST], __builtin_bit_cast(u32x4, df[k]));
+    } else {
+      mfma_s(a[0][k & 1], kf[k % KST], __builtin_bit_cast(u32x4, qf[k]));
+      mfma_s(a[1][k & 1], kf[k % KST], __builtin_bit_cast(u32x4, df[k]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");  // MFMA write -> VALU read distance
+  asm volatile("" : "+v"(a[0][0]), "+v"(a[0][1]), "+v"(a[1][0]), "+v"(a[1][1]));
+  s = a[0][0] + a[0][1];
+  dp = a[1][0] + a[1][1];
+}
+
+template <int CAP>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1))) void smla_bwd_dq16_kernel(
+    const BwdParams p) {
+  __shared__ __attribute__((aligned(16))) BwdSmem16<CAP> sm;
+
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const int li = lane & 15;
+  const int t = p.T - 1 - xcd_remap(blockIdx.x, gridDim.x);  // H <= 16: one head group per token
+  const int head = li;
+
+  bf16x8 qf[16], df[16];
+  float delta, lse_l2;
+  dq_setup(p, t, head, g, qf, df, delta, lse_l2);
+
+  f32x4 acc[32];
+#pragma unroll
+  for (int dt = 0; dt < 32; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t* trow = p.topk + (size_t)t * p.topk_n;
+  const size_t prow = ((size_t)t * p.H + head) * p.TP;  // this lane's P / dS row
+  int jbase = 0;  // compacted position of the segment's first entry (a multiple of 32)
+  for (int seg0 = 0; seg0 < p.topk_n; seg0 += CAP) {
+    const int n = compact_segment<1, BwdSmem16<CAP>, CAP>(trow + seg0, min(CAP, p.topk_n - seg0), p.nkv, sm, lane, 0);
+    const int npos = (n + kBK - 1) / kBK * kBK;
+    for (int i = lane; i < npos; i += 64) {
+      const size_t e = (size_t)t * p.TP + jbase + i;
+      p.ckey[e] = i < n ? (uint32_t)sm.list[i] : p.sentinel;
+      p.cval[e] = (uint32_t)e;
+    }
+    const int ntiles = npos / kBK16;  // tiles past n (at most one) are all-invalid: zero P and dS
+    if (ntiles == 0) continue;
+    {
+      TileIssue<1, kBK16> is;
+      is.init(sm.list, 0, n, true, sm.tile(0), p.kv, lane, 0);
+      is.all(lane);
+    }
+    for (int j = 0; j < ntiles; ++j) {
+      const bool next = j + 1 < ntiles;
+      {
+        // tile j + 1 into the slot whose last reader, P.V of tile j - 1, has completed
+        TileIssue<1, kBK16> is;
+        is.init(sm.list, j + 1, n, next, sm.tile((j + 1) & 1), p.kv, lane, 0);
+        is.all(lane);
+      }
+      wait_vmcnt_le(next ? kBK16 : 0);  // tile j landed (only tile j + 1's loads may be younger)
+      const uint32_t tb = sm.tile(j & 1);
+      f32x4 sv, dpv;
+      tile_sdp16<2>(k_frag_addr(tb, g, li), qf, df, sv, dpv);
+      const int cnt = min(kBK16, n - j * kBK16);
+      bf16x4 pk, pst, dst;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int slot = 4 * g + i;
+        const float pr = slot < cnt ? __builtin_amdgcn_exp2f(sv[i] * p.scale_log2 - lse_l2) : 0.f;
+        const float ds = pr * (dpv[i] * p.kv_scale - delta);
+        pk[i] = (__bf16)ds;
+        pst[i] = (__bf16)pr;
+        dst[i] = (__bf16)(ds * p.scale);
+      }
+      if (head < p.H) {
+        const size_t o0 = prow + jbase + j * kBK16 + 4 * g;
+        *(bf16x4*)(p.pbuf + o0) = pst;
+        *(bf16x4*)(p.dsbuf + o0) = dst;
+      }
+      tile_pv16(v_frag_addr(tb, g, li), pk, acc);  // dQ^T += K^T dS^T (V == K)
+    }
+    jbase += npos;
+  }
+  for (int i = jbase + lane; i < p.TP; i += 64) {
+    const size_t e = (size_t)t * p.TP + i;
+    p.ckey[e] = p.sentinel;
+    p.cval[e] = (uint32_t)e;
+  }
+  if (lane == 0) p.ncount[t] = jbase;
+
+  // dq = scale acc, staged through LDS for whole-row stores (no tile load is
+  // in flight: the last tile issued none, and every earlier one was waited for)
+  const uint32_t ob = sm.stage();
+  mfma_agpr_drain(acc);
+#pragma unroll
+  for (int dt = 0; dt < 32; ++dt) {
+    const f32x4 v = acc[dt] * p.dq_scale;
+    const bf16x4 v4 = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+    *(LDS_AS bf16x4*)(uintptr_t)(ob + li * kRowStride + 32 * dt + 8 * g) = v4;
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const u32x4 val = *(LDS_AS const u32x4*)(uintptr_t)(ob + r * kRowStride + 16 * lane);
+    if (r < p.H) *(u32x4*)(p.dq + ((size_t)t * p.H + r) * kD + 8 * lane) = val;
   }
 }
 
@@ -882,7 +1041,7 @@ int run_backward(const void* q, const void* kv, const void* dout, const void* o,
     bp.dq_scale = scale * kv_scale;
 
     const unsigned g1 = (unsigned)(Tc * head_groups);
-    if (nw == 1) hipLaunchKernelGGL((smla_bwd_dq_kernel<1, 2>), dim3(g1), dim3(64), 0, s, bp);
+    if (nw == 1) hipLaunchKernelGGL((smla_bwd_dq16_kernel<kBwd16Cap>), dim3(g1), dim3(64), 0, s, bp);
     else if (nw == 2) hipLaunchKernelGGL((smla_bwd_dq_kernel<2, 2>), dim3(g1), dim3(128), 0, s, bp);
     else hipLaunchKernelGGL((smla_bwd_dq_kernel<4, 2>), dim3(g1), dim3(256), 0, s, bp);
     err = hipGetLastError();

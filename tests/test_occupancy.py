@@ -101,6 +101,16 @@ def test_forward_kernel_occupancy(resources, kernel):
         kernel, r["Occupancy [waves/SIMD]"], waves)
 
 
+def test_backward_dq16_occupancy(resources_bwd):
+    """The backward's dq phase at H <= 16 runs 16-row tiles so that four one-wave workgroups share a CU (two tiles
+    and a 640-entry list of LDS each), one wave on every SIMD."""
+    hits = [v for k, v in resources_bwd.items() if "smla_bwd_dq16_kernelILi640EE" in k]
+    assert hits, "smla_bwd_dq16_kernel<640> not found in the resource report"
+    r = hits[0]
+    assert LDS_PER_CU // r["LDS Size [bytes/block]"] >= 4, r["LDS Size [bytes/block]"]
+    assert r["Occupancy [waves/SIMD]"] >= 1
+
+
 def _own(res):
     """The library's own kernels (library templates it instantiates are not checked)."""
     return {k: v for k, v in res.items() if "smla_" in k}
