@@ -16,7 +16,8 @@
 //      fragment feeds the S and dP MFMAs; P and dS in fp32; dQ^T += K^T dS^T
 //      from the same tile; writes dq, P and scale dS (bf16, [T][H][TP], TP =
 //      top-k rounded up to 32, compacted positions), the row key and entry id
-//      of every compacted position, and the sink partials.
+//      of every compacted position, and the sink partials. At H <= 16,
+//      smla_bwd_dq16_kernel: the same on 16-row tiles, four workgroups per CU.
 //   B2 smla_bwd_interm_kernel  one workgroup per token: the per-slot dkv
 //      contribution interm[t][j] = [scale dS ; P]^T [q ; dO], one MFMA
 //      contraction over heads (both terms side by side along K).
